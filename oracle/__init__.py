@@ -1,0 +1,217 @@
+"""Reference oracle for the CacheTune hot path -- TEST INFRASTRUCTURE ONLY.
+
+A ctypes wrapper over ``oracle.c`` (plain fp64 C, direct DFT, sort-based
+top-r, scalar RoPE, fp64 softmax attention).  Only the test-suite, the smoke
+entry and the bench's CPU-baseline leg may import this package; the product
+library never loads it and shares no code with it.
+
+Storage convention shared with the product boundary: bf16 tensors are numpy
+``uint16`` arrays of raw bit patterns, fp32 tensors are ``float32`` arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+SRC_PATH = os.path.join(HERE, "oracle.c")
+
+F32, BF16 = 0, 1
+FFT_EXACT_N, FFT_ZEROPAD_POW2 = 0, 1
+NORM_SUM, NORM_MAX, NORM_MINMAX, NORM_NONE = 0, 1, 2, 3
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no GPU code involved)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fopenmp", "-fPIC", "-shared",
+           SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            build()
+        L = C.CDLL(LIB_PATH)
+        i32, f64, vp = C.c_int, C.c_double, C.c_void_p
+        L.orc_nbins.argtypes = [i32]
+        L.orc_kkeep.argtypes = [i32, i32, i32]
+        L.orc_ksel.argtypes = [i32, i32, i32]
+        L.orc_fft_len.argtypes = [i32, i32]
+        L.orc_round_bf16.argtypes = [f64]
+        L.orc_round_bf16.restype = C.c_uint16
+        L.orc_rfft.argtypes = [vp, i32, vp, vp]
+        L.orc_lowpass.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.orc_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+        L.orc_topr.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.orc_offsets.argtypes = [vp, vp, i32, i32, vp]
+        L.orc_rope_freqs.argtypes = [i32, f64, vp]
+        L.orc_rope.argtypes = [vp, i32, f64, f64, i32, vp]
+        L.orc_assemble_chunk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, i32, vp, vp]
+        L.orc_assemble_rows.argtypes = [vp, vp, i32, i32, i32, i32, i32, f64, i32, vp, vp]
+        L.orc_attention.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, f64, f64, i32, vp, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"storage dtype must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """Exact value of stored data as float64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ---- sizes -------------------------------------------------------------
+
+def nbins(n: int) -> int:
+    return lib().orc_nbins(n)
+
+
+def kkeep(nb: int, a_num: int, a_den: int) -> int:
+    return lib().orc_kkeep(nb, a_num, a_den)
+
+
+def ksel(n: int, r_num: int, r_den: int) -> int:
+    return lib().orc_ksel(n, r_num, r_den)
+
+
+def fft_len(n: int, mode: int = FFT_EXACT_N) -> int:
+    return lib().orc_fft_len(n, mode)
+
+
+def round_bf16(x) -> np.ndarray:
+    """RNE rounding of float64 values to bf16 bit patterns (elementwise, slow)."""
+    L = lib()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    out = np.array([L.orc_round_bf16(float(v)) for v in flat], dtype=np.uint16)
+    return out.reshape(np.shape(x))
+
+
+# ---- transforms ----------------------------------------------------------
+
+def rfft(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    n = x.shape[0]
+    re = np.zeros(n // 2 + 1)
+    im = np.zeros(n // 2 + 1)
+    lib().orc_rfft(_p(x), n, _p(re), _p(im))
+    return re + 1j * im
+
+
+def lowpass(x: np.ndarray, a_num: int, a_den: int, mode: int = FFT_EXACT_N) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    lib().orc_lowpass(_p(x), x.shape[0], a_num, a_den, mode, _p(out))
+    return out
+
+
+# ---- scoring / selection ------------------------------------------------
+
+def score_chunk(K: np.ndarray, V: np.ndarray, a_num: int, a_den: int,
+                mode: int = FFT_EXACT_N, norm: int = NORM_SUM, layers: bool = False):
+    """K, V: [L][N][H][D] storage arrays.  Returns score[N] (and [L][N])."""
+    assert K.shape == V.shape and K.ndim == 4 and K.dtype == V.dtype
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    L_, N, H, D = K.shape
+    score = np.zeros(N)
+    ls = np.zeros((L_, N)) if layers else None
+    rc = lib().orc_score_chunk(_p(K), _p(V), _dtype_code(K), L_, N, H, D, a_num, a_den,
+                               mode, norm, _p(ls), _p(score))
+    if rc != 0:
+        raise ValueError("orc_score_chunk rejected its arguments")
+    return (score, ls) if layers else score
+
+
+def topr(score: np.ndarray, k: int):
+    s = np.ascontiguousarray(score, dtype=np.float64)
+    n = s.shape[0]
+    ranking = np.zeros(n, np.int32)
+    sel = np.zeros(max(k, 1), np.int32)
+    comp = np.zeros(max(n - k, 1), np.int32)
+    lib().orc_topr(_p(s), n, k, _p(ranking), _p(sel), _p(comp))
+    return ranking, sel[:k].copy(), comp[:n - k].copy()
+
+
+def offsets(n_per_chunk, order, prefix: int = 0) -> np.ndarray:
+    n = np.ascontiguousarray(n_per_chunk, dtype=np.int32)
+    o = np.ascontiguousarray(order, dtype=np.int32)
+    out = np.zeros(n.shape[0], np.int32)
+    lib().orc_offsets(_p(n), _p(o), n.shape[0], prefix, _p(out))
+    return out
+
+
+# ---- RoPE / assembly ----------------------------------------------------
+
+def rope_freqs(D: int, theta: float) -> np.ndarray:
+    f = np.zeros(D // 2)
+    lib().orc_rope_freqs(D, theta, _p(f))
+    return f
+
+
+def rope(x: np.ndarray, pos: float, theta: float, style: int = ROPE_HALF) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.zeros_like(x)
+    lib().orc_rope(_p(x), x.shape[0], float(pos), float(theta), style, _p(y))
+    return y
+
+
+def assemble_chunk(k_src, v_src, k_rec, v_rec, sel, offset, theta, style, k_out, v_out):
+    """Place one chunk (rows [n][H][D]) into k_out/v_out ([T][H][D]) in place."""
+    n, H, D = k_src.shape
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    k = sel.shape[0]
+    kr = np.ascontiguousarray(k_rec) if k > 0 else np.zeros((1, H, D), k_src.dtype)
+    vr = np.ascontiguousarray(v_rec) if k > 0 else np.zeros((1, H, D), k_src.dtype)
+    lib().orc_assemble_chunk(_p(np.ascontiguousarray(k_src)), _p(np.ascontiguousarray(v_src)),
+                             _p(kr), _p(vr), _p(sel if k > 0 else np.zeros(1, np.int32)), n, k,
+                             int(offset), H, D, _dtype_code(k_src), float(theta), style,
+                             _p(k_out), _p(v_out))
+
+
+def assemble_rows(k_rows, v_rows, start, theta, style, k_out, v_out):
+    n, H, D = k_rows.shape
+    if n == 0:
+        return
+    lib().orc_assemble_rows(_p(np.ascontiguousarray(k_rows)), _p(np.ascontiguousarray(v_rows)),
+                            n, int(start), H, D, _dtype_code(k_rows), float(theta), style,
+                            _p(k_out), _p(v_out))
+
+
+def attention(q_pre, qpos, k, v, scale, theta, style=ROPE_HALF, rows=None):
+    """q_pre: [n_q][Hq][D]; k, v: [T][H][D] (assembled).  Returns (out, lse) in
+    float64 for the requested rows (all rows by default)."""
+    n_q, Hq, D = q_pre.shape
+    T, H, _ = k.shape
+    rows = np.arange(n_q, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    out = np.zeros((rows.shape[0], Hq, D))
+    lse = np.zeros((rows.shape[0], Hq))
+    qp = np.ascontiguousarray(qpos, dtype=np.int32)
+    rc = lib().orc_attention(_p(np.ascontiguousarray(q_pre)), _p(qp), Hq, _p(np.ascontiguousarray(k)),
+                             _p(np.ascontiguousarray(v)), T, H, D, _dtype_code(q_pre), float(scale),
+                             float(theta), style, _p(rows), rows.shape[0], _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("orc_attention rejected its arguments")
+    return out, lse

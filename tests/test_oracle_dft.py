@@ -1,0 +1,165 @@
+"""Pins for the oracle's transform and low-pass reconstruction (App. B.1 of the
+CacheTune page: rFFT along tokens, keep the lowest alpha fraction of the
+floor(N/2)+1 bins, inverse transform with output length N).
+
+Each pin comes from outside the oracle: closed forms of the DFT, Parseval's
+identity, a textbook radix-2 FFT written here, numpy's FFT routines, and
+structural invariants of an ideal low-pass projector."""
+import numpy as np
+import pytest
+
+RNG = np.random.default_rng(1234)
+
+
+def radix2_fft(x):
+    """Textbook recursive Cooley-Tukey FFT (power-of-two lengths)."""
+    x = np.asarray(x, dtype=complex)
+    n = x.shape[0]
+    if n == 1:
+        return x
+    even = radix2_fft(x[0::2])
+    odd = radix2_fft(x[1::2])
+    tw = np.exp(-2j * np.pi * np.arange(n // 2) / n)
+    return np.concatenate([even + tw * odd, even - tw * odd])
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 17, 64])
+def test_impulse_has_flat_spectrum(orc, n):
+    x = np.zeros(n)
+    x[0] = 1.0
+    X = orc.rfft(x)
+    assert X.shape == (n // 2 + 1,)
+    np.testing.assert_allclose(X, np.ones(n // 2 + 1), atol=1e-15)
+
+
+@pytest.mark.parametrize("n", [2, 7, 16, 33])
+def test_constant_only_dc(orc, n):
+    X = orc.rfft(np.full(n, 2.5))
+    assert abs(X[0] - 2.5 * n) < 1e-12
+    np.testing.assert_allclose(X[1:], 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,f", [(16, 3), (17, 5), (64, 1), (30, 7)])
+def test_on_bin_cosine(orc, n, f):
+    A, phi = 1.7, 0.4
+    t = np.arange(n)
+    X = orc.rfft(A * np.cos(2 * np.pi * f * t / n + phi))
+    expect = np.zeros(n // 2 + 1, complex)
+    expect[f] = A * n / 2 * np.exp(1j * phi)
+    np.testing.assert_allclose(X, expect, atol=1e-11)
+
+
+def test_nyquist_bin_real(orc):
+    n = 12
+    x = np.cos(np.pi * np.arange(n))  # (-1)^n: all energy in bin N/2
+    X = orc.rfft(x)
+    assert abs(X[n // 2] - n) < 1e-12 and abs(X[n // 2].imag) == 0.0
+    np.testing.assert_allclose(X[: n // 2], 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [5, 16, 31, 100, 257])
+def test_parseval(orc, n):
+    x = RNG.standard_normal(n)
+    X = orc.rfft(x)
+    w = np.full(n // 2 + 1, 2.0)
+    w[0] = 1.0
+    if n % 2 == 0:
+        w[-1] = 1.0
+    assert abs(np.sum(x * x) - np.sum(w * np.abs(X) ** 2) / n) < 1e-10 * np.sum(x * x)
+
+
+@pytest.mark.parametrize("n", [8, 64, 512])
+def test_matches_textbook_radix2(orc, n):
+    x = RNG.standard_normal(n)
+    np.testing.assert_allclose(orc.rfft(x), radix2_fft(x)[: n // 2 + 1], atol=1e-11 * n)
+
+
+@pytest.mark.parametrize("n", [6, 9, 100, 333])
+def test_matches_numpy_rfft(orc, n):
+    x = RNG.standard_normal(n)
+    np.testing.assert_allclose(orc.rfft(x), np.fft.rfft(x), atol=1e-11 * n)
+
+
+# ---- low-pass -----------------------------------------------------------
+
+def np_lowpass(x, kk, nf=None):
+    """Library-routine construction: numpy rfft, zero bins >= kk, irfft(n)."""
+    n = x.shape[0]
+    nf = n if nf is None else nf
+    xp = np.zeros(nf)
+    xp[:n] = x
+    X = np.fft.rfft(xp)
+    X[kk:] = 0
+    return np.fft.irfft(X, n=nf)[:n]
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 7, 16, 61, 128, 300])
+def test_alpha_one_is_identity(orc, n):
+    x = RNG.standard_normal(n)
+    np.testing.assert_allclose(orc.lowpass(x, 1, 1), x, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,a_num,a_den", [(64, 1, 16), (65, 1, 16), (100, 1, 2), (2048, 1, 16),
+                                           (513, 1, 32), (16, 3, 7), (9, 1, 100)])
+def test_matches_numpy_projector(orc, n, a_num, a_den):
+    x = RNG.standard_normal(n)
+    kk = max(1, (a_num * (n // 2 + 1)) // a_den)
+    np.testing.assert_allclose(orc.lowpass(x, a_num, a_den), np_lowpass(x, kk), atol=1e-11)
+
+
+@pytest.mark.parametrize("n,a_num,a_den", [(100, 1, 16), (600, 1, 32), (33, 1, 2)])
+def test_zeropad_mode_matches_numpy(orc, n, a_num, a_den):
+    x = RNG.standard_normal(n)
+    nf = 1 << (n - 1).bit_length()
+    kk = max(1, (a_num * (nf // 2 + 1)) // a_den)
+    got = orc.lowpass(x, a_num, a_den, orc.FFT_ZEROPAD_POW2)
+    np.testing.assert_allclose(got, np_lowpass(x, kk, nf), atol=1e-11)
+
+
+def test_cosine_passband_and_stopband(orc):
+    n, a_num, a_den = 2048, 1, 16  # keeps bins 0..63
+    t = np.arange(n)
+    below = 1.3 * np.cos(2 * np.pi * 63 * t / n + 0.2)
+    above = 0.8 * np.cos(2 * np.pi * 64 * t / n + 1.1)
+    np.testing.assert_allclose(orc.lowpass(below, a_num, a_den), below, atol=1e-11)
+    np.testing.assert_allclose(orc.lowpass(above, a_num, a_den), 0.0, atol=1e-11)
+
+
+def test_dc_only_gives_mean(orc):
+    x = RNG.standard_normal(40)
+    # alpha so small that only the DC bin survives
+    np.testing.assert_allclose(orc.lowpass(x, 1, 1000), np.full(40, x.mean()), atol=1e-13)
+
+
+@pytest.mark.parametrize("n", [10, 64, 77])
+def test_projector_properties(orc, n):
+    a = RNG.standard_normal(n)
+    b = RNG.standard_normal(n)
+    lp = lambda v: orc.lowpass(v, 1, 4)
+    la = lp(a)
+    np.testing.assert_allclose(lp(la), la, atol=1e-12)                       # idempotent
+    np.testing.assert_allclose(lp(2.0 * a - 3.0 * b), 2.0 * la - 3.0 * lp(b), atol=1e-11)  # linear
+    for s in (1, 5, n - 1):                                                   # shift equivariant
+        np.testing.assert_allclose(lp(np.roll(a, s)), np.roll(la, s), atol=1e-11)
+    rev = lambda v: np.roll(v[::-1], 1)                                       # x[-n mod N]
+    np.testing.assert_allclose(lp(rev(a)), rev(la), atol=1e-11)               # time reversal
+    # orthogonal projector: residual orthogonal to the kept part
+    assert abs(np.dot(a - la, la)) < 1e-9 * np.dot(a, a)
+
+
+@pytest.mark.parametrize("n", [4, 5, 8, 11, 16])
+def test_brute_force_projector_matrix(orc, n):
+    """Explicit N x N projector built from complex exponentials of the kept
+    frequencies (+-j for j < kk, counting the Nyquist frequency once)."""
+    for kk_target in range(1, n // 2 + 2):
+        # choose alpha = kk/(nbins) exactly
+        nb = n // 2 + 1
+        kk = max(1, (kk_target * nb) // nb)
+        freqs = {0}
+        for j in range(1, kk):
+            freqs.add(j % n)
+            freqs.add((-j) % n)
+        F = np.exp(2j * np.pi * np.outer(np.arange(n), sorted(freqs)) / n)
+        P = (F @ F.conj().T).real / n
+        x = RNG.standard_normal(n)
+        np.testing.assert_allclose(orc.lowpass(x, kk_target, nb), P @ x, atol=1e-12)
