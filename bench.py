@@ -1,0 +1,400 @@
+"""Benchmark of the CacheTune hot path on one MI355X.
+
+One step = one pass of the whole hot path over one request of synthetic chunk
+KV resident in HBM:
+  score all chunks (all layers) -> top-r per chunk -> for every layer:
+  assemble the layer's working buffer with deferred RoPE, then causal GQA
+  attention of the selected + suffix queries over it.
+Default workload: 8 chunks x 2048 tokens, Llama-3-8B-shaped (32 layers, 32 Q /
+8 KV heads, head_dim 128), bf16, cutoff 1/16 of the rFFT bins, r = 15% per chunk,
+RoPE theta 500000 at cumulative chunk offsets, 128-token suffix.
+
+Prints ONE JSON line (rank 0).  `value` = chunk-KV tokens (sum of chunk lengths)
+per second of whole-step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+WORKLOADS = {
+    # name: (chunk lengths, L, H, Hq, D, dtype, alpha, r, theta, n_sfx, seed, random order)
+    "llama3-8b-8x2048": dict(ns=[2048] * 8, L=32, H=8, Hq=32, D=128, dtype="bf16", alpha=(1, 16),
+                             r=(15, 100), theta=500000.0, n_sfx=128, seed=20260522, shuffle=False),
+    "single-512-fp32": dict(ns=[512], L=1, H=8, Hq=8, D=64, dtype="f32", alpha=(1, 16), r=(15, 100),
+                            theta=10000.0, n_sfx=16, seed=20260521, shuffle=False),
+    "llama3-8b-16x2048-shuffled": dict(ns=[2048] * 16, L=32, H=8, Hq=32, D=128, dtype="bf16",
+                                       alpha=(1, 16), r=(15, 100), theta=500000.0, n_sfx=128,
+                                       seed=20260523, shuffle=True),
+}
+
+
+def _dev(a):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class Workload:
+    """Device-resident inputs and buffers of one request."""
+
+    def __init__(self, name: str, layers: int | None = None):
+        import torch
+        import non_prefix_kv_token_amd as ct
+        import synth as syn
+
+        cfg = dict(WORKLOADS[name])
+        self.name = name
+        self.cfg = cfg
+        self.ct = ct
+        ns, self.L = cfg["ns"], cfg["L"] if layers is None else layers
+        self.H, self.Hq, self.D = cfg["H"], cfg["Hq"], cfg["D"]
+        self.theta, self.alpha, self.r = cfg["theta"], cfg["alpha"], cfg["r"]
+        self.dtype = cfg["dtype"]
+        self.ns = ns
+        seed = cfg["seed"]
+        self.seed = seed
+        nb = len(ns)
+        order = syn.permutation(seed, 0, nb) if cfg["shuffle"] else np.arange(nb, dtype=np.int32)
+        self.order = order
+        offs = np.zeros(nb, np.int64)
+        pos = 0
+        for p in range(nb):  # chunk order[p] is placed p-th
+            offs[order[p]] = pos
+            pos += ns[order[p]]
+        self.offsets = offs
+        self.T_c = pos
+        self.n_sfx = cfg["n_sfx"]
+        self.T = pos + self.n_sfx
+        L, H, Hq, D = self.L, self.H, self.Hq, self.D
+
+        t0 = time.time()
+        self.chunks = []
+        for b, n in enumerate(ns):
+            k = syn.chunk(seed, syn.K, b, L, n, H, D, self.dtype)
+            v = syn.chunk(seed, syn.V, b, L, n, H, D, self.dtype)
+            self.chunks.append((_dev(k), _dev(v)))
+            del k, v
+        self.gen_seconds = time.time() - t0
+
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        self.score = torch.empty(sum(ns), dtype=torch.float32, device="cuda")
+        self.ws_bytes = ct.cachetune_score_chunk_ws(ns, L, H, D, self.alpha)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.ks = [(self.r[0] * n) // self.r[1] for n in ns]
+        self.ranking = torch.empty(sum(ns), dtype=torch.int32, device="cuda")
+        self.sel = torch.empty(max(1, sum(self.ks)), dtype=torch.int32, device="cuda")
+        self.comp = torch.empty(max(1, sum(ns) - sum(self.ks)), dtype=torch.int32, device="cuda")
+
+        # untimed selection pass: the recomputed rows and queries are inputs that
+        # the model would produce for the selected tokens
+        self.score_and_select()
+        torch.cuda.synchronize()
+        sel_h = self.sel.cpu().numpy()
+        self.sel_host = []
+        o = 0
+        for b, k in enumerate(self.ks):
+            self.sel_host.append(sel_h[o:o + k].copy())
+            o += k
+        qpos = [self.offsets[b] + s for b, s in enumerate(self.sel_host)]
+        qpos.append(np.arange(self.T_c, self.T))
+        qpos = np.sort(np.concatenate(qpos)).astype(np.int32)
+        self.qpos_host = qpos
+        self.qpos = _dev(qpos)
+        self.n_q = len(qpos)
+        # global position -> (chunk, local) for query generation
+        owner = np.empty(self.T, np.int64)
+        local = np.empty(self.T, np.int64)
+        for b, n in enumerate(ns):
+            owner[offs[b]:offs[b] + n] = b
+            local[offs[b]:offs[b] + n] = np.arange(n)
+        owner[self.T_c:] = -1
+        local[self.T_c:] = np.arange(self.n_sfx)
+
+        t0 = time.time()
+        self.rec, self.sfx, self.q = [], [], []
+        for l in range(L):
+            rl = []
+            for b, n in enumerate(ns):
+                s = self.sel_host[b]
+                kr = syn.rows(seed, syn.K, b, l, n, H, D, s, self.dtype, extra_sigma=0.25)
+                vr = syn.rows(seed, syn.V, b, l, n, H, D, s, self.dtype, extra_sigma=0.25)
+                rl.append((_dev(kr), _dev(vr)))
+            self.rec.append(rl)
+            idx = np.arange(self.n_sfx)
+            ksf = syn.rows(seed, syn.K, syn.SUFFIX_CHUNK, l, self.n_sfx, H, D, idx, self.dtype)
+            vsf = syn.rows(seed, syn.V, syn.SUFFIX_CHUNK, l, self.n_sfx, H, D, idx, self.dtype)
+            self.sfx.append((_dev(ksf), _dev(vsf)))
+            qrows = np.empty((self.n_q, Hq, D), dtype=np.uint16 if self.dtype == "bf16" else np.float32)
+            for b, n in enumerate(ns):
+                m = owner[qpos] == b
+                if m.any():
+                    qrows[m] = syn.rows(seed, syn.Q, b, l, n, Hq, D, local[qpos[m]], self.dtype)
+            m = owner[qpos] == -1
+            qrows[m] = syn.rows(seed, syn.Q, syn.SUFFIX_CHUNK, l, self.n_sfx, Hq, D, local[qpos[m]],
+                                self.dtype)
+            self.q.append(_dev(qrows))
+        self.gen_seconds += time.time() - t0
+
+        self.k_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
+        self.v_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
+        self.out = torch.empty((self.n_q, Hq, D), dtype=tdt, device="cuda")
+        self.comp_off, self.sel_off = [], []
+        co = so = 0
+        for b, n in enumerate(ns):
+            self.sel_off.append(so)
+            self.comp_off.append(co)
+            so += self.ks[b]
+            co += n - self.ks[b]
+        esz = 2 if self.dtype == "bf16" else 4
+        self.layer_bytes = [n * H * D * esz for n in ns]
+        self.scale = 1.0 / math.sqrt(D)
+        self._places = {}
+
+    # ---- the hot path ----------------------------------------------------------
+    def score_and_select(self):
+        ct = self.ct
+        ct.cachetune_score_chunk(self.chunks, self.L, self.H, self.D, alpha=self.alpha,
+                                 score=self.score, ws=self.ws)
+        ct.cachetune_select_topr(self.score, self.ns, r=self.r, ranking=self.ranking, sel=self.sel,
+                                 comp=self.comp)
+
+    def places(self, l):
+        if l in self._places:
+            return self._places[l]
+        ct = self.ct
+        out = []
+        for b, n in enumerate(self.ns):
+            k, v = self.chunks[b]
+            kr, vr = self.rec[l][b]
+            k_l, v_l = k[l], v[l]
+            out.append(ct.make_place(k_l, v_l, n, self.ks[b], int(self.offsets[b]),
+                                     sel=self.sel[self.sel_off[b]:],
+                                     comp=self.comp[self.comp_off[b]:], k_rec=kr, v_rec=vr))
+        self._places[l] = out
+        return out
+
+    def assemble(self, l):
+        ksf, vsf = self.sfx[l]
+        self.ct.cachetune_assemble_rope(self.places(l), self.k_asm, self.v_asm, self.H, self.D,
+                                        self.theta, k_sfx=ksf, v_sfx=vsf, n_sfx=self.n_sfx,
+                                        sfx_offset=self.T_c)
+
+    def attend(self, l):
+        self.ct.cachetune_recompute_attn(self.q[l], self.qpos, self.k_asm, self.v_asm, self.scale,
+                                         self.theta, out=self.out)
+
+    def step(self, ev=None):
+        if ev is not None:
+            ev["s0"].record()
+        self.score_and_select()
+        if ev is not None:
+            ev["s1"].record()
+        for l in range(self.L):
+            if ev is not None:
+                ev["a0"][l].record()
+            self.assemble(l)
+            if ev is not None:
+                ev["a1"][l].record()
+            self.attend(l)
+            if ev is not None:
+                ev["a2"][l].record()
+
+    # ---- algorithmic work -----------------------------------------------------------
+    def attn_flops_per_layer(self) -> float:
+        # QK^T and PV: 2 * 2 * D flops per (query head, visible key)
+        return 4.0 * self.D * self.Hq * float(np.sum(self.qpos_host.astype(np.float64) + 1.0))
+
+    def score_bytes(self) -> float:
+        esz = 2 if self.dtype == "bf16" else 4
+        return float(sum(self.ns)) * self.L * 2 * self.H * self.D * esz  # one read of K and V
+
+    def assemble_bytes_per_layer(self) -> float:
+        esz = 2 if self.dtype == "bf16" else 4
+        row = self.H * self.D * esz
+        return float(self.T) * row * 2 * 2 + 4.0 * sum(self.ns)  # read + write K and V, indices
+
+
+def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
+    """The oracle timed on a bounded sample of the same workload, scaled to one
+    step (score of every chunk and layer, top-r, assembly and attention of every
+    layer)."""
+    import oracle as orc
+    import synth as syn
+
+    L, H, Hq, D = w.L, w.H, w.Hq, w.D
+    n0 = w.ns[0]
+    k = syn.chunk(w.seed, syn.K, 0, budget_layers, n0, H, D, w.dtype)
+    v = syn.chunk(w.seed, syn.V, 0, budget_layers, n0, H, D, w.dtype)
+    t0 = time.perf_counter()
+    s = orc.score_chunk(k, v, *w.alpha)
+    t_score = (time.perf_counter() - t0) * (L / budget_layers) * (sum(w.ns) / n0)
+    t0 = time.perf_counter()
+    for _ in range(len(w.ns)):
+        orc.topr(s, orc.ksel(n0, *w.r))
+    t_topr = time.perf_counter() - t0
+    # assembly of one layer
+    edt = np.uint16 if w.dtype == "bf16" else np.float32
+    k_out = np.zeros((w.T, H, D), edt)
+    v_out = np.zeros((w.T, H, D), edt)
+    t_asm_layer = 0.0
+    for b, n in enumerate(w.ns):
+        ks_ = syn.chunk(w.seed, syn.K, b, 1, n, H, D, w.dtype)[0]
+        vs_ = syn.chunk(w.seed, syn.V, b, 1, n, H, D, w.dtype)[0]
+        sel = w.sel_host[b]
+        kr = syn.rows(w.seed, syn.K, b, 0, n, H, D, sel, w.dtype, extra_sigma=0.25)
+        vr = syn.rows(w.seed, syn.V, b, 0, n, H, D, sel, w.dtype, extra_sigma=0.25)
+        t1 = time.perf_counter()  # generation above is not timed
+        orc.assemble_chunk(ks_, vs_, kr, vr, sel, int(w.offsets[b]), w.theta, 0, k_out, v_out)
+        t_asm_layer += time.perf_counter() - t1
+    ksf, vsf = (x.cpu() for x in w.sfx[0])
+    import torch as _t
+    ksf = ksf.view(_t.int16).numpy().view(np.uint16) if w.dtype == "bf16" else ksf.numpy()
+    vsf = vsf.view(_t.int16).numpy().view(np.uint16) if w.dtype == "bf16" else vsf.numpy()
+    t1 = time.perf_counter()
+    orc.assemble_rows(ksf, vsf, w.T_c, w.theta, 0, k_out, v_out)
+    t_asm_layer += time.perf_counter() - t1
+    # attention of a sample of query rows, scaled by visible-key counts
+    rows = np.linspace(0, w.n_q - 1, attn_rows).astype(np.int32)
+    q = w.q[0].cpu()
+    import torch
+    qh = q.view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else q.numpy()
+    t0 = time.perf_counter()
+    orc.attention(qh, w.qpos_host, k_out, v_out, w.scale, w.theta, rows=rows)
+    t_attn_sample = time.perf_counter() - t0
+    frac = float(np.sum(w.qpos_host[rows] + 1.0)) / float(np.sum(w.qpos_host + 1.0))
+    t_attn = t_attn_sample / frac * L
+    t_step = t_score + t_topr + t_asm_layer * L + t_attn
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": sum(w.ns) / t_step,
+        "unit": "chunk-KV tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"score: 1 chunk x {budget_layers} of {L} layers, scaled x{L // budget_layers} layers "
+                   f"x{len(w.ns)} chunks; top-r: all chunks; assembly: layer 0, scaled x{L}; "
+                   f"attention: {attn_rows} query rows x {Hq} heads of layer 0, scaled by visible keys "
+                   f"and x{L}"),
+        "seconds_est_per_step": t_step,
+        "stage_seconds_est": {"score": t_score, "topr": t_topr, "assemble": t_asm_layer * L,
+                              "attention": t_attn},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3-8b-8x2048", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the hot path is single-GPU; see the design notes for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    w = Workload(args.workload)
+    print(f"[bench] inputs generated in {w.gen_seconds:.1f}s; T={w.T} n_q={w.n_q}", file=sys.stderr,
+          flush=True)
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [{"s0": E(), "s1": E(), "a0": [E() for _ in range(w.L)], "a1": [E() for _ in range(w.L)],
+            "a2": [E() for _ in range(w.L)]} for _ in range(args.steps)]
+    start, stop = E(), E()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        w.step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    score_ms = np.mean([e["s0"].elapsed_time(e["s1"]) for e in evs])
+    asm_ms = np.mean([e["a0"][l].elapsed_time(e["a1"][l]) for e in evs for l in range(w.L)])
+    attn_ms = np.mean([e["a1"][l].elapsed_time(e["a2"][l]) for e in evs for l in range(w.L)])
+    tokens = float(sum(w.ns))
+    attn_flops = w.attn_flops_per_layer()
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    score_gbs = w.score_bytes() / (score_ms * 1e-3) / 1e9
+    asm_gbs = w.assemble_bytes_per_layer() / (asm_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "chunk-KV tokens/s through score->top-r->RoPE-assemble (+ selected-query attention); %HBM peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "chunk-KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded value model: N(0,1) + 3 low-bin sinusoids + 4 x5 spike tokens)",
+        "config": {
+            "workload": (f"{len(w.ns)} chunks x {w.ns[0]} tokens, {w.L} layers, {w.Hq} Q / {w.H} KV heads "
+                         f"x {w.D}, {w.dtype}, cutoff {w.alpha[0]}/{w.alpha[1]} of rFFT bins, "
+                         f"r={w.r[0]}/{w.r[1]}, RoPE theta {w.theta:g}, {w.n_sfx}-token suffix"),
+            "name": w.name, "T": w.T, "n_q": w.n_q, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "k_attn (selected-query causal GQA attention, per layer)",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+        "stages": {
+            "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
+            "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
+            "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS,
+            "attention_ms_per_layer": attn_ms, "attention_TFLOPs": attn_tflops,
+            "attention_flops_per_layer": attn_flops,
+            "score_plus_assemble_tokens_per_s": tokens / ((score_ms + asm_ms * w.L) * 1e-3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

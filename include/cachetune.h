@@ -1,0 +1,194 @@
+/*
+ * cachetune.h -- C ABI of the MI355X (gfx950) CacheTune hot path.
+ *
+ * The four calls follow the problem statement of "Adaptive KV Cache Reuse for
+ * Fast Long-Context LLM Serving" (CacheTune):
+ *   cachetune_score_chunk     App. B.1: frequency-domain importance score of
+ *                             each independently encoded chunk
+ *   cachetune_select_topr     App. B.1: stored ranking and the top-rN
+ *                             recomputation set / reuse complement
+ *   cachetune_assemble_rope   App. B.2 and B.3: per-layer working buffer
+ *                             assembled from reused and recomputed rows, keys
+ *                             rotated at their global positions
+ *   cachetune_recompute_attn  Sec. 4.1 "Recomputing in the new context" and
+ *                             App. B.2 "check layer": the selected queries
+ *                             attend causally over the assembled layer
+ *
+ * Conventions shared by every call:
+ *  - Memory: the caller owns all buffers.  "device" pointers are HIP device
+ *    memory of the current device; "host" pointers are ordinary host memory
+ *    read before the call returns.  The library allocates nothing.
+ *  - Asynchrony: arguments are validated synchronously; work is then enqueued
+ *    on `stream` and the call returns without synchronising.  A call that
+ *    fails validation enqueues nothing.
+ *  - Errors: every call returns a ct_status; no exception crosses the ABI.
+ *    cachetune_last_error() gives a message for the calling thread's last
+ *    failure.  CT_E_HIP means a HIP launch failed (the stream may hold work
+ *    enqueued by earlier launches of the same call).
+ *  - Storage types: CT_F32 (IEEE binary32) and CT_BF16 (bfloat16).  Results
+ *    are rounded once, to nearest even.
+ *  - Layout: per-layer tensors are row-major [rows][H][D] (token-major, the
+ *    H*D channels of one token contiguous).  Chunk tensors are [L][n][H][D].
+ *  - Determinism: identical inputs give bit-identical outputs (no floating
+ *    point atomics, fixed reduction orders).
+ *  - Concurrency: calls on different streams may run concurrently as long as
+ *    their output and workspace buffers do not overlap.
+ *  - Positions and indices are 0-based: chunk b placed at global offset o_b
+ *    maps its local row i to o_b + i (App. B.1 writes this 1-based as
+ *    o_b + i - 1).
+ */
+#ifndef CACHETUNE_H
+#define CACHETUNE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CT_OK = 0,
+  CT_E_INVALID = -1,     /* bad argument (null pointer, size, ratio ...) */
+  CT_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim) */
+  CT_E_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  CT_E_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} ct_status;
+
+typedef enum { CT_F32 = 0, CT_BF16 = 1 } ct_dtype;
+
+/* Per-layer normalisation of the chunk scores (App. B.1 states only that the
+ * scores are normalised within each layer).  CT_NORM_SUM divides by the layer
+ * sum (a layer whose sum is 0 becomes uniform 1/n); CT_NORM_MAX divides by the
+ * layer maximum; CT_NORM_MINMAX maps [min, max] to [0, 1]; CT_NORM_NONE keeps
+ * the raw values.  Degenerate MAX / MINMAX layers become 0. */
+typedef enum { CT_NORM_SUM = 0, CT_NORM_MAX = 1, CT_NORM_MINMAX = 2, CT_NORM_NONE = 3 } ct_norm;
+
+/* RoPE pairing: rotate-half pairs (j, j + D/2); interleaved pairs (2j, 2j+1).
+ * Pair j turns by pos * theta^(-2j/D). */
+typedef enum { CT_ROPE_HALF = 0, CT_ROPE_INTERLEAVED = 1 } ct_rope;
+
+/* Transform length of a chunk of n tokens: the exact length n (App. B.1), or
+ * the next power of two with the chunk zero-padded (the retained-bin count is
+ * then taken over that length's bins and positions [0, n) are scored). */
+typedef enum { CT_FFT_EXACT_N = 0, CT_FFT_ZEROPAD_POW2 = 1 } ct_fftlen;
+
+/* One independently encoded chunk: pre-RoPE keys and values, [L][n][H][D],
+ * device memory.  n in [2, 8192]. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t n;
+} ct_chunk;
+
+/* One chunk placed in a request, for ONE layer (App. B.2 fusion).
+ *  k_src, v_src  cached pre-RoPE rows of the layer (device):
+ *                src_rows == NULL: the full chunk layer [n][H][D], indexed by
+ *                                  local row; the reused rows are comp[0..n-k)
+ *                src_rows != NULL: a packed buffer [n-k][H][D] whose row j holds
+ *                                  local row src_rows[j] (device array)
+ *  k_rec, v_rec  recomputed pre-RoPE rows [k][H][D] (device); row t belongs to
+ *                local row sel[t]
+ *  sel           device, k ascending local indices of the recomputation set
+ *  comp          device, n-k ascending local indices of the reuse complement
+ *                (only read when src_rows == NULL)
+ *  n, k, offset  rows of the chunk, recomputed rows, global start o_b
+ * The output rows offset .. offset+n-1 are written. */
+typedef struct {
+  const void* k_src;
+  const void* v_src;
+  const int32_t* src_rows;
+  const void* k_rec;
+  const void* v_rec;
+  const int32_t* sel;
+  const int32_t* comp;
+  int32_t n;
+  int32_t k;
+  int32_t offset;
+} ct_place;
+
+const char* cachetune_status_string(int32_t status);
+const char* cachetune_last_error(void);
+int32_t cachetune_version(void);
+
+/* ---- scoring (App. B.1) ---------------------------------------------------
+ * For each chunk and layer: along the token axis of every (head, channel)
+ * sequence, a real DFT; bins at and above K_keep = max(1, floor(alpha * (m/2+1)))
+ * are zeroed (m = transform length, alpha = alpha_num / alpha_den in (0, 1]);
+ * the inverse transform with output length m gives the low-frequency tensor
+ * at the original positions.  Per token: a = L2 norm of the low-passed K over
+ * its H*D channels, b = the same for V; s = a/2 + b/2; s is normalised within
+ * the layer (`norm`); the chunk score is the mean over the L layers.
+ *
+ * Workspace query: writes the required workspace size for these shapes.
+ *   n_per_chunk: host, n_chunks entries. */
+ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                   int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
+                                   ct_fftlen fftlen, size_t* bytes);
+
+/* chunks: host array of n_chunks descriptors (1 <= n_chunks <= 4096).
+ * H*D must be a multiple of 64 and at most 8192; L in [1, 256].
+ * score:       device float[sum n], chunk scores concatenated in the order of
+ *              `chunks` (fp32, computed through fp64 reductions)
+ * layer_score: device float[L][sum n] normalised per-layer scores, or NULL
+ * ws/ws_bytes: device workspace of at least cachetune_score_chunk_ws bytes,
+ *              256-byte aligned; its contents are scratch. */
+ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
+                                ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- selection (App. B.1) -------------------------------------------------
+ * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].
+ * Ranking order: higher score first, equal scores by lower local index (the
+ * fp32 values are compared exactly; -0 equals +0; NaN ranks last).
+ *  score:       device float[sum n] (as written by cachetune_score_chunk)
+ *  n_per_chunk: host, n_chunks entries, each in [1, 8192]
+ *  ranking:     device int32[sum n] local indices in rank order, or NULL
+ *  sel:         device int32[sum k] the first k of each ranking, ascending
+ *  comp:        device int32[sum (n-k)] the rest, ascending, or NULL
+ *  k_per_chunk: host int32[n_chunks], written before the call returns. */
+ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
+                                int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
+                                int32_t* comp, int32_t* k_per_chunk, hipStream_t stream);
+
+/* ---- assembly with deferred RoPE (App. B.2, B.3) ---------------------------
+ * Builds one layer's working buffer k_out/v_out [T][H][D] (device):
+ *   reused rows: V copied, K rotated at the row's global position;
+ *   recomputed rows: from k_rec/v_rec, K rotated at the global position;
+ *   n_sfx uncached rows (k_sfx/v_sfx [n_sfx][H][D] pre-RoPE, device) at
+ *   positions sfx_offset .. sfx_offset + n_sfx - 1, K rotated likewise.
+ * Rows of k_out/v_out not covered by any place or the suffix are left as they
+ * are.  Every written row must lie in [0, T).  places: host array.
+ * The rotation angle pos * theta^(-2j/D) and its sine and cosine are formed in
+ * fp64; the rotated value is rounded once to the storage type.
+ * D must be 64 or 128; device index arrays are trusted (not range-checked). */
+ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, const void* k_sfx,
+                                  const void* v_sfx, int32_t n_sfx, int32_t sfx_offset, int32_t H,
+                                  int32_t D, ct_dtype dtype, double rope_theta, ct_rope style,
+                                  void* k_out, void* v_out, int32_t T, hipStream_t stream);
+
+/* ---- selected-query causal attention (Sec. 4.1, App. B.2) ------------------
+ *  q_pre: device [n_q][Hq][D] pre-RoPE queries of the selected and uncached rows
+ *  q_pos: device int32[n_q] their global positions, each in [0, T)
+ *  k, v:  device [T][H][D] assembled layer (keys already rotated)
+ * Query head h uses KV head floor(h * H / Hq) (Hq % H == 0).  Each query is
+ * rotated to its position, then attends to keys at positions <= its own:
+ *   out = softmax(softmax_scale * q . k_t) . v_t   (fp32 accumulation; the
+ * rotated query, the probabilities and fp32 inputs enter the matrix cores as
+ * bf16).
+ *  out: device [n_q][Hq][D] in `dtype`
+ *  lse: device float[n_q][Hq] natural-log sum of exp of the scaled logits, or NULL.
+ * D must be 64 or 128; n_q >= 0; T >= 1. */
+ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+                                   int32_t Hq, const void* k, const void* v, int32_t T,
+                                   int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
+                                   double rope_theta, ct_rope style, void* out, float* lse,
+                                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CACHETUNE_H */

@@ -1,0 +1,200 @@
+"""Python binding of ``libcachetune.so`` (MI355X / gfx950 CacheTune hot path).
+
+The functions carry the C ABI names (see ``include/cachetune.h`` for the
+operation, layouts and error behaviour of each).  This module only marshals
+arguments: torch tensors supply device memory and the current HIP stream; all
+computation runs in the library's HIP kernels.  If the library is missing the
+import of a function raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcachetune.so")
+
+CT_OK, CT_E_INVALID, CT_E_UNSUPPORTED, CT_E_WORKSPACE, CT_E_HIP = 0, -1, -2, -3, -4
+CT_F32, CT_BF16 = 0, 1
+CT_NORM_SUM, CT_NORM_MAX, CT_NORM_MINMAX, CT_NORM_NONE = 0, 1, 2, 3
+CT_ROPE_HALF, CT_ROPE_INTERLEAVED = 0, 1
+CT_FFT_EXACT_N, CT_FFT_ZEROPAD_POW2 = 0, 1
+
+
+class ct_chunk(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n", C.c_int32)]
+
+
+class ct_place(C.Structure):
+    _fields_ = [("k_src", C.c_void_p), ("v_src", C.c_void_p), ("src_rows", C.c_void_p),
+                ("k_rec", C.c_void_p), ("v_rec", C.c_void_p), ("sel", C.c_void_p),
+                ("comp", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32), ("offset", C.c_int32)]
+
+
+class CacheTuneError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version",
+           "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
+           "cachetune_assemble_rope", "cachetune_recompute_attn"]
+
+_lib = None
+
+
+def lib():
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with non_prefix_kv_token_amd.build")
+        L = C.CDLL(LIB_PATH)
+        i32, vp, f64, f32, sz = C.c_int32, C.c_void_p, C.c_double, C.c_float, C.c_size_t
+        L.cachetune_status_string.argtypes = [i32]
+        L.cachetune_status_string.restype = C.c_char_p
+        L.cachetune_last_error.restype = C.c_char_p
+        L.cachetune_version.restype = i32
+        L.cachetune_score_chunk_ws.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_score_chunk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                                            vp, sz, vp]
+        L.cachetune_select_topr.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.cachetune_assemble_rope.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, f64, i32,
+                                              vp, vp, i32, vp]
+        L.cachetune_recompute_attn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
+                                               f64, i32, vp, vp, vp]
+        for name in SYMBOLS[3:]:
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != CT_OK:
+        raise CacheTuneError(status, lib().cachetune_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CT_BF16
+    if t.dtype == torch.float32:
+        return CT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _i32_array(vals):
+    arr = (C.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+# ---- scoring -----------------------------------------------------------------
+
+def cachetune_score_chunk_ws(n_per_chunk, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N) -> int:
+    arr = _i32_array(n_per_chunk)
+    out = C.c_size_t(0)
+    _check(lib().cachetune_score_chunk_ws(arr, len(n_per_chunk), L, H, D, alpha[0], alpha[1],
+                                          fftlen, C.byref(out)))
+    return out.value
+
+
+def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N, norm=CT_NORM_SUM,
+                          score=None, layer_score=None, ws=None, want_layers=False, stream=None):
+    """chunks: list of (K, V) device tensors [L][n][H][D].  Returns (score,
+    layer_score) fp32 device tensors (layer_score None unless requested)."""
+    import torch
+    dev = chunks[0][0].device
+    ns = [int(k.shape[1]) for k, _ in chunks]
+    total = sum(ns)
+    if score is None:
+        score = torch.empty(total, dtype=torch.float32, device=dev)
+    if want_layers and layer_score is None:
+        layer_score = torch.empty((L, total), dtype=torch.float32, device=dev)
+    need = cachetune_score_chunk_ws(ns, L, H, D, alpha, fftlen)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    arr = (ct_chunk * len(chunks))()
+    for i, (k, v) in enumerate(chunks):
+        arr[i].k, arr[i].v, arr[i].n = k.data_ptr(), v.data_ptr(), int(k.shape[1])
+    _check(lib().cachetune_score_chunk(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
+                                       alpha[1], fftlen, norm, _ptr(score), _ptr(layer_score),
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+    return score, layer_score
+
+
+# ---- selection ----------------------------------------------------------------
+
+def cachetune_select_topr(score, n_per_chunk, r=(15, 100), ranking=None, sel=None, comp=None,
+                          want_ranking=True, want_comp=True, stream=None):
+    """Returns (k_per_chunk list, ranking, sel, comp) with device int32 tensors."""
+    import torch
+    dev = score.device
+    ns = [int(n) for n in n_per_chunk]
+    ks = [(r[0] * n) // r[1] for n in ns]
+    if ranking is None and want_ranking:
+        ranking = torch.empty(sum(ns), dtype=torch.int32, device=dev)
+    if sel is None:
+        sel = torch.empty(max(1, sum(ks)), dtype=torch.int32, device=dev)
+    if comp is None and want_comp:
+        comp = torch.empty(max(1, sum(ns) - sum(ks)), dtype=torch.int32, device=dev)
+    arr = _i32_array(ns)
+    kout = (C.c_int32 * len(ns))()
+    _check(lib().cachetune_select_topr(_ptr(score), arr, len(ns), r[0], r[1], _ptr(ranking),
+                                       _ptr(sel), _ptr(comp), kout, _stream(stream)))
+    return list(kout), ranking, sel, comp
+
+
+# ---- assembly -----------------------------------------------------------------
+
+def make_place(k_src, v_src, n, k, offset, sel=None, comp=None, k_rec=None, v_rec=None,
+               src_rows=None) -> ct_place:
+    p = ct_place()
+    p.k_src = None if k_src is None else k_src.data_ptr()
+    p.v_src = None if v_src is None else v_src.data_ptr()
+    p.src_rows = None if src_rows is None else src_rows.data_ptr()
+    p.k_rec = None if k_rec is None else k_rec.data_ptr()
+    p.v_rec = None if v_rec is None else v_rec.data_ptr()
+    p.sel = None if sel is None else sel.data_ptr()
+    p.comp = None if comp is None else comp.data_ptr()
+    p.n, p.k, p.offset = int(n), int(k), int(offset)
+    return p
+
+
+def cachetune_assemble_rope(places, k_out, v_out, H, D, rope_theta, style=CT_ROPE_HALF,
+                            k_sfx=None, v_sfx=None, n_sfx=0, sfx_offset=0, stream=None):
+    arr = (ct_place * max(1, len(places)))(*places)
+    T = int(k_out.shape[0])
+    _check(lib().cachetune_assemble_rope(arr, len(places), _ptr(k_sfx), _ptr(v_sfx), n_sfx,
+                                         sfx_offset, H, D, _dtype(k_out), rope_theta, style,
+                                         _ptr(k_out), _ptr(v_out), T, _stream(stream)))
+
+
+# ---- attention ----------------------------------------------------------------
+
+def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, style=CT_ROPE_HALF,
+                             out=None, lse=None, want_lse=False, stream=None):
+    """q_pre [n_q][Hq][D], q_pos int32 [n_q], k/v [T][H][D]; returns (out, lse)."""
+    import torch
+    n_q, Hq, D = (int(x) for x in q_pre.shape)
+    T, H = int(k.shape[0]), int(k.shape[1])
+    if out is None:
+        out = torch.empty_like(q_pre)
+    if want_lse and lse is None:
+        lse = torch.empty((n_q, Hq), dtype=torch.float32, device=q_pre.device)
+    _check(lib().cachetune_recompute_attn(_ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T,
+                                          H, D, _dtype(q_pre), float(softmax_scale),
+                                          float(rope_theta), style, _ptr(out), _ptr(lse),
+                                          _stream(stream)))
+    return out, lse

@@ -1,0 +1,271 @@
+// C ABI entry points: argument validation, launch planning, error reporting.
+// The operations themselves are defined in the header (include/cachetune.h)
+// with their citations; this file only checks arguments and enqueues kernels.
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <string>
+#include <vector>
+
+#include "ct_internal.h"
+
+namespace ct {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+ct_status fail(ct_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+ct_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(CT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return CT_OK;
+}
+
+static bool dtype_ok(int dt) { return dt == CT_F32 || dt == CT_BF16; }
+
+static void fill_inv_freq(double* f, int D, double theta) {
+  for (int j = 0; j < 64; ++j) f[j] = 0.0;
+  for (int j = 0; j < D / 2; ++j) f[j] = std::pow(theta, -2.0 * (double)j / (double)D);
+}
+
+}  // namespace ct
+
+using namespace ct;
+
+#define CT_GUARD_BEGIN try {
+#define CT_GUARD_END                                                   \
+  }                                                                    \
+  catch (const std::exception& e) {                                    \
+    return fail(CT_E_INVALID, std::string("internal error: ") + e.what()); \
+  }                                                                    \
+  catch (...) {                                                        \
+    return fail(CT_E_INVALID, "internal error");                       \
+  }
+
+extern "C" {
+
+const char* cachetune_status_string(int32_t s) {
+  switch (s) {
+    case CT_OK: return "ok";
+    case CT_E_INVALID: return "invalid argument";
+    case CT_E_UNSUPPORTED: return "unsupported configuration";
+    case CT_E_WORKSPACE: return "workspace missing or too small";
+    case CT_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* cachetune_last_error(void) { return g_last_error.c_str(); }
+
+int32_t cachetune_version(void) { return 1; }
+
+static ct_status check_score_shapes(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                    int32_t H, int32_t D, int32_t a_num, int32_t a_den,
+                                    int32_t fftlen) {
+  if (!n_per_chunk) return fail(CT_E_INVALID, "n_per_chunk is NULL");
+  if (n_chunks < 1 || n_chunks > 4096) return fail(CT_E_INVALID, "n_chunks must be in [1, 4096]");
+  if (L < 1 || L > 256) return fail(CT_E_INVALID, "L must be in [1, 256]");
+  if (H < 1 || D < 1) return fail(CT_E_INVALID, "H and D must be positive");
+  long long C = (long long)H * D;
+  if (C % 64 != 0 || C > 8192) return fail(CT_E_UNSUPPORTED, "H*D must be a multiple of 64, at most 8192");
+  if (a_den <= 0 || a_num <= 0 || a_num > a_den)
+    return fail(CT_E_INVALID, "alpha = alpha_num/alpha_den must lie in (0, 1]");
+  if (fftlen != CT_FFT_EXACT_N && fftlen != CT_FFT_ZEROPAD_POW2)
+    return fail(CT_E_INVALID, "unknown fftlen mode");
+  for (int b = 0; b < n_chunks; ++b) {
+    int n = n_per_chunk[b];
+    if (n < 2 || n > kMaxN) return fail(CT_E_INVALID, "chunk length must be in [2, 8192]");
+    if (fft_len(n, (ct_fftlen)fftlen) > kMaxN) return fail(CT_E_UNSUPPORTED, "transform length above 8192");
+  }
+  return CT_OK;
+}
+
+ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                   int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
+                                   ct_fftlen fftlen, size_t* bytes) {
+  CT_GUARD_BEGIN
+  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  if (ct_status s = check_score_shapes(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen))
+    return s;
+  return score_plan(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen, bytes, nullptr);
+  CT_GUARD_END
+}
+
+ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
+                                ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!chunks) return fail(CT_E_INVALID, "chunks is NULL");
+  if (n_chunks < 1 || n_chunks > 4096) return fail(CT_E_INVALID, "n_chunks must be in [1, 4096]");
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (norm < CT_NORM_SUM || norm > CT_NORM_NONE) return fail(CT_E_INVALID, "unknown norm");
+  if (!score) return fail(CT_E_INVALID, "score is NULL");
+  std::vector<int32_t> ns(n_chunks);
+  for (int b = 0; b < n_chunks; ++b) {
+    if (!chunks[b].k || !chunks[b].v) return fail(CT_E_INVALID, "chunk K or V pointer is NULL");
+    ns[b] = chunks[b].n;
+  }
+  if (ct_status s = check_score_shapes(ns.data(), n_chunks, L, H, D, alpha_num, alpha_den, fftlen))
+    return s;
+  size_t need = 0;
+  std::vector<ScoreLaunch> launches;
+  if (ct_status s = score_plan(ns.data(), n_chunks, L, H, D, alpha_num, alpha_den, fftlen, &need,
+                               &launches))
+    return s;
+  if (!ws || ws_bytes < need)
+    return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  int b0 = 0;
+  for (ScoreLaunch& sl : launches) {
+    sl.dtype = dtype;
+    sl.norm = norm;
+    for (int i = 0; i < sl.n_chunks; ++i) {
+      sl.c[i].k = chunks[b0 + i].k;
+      sl.c[i].v = chunks[b0 + i].v;
+    }
+    b0 += sl.n_chunks;
+  }
+  return score_run(launches, reinterpret_cast<char*>(ws), score, layer_score, stream);
+  CT_GUARD_END
+}
+
+ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
+                                int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
+                                int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!score || !n_per_chunk || !k_per_chunk) return fail(CT_E_INVALID, "NULL argument");
+  if (n_chunks < 1 || n_chunks > 65536) return fail(CT_E_INVALID, "n_chunks must be in [1, 65536]");
+  if (r_den <= 0 || r_num < 0 || r_num > r_den) return fail(CT_E_INVALID, "r must lie in [0, 1]");
+  long long tok = 0, sk = 0, sc = 0;
+  std::vector<int32_t> ks(n_chunks);
+  for (int b = 0; b < n_chunks; ++b) {
+    int n = n_per_chunk[b];
+    if (n < 1 || n > kMaxN) return fail(CT_E_INVALID, "chunk length must be in [1, 8192]");
+    ks[b] = (int32_t)(((long long)r_num * n) / r_den);
+  }
+  bool any_sel = false;
+  for (int b = 0; b < n_chunks; ++b) any_sel |= ks[b] > 0;
+  if (any_sel && !sel) return fail(CT_E_INVALID, "sel is NULL");
+  for (int b0 = 0; b0 < n_chunks; b0 += kMaxChunksPerLaunch) {
+    TopRLaunch tl{};
+    tl.n_chunks = std::min(kMaxChunksPerLaunch, n_chunks - b0);
+    for (int i = 0; i < tl.n_chunks; ++i) {
+      int b = b0 + i;
+      tl.c[i].n = n_per_chunk[b];
+      tl.c[i].k = ks[b];
+      tl.c[i].tok_off = tok;
+      tl.c[i].sel_off = sk;
+      tl.c[i].comp_off = sc;
+      tok += n_per_chunk[b];
+      sk += ks[b];
+      sc += n_per_chunk[b] - ks[b];
+    }
+    if (ct_status s = topr_run(tl, score, ranking, sel, comp, stream)) return s;
+  }
+  for (int b = 0; b < n_chunks; ++b) k_per_chunk[b] = ks[b];
+  return CT_OK;
+  CT_GUARD_END
+}
+
+ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, const void* k_sfx,
+                                  const void* v_sfx, int32_t n_sfx, int32_t sfx_offset, int32_t H,
+                                  int32_t D, ct_dtype dtype, double rope_theta, ct_rope style,
+                                  void* k_out, void* v_out, int32_t T, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (D != 64 && D != 128) return fail(CT_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (H < 1) return fail(CT_E_INVALID, "H must be positive");
+  if (style != CT_ROPE_HALF && style != CT_ROPE_INTERLEAVED) return fail(CT_E_INVALID, "unknown RoPE style");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return fail(CT_E_INVALID, "rope_theta must be > 1");
+  if (!k_out || !v_out) return fail(CT_E_INVALID, "output is NULL");
+  if (T < 1) return fail(CT_E_INVALID, "T must be positive");
+  if (n_places < 0 || (n_places > 0 && !places)) return fail(CT_E_INVALID, "places invalid");
+  if (n_sfx < 0) return fail(CT_E_INVALID, "n_sfx must be >= 0");
+  if (n_sfx > 0) {
+    if (!k_sfx || !v_sfx) return fail(CT_E_INVALID, "suffix pointers are NULL");
+    if (sfx_offset < 0 || (long long)sfx_offset + n_sfx > T) return fail(CT_E_INVALID, "suffix rows outside [0, T)");
+  }
+  for (int i = 0; i < n_places; ++i) {
+    const ct_place& p = places[i];
+    if (p.n < 1 || p.k < 0 || p.k > p.n) return fail(CT_E_INVALID, "place: need 0 <= k <= n, n >= 1");
+    if (p.offset < 0 || (long long)p.offset + p.n > T) return fail(CT_E_INVALID, "place rows outside [0, T)");
+    if (p.k < p.n && (!p.k_src || !p.v_src)) return fail(CT_E_INVALID, "place: cached rows are NULL");
+    if (p.k < p.n && !p.src_rows && !p.comp) return fail(CT_E_INVALID, "place: comp and src_rows are both NULL");
+    if (p.k > 0 && (!p.k_rec || !p.v_rec || !p.sel)) return fail(CT_E_INVALID, "place: recomputed rows are NULL");
+  }
+  std::vector<AsmPlace> all;
+  for (int i = 0; i < n_places; ++i) {
+    const ct_place& p = places[i];
+    AsmPlace a{p.k_src, p.v_src, p.src_rows, p.k_rec, p.v_rec, p.sel, p.comp, p.n, p.k, p.offset, 0};
+    all.push_back(a);
+  }
+  if (n_sfx > 0) {
+    AsmPlace a{k_sfx, v_sfx, nullptr, nullptr, nullptr, nullptr, nullptr, n_sfx, 0, sfx_offset, 1};
+    all.push_back(a);
+  }
+  for (size_t i0 = 0; i0 < all.size(); i0 += kMaxPlacesPerLaunch) {
+    AsmLaunch al{};
+    al.n_places = (int32_t)std::min<size_t>(kMaxPlacesPerLaunch, all.size() - i0);
+    al.max_rows = 0;
+    for (int i = 0; i < al.n_places; ++i) {
+      al.p[i] = all[i0 + i];
+      al.max_rows = std::max(al.max_rows, al.p[i].n);
+    }
+    al.H = H;
+    al.D = D;
+    al.dtype = dtype;
+    al.style = style;
+    fill_inv_freq(al.inv_freq, D, rope_theta);
+    if (ct_status s = assemble_run(al, k_out, v_out, stream)) return s;
+  }
+  return CT_OK;
+  CT_GUARD_END
+}
+
+ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+                                   int32_t Hq, const void* k, const void* v, int32_t T,
+                                   int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
+                                   double rope_theta, ct_rope style, void* out, float* lse,
+                                   hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (D != 64 && D != 128) return fail(CT_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (H < 1 || Hq < 1 || Hq % H != 0) return fail(CT_E_INVALID, "need Hq % H == 0");
+  if (style != CT_ROPE_HALF && style != CT_ROPE_INTERLEAVED) return fail(CT_E_INVALID, "unknown RoPE style");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return fail(CT_E_INVALID, "rope_theta must be > 1");
+  if (!std::isfinite(softmax_scale)) return fail(CT_E_INVALID, "softmax_scale must be finite");
+  if (n_q < 0 || T < 1) return fail(CT_E_INVALID, "need n_q >= 0, T >= 1");
+  if (n_q > 0 && (!q_pre || !q_pos || !k || !v || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if ((long long)(n_q + 31) / 32 * (Hq / H) > (long long)INT32_MAX / 4)
+    return fail(CT_E_UNSUPPORTED, "too many query rows");
+  AttnArgs a{};
+  a.q = q_pre;
+  a.qpos = q_pos;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.n_q = n_q;
+  a.Hq = Hq;
+  a.T = T;
+  a.H = H;
+  a.D = D;
+  a.dtype = dtype;
+  a.style = style;
+  a.group = Hq / H;
+  a.scale = softmax_scale;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  fill_inv_freq(a.inv_freq, D, rope_theta);
+  return attn_run(a, stream);
+  CT_GUARD_END
+}
+
+}  // extern "C"

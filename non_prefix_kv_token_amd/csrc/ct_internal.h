@@ -1,0 +1,117 @@
+// Internal declarations of the gfx950 CacheTune library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "cachetune.h"
+
+namespace ct {
+
+// ---------------------------------------------------------------- errors
+void set_error(const std::string& msg);
+ct_status fail(ct_status s, const std::string& msg);
+ct_status check_launch(const char* what);
+
+// ------------------------------------------------------- shared constants
+constexpr int kMaxChunksPerLaunch = 32;  // descriptors passed by value in kernel arguments
+constexpr int kMaxN = 8192;              // tokens per chunk
+constexpr int kPTile = 128;              // band rows per projection block
+
+// Retained bins and transform length (App. B.1).
+int fft_len(int n, ct_fftlen mode);
+int kkeep(int nf, int a_num, int a_den);
+inline int band_rows_padded(int kk) { return ((2 * kk + 31) / 32) * 32; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// -------------------------------------------------------------- score path
+// Descriptor of one chunk in a score launch.  Byte offsets are into the
+// caller's workspace.
+struct ScoreChunkDesc {
+  const void* k;
+  const void* v;
+  int32_t n;         // tokens
+  int32_t nf;        // transform length
+  int32_t kk;        // retained bins
+  int32_t ppad;      // padded band rows (multiple of 32, >= 2*kk)
+  int32_t ntok_pad;  // twiddle table row length (multiple of 32, >= n)
+  int32_t tw_owner;  // 1: this chunk writes the shared twiddle table
+  int64_t tw_off;    // bf16 twiddle planes [3][ppad][ntok_pad]
+  int64_t trig_off;  // fp64 (cos, sin) of 2*pi*m/nf, m < nf
+  int64_t y_off;     // fp32 band coefficients [L][2][ppad][C]
+  int64_t e_off;     // fp64 low-pass energies [L][2][n]
+  int64_t tok_off;   // first token of this chunk in the concatenated score vector
+};
+
+struct ScoreLaunch {
+  ScoreChunkDesc c[kMaxChunksPerLaunch];
+  int32_t n_chunks;
+  int32_t L, H, D, C;  // C = H * D
+  int32_t dtype;
+  int32_t norm;
+  int32_t max_ppad;
+  int32_t n_slots;     // Gram scratch slots
+  int32_t slot_p2;     // rows of the largest Gram handled (2 * max kk)
+  int64_t slot_off;    // byte offset of the Gram slots
+  int64_t slot_bytes;  // bytes per slot
+  int64_t total_tokens;
+};
+
+ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
+                     int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
+                     std::vector<ScoreLaunch>* launches);
+ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
+                    float* layer_score, hipStream_t stream);
+
+// ------------------------------------------------------------- selection
+struct TopRChunk {
+  int32_t n, k;
+  int64_t tok_off, sel_off, comp_off;
+};
+struct TopRLaunch {
+  TopRChunk c[kMaxChunksPerLaunch];
+  int32_t n_chunks;
+};
+ct_status topr_run(const TopRLaunch& tl, const float* score, int32_t* ranking, int32_t* sel,
+                   int32_t* comp, hipStream_t stream);
+
+// -------------------------------------------------------------- assembly
+struct AsmPlace {
+  const void* k_src;
+  const void* v_src;
+  const int32_t* src_rows;
+  const void* k_rec;
+  const void* v_rec;
+  const int32_t* sel;
+  const int32_t* comp;
+  int32_t n, k, offset, pad_;
+};
+constexpr int kMaxPlacesPerLaunch = 32;
+struct AsmLaunch {
+  AsmPlace p[kMaxPlacesPerLaunch];
+  int32_t n_places;
+  int32_t max_rows;
+  int32_t H, D, dtype, style;
+  double inv_freq[64];
+};
+ct_status assemble_run(const AsmLaunch& al, void* k_out, void* v_out, hipStream_t stream);
+
+// ------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;
+  const int32_t* qpos;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int32_t n_q, Hq, T, H, D, dtype, style, group;
+  float scale_log2;  // softmax_scale * log2(e)
+  float scale;
+  double inv_freq[64];
+};
+ct_status attn_run(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace ct

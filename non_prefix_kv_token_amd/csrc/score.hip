@@ -1,0 +1,592 @@
+// Chunk scoring on gfx950 -- "Adaptive KV Cache Reuse for Fast Long-Context
+// LLM Serving" (CacheTune), App. B.1 "Offline Preparation".
+//
+// For every (chunk, layer, K|V) problem with channels c = (head, dim) and
+// tokens n < N, the low-frequency energy per token
+//     E[n] = sum_c xlow_c[n]^2,
+//     xlow_c = inverse real DFT (length nf) of the lowest kk bins of x_c,
+// is computed exactly (up to rounding) without forming xlow:
+//  1. band projection on the matrix cores: Y = [cos | sin](j*n) . X, i.e. the
+//     real and imaginary parts R_j, S_j (j < kk) of the retained bins for all
+//     channels at once.  The twiddles are split into three bf16 planes
+//     (t = t1 + t2 + t3 to ~2^-24), bf16 data are exact, products are exact in
+//     fp32, so one pass of three bf16 MFMAs gives fp32-accurate coefficients;
+//     fp32 data are split the same way (six MFMAs).
+//  2. the channel Gram G = Y Y^T (fp64);
+//  3. E[n] as a trigonometric polynomial of degree 2(kk-1) in phi = 2*pi*n/nf,
+//     whose coefficients are diagonal and anti-diagonal sums of G; evaluated
+//     with a complex Horner scheme in fp64.
+//  4. per token a = sqrt(E_K), b = sqrt(E_V), s = a/2 + b/2, per-layer
+//     normalisation, mean over layers (fp64, fixed-order reductions).
+#include "ct_internal.h"
+
+namespace ct {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---- rounding helpers ----------------------------------------------------
+
+__device__ inline uint32_t bf16_rne_from_f32_bits(uint32_t u) {
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Round a double to bf16 with a single rounding: truncate to binary32 with a
+// sticky bit (round-to-odd), then round to nearest even.
+__device__ inline uint16_t bf16_from_f64(double d) {
+  float f = __double2float_rz(d);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != d) u |= 1u;
+  return (uint16_t)bf16_rne_from_f32_bits(u);
+}
+
+__device__ inline double f64_from_bf16(uint16_t h) {
+  return (double)__uint_as_float(((uint32_t)h) << 16);
+}
+
+// cos and sin of 2*pi*m/nf (0 <= m < nf): quarter turns are taken out exactly
+// so that multiples of pi/2 give exact 0 and +-1.
+__device__ inline void turn_sincos(long long m, int nf, double* s, double* c) {
+  long long t = 4 * m;
+  long long q = t / nf;
+  long long rem = t - q * nf;
+  double a = 1.5707963267948966 * ((double)rem / (double)nf);
+  double sa, ca;
+  sincos(a, &sa, &ca);
+  if (rem == 0) { sa = 0.0; ca = 1.0; }
+  switch ((int)(q & 3)) {
+    case 0: *c = ca;  *s = sa;  break;
+    case 1: *c = -sa; *s = ca;  break;
+    case 2: *c = -ca; *s = -sa; break;
+    default: *c = sa; *s = -ca; break;
+  }
+}
+
+// ---- 1a. twiddle planes ----------------------------------------------------
+// Row p < kk holds cos(2*pi*p*n/nf); row kk + j holds sin(2*pi*j*n/nf);
+// rows >= 2kk are zero.  Each value is stored as three bf16 planes.
+__global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl, char* ws) {
+  const ScoreChunkDesc& d = sl.c[blockIdx.y];
+  if (!d.tw_owner) return;
+  const int ppad = d.ppad, ntp = d.ntok_pad, kk = d.kk, nf = d.nf;
+  uint16_t* tw = reinterpret_cast<uint16_t*>(ws + d.tw_off);
+  const long long plane = (long long)ppad * ntp;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < plane;
+       e += (long long)gridDim.x * blockDim.x) {
+    int p = (int)(e / ntp), n = (int)(e % ntp);
+    double v = 0.0;
+    if (p < 2 * kk) {
+      int j = p < kk ? p : p - kk;
+      double s, c;
+      turn_sincos(((long long)j * n) % nf, nf, &s, &c);
+      v = p < kk ? c : s;
+    }
+    uint16_t t1 = bf16_from_f64(v);
+    double r1 = v - f64_from_bf16(t1);
+    uint16_t t2 = bf16_from_f64(r1);
+    double r2 = r1 - f64_from_bf16(t2);
+    uint16_t t3 = bf16_from_f64(r2);
+    tw[e] = t1;
+    tw[plane + e] = t2;
+    tw[2 * plane + e] = t3;
+  }
+  double2* trig = reinterpret_cast<double2*>(ws + d.trig_off);
+  for (long long m = (long long)blockIdx.x * blockDim.x + threadIdx.x; m < nf;
+       m += (long long)gridDim.x * blockDim.x) {
+    double s, c;
+    turn_sincos(m, nf, &s, &c);
+    trig[m] = make_double2(c, s);
+  }
+}
+
+// ---- 1b. band projection on the matrix cores --------------------------------
+// Block: 256 threads = 4 waves; one (chunk, layer, K|V) problem, 128 band rows,
+// 256 channels (64 per wave).  Per 32-token step the three twiddle planes of
+// the 128 rows are staged in LDS (row stride 40 bf16 = 80 B, conflict-free for
+// 16-byte fragment reads); each lane loads its 2 channels for 8 tokens directly
+// from HBM and transposes them in registers into MFMA B fragments.
+//   v_mfma_f32_32x32x16_bf16:  D[i][j] += sum_k A[i][k] B[k][j]
+//   A (band rows x tokens): lane -> row lane%32, tokens 8*(lane/32) + 0..7
+//   B (tokens x channels):  lane -> col lane%32, same tokens
+//   D: lane -> col lane%32, rows 8*(v/4) + 4*(lane/32) + v%4, v < 16
+// Channel of column j in B tile m (m = 0, 1): base + 2j + m.
+constexpr int kTwStride = 40;
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * 128 * kTwStride];
+
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.z;
+  const int b = prob / (2 * L);
+  const int layer = (prob / 2) % L;
+  const int kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int pbase = blockIdx.y * 128;
+  if (pbase >= d.ppad) return;
+  const int ntiles = min(4, (d.ppad - pbase) / 32);
+  const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int cbase = blockIdx.x * 256 + wave * 64;
+  const bool active = cbase < C;
+  const int c0 = cbase + 2 * col;
+
+  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + d.tw_off);
+  const long long plane = (long long)ppad * ntp;
+  const char* src = reinterpret_cast<const char*>(kv ? d.v : d.k);
+  const size_t esz = DT == CT_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)C * esz;
+  const char* xbase = src + ((size_t)layer * N) * row_bytes + (size_t)c0 * esz;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][m][v] = 0.f;
+
+  for (int n0 = 0; n0 < N; n0 += 32) {
+    // stage the twiddle slab: 3 planes x 128 rows x 32 tokens
+    for (int item = tid; item < 3 * 128 * 4; item += 256) {
+      int q = item / 512, r = (item / 4) % 128, i = item % 4;
+      if (r < ntiles * 32) {
+        const u32x4_t* gsrc = reinterpret_cast<const u32x4_t*>(
+            tw + q * plane + (long long)(pbase + r) * ntp + n0 + 8 * i);
+        *reinterpret_cast<u32x4_t*>(&lds[(q * 128 + r) * kTwStride + 8 * i]) = *gsrc;
+      }
+    }
+    // this lane's data: 2 k-steps x 8 tokens x 2 channels
+    uint32_t wb[2][8];
+    float2 wf[2][8];
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          int n = n0 + 16 * s + 8 * g + t;
+          if constexpr (DT == CT_BF16) {
+            wb[s][t] = n < N ? *reinterpret_cast<const uint32_t*>(xbase + (size_t)n * row_bytes) : 0u;
+          } else {
+            wf[s][t] = n < N ? *reinterpret_cast<const float2*>(xbase + (size_t)n * row_bytes)
+                             : make_float2(0.f, 0.f);
+          }
+        }
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8_t a[4][3];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          if (pt < ntiles)
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+              a[pt][q] = *reinterpret_cast<const bf16x8_t*>(
+                  &lds[(q * 128 + pt * 32 + col) * kTwStride + 16 * s + 8 * g]);
+        if constexpr (DT == CT_BF16) {
+          u32x4_t bu[2];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            uint32_t w0 = wb[s][2 * h], w1 = wb[s][2 * h + 1];
+            bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
+            bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+          }
+          bf16x8_t bfr[2] = {__builtin_bit_cast(bf16x8_t, bu[0]), __builtin_bit_cast(bf16x8_t, bu[1])};
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+            if (pt < ntiles)
+#pragma unroll
+              for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                  acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], bfr[m], acc[pt][m], 0, 0, 0);
+        } else {
+          // exact three-way bf16 split of each fp32 value
+          u32x4_t bu[3][2];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            uint32_t lo[3][2], hi[3][2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float2 v2 = wf[s][2 * h + e];
+#pragma unroll
+              for (int m = 0; m < 2; ++m) {
+                float x = m ? v2.y : v2.x;
+                uint32_t p1 = bf16_rne_from_f32_bits(__float_as_uint(x));
+                float r1 = x - __uint_as_float(p1 << 16);
+                uint32_t p2 = bf16_rne_from_f32_bits(__float_as_uint(r1));
+                float r2 = r1 - __uint_as_float(p2 << 16);
+                uint32_t p3 = bf16_rne_from_f32_bits(__float_as_uint(r2));
+                uint32_t parts[3] = {p1, p2, p3};
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) {
+                  if (e == 0) lo[pl][m] = parts[pl];
+                  else hi[pl][m] = parts[pl];
+                }
+              }
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+              for (int m = 0; m < 2; ++m) bu[pl][m][h] = lo[pl][m] | (hi[pl][m] << 16);
+          }
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+            if (pt < ntiles)
+#pragma unroll
+              for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                  for (int q = 0; q < 3; ++q)
+                    if (pl + q <= 2)
+                      acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                          a[pt][q], __builtin_bit_cast(bf16x8_t, bu[pl][m]), acc[pt][m], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    if (pt >= ntiles) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int row = pbase + pt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
+    }
+  }
+}
+
+// ---- 2/3. Gram of the band coefficients and energy evaluation ----------------
+// One block per (chunk, layer, K|V) problem (blocks loop over problems); the
+// block's Gram and polynomial coefficients live in its workspace slot.
+__global__ __launch_bounds__(256) void k_gram_eval(ScoreLaunch sl, char* ws, int n_probs) {
+  __shared__ float sa[32][132];
+  __shared__ float sb[32][132];
+  const int L = sl.L, C = sl.C;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  double* slot = reinterpret_cast<double*>(ws + sl.slot_off + (size_t)blockIdx.x * sl.slot_bytes);
+
+  for (int prob = blockIdx.x; prob < n_probs; prob += gridDim.x) {
+    const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
+    const ScoreChunkDesc& d = sl.c[b];
+    const int kk = d.kk, P2 = 2 * kk, ppad = d.ppad, nf = d.nf, N = d.n;
+    const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+    double* G = slot;                          // [P2][P2]
+    double* coef = slot + (size_t)P2 * P2;     // [2][2kk-1]: cos then sin coefficients
+    const int nblk = (P2 + 127) / 128;
+
+    for (int bi = 0; bi < nblk; ++bi)
+      for (int bj = 0; bj < nblk; ++bj) {
+        double acc[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+        for (int cc = 0; cc < C; cc += 32) {
+          __syncthreads();
+          for (int item = tid; item < 128 * 8; item += 256) {
+            int r = item >> 3, q4 = (item & 7) * 4;
+            int ra = bi * 128 + r, rb = bj * 128 + r;
+            float4 va = ra < P2 ? *reinterpret_cast<const float4*>(Y + (size_t)ra * C + cc + q4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            float4 vb = rb < P2 ? *reinterpret_cast<const float4*>(Y + (size_t)rb * C + cc + q4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            sa[q4 + 0][r] = va.x; sa[q4 + 1][r] = va.y; sa[q4 + 2][r] = va.z; sa[q4 + 3][r] = va.w;
+            sb[q4 + 0][r] = vb.x; sb[q4 + 1][r] = vb.y; sb[q4 + 2][r] = vb.z; sb[q4 + 3][r] = vb.w;
+          }
+          __syncthreads();
+#pragma unroll 4
+          for (int ch = 0; ch < 32; ++ch) {
+            double a[8], bv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = (double)sa[ch][8 * ty + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = (double)sb[ch][8 * tx + j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            int r = bi * 128 + 8 * ty + i, c = bj * 128 + 8 * tx + j;
+            if (r < P2 && c < P2) G[(size_t)r * P2 + c] = acc[i][j];
+          }
+      }
+    __syncthreads();
+
+    // Coefficients of E * nf^2 = sum_k A_k cos(k phi) + B_k sin(k phi), k < 2kk-1.
+    // With weights w_j (1 for DC and the Nyquist bin, 2 otherwise) and
+    // RR = G[j][j'], SS = G[kk+j][kk+j'], RS = G[j][kk+j']:
+    //   alpha_d = sum_{j-j'=d} w w (RR+SS),  beta_s = sum_{j+j'=s} w w (RR-SS),
+    //   gamma_s = 2 sum_{j+j'=s} w w RS,     delta_d = 2 sum_{j-j'=d} w w RS,
+    //   A_0 = (alpha_0 + beta_0)/2,  A_k = (2 alpha_k + beta_k)/2,
+    //   B_k = (gamma_k - delta_k + delta_{-k})/2.
+    const int K2 = 2 * kk - 1;
+    const bool even = (nf % 2) == 0;
+    for (int k = tid; k < K2; k += 256) {
+      double alpha = 0.0, beta = 0.0, gamma = 0.0, dpos = 0.0, dneg = 0.0;
+      for (int j = 0; j < kk; ++j) {
+        double wj = (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0;
+        int jp = j - k;  // j - j' = k
+        if (jp >= 0) {
+          double wjp = (jp == 0 || (even && 2 * jp == nf)) ? 1.0 : 2.0;
+          double w = wj * wjp;
+          alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
+          dpos += w * G[(size_t)j * P2 + kk + jp];
+        }
+        int jn = j + k;  // j - j' = -k
+        if (k > 0 && jn < kk) {
+          double wjn = (jn == 0 || (even && 2 * jn == nf)) ? 1.0 : 2.0;
+          dneg += wj * wjn * G[(size_t)j * P2 + kk + jn];
+        }
+        int js = k - j;  // j + j' = k
+        if (js >= 0 && js < kk) {
+          double wjs = (js == 0 || (even && 2 * js == nf)) ? 1.0 : 2.0;
+          double w = wj * wjs;
+          beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
+          gamma += w * G[(size_t)j * P2 + kk + js];
+        }
+      }
+      double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
+      double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
+      coef[k] = A;
+      coef[K2 + k] = B;
+    }
+    __syncthreads();
+
+    // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.
+    const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+    double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
+    const double inv = 1.0 / ((double)nf * (double)nf);
+    for (int n = tid; n < N; n += 256) {
+      double2 z = trig[n];
+      double pr = coef[K2 - 1], pi = -coef[2 * K2 - 1];
+      for (int k = K2 - 2; k >= 0; --k) {
+        double nr = pr * z.x - pi * z.y + coef[k];
+        double ni = pr * z.y + pi * z.x - coef[K2 + k];
+        pr = nr;
+        pi = ni;
+      }
+      E[n] = pr * inv;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- 4. magnitudes, per-layer normalisation, mean over layers ----------------
+constexpr int kFinThreads = 1024;
+constexpr int kFinPer = kMaxN / kFinThreads;  // tokens per thread
+
+__device__ double block_reduce(double v, int op, double* red) {
+  // op: 0 sum, 1 max, 2 min -- fixed pairing order, deterministic
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = kFinThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      double a = red[tid], b = red[tid + s];
+      red[tid] = op == 0 ? a + b : (op == 1 ? fmax(a, b) : fmin(a, b));
+    }
+    __syncthreads();
+  }
+  double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kFinThreads) void k_finalize(ScoreLaunch sl, char* ws, float* score,
+                                                          float* layer_score) {
+  __shared__ double red[kFinThreads];
+  const ScoreChunkDesc& d = sl.c[blockIdx.x];
+  const int N = d.n, L = sl.L, tid = threadIdx.x;
+  const double* E = reinterpret_cast<const double*>(ws + d.e_off);
+  double acc[kFinPer];
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i) acc[i] = 0.0;
+  for (int l = 0; l < L; ++l) {
+    const double* ek = E + (size_t)(l * 2) * N;
+    const double* ev = E + (size_t)(l * 2 + 1) * N;
+    double s[kFinPer];
+    double part_sum = 0.0, part_max = -INFINITY, part_min = INFINITY;
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      int n = tid * kFinPer + i;
+      s[i] = 0.0;
+      if (n < N) {
+        s[i] = 0.5 * sqrt(fmax(ek[n], 0.0)) + 0.5 * sqrt(fmax(ev[n], 0.0));
+        part_sum += s[i];
+        part_max = fmax(part_max, s[i]);
+        part_min = fmin(part_min, s[i]);
+      }
+    }
+    // normalisation: v = (s - shift) / denom, or the constant `fill`
+    double denom = 1.0, shift = 0.0, fill = -1.0;
+    if (sl.norm == CT_NORM_SUM) {
+      double t = block_reduce(part_sum, 0, red);
+      if (t > 0.0) denom = t; else fill = 1.0 / (double)N;
+    } else if (sl.norm == CT_NORM_MAX) {
+      double mx = block_reduce(part_max, 1, red);
+      if (mx > 0.0) denom = mx; else fill = 0.0;
+    } else if (sl.norm == CT_NORM_MINMAX) {
+      double mx = block_reduce(part_max, 1, red);
+      double mn = block_reduce(part_min, 2, red);
+      if (mx - mn > 0.0) { denom = mx - mn; shift = mn; } else fill = 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      int n = tid * kFinPer + i;
+      if (n < N) {
+        double v = fill >= 0.0 ? fill : (s[i] - shift) / denom;
+        if (sl.norm == CT_NORM_NONE) v = s[i];
+        acc[i] += v;
+        if (layer_score) layer_score[(size_t)l * sl.total_tokens + d.tok_off + n] = (float)v;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i) {
+    int n = tid * kFinPer + i;
+    if (n < N) score[d.tok_off + n] = (float)(acc[i] / (double)L);
+  }
+}
+
+}  // namespace
+
+// ---- host side ----------------------------------------------------------------
+
+int fft_len(int n, ct_fftlen mode) {
+  if (mode == CT_FFT_EXACT_N) return n;
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+int kkeep(int nf, int a_num, int a_den) {
+  long long nb = nf / 2 + 1;
+  long long k = ((long long)a_num * nb) / a_den;
+  if (k < 1) k = 1;
+  if (k > nb) k = nb;
+  return (int)k;
+}
+
+ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
+                     int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
+                     std::vector<ScoreLaunch>* launches) {
+  const int C = H * D;
+  size_t off = 0;
+  struct Tab { int nf, kk, ntp; int64_t tw, trig; };
+  std::vector<Tab> tabs;
+  std::vector<ScoreChunkDesc> desc(n_chunks);
+  int max_p2 = 0;
+  int64_t tok = 0;
+  for (int b = 0; b < n_chunks; ++b) {
+    ScoreChunkDesc& d = desc[b];
+    d = ScoreChunkDesc{};
+    d.n = n_per_chunk[b];
+    d.nf = fft_len(d.n, fftlen);
+    d.kk = kkeep(d.nf, a_num, a_den);
+    d.ppad = band_rows_padded(d.kk);
+    d.ntok_pad = ((d.n + 31) / 32) * 32;
+    d.tok_off = tok;
+    tok += d.n;
+    if (2 * d.kk > max_p2) max_p2 = 2 * d.kk;
+    int found = -1;
+    for (size_t t = 0; t < tabs.size(); ++t)
+      if (tabs[t].nf == d.nf && tabs[t].kk == d.kk && tabs[t].ntp == d.ntok_pad) found = (int)t;
+    if (found < 0) {
+      Tab t{d.nf, d.kk, d.ntok_pad, 0, 0};
+      t.tw = (int64_t)off;
+      off = align256(off + (size_t)3 * d.ppad * d.ntok_pad * 2);
+      t.trig = (int64_t)off;
+      off = align256(off + (size_t)d.nf * 16);
+      tabs.push_back(t);
+      d.tw_owner = 1;
+      found = (int)tabs.size() - 1;
+    }
+    d.tw_off = tabs[found].tw;
+    d.trig_off = tabs[found].trig;
+  }
+  for (int b = 0; b < n_chunks; ++b) {
+    desc[b].y_off = (int64_t)off;
+    off = align256(off + (size_t)L * 2 * desc[b].ppad * C * 4);
+  }
+  for (int b = 0; b < n_chunks; ++b) {
+    desc[b].e_off = (int64_t)off;
+    off = align256(off + (size_t)L * 2 * desc[b].n * 8);
+  }
+  const int64_t slot_bytes = (int64_t)align256(((size_t)max_p2 * max_p2 + 2 * (size_t)max_p2) * 8);
+  int64_t probs_max = (int64_t)std::min(n_chunks, kMaxChunksPerLaunch) * L * 2;
+  int64_t n_slots = std::min<int64_t>(probs_max, 1024);
+  const int64_t slot_budget = (int64_t)1 << 30;
+  while (n_slots > 1 && n_slots * slot_bytes > slot_budget) n_slots /= 2;
+  const int64_t slot_off = (int64_t)off;
+  off += (size_t)(n_slots * slot_bytes);
+  *bytes = align256(off);
+
+  if (launches) {
+    launches->clear();
+    for (int b0 = 0; b0 < n_chunks; b0 += kMaxChunksPerLaunch) {
+      ScoreLaunch sl{};
+      sl.n_chunks = std::min(kMaxChunksPerLaunch, n_chunks - b0);
+      sl.L = L; sl.H = H; sl.D = D; sl.C = C;
+      sl.total_tokens = tok;
+      sl.n_slots = (int32_t)n_slots;
+      sl.slot_p2 = max_p2;
+      sl.slot_off = slot_off;
+      sl.slot_bytes = slot_bytes;
+      sl.max_ppad = 0;
+      for (int i = 0; i < sl.n_chunks; ++i) {
+        sl.c[i] = desc[b0 + i];
+        sl.max_ppad = std::max(sl.max_ppad, sl.c[i].ppad);
+      }
+      launches->push_back(sl);
+    }
+  }
+  return CT_OK;
+}
+
+ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
+                    float* layer_score, hipStream_t stream) {
+  for (const ScoreLaunch& sl : launches) {
+    int max_elems = 0;
+    for (int i = 0; i < sl.n_chunks; ++i)
+      max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
+    dim3 gt((max_elems + 255) / 256 < 2048 ? (max_elems + 255) / 256 : 2048, sl.n_chunks);
+    hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
+    if (ct_status s = check_launch("twiddle")) return s;
+
+    dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
+    if (sl.dtype == CT_BF16)
+      hipLaunchKernelGGL(k_band_fwd<CT_BF16>, gb, dim3(256), 0, stream, sl, ws);
+    else
+      hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
+    if (ct_status s = check_launch("band projection")) return s;
+
+    int n_probs = sl.n_chunks * sl.L * 2;
+    int grid = std::min(n_probs, sl.n_slots);
+    hipLaunchKernelGGL(k_gram_eval, dim3(grid), dim3(256), 0, stream, sl, ws, n_probs);
+    if (ct_status s = check_launch("gram/eval")) return s;
+
+    hipLaunchKernelGGL(k_finalize, dim3(sl.n_chunks), dim3(kFinThreads), 0, stream, sl, ws, score,
+                       layer_score);
+    if (ct_status s = check_launch("finalize")) return s;
+  }
+  return CT_OK;
+}
+
+}  // namespace ct

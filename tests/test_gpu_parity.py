@@ -1,0 +1,275 @@
+"""GPU parity: every C-ABI call against the oracle on the same seeded inputs,
+at sizes the oracle finishes in seconds (several tiles, ragged tails), plus
+edge cases.  Tolerances: index sets bit-exact (outside a 1e-6 relative tie
+band around the k-th score when the GPU ranks its own scores); fp32 scores
+1e-4 relative; assembled V bit-exact and K within 1 ulp (>= 99.9% bit-exact);
+attention outputs 2e-2 absolute for the computation, plus half an ulp of the
+output's own storage rounding (a bf16 value in [16, 32) is only resolved to
+0.0625)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (check_index_sets, half_ulp_bf16, need_gpu, to_dev, to_host,
+                      ulp_distance_bf16, ulp_distance_f32, widen)
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20260600
+
+
+def _chunks(syn, ns, L, H, D, dtype, seed=SEED):
+    return [(syn.chunk(seed, syn.K, b, L, n, H, D, dtype), syn.chunk(seed, syn.V, b, L, n, H, D, dtype))
+            for b, n in enumerate(ns)]
+
+
+def _score_both(orc, syn, ns, L, H, D, dtype, alpha, mode=0, norm=0):
+    ct = need_gpu()
+    host = _chunks(syn, ns, L, H, D, dtype)
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    s_gpu, ls_gpu = ct.cachetune_score_chunk(dev, L, H, D, alpha=alpha, fftlen=mode, norm=norm,
+                                             want_layers=True)
+    torch.cuda.synchronize()
+    s_gpu, ls_gpu = to_host(s_gpu), to_host(ls_gpu)
+    s_orc, ls_orc = [], []
+    for k, v in host:
+        s, ls = orc.score_chunk(k, v, alpha[0], alpha[1], mode, norm, layers=True)
+        s_orc.append(s)
+        ls_orc.append(ls)
+    return s_gpu, ls_gpu, np.concatenate(s_orc), np.concatenate(ls_orc, axis=1)
+
+
+def _rel_close(got, want, rtol=1e-4, floor=0.0):
+    scale = np.maximum(np.abs(want), floor)
+    err = np.abs(got.astype(np.float64) - want)
+    bad = err > rtol * scale
+    assert not bad.any(), f"max rel err {np.max(err / np.maximum(scale, 1e-300))}"
+
+
+@pytest.mark.parametrize("ns,L,H,D,alpha", [
+    ([300, 512, 1000, 64], 2, 2, 64, (1, 16)),     # ragged tails, several 32-token steps
+    ([2048], 2, 8, 128, (1, 16)),                   # bench shapes, two layers
+    ([96, 257], 2, 1, 64, (1, 2)),                  # the paper's default alpha
+    ([130, 77], 1, 1, 64, (1, 1)),                  # alpha = 1: every bin (odd N, Nyquist)
+    ([600, 4096], 1, 1, 64, (1, 32)),               # 1/32 cutoff, shortest/longest lengths
+])
+def test_score_parity_bf16(orc, syn, ns, L, H, D, alpha):
+    s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
+    _rel_close(s_gpu, s_orc)
+    _rel_close(ls_gpu, ls_orc)
+
+
+def test_score_parity_fp32_single_chunk(orc, syn):
+    """The 1 x 512-token fp32 workload: L=1, 8 KV heads x 64."""
+    s_gpu, ls_gpu, s_orc, _ = _score_both(orc, syn, [512], 1, 8, 64, "f32", (1, 16))
+    _rel_close(s_gpu, s_orc)
+
+
+@pytest.mark.parametrize("mode", [1])
+def test_score_parity_zeropad(orc, syn, mode):
+    s_gpu, _, s_orc, _ = _score_both(orc, syn, [300, 700], 2, 1, 64, "bf16", (1, 16), mode=mode)
+    _rel_close(s_gpu, s_orc)
+
+
+@pytest.mark.parametrize("norm", [1, 2, 3])
+def test_score_parity_norm_modes(orc, syn, norm):
+    s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, [200, 333], 3, 1, 64, "bf16", (1, 8), norm=norm)
+    floor = 1e-3 if norm == 2 else 0.0
+    _rel_close(ls_gpu, ls_orc, floor=floor)
+    _rel_close(s_gpu, s_orc, floor=floor)
+
+
+def test_score_many_chunks_multiple_launches(orc, syn):
+    ns = [64 + 3 * i for i in range(40)]
+    s_gpu, _, s_orc, _ = _score_both(orc, syn, ns, 1, 1, 64, "bf16", (1, 16))
+    _rel_close(s_gpu, s_orc)
+
+
+def test_score_deterministic(syn):
+    ct = need_gpu()
+    host = _chunks(syn, [700, 1500], 2, 2, 64, "bf16")
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    a, _ = ct.cachetune_score_chunk(dev, 2, 2, 64)
+    b, _ = ct.cachetune_score_chunk(dev, 2, 2, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---- selection ---------------------------------------------------------------
+
+def _topr_exact(orc, scores_list, r):
+    ct = need_gpu()
+    ns = [len(s) for s in scores_list]
+    flat = np.concatenate(scores_list).astype(np.float32)
+    ks, ranking, sel, comp = ct.cachetune_select_topr(to_dev(flat), ns, r=r)
+    torch.cuda.synchronize()
+    ranking, sel, comp = to_host(ranking), to_host(sel), to_host(comp)
+    o = so = co = 0
+    for n, k, s in zip(ns, ks, scores_list):
+        assert k == orc.ksel(n, *r)
+        want_r, want_s, want_c = orc.topr(np.asarray(s, np.float32).astype(np.float64), k)
+        np.testing.assert_array_equal(ranking[o:o + n], want_r)
+        np.testing.assert_array_equal(sel[so:so + k], want_s)
+        np.testing.assert_array_equal(comp[co:co + n - k], want_c)
+        o, so, co = o + n, so + k, co + n - k
+
+
+def test_topr_exact_on_oracle_scores(orc, syn):
+    scores = []
+    for n in (512, 2048, 1000, 3):
+        k, v = _chunks(syn, [n], 1, 1, 64, "bf16", seed=n)[0]
+        scores.append(orc.score_chunk(k, v, 1, 16))
+    for r in ((15, 100), (5, 100), (30, 100), (0, 1), (1, 1)):
+        _topr_exact(orc, scores, r)
+
+
+def test_topr_ties_and_signed_zero(orc):
+    rng = np.random.default_rng(3)
+    a = np.round(rng.random(700) * 5) / 5          # many exact ties
+    b = np.zeros(64)
+    b[::3] = -0.0                                   # -0 equals +0
+    b[5] = 1.0
+    c = np.array([0.25])                            # single-token chunk
+    d = np.full(8192, 0.5)                          # maximum length, all equal
+    d[8191] = 0.75
+    _topr_exact(orc, [a, b, c, d], (15, 100))
+    _topr_exact(orc, [a, b, c, d], (1, 2))
+
+
+def test_topr_many_chunks(orc):
+    rng = np.random.default_rng(4)
+    scores = [rng.random(int(n)) for n in rng.integers(1, 300, 75)]
+    _topr_exact(orc, scores, (15, 100))
+
+
+@pytest.mark.parametrize("ns,L,H,D,alpha", [([512, 2048, 999], 2, 2, 64, (1, 16)),
+                                            ([2048], 3, 8, 128, (1, 16))])
+def test_index_sets_end_to_end(orc, syn, ns, L, H, D, alpha):
+    """GPU scores ranked on the GPU vs oracle scores ranked by the oracle."""
+    ct = need_gpu()
+    s_gpu, _, s_orc, _ = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
+    ks, _, sel, _ = ct.cachetune_select_topr(to_dev(s_gpu), ns, r=(15, 100))
+    torch.cuda.synchronize()
+    sel = to_host(sel)
+    o = so = 0
+    for n, k in zip(ns, ks):
+        _, want, _ = orc.topr(s_orc[o:o + n], k)
+        check_index_sets(sel[so:so + k], want, s_orc[o:o + n], k)
+        o, so = o + n, so + k
+
+
+# ---- assembly ------------------------------------------------------------------
+
+def _assembly_case(orc, syn, ns, H, D, dtype, theta, style, prefix, n_sfx, packed):
+    ct = need_gpu()
+    rng = np.random.default_rng(sum(ns) + D)
+    order = rng.permutation(len(ns)).astype(np.int32)
+    offs = orc.offsets(ns, order, prefix)
+    T = prefix + sum(ns) + n_sfx
+    edt = np.uint16 if dtype == "bf16" else np.float32
+    k_ref = np.zeros((T, H, D), edt)
+    v_ref = np.zeros((T, H, D), edt)
+    places, keep = [], []
+    for b, n in enumerate(ns):
+        ks = syn.rows(SEED, syn.K, b, 5, n, H, D, np.arange(n), dtype)
+        vs = syn.rows(SEED, syn.V, b, 5, n, H, D, np.arange(n), dtype)
+        k = orc.ksel(n, 15, 100)
+        sel = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
+        comp = np.setdiff1d(np.arange(n, dtype=np.int32), sel).astype(np.int32)
+        kr = syn.rows(SEED, syn.K, b, 5, n, H, D, sel, dtype, extra_sigma=0.25)
+        vr = syn.rows(SEED, syn.V, b, 5, n, H, D, sel, dtype, extra_sigma=0.25)
+        orc.assemble_chunk(ks, vs, kr, vr, sel, offs[b], theta, style, k_ref, v_ref)
+        if packed:  # staging buffer: reused rows in an arbitrary (here: reversed) order
+            src_rows = comp[::-1].copy()
+            d = dict(k_src=to_dev(ks[src_rows]), v_src=to_dev(vs[src_rows]), src_rows=to_dev(src_rows))
+        else:
+            d = dict(k_src=to_dev(ks), v_src=to_dev(vs), comp=to_dev(comp))
+        d.update(sel=to_dev(sel), k_rec=to_dev(kr) if k else None, v_rec=to_dev(vr) if k else None)
+        keep.append(d)
+        places.append(ct.make_place(n=n, k=k, offset=int(offs[b]), **d))
+    ksf = syn.rows(SEED, syn.K, syn.SUFFIX_CHUNK, 5, n_sfx, H, D, np.arange(n_sfx), dtype)
+    vsf = syn.rows(SEED, syn.V, syn.SUFFIX_CHUNK, 5, n_sfx, H, D, np.arange(n_sfx), dtype)
+    orc.assemble_rows(ksf, vsf, prefix + sum(ns), theta, style, k_ref, v_ref)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k_out = torch.zeros((T, H, D), dtype=dt, device="cuda")
+    v_out = torch.zeros((T, H, D), dtype=dt, device="cuda")
+    ct.cachetune_assemble_rope(places, k_out, v_out, H, D, theta, style,
+                               k_sfx=to_dev(ksf) if n_sfx else None,
+                               v_sfx=to_dev(vsf) if n_sfx else None,
+                               n_sfx=n_sfx, sfx_offset=prefix + sum(ns))
+    torch.cuda.synchronize()
+    kg, vg = to_host(k_out), to_host(v_out)
+    np.testing.assert_array_equal(vg, v_ref)
+    ulp = (ulp_distance_bf16 if dtype == "bf16" else ulp_distance_f32)(kg, k_ref)
+    assert ulp.max() <= 1
+    assert (ulp == 0).mean() >= 0.999
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("style", [0, 1])
+def test_assemble_parity_bf16(orc, syn, D, style):
+    _assembly_case(orc, syn, [300, 129, 512], 2, D, "bf16", 500000.0, style, prefix=17, n_sfx=33,
+                   packed=False)
+
+
+def test_assemble_parity_fp32_packed(orc, syn):
+    _assembly_case(orc, syn, [200, 71], 8, 64, "f32", 10000.0, 0, prefix=0, n_sfx=16, packed=True)
+
+
+def test_assemble_large_positions(orc, syn):
+    """Positions around 1.5e5 (128K-context offsets): fp64 angles keep K exact."""
+    _assembly_case(orc, syn, [256, 300], 1, 128, "bf16", 1000000.0, 0, prefix=150000, n_sfx=5,
+                   packed=True)
+
+
+def test_assemble_many_places(orc, syn):
+    _assembly_case(orc, syn, [20 + i for i in range(37)], 1, 64, "bf16", 500000.0, 0, prefix=3,
+                   n_sfx=0, packed=False)
+
+
+# ---- attention -------------------------------------------------------------------
+
+def _attn_case(orc, syn, T, H, Hq, D, n_q, dtype, theta, style, scale=None):
+    ct = need_gpu()
+    rng = np.random.default_rng(T + n_q + D)
+    k = syn.rows(SEED, syn.K, 0, 1, T, H, D, np.arange(T), dtype)
+    v = syn.rows(SEED, syn.V, 0, 1, T, H, D, np.arange(T), dtype)
+    if n_q:
+        qpos = np.sort(rng.choice(np.arange(1, T - 1), max(0, n_q - 2), replace=False))
+        qpos = np.concatenate([[0], qpos, [T - 1]])[:n_q].astype(np.int32)
+        qpos.sort()
+    else:
+        qpos = np.zeros(0, np.int32)
+    q = syn.rows(SEED, syn.Q, 0, 1, T, Hq, D, qpos, dtype)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    out, lse = ct.cachetune_recompute_attn(to_dev(q) if n_q else torch.zeros((0, Hq, D), device="cuda"),
+                                           to_dev(qpos) if n_q else torch.zeros(0, dtype=torch.int32, device="cuda"),
+                                           to_dev(k), to_dev(v), scale, theta, style, want_lse=True)
+    torch.cuda.synchronize()
+    if n_q == 0:
+        return
+    og, lg = widen(to_host(out)), to_host(lse).astype(np.float64)
+    ref, lref = orc.attention(q, qpos, k, v, scale, theta, style)
+    err = np.abs(og - ref)
+    tol = 2e-2 + (half_ulp_bf16(ref) if dtype == "bf16" else 0.0)
+    assert (err <= tol).all(), (err.max(), (err - tol).max())
+    assert np.abs(lg - lref).max() <= 2e-2 * np.maximum(1.0, np.abs(lref)).max()
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_parity_bf16(orc, syn, D):
+    _attn_case(orc, syn, 1100, 2, 8, D, 150, "bf16", 500000.0, 0)
+
+
+def test_attention_parity_fp32_mha(orc, syn):
+    """Group size 1 (8 query heads over 8 KV heads), fp32 storage, theta 1e4."""
+    _attn_case(orc, syn, 528, 8, 8, 64, 92, "f32", 10000.0, 0)
+
+
+@pytest.mark.parametrize("n_q", [0, 1, 33])
+def test_attention_edge_sizes(orc, syn, n_q):
+    _attn_case(orc, syn, 300, 1, 4, 128, n_q, "bf16", 500000.0, 1)
+
+
+def test_attention_group8_long(orc, syn):
+    _attn_case(orc, syn, 3000, 1, 8, 128, 70, "bf16", 500000.0, 0, scale=0.1)
