@@ -152,6 +152,9 @@ class Workload:
         self.k_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
         self.v_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
         self.out = torch.empty((self.n_q, Hq, D), dtype=tdt, device="cuda")
+        ws = ct.cachetune_recompute_attn_ws(self.n_q, Hq, self.T, H, D,
+                                            ct.CT_BF16 if self.dtype == "bf16" else ct.CT_F32)
+        self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
         self.comp_off, self.sel_off = [], []
         co = so = 0
         for b, n in enumerate(ns):
@@ -195,7 +198,7 @@ class Workload:
 
     def attend(self, l):
         self.ct.cachetune_recompute_attn(self.q[l], self.qpos, self.k_asm, self.v_asm, self.scale,
-                                         self.theta, out=self.out)
+                                         self.theta, out=self.out, ws=self.attn_ws)
 
     def step(self, ev=None):
         if ev is not None:

@@ -171,21 +171,33 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
 
 /* ---- selected-query causal attention (Sec. 4.1, App. B.2) ------------------
  *  q_pre: device [n_q][Hq][D] pre-RoPE queries of the selected and uncached rows
- *  q_pos: device int32[n_q] their global positions, each in [0, T)
+ *  q_pos: device int32[n_q] their global positions, each in [0, T); any order
+ *         (ascending order keeps the causal work of neighbouring rows alike)
  *  k, v:  device [T][H][D] assembled layer (keys already rotated)
  * Query head h uses KV head floor(h * H / Hq) (Hq % H == 0).  Each query is
  * rotated to its position, then attends to keys at positions <= its own:
- *   out = softmax(softmax_scale * q . k_t) . v_t   (fp32 accumulation; the
- * rotated query, the probabilities and fp32 inputs enter the matrix cores as
- * bf16).
+ *   out = softmax(softmax_scale * q . k_t) . v_t
+ * Arithmetic: fp32 accumulation on the matrix cores.  bf16 storage: the
+ * rotated, scaled query enters as a bf16 pair carrying 16 significant bits,
+ * probabilities and V as fp16 (V exact while |v| < 65536; otherwise that 64-key
+ * block takes V as bf16 and the probabilities as a bf16 pair).  fp32 storage:
+ * query, probabilities, K and V all enter as bf16 pairs.
  *  out: device [n_q][Hq][D] in `dtype`
  *  lse: device float[n_q][Hq] natural-log sum of exp of the scaled logits, or NULL.
+ *  ws/ws_bytes: device workspace of at least cachetune_recompute_attn_ws bytes
+ *         (may be NULL when that size is 0), 256-byte aligned; it holds the
+ *         partial results of rows whose keys are split over several segments.
  * D must be 64 or 128; n_q >= 0; T >= 1. */
 ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                    int32_t Hq, const void* k, const void* v, int32_t T,
                                    int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
                                    double rope_theta, ct_rope style, void* out, float* lse,
-                                   hipStream_t stream);
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace query for cachetune_recompute_attn with these shapes on the
+ * current device (the size depends on the device's compute-unit count). */
+ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
+                                      ct_dtype dtype, size_t* bytes);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ class CacheTuneError(RuntimeError):
 
 SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version",
            "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
-           "cachetune_assemble_rope", "cachetune_recompute_attn"]
+           "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws"]
 
 _lib = None
 
@@ -63,7 +63,8 @@ def lib():
         L.cachetune_assemble_rope.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, f64, i32,
                                               vp, vp, i32, vp]
         L.cachetune_recompute_attn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
-                                               f64, i32, vp, vp, vp]
+                                               f64, i32, vp, vp, vp, sz, vp]
+        L.cachetune_recompute_attn_ws.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -183,9 +184,16 @@ def cachetune_assemble_rope(places, k_out, v_out, H, D, rope_theta, style=CT_ROP
 
 # ---- attention ----------------------------------------------------------------
 
+def cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dtype=CT_BF16) -> int:
+    out = C.c_size_t(0)
+    _check(lib().cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dtype, C.byref(out)))
+    return out.value
+
+
 def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, style=CT_ROPE_HALF,
-                             out=None, lse=None, want_lse=False, stream=None):
-    """q_pre [n_q][Hq][D], q_pos int32 [n_q], k/v [T][H][D]; returns (out, lse)."""
+                             out=None, lse=None, want_lse=False, ws=None, stream=None):
+    """q_pre [n_q][Hq][D], q_pos int32 [n_q], k/v [T][H][D]; returns (out, lse).
+    ws: optional uint8 device tensor, allocated here when missing or too small."""
     import torch
     n_q, Hq, D = (int(x) for x in q_pre.shape)
     T, H = int(k.shape[0]), int(k.shape[1])
@@ -193,8 +201,12 @@ def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, styl
         out = torch.empty_like(q_pre)
     if want_lse and lse is None:
         lse = torch.empty((n_q, Hq), dtype=torch.float32, device=q_pre.device)
+    dt = _dtype(q_pre)
+    need = cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dt)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=q_pre.device)
     _check(lib().cachetune_recompute_attn(_ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T,
-                                          H, D, _dtype(q_pre), float(softmax_scale),
-                                          float(rope_theta), style, _ptr(out), _ptr(lse),
-                                          _stream(stream)))
+                                          H, D, dt, float(softmax_scale), float(rope_theta), style,
+                                          _ptr(out), _ptr(lse), _ptr(ws) if need else None,
+                                          ws.numel() if need else 0, _stream(stream)))
     return out, lse

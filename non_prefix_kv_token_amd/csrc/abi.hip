@@ -29,6 +29,14 @@ ct_status check_launch(const char* what) {
 
 static bool dtype_ok(int dt) { return dt == CT_F32 || dt == CT_BF16; }
 
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 static void fill_inv_freq(double* f, int D, double theta) {
   for (int j = 0; j < 64; ++j) f[j] = 0.0;
   for (int j = 0; j < D / 2; ++j) f[j] = std::pow(theta, -2.0 * (double)j / (double)D);
@@ -230,12 +238,10 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
   CT_GUARD_END
 }
 
-ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
-                                   int32_t Hq, const void* k, const void* v, int32_t T,
-                                   int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
-                                   double rope_theta, ct_rope style, void* out, float* lse,
-                                   hipStream_t stream) {
-  CT_GUARD_BEGIN
+static ct_status attn_args(const void* q_pre, const int32_t* q_pos, int32_t n_q, int32_t Hq,
+                           const void* k, const void* v, int32_t T, int32_t H, int32_t D,
+                           int32_t dtype, float softmax_scale, double rope_theta, int32_t style,
+                           void* out, float* lse, bool need_ptrs, AttnArgs* a) {
   if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
   if (D != 64 && D != 128) return fail(CT_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (H < 1 || Hq < 1 || Hq % H != 0) return fail(CT_E_INVALID, "need Hq % H == 0");
@@ -243,28 +249,57 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
   if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return fail(CT_E_INVALID, "rope_theta must be > 1");
   if (!std::isfinite(softmax_scale)) return fail(CT_E_INVALID, "softmax_scale must be finite");
   if (n_q < 0 || T < 1) return fail(CT_E_INVALID, "need n_q >= 0, T >= 1");
-  if (n_q > 0 && (!q_pre || !q_pos || !k || !v || !out)) return fail(CT_E_INVALID, "NULL argument");
-  if ((long long)(n_q + 31) / 32 * (Hq / H) > (long long)INT32_MAX / 4)
+  if (need_ptrs && n_q > 0 && (!q_pre || !q_pos || !k || !v || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if ((long long)(n_q + 31) / 32 * Hq > (long long)INT32_MAX / 64)
     return fail(CT_E_UNSUPPORTED, "too many query rows");
-  AttnArgs a{};
-  a.q = q_pre;
-  a.qpos = q_pos;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.lse = lse;
-  a.n_q = n_q;
-  a.Hq = Hq;
-  a.T = T;
-  a.H = H;
-  a.D = D;
-  a.dtype = dtype;
-  a.style = style;
-  a.group = Hq / H;
-  a.scale = softmax_scale;
-  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  fill_inv_freq(a.inv_freq, D, rope_theta);
-  return attn_run(a, stream);
+  *a = AttnArgs{};
+  a->q = q_pre;
+  a->qpos = q_pos;
+  a->k = k;
+  a->v = v;
+  a->out = out;
+  a->lse = lse;
+  a->n_q = n_q;
+  a->Hq = Hq;
+  a->T = T;
+  a->H = H;
+  a->D = D;
+  a->dtype = dtype;
+  a->style = style;
+  a->group = Hq / H;
+  a->scale = softmax_scale;
+  a->scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  fill_inv_freq(a->inv_freq, D, rope_theta);
+  attn_plan(a, device_cu_count());
+  return CT_OK;
+}
+
+ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
+                                      ct_dtype dtype, size_t* bytes) {
+  CT_GUARD_BEGIN
+  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  AttnArgs a;
+  if (ct_status s = attn_args(nullptr, nullptr, n_q, Hq, nullptr, nullptr, T, H, D, dtype, 1.f,
+                              10000.0, CT_ROPE_HALF, nullptr, nullptr, false, &a))
+    return s;
+  *bytes = attn_ws_bytes(a);
+  return CT_OK;
+  CT_GUARD_END
+}
+
+ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+                                   int32_t Hq, const void* k, const void* v, int32_t T,
+                                   int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
+                                   double rope_theta, ct_rope style, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  AttnArgs a;
+  if (ct_status s = attn_args(q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
+                              rope_theta, style, out, lse, true, &a))
+    return s;
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  return attn_run(a, ws, ws_bytes, stream);
   CT_GUARD_END
 }
 

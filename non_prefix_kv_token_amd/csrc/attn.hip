@@ -1,156 +1,278 @@
-// Selected-query causal GQA attention -- "Adaptive KV Cache Reuse for Fast
-// Long-Context LLM Serving" (CacheTune), Sec. 4.1 "Recomputing in the new
-// context" and App. B.2 (check layer: the selected positions' queries attend
-// over the complete assembled layer under the causal mask).
+// Selected-query causal GQA attention, bf16 storage -- "Adaptive KV Cache
+// Reuse for Fast Long-Context LLM Serving" (CacheTune), Sec. 4.1
+// "Recomputing in the new context" and App. B.2 (check layer: the selected
+// positions' queries attend over the complete assembled layer under the
+// causal mask).
 //
-// Flash-style kernel on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16),
-// computed transposed so that each query's softmax row lives in two lanes:
-//   S^T (keys x queries) = K . Q^T      A = K rows from LDS, B = Q (registers)
-//   O^T (dims x queries) += V^T . P^T   A = V^T from LDS,   B = P (registers)
-// A wave owns 32 query rows of one query head; a block has 4 waves that share
-// one KV head (grouped-query attention), so each 64-key K/V block staged in
-// LDS serves all of them.  Queries are rotated to their positions (fp64 angle
-// and sincos); softmax runs in fp32 with exp2.
-// Precision: one bf16 rounding of the rotated query or of the probabilities
-// moves the output by up to ~0.5 on inputs whose logits reach tens, so both
-// enter the matrix cores as a bf16 hi + lo pair (16 significant bits; two
-// MFMAs each).  fp32 K and V are split the same way (K_hi q_hi + K_hi q_lo +
-// K_lo q_hi, and likewise for V and P).
-// MFMA layouts (32x32x16): A lane -> row lane%32, k-group lane/32; B lane ->
-// col lane%32, k-group lane/32; D lane -> col lane%32, rows
-// 8*(v/4) + 4*(lane/32) + v%4.  The contraction index of a k-group only has
-// to agree between A and B, which lets P stay in the accumulator layout.
+// Flash-style kernel on the gfx950 matrix cores, computed transposed so that a
+// query's softmax row lives in the two lanes (lane, lane ^ 32) of one wave:
+//   S^T (keys x queries) = K . Q^T    A = K rows from LDS,   B = Q (registers)
+//   O^T (dims x queries) += V^T . P^T A = V^T from LDS,      B = P (registers)
+// MFMA layouts (32x32x16): A lane -> row lane%32, k-group lane/32 (8 values);
+// B lane -> col lane%32, k-group lane/32; D lane -> col lane%32, rows
+// 8*(v/4) + 4*(lane/32) + v%4.  The contraction index inside a k-group only has
+// to agree between A and B, which lets P stay in the accumulator layout: V^T is
+// written to LDS with its keys permuted so that each lane's 8 keys of a k-step
+// are contiguous (one 16-byte read).
+//
+// Work decomposition.  A block of 8 waves shares one KV head and one 64-key
+// K/V block in LDS (double-buffered, next block prefetched into registers
+// while the current one is consumed).  Each wave owns 32 query rows of one
+// query head of the group (grouped-query attention: the 4 query heads of a KV
+// head and 2 row tiles for a group of 4).  The causal key range of a block is
+// cut into segments of S keys (split-KV) so that long rows do not serialise
+// the launch; a row whose keys span several segments gets partial results
+// (normalised output and log2-sum-exp) that k_attn_merge combines.  Block ids
+// run fastest over the KV head, so each XCD (blocks are dealt round-robin over
+// the 8 XCDs) serves one KV head and its L2 holds the keys of the segment that
+// its CUs are working on.
+//
+// Precision.  Logits of these inputs reach the hundreds, so one bf16 rounding
+// of the rotated query would move outputs by O(1): the query (rotated in fp32
+// from an fp64-reduced angle, pre-multiplied by softmax_scale*log2(e)) enters
+// the matrix cores as a bf16 hi + lo pair (16 significant bits, two MFMAs).
+// Probabilities and V enter the PV product as fp16 (11 bits): bf16 V converts
+// to fp16 exactly whenever |v| < 65536 (values below 2^-14 land on the fp16
+// subnormal grid, an absolute change below 2^-25).  A 64-key block holding a
+// larger or non-finite V falls back to bf16 V with P as a bf16 hi + lo pair.
+// Softmax runs in fp32 with exp2; the running maximum is only raised when a
+// block's maximum exceeds it by more than 8 (log2 units), so probabilities stay
+// below 2^8 and most blocks skip the accumulator rescale.
+#include <climits>
+
 #include "ct_internal.h"
 
 namespace ct {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;   // keys per block
-constexpr int VTS = 68;  // V^T row stride (bf16): 136 B keeps 8-byte reads conflict-free
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int BK = 64;              // keys per LDS block
+constexpr int VTS = BK + 8;         // V^T row stride (16-bit elements): 144 B
+constexpr float kLazyThr = 8.f;     // running-max slack before a rescale (log2 units)
 
 __device__ inline uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ inline uint16_t bf16_from_f64(double d) {
-  float f = __double2float_rz(d);
-  uint32_t u = __float_as_uint(f);
-  if ((double)f != d) u |= 1u;
-  return (uint16_t)bf16_bits_rne(__uint_as_float(u));
+__device__ inline float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline uint32_t pack_f16(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-template <int DT>
-__device__ inline double ld_q(const void* p, size_t i) {
-  if constexpr (DT == CT_F32) return (double)reinterpret_cast<const float*>(p)[i];
-  else return (double)__uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+// sin and cos of pos * f in fp64 without branches: Cody-Waite reduction by
+// quarter turns (pi/2 split into two doubles), then Taylor polynomials on
+// |r| <= pi/4 (sin to degree 13, cos to degree 14: truncation below 1e-14).
+__device__ inline void rope_sincos(int pos, double f, float* s, float* c) {
+  const double ang = (double)pos * f;
+  const double q = rint(ang * 0.6366197723675814);
+  double r = fma(-q, 1.5707963267948966, ang);
+  r = fma(-q, 6.123233995736766e-17, r);
+  const double r2 = r * r;
+  double ps = 1.6059043836821613e-10;              // 1/13!
+  ps = fma(ps, r2, -2.505210838544172e-08);        // -1/11!
+  ps = fma(ps, r2, 2.7557319223985893e-06);        // 1/9!
+  ps = fma(ps, r2, -1.984126984126984e-04);        // -1/7!
+  ps = fma(ps, r2, 8.333333333333333e-03);         // 1/5!
+  ps = fma(ps, r2, -1.6666666666666666e-01);       // -1/3!
+  const double sr = fma(ps * r2, r, r);
+  double pc = -1.1470745597729725e-11;             // -1/14!
+  pc = fma(pc, r2, 2.08767569878681e-09);          // 1/12!
+  pc = fma(pc, r2, -2.755731922398589e-07);        // -1/10!
+  pc = fma(pc, r2, 2.48015873015873e-05);          // 1/8!
+  pc = fma(pc, r2, -1.388888888888889e-03);        // -1/6!
+  pc = fma(pc, r2, 4.1666666666666664e-02);        // 1/4!
+  pc = fma(pc, r2, -0.5);
+  const double cr = fma(pc, r2, 1.0);
+  const int quad = (int)((long long)q & 3);
+  const double sv = (quad & 1) ? cr : sr, cv = (quad & 1) ? sr : cr;
+  *s = (float)((quad & 2) ? -sv : sv);
+  *c = (float)((quad == 1 || quad == 2) ? -cv : cv);
 }
 
-// 8 consecutive elements as packed bf16 (hi); fp32 inputs also give the bf16
-// residual (lo), so that hi + lo carries 16 significant bits.
-template <int DT>
-__device__ inline void ld8_split(const void* base, size_t i, u32x4_t* hi, u32x4_t* lo) {
-  if constexpr (DT == CT_BF16) {
-    *hi = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + i);
-  } else {
-    const float4* f = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
-    float4 a = f[0], b = f[1];
-    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      uint32_t h0 = bf16_bits_rne(x[2 * h]), h1 = bf16_bits_rne(x[2 * h + 1]);
-      float r0 = x[2 * h] - __uint_as_float(h0 << 16), r1 = x[2 * h + 1] - __uint_as_float(h1 << 16);
-      (*hi)[h] = h0 | (h1 << 16);
-      (*lo)[h] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
-    }
-  }
+// Column of key u (0..63) in the permuted V^T layout: inside each group of 16
+// keys, keys {4h+i, 8+4h+i} (h = 0, 1; i < 4) go to columns 8h+i and 8h+4+i.
+__device__ inline int vt_col(int u) {
+  int w = u & 15;
+  return (u & ~15) + 8 * ((w & 7) >> 2) + (w & 3) + 4 * (w >> 3);
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  constexpr int KS = D + 8;        // K row stride (bf16): 16-byte reads conflict-free
-  constexpr int NS = D / 16;       // k-steps over the head dimension
-  constexpr int NDT = D / 32;      // output tiles over the head dimension
-  constexpr int NPL = DT == CT_F32 ? 2 : 1;  // bf16 planes of K and V in LDS
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NPL][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[NPL][D * VTS];
-  __shared__ int wmax[4];
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
+  constexpr int KS = D + 8;          // K row stride (bf16): 16-byte reads conflict-free
+  constexpr int NS = D / 16;         // k-steps over the head dimension
+  constexpr int NDT = D / 32;        // output tiles over the head dimension
+  constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  constexpr int KIT = BK * KCH / kThreads;  // K chunks staged per thread
+  constexpr int DPG = D / 16;        // V dims per thread (2 keys x DPG dims)
+  static_assert(KIT >= 1 && BK * KCH == KIT * kThreads, "K staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vh[2][D * VTS];  // V^T, fp16
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[2][D * VTS];  // V^T, bf16
+  __shared__ int s_wide[2][kWaves];  // wave saw a V outside the fp16 range
+  __shared__ int s_wmax[kWaves];
 
+  const int H = a.H, G = a.group, T = a.T, Hq = a.Hq, S = a.seg_keys;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, col = lane & 31;
-  const int G = a.group, H = a.H, Hq = a.Hq, T = a.T;
-  const int kvh = blockIdx.y;
-  const int ntiles = (a.n_q + 31) / 32;
-  const int n_units = ntiles * G;
-  const int wg = gridDim.x - 1 - blockIdx.x;  // latest (longest) rows first
-  const int unit = wg * 4 + wave;
-  const bool active = unit < n_units;
-  const int tile = active ? unit / G : 0;
-  const int hq = kvh * G + (active ? unit % G : 0);
+
+  // ---- block -> (KV head, segment, tile group, head chunk)
+  const int kvh = blockIdx.x % H;
+  const int rest = blockIdx.x / H;
+  const int per_seg = a.n_tg * a.n_hc;
+  const int seg = rest / per_seg;
+  const int u_ = rest % per_seg;
+  const int tg = a.n_tg - 1 - u_ / a.n_hc;  // latest rows first inside a segment
+  const int hc = u_ % a.n_hc;
+  const int wt = wave / a.hpb, wh = wave % a.hpb;
+  const int tile = tg * a.tpb + wt;
+  const int hig = hc * a.hpb + wh;  // head inside the group
+  const bool wave_on = wt < a.tpb && hig < G && tile * 32 < a.n_q;
+  const int hq = kvh * G + hig;
   const int row = tile * 32 + col;
-  const bool valid = active && row < a.n_q;
-  const int pos = valid ? a.qpos[row] : -1;
+  const bool valid = wave_on && row < a.n_q;
+  const int pos = valid ? min(a.qpos[row], T - 1) : -1;
 
-  // key range of the block: up to its largest query position
-  int mx = pos;
+  int wmax = pos, wmin = valid ? pos : INT_MAX;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-  if (lane == 0) wmax[wave] = mx;
+  for (int o = 32; o > 0; o >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, o));
+    wmin = min(wmin, __shfl_xor(wmin, o));
+  }
+  if (lane == 0) s_wmax[wave] = wmax;
   __syncthreads();
-  int bmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  bmax = min(bmax, T - 1);
-  const int nkb = bmax < 0 ? 0 : bmax / BK + 1;
+  int bmax = -1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) bmax = max(bmax, s_wmax[w]);
+  const int nkeys = bmax + 1;
+  const int seg_lo = seg * S;
+  if (seg_lo >= nkeys) return;  // uniform over the block
+  const int seg_hi = min(seg_lo + S, nkeys);
+  const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
-  // Rotated query as bf16 hi + lo fragments (B operand): d = 16*s + 8*g + t.
+  // ---- rotated, scaled query as bf16 hi + lo (B operand): d = 16*s + 8*g + t
   u32x4_t qh[NS], ql[NS];
-  {
-    const size_t qb = ((size_t)row * Hq + hq) * D;
-    const double fpos = (double)max(pos, 0);
-    auto put = [&](int s, int t, double y) {
-      uint32_t hi = bf16_from_f64(y);
-      double r = y - (double)__uint_as_float(hi << 16);
-      uint32_t lo = bf16_from_f64(r);
-      int w = t >> 1, sh = 16 * (t & 1);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { qh[s][w] = 0u; ql[s][w] = 0u; }
+  if (valid) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * Hq + hq) * D;
+    const float c = a.scale_log2;
+    auto put = [&](int s, int t, float y) {
+      uint32_t hi = bf16_bits_rne(y);
+      uint32_t lo = bf16_bits_rne(y - __uint_as_float(hi << 16));
+      const int w = t >> 1, sh = 16 * (t & 1);
       qh[s][w] |= hi << sh;
       ql[s][w] |= lo << sh;
     };
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) { qh[s][w] = 0u; ql[s][w] = 0u; }
     if (a.style == CT_ROPE_HALF) {
 #pragma unroll
-      for (int s = 0; s < NS / 2; ++s)
+      for (int s = 0; s < NS / 2; ++s) {
+        const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 16 * s + 8 * g);
+        const u32x4_t y4 = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + 16 * s + 8 * g);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int j = 16 * s + 8 * g + t;  // pair (j, j + D/2): steps s and s + NS/2
-          double u = valid ? ld_q<DT>(a.q, qb + j) : 0.0;
-          double w = valid ? ld_q<DT>(a.q, qb + j + D / 2) : 0.0;
-          double sn, cs;
-          sincos(fpos * a.inv_freq[j], &sn, &cs);
-          put(s, t, u * cs - w * sn);
-          put(s + NS / 2, t, u * sn + w * cs);
+          const float x = (t & 1) ? bf16_hi_to_f32(x4[t >> 1]) : bf16_lo_to_f32(x4[t >> 1]);
+          const float y = (t & 1) ? bf16_hi_to_f32(y4[t >> 1]) : bf16_lo_to_f32(y4[t >> 1]);
+          float sn, cs;
+          rope_sincos(pos, a.inv_freq[j], &sn, &cs);
+          put(s, t, (x * cs - y * sn) * c);
+          put(s + NS / 2, t, (x * sn + y * cs) * c);
         }
+      }
     } else {
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s) {
+        const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 16 * s + 8 * g);
 #pragma unroll
         for (int t = 0; t < 8; t += 2) {
           const int d = 16 * s + 8 * g + t;  // pair (d, d + 1), frequency index d/2
-          double u = valid ? ld_q<DT>(a.q, qb + d) : 0.0;
-          double w = valid ? ld_q<DT>(a.q, qb + d + 1) : 0.0;
-          double sn, cs;
-          sincos(fpos * a.inv_freq[d / 2], &sn, &cs);
-          put(s, t, u * cs - w * sn);
-          put(s, t + 1, u * sn + w * cs);
+          const float x = bf16_lo_to_f32(x4[t >> 1]);
+          const float y = bf16_hi_to_f32(x4[t >> 1]);
+          float sn, cs;
+          rope_sincos(pos, a.inv_freq[d / 2], &sn, &cs);
+          put(s, t, (x * cs - y * sn) * c);
+          put(s, t + 1, (x * sn + y * cs) * c);
         }
+      }
     }
   }
+
+  // ---- staging: K rows as 16-byte chunks; V as 2 keys x DPG dims per thread
+  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v);
+  const int kp = tid & 31, dg = tid >> 5;  // V: key pair, dim group
+  u32x4_t kreg[KIT];
+  uint32_t vreg[2][DPG / 2];
+
+  auto load = [&](int kb) {
+    const int k0 = kb * BK;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int item = tid + it * kThreads;
+      const int key = k0 + item / KCH, ch = item % KCH;
+      kreg[it] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (key < T) kreg[it] = *reinterpret_cast<const u32x4_t*>(Kg + ((size_t)key * H + kvh) * D + 8 * ch);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = k0 + 2 * kp + e;
+      const uint16_t* src = Vg + ((size_t)key * H + kvh) * D + dg * DPG;
+      if constexpr (DPG == 8) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (key < T) w = *reinterpret_cast<const u32x4_t*>(src);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vreg[e][i] = w[i];
+      } else {
+        u32x2_t w = {0u, 0u};
+        if (key < T) w = *reinterpret_cast<const u32x2_t*>(src);
+        vreg[e][0] = w[0];
+        vreg[e][1] = w[1];
+      }
+    }
+  };
+
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int item = tid + it * kThreads;
+      *reinterpret_cast<u32x4_t*>(&Ks[buf][(item / KCH) * KS + 8 * (item % KCH)]) = kreg[it];
+    }
+    const int cpos = vt_col(2 * kp);
+    uint32_t wide = 0u;
+#pragma unroll
+    for (int i = 0; i < DPG / 2; ++i) {
+      const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];  // dims 2i, 2i+1 of keys 2kp, 2kp+1
+      wide = max(wide, max(w0 & 0x7fffu, (w0 >> 16) & 0x7fffu));
+      wide = max(wide, max(w1 & 0x7fffu, (w1 >> 16) & 0x7fffu));
+      const int d0 = dg * DPG + 2 * i;
+      const uint32_t blo = (w0 & 0xffffu) | (w1 << 16);          // dim d0, keys (2kp, 2kp+1)
+      const uint32_t bhi = (w0 >> 16) | (w1 & 0xffff0000u);      // dim d0 + 1
+      *reinterpret_cast<uint32_t*>(&Vb[buf][d0 * VTS + cpos]) = blo;
+      *reinterpret_cast<uint32_t*>(&Vb[buf][(d0 + 1) * VTS + cpos]) = bhi;
+      *reinterpret_cast<uint32_t*>(&Vh[buf][d0 * VTS + cpos]) =
+          pack_f16(bf16_lo_to_f32(w0), bf16_lo_to_f32(w1));
+      *reinterpret_cast<uint32_t*>(&Vh[buf][(d0 + 1) * VTS + cpos]) =
+          pack_f16(bf16_hi_to_f32(w0), bf16_hi_to_f32(w1));
+    }
+    // 0x4780 is 65536 in bf16: the first magnitude fp16 cannot hold
+    const int any_wide = __any(wide >= 0x4780u);
+    if (lane == 0) s_wide[buf][wave] = any_wide;
+  };
 
   f32x16_t o[NDT];
 #pragma unroll
@@ -158,161 +280,254 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * BK;
-    __syncthreads();
-    // K block -> Ks[plane][key][d]
-    for (int item = tid; item < BK * (D / 8); item += 256) {
-      int key = item / (D / 8), c = item % (D / 8);
-      u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (k0 + key < T) ld8_split<DT>(a.k, ((size_t)(k0 + key) * H + kvh) * D + 8 * c, &hi, &lo);
-      *reinterpret_cast<u32x4_t*>(&Ks[0][key * KS + 8 * c]) = hi;
-      if constexpr (NPL == 2) *reinterpret_cast<u32x4_t*>(&Ks[NPL - 1][key * KS + 8 * c]) = lo;
-    }
-    // V block -> Vt[plane][d][key], two keys packed per 32-bit store
-    for (int item = tid; item < (BK / 2) * (D / 8); item += 256) {
-      int pr = item / (D / 8), c = item % (D / 8);
-      int key0 = k0 + 2 * pr;
-      u32x4_t h0 = {0u, 0u, 0u, 0u}, l0 = h0, h1 = h0, l1 = h0;
-      if (key0 < T) ld8_split<DT>(a.v, ((size_t)key0 * H + kvh) * D + 8 * c, &h0, &l0);
-      if (key0 + 1 < T) ld8_split<DT>(a.v, ((size_t)(key0 + 1) * H + kvh) * D + 8 * c, &h1, &l1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        uint32_t x0 = (h0[e >> 1] >> sh) & 0xffffu, x1 = (h1[e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(&Vt[0][(8 * c + e) * VTS + 2 * pr]) = x0 | (x1 << 16);
-        if constexpr (NPL == 2) {
-          uint32_t y0 = (l0[e >> 1] >> sh) & 0xffffu, y1 = (l1[e >> 1] >> sh) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(&Vt[NPL - 1][(8 * c + e) * VTS + 2 * pr]) = y0 | (y1 << 16);
-        }
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-
-    // S^T = K . Q^T for 64 keys (two 32-key tiles)
-    f32x16_t st[2];
+  // one 64-key block: S^T = K . Q^T, causal mask, online softmax (P in st)
+  auto scores = [&](int cur, int k0, f32x16_t* st) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[kt][v] = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int ofs = (kt * 32 + col) * KS + 16 * s + 8 * g;
-        bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&Ks[0][ofs]);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&Ks[cur][(kt * 32 + col) * KS + 16 * s + 8 * g]);
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8_t, qh[s]), st[kt], 0, 0, 0);
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8_t, ql[s]), st[kt], 0, 0, 0);
-        if constexpr (NPL == 2) {
-          bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&Ks[NPL - 1][ofs]);
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, __builtin_bit_cast(bf16x8_t, qh[s]), st[kt], 0, 0, 0);
-        }
       }
     }
-    // scale, causal mask, block max
+    // causal mask, only where the block reaches past the wave's first row
+    if (k0 + BK - 1 > wmin) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (key > pos) st[kt][v] = -INFINITY;
+        }
+    }
     float bm = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        float z = key <= pos ? st[kt][v] * sl2 : -INFINITY;
-        st[kt][v] = z;
-        bm = fmaxf(bm, z);
-      }
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      for (int v = 0; v < 16; ++v) bm = fmaxf(bm, st[kt][v]);
+    if (__any(bm > m_run + kLazyThr)) {
+      const float m_new = fmaxf(m_run, fmaxf(bm, __shfl_xor(bm, 32)));
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mu = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float p = st[kt][v] == -INFINITY ? 0.f : exp2f(st[kt][v] - m_new);
+        const float p = __builtin_amdgcn_exp2f(st[kt][v] - mu);
         st[kt][v] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    l_run += rs;
+  };
+
+  // Main pass: P and V^T as fp16.  A block whose V does not fit fp16 stops
+  // it; the segment is then redone below with bf16 V and P as a bf16 pair.
+  bool redo = false;
+  load(kb0);
+  store(0);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int cur = (kb - kb0) & 1;
+    const bool more = kb + 1 < kb1;
+    if (more) load(kb + 1);
+    __syncthreads();
+    const int* fl = s_wide[cur];
+    if ((fl[0] | fl[1] | fl[2] | fl[3] | fl[4] | fl[5] | fl[6] | fl[7]) != 0) {
+      redo = true;  // same decision in every wave of the block
+      break;
+    }
+    const int k0 = kb * BK;
+    if (wave_on && k0 <= wmax) {
+      f32x16_t st[2];
+      scores(cur, k0, st);
+      // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4_t pw;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) pw[h] = pack_f16(st[kt][8 * h2 + 2 * h], st[kt][8 * h2 + 2 * h + 1]);
+          const f16x8_t pf = __builtin_bit_cast(f16x8_t, pw);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
+                &Vh[cur][(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, o[dt], 0, 0, 0);
+          }
+        }
+    }
+    if (more) store(cur ^ 1);
+  }
+
+  if (redo) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-
-    // O^T += V^T . P^T ; k-step (kt, h2): keys kt*32 + 16*h2 + 4*g + {0..3, 8..11}
+      for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    for (int kb = kb0; kb < kb1; ++kb) {
+      __syncthreads();  // previous readers of buffer 0 are done
+      load(kb);
+      store(0);
+      __syncthreads();
+      const int k0 = kb * BK;
+      if (wave_on && k0 <= wmax) {
+        f32x16_t st[2];
+        scores(0, k0, st);
+#pragma unroll 1
+        for (int ks = 0; ks < 4; ++ks) {
+          const int kt = ks >> 1, h2 = ks & 1;
+          u32x4_t ph, pl;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+          for (int h = 0; h < 4; ++h) {
+            const float p0 = st[kt][8 * h2 + 2 * h], p1 = st[kt][8 * h2 + 2 * h + 1];
+            const uint32_t a0 = bf16_bits_rne(p0), a1 = bf16_bits_rne(p1);
+            ph[h] = a0 | (a1 << 16);
+            pl[h] = bf16_bits_rne(p0 - __uint_as_float(a0 << 16)) |
+                    (bf16_bits_rne(p1 - __uint_as_float(a1 << 16)) << 16);
+          }
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4_t ph, pl;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          float p0 = st[kt][8 * h2 + 2 * h], p1 = st[kt][8 * h2 + 2 * h + 1];
-          uint32_t a0 = bf16_bits_rne(p0), a1 = bf16_bits_rne(p1);
-          float r0 = p0 - __uint_as_float(a0 << 16), r1 = p1 - __uint_as_float(a1 << 16);
-          ph[h] = a0 | (a1 << 16);
-          pl[h] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
-        }
-        const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, ph);
-        const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, pl);
-        const int kofs = kt * 32 + 16 * h2 + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int ofs = (dt * 32 + col) * VTS + kofs;
-          u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&Vt[0][ofs]);
-          u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&Vt[0][ofs + 8]);
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo[0], lo[1], hi[0], hi[1]});
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pfh, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pfl, o[dt], 0, 0, 0);
-          if constexpr (NPL == 2) {
-            u32x2_t lo2 = *reinterpret_cast<const u32x2_t*>(&Vt[NPL - 1][ofs]);
-            u32x2_t hi2 = *reinterpret_cast<const u32x2_t*>(&Vt[NPL - 1][ofs + 8]);
-            const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo2[0], lo2[1], hi2[0], hi2[1]});
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, pfh, o[dt], 0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
+                &Vb[0][(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, ph), o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, pl), o[dt], 0, 0, 0);
           }
         }
       }
+    }
   }
 
-  if (!valid) return;
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-  const size_t obase = ((size_t)row * Hq + hq) * D;
+  if (!wave_on) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!valid || pos < seg_lo) return;
+  const float inv_l = 1.f / l_tot;
+  const float lse2 = m_run + __log2f(l_tot);
+  if (seg == 0 && pos < S) {  // every key of this row lies in segment 0
+    const size_t obase = ((size_t)row * Hq + hq) * D;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      int d0 = dt * 32 + 8 * v4 + 4 * g;
-      float r0 = o[dt][4 * v4] * inv_l, r1 = o[dt][4 * v4 + 1] * inv_l;
-      float r2 = o[dt][4 * v4 + 2] * inv_l, r3 = o[dt][4 * v4 + 3] * inv_l;
-      if constexpr (DT == CT_BF16) {
-        u32x2_t w = {bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16), bf16_bits_rne(r2) | (bf16_bits_rne(r3) << 16)};
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = dt * 32 + 8 * v4 + 4 * g;
+        u32x2_t w = {bf16_bits_rne(o[dt][4 * v4] * inv_l) | (bf16_bits_rne(o[dt][4 * v4 + 1] * inv_l) << 16),
+                     bf16_bits_rne(o[dt][4 * v4 + 2] * inv_l) | (bf16_bits_rne(o[dt][4 * v4 + 3] * inv_l) << 16)};
         *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + obase + d0) = w;
-      } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + obase + d0) = make_float4(r0, r1, r2, r3);
       }
-    }
-  if (a.lse && g == 0)
-    a.lse[(size_t)row * Hq + hq] = l_run > 0.f ? 0.6931471805599453f * (m_run + log2f(l_run)) : -INFINITY;
+    if (a.lse && g == 0) a.lse[(size_t)row * Hq + hq] = 0.6931471805599453f * lse2;
+  } else {
+    const size_t pb = (((size_t)seg * a.n_q + row) * Hq + hq);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = dt * 32 + 8 * v4 + 4 * g;
+        *reinterpret_cast<float4*>(a.part_o + pb * D + d0) =
+            make_float4(o[dt][4 * v4] * inv_l, o[dt][4 * v4 + 1] * inv_l, o[dt][4 * v4 + 2] * inv_l,
+                        o[dt][4 * v4 + 3] * inv_l);
+      }
+    if (g == 0) a.part_lse[pb] = lse2;
+  }
 }
 
-template <int DT, int D>
+// Combine the per-segment results of rows whose keys span several segments:
+// out = sum_s 2^(lse2_s - M) o_s / sum_s 2^(lse2_s - M).  One wave per
+// (row, query head); rows in segment 0 only were written by k_attn_bf16.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int PER = D / 64;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (w >= a.n_q * a.Hq) return;
+  const int row = w / a.Hq, hq = w % a.Hq;
+  const int pos = min(a.qpos[row], a.T - 1);
+  const int S = a.seg_keys;
+  if (pos < S) return;
+  const int ns = pos / S + 1;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[((size_t)s * a.n_q + row) * a.Hq + hq]);
+  float wsum = 0.f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const size_t pb = ((size_t)s * a.n_q + row) * a.Hq + hq;
+    const float wgt = __builtin_amdgcn_exp2f(a.part_lse[pb] - M);
+    wsum += wgt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += wgt * a.part_o[pb * D + lane * PER + i];
+  }
+  const float inv = 1.f / wsum;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.Hq + hq) * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[i] = (uint16_t)bf16_bits_rne(acc[i] * inv);
+  if (a.lse && lane == 0) a.lse[(size_t)row * a.Hq + hq] = 0.6931471805599453f * (M + __log2f(wsum));
+}
+
+template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
-  const int ntiles = (a.n_q + 31) / 32;
-  const int units = ntiles * a.group;
-  dim3 grid((units + 3) / 4, a.H);
-  hipLaunchKernelGGL((k_attn<DT, D>), grid, dim3(256), 0, stream, a);
-  return check_launch("attention");
+  const int blocks = a.H * a.n_tg * a.n_hc * a.nseg;
+  hipLaunchKernelGGL((k_attn_bf16<D>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  if (ct_status s = check_launch("attention")) return s;
+  if (a.nseg > 1) {
+    const long long waves = (long long)a.n_q * a.Hq;
+    hipLaunchKernelGGL((k_attn_merge<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    if (ct_status s = check_launch("attention merge")) return s;
+  }
+  return CT_OK;
 }
 
 }  // namespace
 
-ct_status attn_run(const AttnArgs& a, hipStream_t stream) {
+void attn_plan(AttnArgs* a, int n_cu) {
+  const int G = a->group;
+  a->hpb = G < kWaves ? G : kWaves;
+  a->tpb = kWaves / a->hpb;
+  a->n_hc = (G + a->hpb - 1) / a->hpb;
+  const int ntiles = (a->n_q + 31) / 32;
+  a->n_tg = (ntiles + a->tpb - 1) / a->tpb;
+  // Segment length: the causal triangle (about units * T / 2 keys of block
+  // work) spread over four blocks per CU, at least 1024 keys, a multiple of
+  // the LDS block.
+  const long long units = (long long)a->H * a->n_tg * a->n_hc;
+  long long s = units * (long long)a->T / (2LL * 4 * (n_cu > 0 ? n_cu : 256));
+  if (const char* env = getenv("CACHETUNE_ATTN_SEG")) s = atoll(env);
+  if (s < 1024) s = 1024;
+  s = (s + BK - 1) / BK * BK;
+  if (s > a->T) s = (a->T + BK - 1) / BK * BK;
+  a->seg_keys = (int32_t)s;
+  a->nseg = (a->T + a->seg_keys - 1) / a->seg_keys;
+}
+
+size_t attn_ws_bytes(const AttnArgs& a) {
+  if (a.dtype != CT_BF16 || a.nseg <= 1) return 0;
+  const size_t rows = (size_t)a.nseg * a.n_q * a.Hq;
+  return align256(rows * a.D * 4) + align256(rows * 4);
+}
+
+ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return CT_OK;
-  if (a.dtype == CT_BF16)
-    return a.D == 128 ? launch<CT_BF16, 128>(a, stream) : launch<CT_BF16, 64>(a, stream);
-  return a.D == 128 ? launch<CT_F32, 128>(a, stream) : launch<CT_F32, 64>(a, stream);
+  if (a.dtype == CT_F32) return attn_f32_run(a, stream);
+  const size_t need = attn_ws_bytes(a);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
+    const size_t rows = (size_t)a.nseg * a.n_q * a.Hq;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(rows * a.D * 4));
+  }
+  return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
 }
 
 }  // namespace ct

@@ -111,7 +111,19 @@ struct AttnArgs {
   float scale_log2;  // softmax_scale * log2(e)
   float scale;
   double inv_freq[64];
+  // bf16 path: launch plan (attn_plan) and split-KV partials in the workspace
+  int32_t seg_keys;  // keys per segment (multiple of 64)
+  int32_t nseg;      // segments covering [0, T)
+  int32_t hpb, tpb;  // query heads and 32-row tiles per block (hpb * tpb <= 8)
+  int32_t n_hc;      // head chunks per group
+  int32_t n_tg;      // tile groups
+  float* part_o;     // [nseg][n_q][Hq][D] normalised partial outputs
+  float* part_lse;   // [nseg][n_q][Hq] log2-sum-exp of the partials
 };
-ct_status attn_run(const AttnArgs& a, hipStream_t stream);
+void attn_plan(AttnArgs* a, int n_cu);
+size_t attn_ws_bytes(const AttnArgs& a);
+ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream);
+ct_status attn_f32_run(const AttnArgs& a, hipStream_t stream);
+int device_cu_count();
 
 }  // namespace ct

@@ -229,11 +229,15 @@ def test_assemble_many_places(orc, syn):
 
 # ---- attention -------------------------------------------------------------------
 
-def _attn_case(orc, syn, T, H, Hq, D, n_q, dtype, theta, style, scale=None):
+def _attn_case(orc, syn, T, H, Hq, D, n_q, dtype, theta, style, scale=None, v_mul=None):
     ct = need_gpu()
     rng = np.random.default_rng(T + n_q + D)
     k = syn.rows(SEED, syn.K, 0, 1, T, H, D, np.arange(T), dtype)
     v = syn.rows(SEED, syn.V, 0, 1, T, H, D, np.arange(T), dtype)
+    if v_mul is not None:  # scale some rows of V by a power of two (exact in bf16)
+        rows_, mul = v_mul
+        v = v.copy()
+        v[rows_] = (v[rows_].astype(np.uint32) + (int(np.log2(mul)) << 7)).astype(np.uint16)
     if n_q:
         qpos = np.sort(rng.choice(np.arange(1, T - 1), max(0, n_q - 2), replace=False))
         qpos = np.concatenate([[0], qpos, [T - 1]])[:n_q].astype(np.int32)
@@ -252,6 +256,12 @@ def _attn_case(orc, syn, T, H, Hq, D, n_q, dtype, theta, style, scale=None):
     ref, lref = orc.attention(q, qpos, k, v, scale, theta, style)
     err = np.abs(og - ref)
     tol = 2e-2 + (half_ulp_bf16(ref) if dtype == "bf16" else 0.0)
+    if v_mul is not None:
+        # Huge V rows can cancel: the output's rounding then scales with
+        # sum_t p_t |v_t| (the oracle run on |V|), not with the output itself.
+        absv = (v & 0x7FFF) if dtype == "bf16" else np.abs(v)
+        ref_abs, _ = orc.attention(q, qpos, k, absv, scale, theta, style)
+        tol = tol + 2.0 ** -14 * ref_abs
     assert (err <= tol).all(), (err.max(), (err - tol).max())
     assert np.abs(lg - lref).max() <= 2e-2 * np.maximum(1.0, np.abs(lref)).max()
 
@@ -269,6 +279,17 @@ def test_attention_parity_fp32_mha(orc, syn):
 @pytest.mark.parametrize("n_q", [0, 1, 33])
 def test_attention_edge_sizes(orc, syn, n_q):
     _attn_case(orc, syn, 300, 1, 4, 128, n_q, "bf16", 500000.0, 1)
+
+
+def test_attention_wide_values(orc, syn):
+    """V rows beyond the fp16 range (|v| >= 65536) in a few 64-key blocks: those
+    segments take the bf16 path, the rest stays on fp16."""
+    _attn_case(orc, syn, 1500, 2, 8, 128, 90, "bf16", 500000.0, 0, v_mul=([5, 700, 1400], 2.0 ** 16))
+
+
+def test_attention_long_split(orc, syn):
+    """Rows whose keys span several split-KV segments (T = 9000), ragged tile."""
+    _attn_case(orc, syn, 9000, 1, 4, 128, 77, "bf16", 500000.0, 0)
 
 
 def test_attention_group8_long(orc, syn):
