@@ -29,6 +29,8 @@
  *    are rounded once, to nearest even.
  *  - Layout: per-layer tensors are row-major [rows][H][D] (token-major, the
  *    H*D channels of one token contiguous).  Chunk tensors are [L][n][H][D].
+ *    Row-data pointers (keys, values, queries, outputs) must be 16-byte
+ *    aligned; a misaligned one is rejected with CT_E_INVALID.
  *  - Determinism: identical inputs give bit-identical outputs (no floating
  *    point atomics, fixed reduction orders).
  *  - Concurrency: calls on different streams may run concurrently as long as

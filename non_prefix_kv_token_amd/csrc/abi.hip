@@ -29,6 +29,8 @@ ct_status check_launch(const char* what) {
 
 static bool dtype_ok(int dt) { return dt == CT_F32 || dt == CT_BF16; }
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -209,6 +211,11 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
     if (p.k < p.n && !p.src_rows && !p.comp) return fail(CT_E_INVALID, "place: comp and src_rows are both NULL");
     if (p.k > 0 && (!p.k_rec || !p.v_rec || !p.sel)) return fail(CT_E_INVALID, "place: recomputed rows are NULL");
   }
+  bool al_ok = aligned16(k_out) && aligned16(v_out) && aligned16(k_sfx) && aligned16(v_sfx);
+  for (int i = 0; i < n_places; ++i)
+    al_ok = al_ok && aligned16(places[i].k_src) && aligned16(places[i].v_src) &&
+            aligned16(places[i].k_rec) && aligned16(places[i].v_rec);
+  if (!al_ok) return fail(CT_E_INVALID, "row buffers must be 16-byte aligned");
   std::vector<AsmPlace> all;
   for (int i = 0; i < n_places; ++i) {
     const ct_place& p = places[i];
@@ -250,6 +257,8 @@ static ct_status attn_args(const void* q_pre, const int32_t* q_pos, int32_t n_q,
   if (!std::isfinite(softmax_scale)) return fail(CT_E_INVALID, "softmax_scale must be finite");
   if (n_q < 0 || T < 1) return fail(CT_E_INVALID, "need n_q >= 0, T >= 1");
   if (need_ptrs && n_q > 0 && (!q_pre || !q_pos || !k || !v || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if (need_ptrs && !(aligned16(q_pre) && aligned16(k) && aligned16(v) && aligned16(out)))
+    return fail(CT_E_INVALID, "q_pre, k, v and out must be 16-byte aligned");
   if ((long long)(n_q + 31) / 32 * Hq > (long long)INT32_MAX / 64)
     return fail(CT_E_UNSUPPORTED, "too many query rows");
   *a = AttnArgs{};

@@ -5,40 +5,103 @@
 // rotated at their global position when reused).
 //
 // One pass over HBM: every output row is read once from its source (cache,
-// recomputation buffer or suffix) and written once.  A group of D/8 threads
-// handles one row: thread q owns RoPE pairs 4q..4q+3 of every head, so the
-// four angles (fp64 sincos) are formed once per row and reused for all H heads.
-// The rotation is done in fp64 and rounded once to the storage type.
+// recomputation buffer or suffix) and written once.  One wave per token row;
+// a lane owns 8 RoPE pairs of one head (two 16-byte bf16 vectors, or two
+// 32-byte fp32 vectors), so all loads and stores are full vectors and a row's
+// H*D elements move in one or two passes of the wave.  The rotation angle and
+// its sine and cosine are formed in fp64, the rotated value is rounded once to
+// the storage type.
 #include "ct_internal.h"
 
 namespace ct {
 namespace {
 
-__device__ inline double ld_elem(const void* p, size_t i, int dt) {
-  if (dt == CT_F32) return (double)reinterpret_cast<const float*>(p)[i];
-  return (double)__uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(p)[i]) << 16);
-}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline uint16_t bf16_from_f64(double d) {
   float f = __double2float_rz(d);
   uint32_t u = __float_as_uint(f);
-  if ((double)f != d) u |= 1u;
+  if ((double)f != d) u |= 1u;  // sticky bit: the second rounding cannot double-round
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <int DT>
-__device__ inline void st_elem(void* p, size_t i, double v) {
-  if constexpr (DT == CT_F32) reinterpret_cast<float*>(p)[i] = (float)v;
-  else reinterpret_cast<uint16_t*>(p)[i] = bf16_from_f64(v);
+// sin and cos of pos * f in fp64 without branches: Cody-Waite reduction by
+// quarter turns (pi/2 split into two doubles), then Taylor polynomials on
+// |r| <= pi/4 (sin to degree 13, cos to degree 14: truncation below 1e-14).
+__device__ inline void sincos_pos(long long pos, double f, double* s, double* c) {
+  const double ang = (double)pos * f;
+  const double q = rint(ang * 0.6366197723675814);
+  double r = fma(-q, 1.5707963267948966, ang);
+  r = fma(-q, 6.123233995736766e-17, r);
+  const double r2 = r * r;
+  double ps = 1.6059043836821613e-10;
+  ps = fma(ps, r2, -2.505210838544172e-08);
+  ps = fma(ps, r2, 2.7557319223985893e-06);
+  ps = fma(ps, r2, -1.984126984126984e-04);
+  ps = fma(ps, r2, 8.333333333333333e-03);
+  ps = fma(ps, r2, -1.6666666666666666e-01);
+  const double sr = fma(ps * r2, r, r);
+  double pc = -1.1470745597729725e-11;
+  pc = fma(pc, r2, 2.08767569878681e-09);
+  pc = fma(pc, r2, -2.755731922398589e-07);
+  pc = fma(pc, r2, 2.48015873015873e-05);
+  pc = fma(pc, r2, -1.388888888888889e-03);
+  pc = fma(pc, r2, 4.1666666666666664e-02);
+  pc = fma(pc, r2, -0.5);
+  const double cr = fma(pc, r2, 1.0);
+  const int quad = (int)((long long)q & 3);
+  const double sv = (quad & 1) ? cr : sr, cv = (quad & 1) ? sr : cr;
+  *s = (quad & 2) ? -sv : sv;
+  *c = (quad == 1 || quad == 2) ? -cv : cv;
 }
+
+// 8 consecutive stored elements <-> 8 doubles.
+template <int DT> struct Vec8;
+template <> struct Vec8<CT_BF16> {
+  u32x4_t w;
+  __device__ void load(const void* p, size_t i) { w = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(p) + i); }
+  __device__ void store(void* p, size_t i) const { *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p) + i) = w; }
+  __device__ double get(int t) const {
+    const uint32_t x = w[t >> 1];
+    return (double)__uint_as_float((t & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  __device__ void set(int t, double v) {
+    const uint32_t b = bf16_from_f64(v);
+    const int i = t >> 1;
+    w[i] = (t & 1) ? ((w[i] & 0xffffu) | (b << 16)) : ((w[i] & 0xffff0000u) | b);
+  }
+};
+template <> struct Vec8<CT_F32> {
+  float4 a, b;
+  __device__ void load(const void* p, size_t i) {
+    const float4* f = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    a = f[0];
+    b = f[1];
+  }
+  __device__ void store(void* p, size_t i) const {
+    float4* f = reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i);
+    f[0] = a;
+    f[1] = b;
+  }
+  __device__ double get(int t) const {
+    const float4& v = t < 4 ? a : b;
+    const int k = t & 3;
+    return (double)(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+  }
+  __device__ void set(int t, double x) {
+    float4& v = t < 4 ? a : b;
+    const int k = t & 3;
+    const float f = (float)x;
+    if (k == 0) v.x = f; else if (k == 1) v.y = f; else if (k == 2) v.z = f; else v.w = f;
+  }
+};
 
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, void* v_out) {
-  constexpr int TPR = D / 8;            // threads per row
-  constexpr int RPB = 256 / TPR;        // rows per block
+  constexpr int CPH = D / 16;  // 8-pair chunks per head
   const AsmPlace& pl = al.p[blockIdx.y];
-  const int q = threadIdx.x % TPR;
-  const int r = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= pl.n) return;
   const int H = al.H;
 
@@ -61,48 +124,64 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
     ks = pl.k_src;
     vs = pl.v_src;
   } else {  // recomputed row
-    int t = r - (pl.n - pl.k);
+    const int t = r - (pl.n - pl.k);
     local = pl.sel[t];
     srow = t;
     ks = pl.k_rec;
     vs = pl.v_rec;
   }
   const long long gpos = (long long)pl.offset + local;
-
-  double cs[4], sn[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    double ang = (double)gpos * al.inv_freq[4 * q + i];
-    sincos(ang, &sn[i], &cs[i]);
-  }
-
   const size_t src_base = (size_t)srow * H * D;
   const size_t dst_base = (size_t)gpos * H * D;
-  for (int h = 0; h < H; ++h) {
+  const bool half = al.style == CT_ROPE_HALF;
+
+  for (int item = lane; item < H * CPH; item += 64) {
+    const int h = item / CPH, c = item % CPH;
+    // element offsets (within the head) of the two 8-element vectors
+    const int ea = half ? 8 * c : 16 * c;
+    const int eb = half ? D / 2 + 8 * c : 16 * c + 8;
     const size_t so = src_base + (size_t)h * D, dof = dst_base + (size_t)h * D;
+    Vec8<DT> xa, xb, va, vb;
+    xa.load(ks, so + ea);
+    xb.load(ks, so + eb);
+    va.load(vs, so + ea);
+    vb.load(vs, so + eb);
+    Vec8<DT> ya = xa, yb = xb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int j = 4 * q + i;
-      int e0 = al.style == CT_ROPE_HALF ? j : 2 * j;
-      int e1 = al.style == CT_ROPE_HALF ? j + D / 2 : 2 * j + 1;
-      double a = ld_elem(ks, so + e0, DT), b = ld_elem(ks, so + e1, DT);
-      st_elem<DT>(k_out, dof + e0, a * cs[i] - b * sn[i]);
-      st_elem<DT>(k_out, dof + e1, a * sn[i] + b * cs[i]);
-      if constexpr (DT == CT_F32) {
-        reinterpret_cast<float*>(v_out)[dof + e0] = reinterpret_cast<const float*>(vs)[so + e0];
-        reinterpret_cast<float*>(v_out)[dof + e1] = reinterpret_cast<const float*>(vs)[so + e1];
+    for (int t = 0; t < 8; ++t) {
+      // pair t of this lane: frequency index 8c + t
+      double sn, cs;
+      sincos_pos(gpos, al.inv_freq[8 * c + t], &sn, &cs);
+      double x0, x1;
+      if (half) {
+        x0 = xa.get(t);
+        x1 = xb.get(t);
+      } else {  // interleaved: pairs (2t', 2t'+1) of the 16 elements
+        x0 = t < 4 ? xa.get(2 * t) : xb.get(2 * t - 8);
+        x1 = t < 4 ? xa.get(2 * t + 1) : xb.get(2 * t - 7);
+      }
+      const double y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+      if (half) {
+        ya.set(t, y0);
+        yb.set(t, y1);
+      } else if (t < 4) {
+        ya.set(2 * t, y0);
+        ya.set(2 * t + 1, y1);
       } else {
-        reinterpret_cast<uint16_t*>(v_out)[dof + e0] = reinterpret_cast<const uint16_t*>(vs)[so + e0];
-        reinterpret_cast<uint16_t*>(v_out)[dof + e1] = reinterpret_cast<const uint16_t*>(vs)[so + e1];
+        yb.set(2 * t - 8, y0);
+        yb.set(2 * t - 7, y1);
       }
     }
+    ya.store(k_out, dof + ea);
+    yb.store(k_out, dof + eb);
+    va.store(v_out, dof + ea);
+    vb.store(v_out, dof + eb);
   }
 }
 
 template <int DT, int D>
 ct_status launch(const AsmLaunch& al, void* k_out, void* v_out, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
-  dim3 grid((al.max_rows + RPB - 1) / RPB, al.n_places);
+  dim3 grid((al.max_rows + 3) / 4, al.n_places);
   hipLaunchKernelGGL((k_assemble<DT, D>), grid, dim3(256), 0, stream, al, k_out, v_out);
   return check_launch("assemble");
 }

@@ -52,9 +52,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int BK = 64;              // keys per LDS block
 constexpr int VTS = BK + 8;         // V^T row stride (16-bit elements): 144 B
 constexpr float kLazyThr = 8.f;     // running-max slack before a rescale (log2 units)
@@ -109,20 +108,27 @@ __device__ inline int vt_col(int u) {
   return (u & ~15) + 8 * ((w & 7) >> 2) + (w & 3) + 4 * (w >> 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
+// NW waves per block; each wave owns QT tiles of 32 query rows of one query
+// head.  QT = 2 runs one wave per SIMD with the whole register file, so every
+// K / V^T fragment read from LDS feeds two tiles; QT = 1 runs two waves per
+// SIMD.
+template <int D, int NW, int QT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 2 : 1, QT == 1 ? 2 : 1)))
+void k_attn_bf16(AttnArgs a) {
+  constexpr int NT = 64 * NW;        // threads per block
   constexpr int KS = D + 8;          // K row stride (bf16): 16-byte reads conflict-free
   constexpr int NS = D / 16;         // k-steps over the head dimension
   constexpr int NDT = D / 32;        // output tiles over the head dimension
   constexpr int KCH = D / 8;         // 16-byte chunks per K row
-  constexpr int KIT = BK * KCH / kThreads;  // K chunks staged per thread
-  constexpr int DPG = D / 16;        // V dims per thread (2 keys x DPG dims)
-  static_assert(KIT >= 1 && BK * KCH == KIT * kThreads, "K staging split");
+  constexpr int KIT = BK * KCH / NT; // K chunks staged per thread
+  constexpr int NDG = NT / 32;       // V staging: 32 key pairs x NDG dim groups
+  constexpr int DPG = D / NDG;       // V dims per thread (2 keys x DPG dims)
+  static_assert(KIT >= 1 && BK * KCH == KIT * NT, "K staging split");
+  static_assert(DPG >= 4 && DPG % 4 == 0, "V staging split");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vh[2][D * VTS];  // V^T, fp16
-  __shared__ __attribute__((aligned(16))) uint16_t Vb[2][D * VTS];  // V^T, bf16
-  __shared__ int s_wide[2][kWaves];  // wave saw a V outside the fp16 range
-  __shared__ int s_wmax[kWaves];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VTS];  // V^T: fp16 (bf16 when redone)
+  __shared__ int s_wide[2][NW];  // wave saw a V outside the fp16 range
+  __shared__ int s_wmax[NW];
 
   const int H = a.H, G = a.group, T = a.T, Hq = a.Hq, S = a.seg_keys;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -137,15 +143,21 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
   const int tg = a.n_tg - 1 - u_ / a.n_hc;  // latest rows first inside a segment
   const int hc = u_ % a.n_hc;
   const int wt = wave / a.hpb, wh = wave % a.hpb;
-  const int tile = tg * a.tpb + wt;
-  const int hig = hc * a.hpb + wh;  // head inside the group
-  const bool wave_on = wt < a.tpb && hig < G && tile * 32 < a.n_q;
+  const int tile0 = (tg * a.tpb + wt) * QT;  // first 32-row tile of the wave
+  const int hig = hc * a.hpb + wh;           // head inside the group
+  const bool wave_on = wt < a.tpb && hig < G && tile0 * 32 < a.n_q;
   const int hq = kvh * G + hig;
-  const int row = tile * 32 + col;
-  const bool valid = wave_on && row < a.n_q;
-  const int pos = valid ? min(a.qpos[row], T - 1) : -1;
-
-  int wmax = pos, wmin = valid ? pos : INT_MAX;
+  int row[QT], pos[QT];
+  bool valid[QT];
+  int wmax = -1, wmin = INT_MAX;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    row[qt] = (tile0 + qt) * 32 + col;
+    valid[qt] = wave_on && row[qt] < a.n_q;
+    pos[qt] = valid[qt] ? min(a.qpos[row[qt]], T - 1) : -1;
+    wmax = max(wmax, pos[qt]);
+    if (valid[qt]) wmin = min(wmin, pos[qt]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     wmax = max(wmax, __shfl_xor(wmax, o));
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
   __syncthreads();
   int bmax = -1;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) bmax = max(bmax, s_wmax[w]);
+  for (int w = 0; w < NW; ++w) bmax = max(bmax, s_wmax[w]);
   const int nkeys = bmax + 1;
   const int seg_lo = seg * S;
   if (seg_lo >= nkeys) return;  // uniform over the block
@@ -163,20 +175,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
   const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
   // ---- rotated, scaled query as bf16 hi + lo (B operand): d = 16*s + 8*g + t
-  u32x4_t qh[NS], ql[NS];
+  u32x4_t qh[QT][NS], ql[QT][NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) { qh[s][w] = 0u; ql[s][w] = 0u; }
-  if (valid) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * Hq + hq) * D;
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { qh[qt][s][w] = 0u; ql[qt][s][w] = 0u; }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    if (!valid[qt]) continue;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row[qt] * Hq + hq) * D;
     const float c = a.scale_log2;
     auto put = [&](int s, int t, float y) {
       uint32_t hi = bf16_bits_rne(y);
       uint32_t lo = bf16_bits_rne(y - __uint_as_float(hi << 16));
       const int w = t >> 1, sh = 16 * (t & 1);
-      qh[s][w] |= hi << sh;
-      ql[s][w] |= lo << sh;
+      qh[qt][s][w] |= hi << sh;
+      ql[qt][s][w] |= lo << sh;
     };
     if (a.style == CT_ROPE_HALF) {
 #pragma unroll
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
           const float x = (t & 1) ? bf16_hi_to_f32(x4[t >> 1]) : bf16_lo_to_f32(x4[t >> 1]);
           const float y = (t & 1) ? bf16_hi_to_f32(y4[t >> 1]) : bf16_lo_to_f32(y4[t >> 1]);
           float sn, cs;
-          rope_sincos(pos, a.inv_freq[j], &sn, &cs);
+          rope_sincos(pos[qt], a.inv_freq[j], &sn, &cs);
           put(s, t, (x * cs - y * sn) * c);
           put(s + NS / 2, t, (x * sn + y * cs) * c);
         }
@@ -204,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
           const float x = bf16_lo_to_f32(x4[t >> 1]);
           const float y = bf16_hi_to_f32(x4[t >> 1]);
           float sn, cs;
-          rope_sincos(pos, a.inv_freq[d / 2], &sn, &cs);
+          rope_sincos(pos[qt], a.inv_freq[d / 2], &sn, &cs);
           put(s, t, (x * cs - y * sn) * c);
           put(s, t + 1, (x * sn + y * cs) * c);
         }
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
     const int k0 = kb * BK;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int item = tid + it * kThreads;
+      const int item = tid + it * NT;
       const int key = k0 + item / KCH, ch = item % KCH;
       kreg[it] = (u32x4_t){0u, 0u, 0u, 0u};
       if (key < T) kreg[it] = *reinterpret_cast<const u32x4_t*>(Kg + ((size_t)key * H + kvh) * D + 8 * ch);
@@ -232,11 +248,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
     for (int e = 0; e < 2; ++e) {
       const int key = k0 + 2 * kp + e;
       const uint16_t* src = Vg + ((size_t)key * H + kvh) * D + dg * DPG;
-      if constexpr (DPG == 8) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key < T) w = *reinterpret_cast<const u32x4_t*>(src);
+      if constexpr (DPG >= 8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vreg[e][i] = w[i];
+        for (int c8 = 0; c8 < DPG / 8; ++c8) {
+          u32x4_t w = {0u, 0u, 0u, 0u};
+          if (key < T) w = *reinterpret_cast<const u32x4_t*>(src + 8 * c8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vreg[e][4 * c8 + i] = w[i];
+        }
       } else {
         u32x2_t w = {0u, 0u};
         if (key < T) w = *reinterpret_cast<const u32x2_t*>(src);
@@ -246,165 +265,226 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
     }
   };
 
-  auto store = [&](int buf) {
+  // fp16 == true: V^T as fp16 and the wave's range flag; false: V^T as bf16
+  auto store = [&](int buf, bool fp16) {
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int item = tid + it * kThreads;
+      const int item = tid + it * NT;
       *reinterpret_cast<u32x4_t*>(&Ks[buf][(item / KCH) * KS + 8 * (item % KCH)]) = kreg[it];
     }
     const int cpos = vt_col(2 * kp);
-    uint32_t wide = 0u;
+    u16x2_t wide = {0, 0};
 #pragma unroll
     for (int i = 0; i < DPG / 2; ++i) {
       const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];  // dims 2i, 2i+1 of keys 2kp, 2kp+1
-      wide = max(wide, max(w0 & 0x7fffu, (w0 >> 16) & 0x7fffu));
-      wide = max(wide, max(w1 & 0x7fffu, (w1 >> 16) & 0x7fffu));
       const int d0 = dg * DPG + 2 * i;
-      const uint32_t blo = (w0 & 0xffffu) | (w1 << 16);          // dim d0, keys (2kp, 2kp+1)
-      const uint32_t bhi = (w0 >> 16) | (w1 & 0xffff0000u);      // dim d0 + 1
-      *reinterpret_cast<uint32_t*>(&Vb[buf][d0 * VTS + cpos]) = blo;
-      *reinterpret_cast<uint32_t*>(&Vb[buf][(d0 + 1) * VTS + cpos]) = bhi;
-      *reinterpret_cast<uint32_t*>(&Vh[buf][d0 * VTS + cpos]) =
-          pack_f16(bf16_lo_to_f32(w0), bf16_lo_to_f32(w1));
-      *reinterpret_cast<uint32_t*>(&Vh[buf][(d0 + 1) * VTS + cpos]) =
-          pack_f16(bf16_hi_to_f32(w0), bf16_hi_to_f32(w1));
+      uint32_t lo, hi;
+      if (fp16) {
+        wide = __builtin_elementwise_max(wide, __builtin_bit_cast(u16x2_t, w0 & 0x7fff7fffu));
+        wide = __builtin_elementwise_max(wide, __builtin_bit_cast(u16x2_t, w1 & 0x7fff7fffu));
+        lo = pack_f16(bf16_lo_to_f32(w0), bf16_lo_to_f32(w1));
+        hi = pack_f16(bf16_hi_to_f32(w0), bf16_hi_to_f32(w1));
+      } else {
+        lo = (w0 & 0xffffu) | (w1 << 16);        // dim d0, keys (2kp, 2kp+1)
+        hi = (w0 >> 16) | (w1 & 0xffff0000u);    // dim d0 + 1
+      }
+      *reinterpret_cast<uint32_t*>(&Vs[buf][d0 * VTS + cpos]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vs[buf][(d0 + 1) * VTS + cpos]) = hi;
     }
-    // 0x4780 is 65536 in bf16: the first magnitude fp16 cannot hold
-    const int any_wide = __any(wide >= 0x4780u);
-    if (lane == 0) s_wide[buf][wave] = any_wide;
+    if (fp16) {
+      // 0x4780 is 65536 in bf16: the first magnitude fp16 cannot hold
+      const int any_wide = __any(max(wide[0], wide[1]) >= 0x4780);
+      if (lane == 0) s_wide[buf][wave] = any_wide;
+    }
   };
 
-  f32x16_t o[NDT];
+  f32x16_t o[QT][NDT];
 #pragma unroll
-  for (int i = 0; i < NDT; ++i)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[qt][i][v] = 0.f;
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
 
-  // one 64-key block: S^T = K . Q^T, causal mask, online softmax (P in st)
-  auto scores = [&](int cur, int k0, f32x16_t* st) {
+  // S^T = K . Q^T for the 64 keys of a buffer: each K fragment feeds all QT
+  // tiles; causal mask where the block reaches past the wave's first row.
+  auto scores = [&](const uint16_t* kbuf, int k0, f32x16_t (*st)[2]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[kt][v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&Ks[cur][(kt * 32 + col) * KS + 16 * s + 8 * g]);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8_t, qh[s]), st[kt], 0, 0, 0);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8_t, ql[s]), st[kt], 0, 0, 0);
-      }
-    }
-    // causal mask, only where the block reaches past the wave's first row
-    if (k0 + BK - 1 > wmin) {
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-          if (key > pos) st[kt][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v) st[qt][kt][v] = 0.f;
+    // fragments of the next k-step are read before the MFMAs of this one
+    const uint16_t* kb_ = kbuf + col * KS + 8 * g;
+    bf16x8_t ka[2], kn[2];
+    ka[0] = *reinterpret_cast<const bf16x8_t*>(kb_);
+    ka[1] = *reinterpret_cast<const bf16x8_t*>(kb_ + 32 * KS);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) {
+        kn[0] = *reinterpret_cast<const bf16x8_t*>(kb_ + 16 * (s + 1));
+        kn[1] = *reinterpret_cast<const bf16x8_t*>(kb_ + 32 * KS + 16 * (s + 1));
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, qh[qt][s]);
+        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, ql[qt][s]);
+        st[qt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], bh, st[qt][0], 0, 0, 0);
+        st[qt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], bh, st[qt][1], 0, 0, 0);
+        st[qt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], bl, st[qt][0], 0, 0, 0);
+        st[qt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], bl, st[qt][1], 0, 0, 0);
+      }
+      if (s + 1 < NS) {
+        ka[0] = kn[0];
+        ka[1] = kn[1];
+      }
     }
-    float bm = -INFINITY;
+    if (k0 + BK - 1 > wmin) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) bm = fmaxf(bm, st[kt][v]);
-    if (__any(bm > m_run + kLazyThr)) {
-      const float m_new = fmaxf(m_run, fmaxf(bm, __shfl_xor(bm, 32)));
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+            if (key > pos[qt]) st[qt][kt][v] = -INFINITY;
+          }
+    }
+  };
+
+  // Online softmax of one 32-key tile of tile qt (16 logits per lane): lazy
+  // maximum, probabilities exp2(s - m) in place.
+  auto softmax_tile = [&](int qt, f32x16_t& st) {
+    float bm = fmaxf(fmaxf(st[0], st[1]), st[2]);
+#pragma unroll
+    for (int v = 3; v < 15; v += 2) bm = fmaxf(bm, fmaxf(st[v], st[v + 1]));
+    bm = fmaxf(bm, st[15]);
+    if (__any(bm > m_run[qt] + kLazyThr)) {
+      const float m_new = fmaxf(m_run[qt], fmaxf(bm, __shfl_xor(bm, 32)));
+      const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
+        for (int v = 0; v < 16; ++v) o[qt][i][v] *= alpha;
+      l_run[qt] *= alpha;
+      m_run[qt] = m_new;
     }
-    const float mu = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
+    const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(st[kt][v] - mu);
-        st[kt][v] = p;
-        rs += p;
-      }
-    l_run += rs;
+    for (int v = 0; v < 16; ++v) st[v] = __builtin_amdgcn_exp2f(st[v] - mu);
   };
 
   // Main pass: P and V^T as fp16.  A block whose V does not fit fp16 stops
   // it; the segment is then redone below with bf16 V and P as a bf16 pair.
+  const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
   bool redo = false;
   load(kb0);
-  store(0);
+  store(0, true);
   for (int kb = kb0; kb < kb1; ++kb) {
     const int cur = (kb - kb0) & 1;
     const bool more = kb + 1 < kb1;
     if (more) load(kb + 1);
     __syncthreads();
-    const int* fl = s_wide[cur];
-    if ((fl[0] | fl[1] | fl[2] | fl[3] | fl[4] | fl[5] | fl[6] | fl[7]) != 0) {
+    int wide_any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wide_any |= s_wide[cur][w];
+    if (wide_any) {
       redo = true;  // same decision in every wave of the block
       break;
     }
     const int k0 = kb * BK;
     if (wave_on && k0 <= wmax) {
-      f32x16_t st[2];
-      scores(cur, k0, st);
-      // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
+      const uint16_t* kbuf = Ks[cur];
+      const uint16_t* vbuf = Vs[cur];
+      f32x16_t st[QT][2];
+      scores(kbuf, k0, st);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) softmax_tile(qt, st[qt][kt]);
+        // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4_t pw;
+          // (the dot product takes the converted pair itself: hipcc reads the
+          // wrong register when it is given a bit-cast element of pw)
+          f16x8_t pf[QT];
 #pragma unroll
-          for (int h = 0; h < 4; ++h) pw[h] = pack_f16(st[kt][8 * h2 + 2 * h], st[kt][8 * h2 + 2 * h + 1]);
-          const f16x8_t pf = __builtin_bit_cast(f16x8_t, pw);
+          for (int qt = 0; qt < QT; ++qt) {
+            u32x4_t pw;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const f32x2_t pv = {st[qt][kt][8 * h2 + 2 * h], st[qt][kt][8 * h2 + 2 * h + 1]};
+              const f16x2_t ph = __builtin_convertvector(pv, f16x2_t);
+              l_run[qt] = __builtin_amdgcn_fdot2(ph, ones, l_run[qt], false);
+              pw[h] = __builtin_bit_cast(uint32_t, ph);
+            }
+            pf[qt] = __builtin_bit_cast(f16x8_t, pw);
+          }
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
-                &Vh[cur][(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, o[dt], 0, 0, 0);
+                &vbuf[(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+              o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qt], o[qt][dt], 0, 0, 0);
           }
         }
+      }
     }
-    if (more) store(cur ^ 1);
+    if (more) store(cur ^ 1, true);
   }
 
   if (redo) {
 #pragma unroll
-    for (int i = 0; i < NDT; ++i)
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-    m_run = -INFINITY;
-    l_run = 0.f;
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[qt][i][v] = 0.f;
+      m_run[qt] = -INFINITY;
+      l_run[qt] = 0.f;
+    }
     for (int kb = kb0; kb < kb1; ++kb) {
       __syncthreads();  // previous readers of buffer 0 are done
       load(kb);
-      store(0);
+      store(0, false);
       __syncthreads();
       const int k0 = kb * BK;
       if (wave_on && k0 <= wmax) {
-        f32x16_t st[2];
-        scores(0, k0, st);
+        f32x16_t st[QT][2];
+        scores(Ks[0], k0, st);
 #pragma unroll 1
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kt = ks >> 1, h2 = ks & 1;
-          u32x4_t ph, pl;
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float p0 = st[kt][8 * h2 + 2 * h], p1 = st[kt][8 * h2 + 2 * h + 1];
-            const uint32_t a0 = bf16_bits_rne(p0), a1 = bf16_bits_rne(p1);
-            ph[h] = a0 | (a1 << 16);
-            pl[h] = bf16_bits_rne(p0 - __uint_as_float(a0 << 16)) |
-                    (bf16_bits_rne(p1 - __uint_as_float(a1 << 16)) << 16);
-          }
+          for (int qt = 0; qt < QT; ++qt) {
+            softmax_tile(qt, st[qt][kt]);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-                &Vb[0][(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, ph), o[dt], 0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, pl), o[dt], 0, 0, 0);
+            for (int h2 = 0; h2 < 2; ++h2) {
+              u32x4_t ph, pl;
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const float p0 = st[qt][kt][8 * h2 + 2 * h], p1 = st[qt][kt][8 * h2 + 2 * h + 1];
+                l_run[qt] += p0 + p1;
+                const uint32_t a0 = bf16_bits_rne(p0), a1 = bf16_bits_rne(p1);
+                ph[h] = a0 | (a1 << 16);
+                pl[h] = bf16_bits_rne(p0 - __uint_as_float(a0 << 16)) |
+                        (bf16_bits_rne(p1 - __uint_as_float(a1 << 16)) << 16);
+              }
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) {
+                const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
+                    &Vs[0][(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
+                o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, ph), o[qt][dt], 0, 0, 0);
+                o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, pl), o[qt][dt], 0, 0, 0);
+              }
+            }
           }
         }
       }
@@ -412,34 +492,39 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16(AttnArgs a) {
   }
 
   if (!wave_on) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!valid || pos < seg_lo) return;
-  const float inv_l = 1.f / l_tot;
-  const float lse2 = m_run + __log2f(l_tot);
-  if (seg == 0 && pos < S) {  // every key of this row lies in segment 0
-    const size_t obase = ((size_t)row * Hq + hq) * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 32);
+    if (!valid[qt] || pos[qt] < seg_lo) continue;
+    const float inv_l = 1.f / l_tot;
+    const float lse2 = m_run[qt] + __log2f(l_tot);
+    if (seg == 0 && pos[qt] < S) {  // every key of this row lies in segment 0
+      const size_t obase = ((size_t)row[qt] * Hq + hq) * D;
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int d0 = dt * 32 + 8 * v4 + 4 * g;
-        u32x2_t w = {bf16_bits_rne(o[dt][4 * v4] * inv_l) | (bf16_bits_rne(o[dt][4 * v4 + 1] * inv_l) << 16),
-                     bf16_bits_rne(o[dt][4 * v4 + 2] * inv_l) | (bf16_bits_rne(o[dt][4 * v4 + 3] * inv_l) << 16)};
-        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + obase + d0) = w;
-      }
-    if (a.lse && g == 0) a.lse[(size_t)row * Hq + hq] = 0.6931471805599453f * lse2;
-  } else {
-    const size_t pb = (((size_t)seg * a.n_q + row) * Hq + hq);
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int d0 = dt * 32 + 8 * v4 + 4 * g;
+          const f32x16_t& oo = o[qt][dt];
+          u32x2_t w = {bf16_bits_rne(oo[4 * v4] * inv_l) | (bf16_bits_rne(oo[4 * v4 + 1] * inv_l) << 16),
+                       bf16_bits_rne(oo[4 * v4 + 2] * inv_l) | (bf16_bits_rne(oo[4 * v4 + 3] * inv_l) << 16)};
+          *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + obase + d0) = w;
+        }
+      if (a.lse && g == 0) a.lse[(size_t)row[qt] * Hq + hq] = 0.6931471805599453f * lse2;
+    } else {
+      const size_t pb = (((size_t)seg * a.n_q + row[qt]) * Hq + hq);
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int d0 = dt * 32 + 8 * v4 + 4 * g;
-        *reinterpret_cast<float4*>(a.part_o + pb * D + d0) =
-            make_float4(o[dt][4 * v4] * inv_l, o[dt][4 * v4 + 1] * inv_l, o[dt][4 * v4 + 2] * inv_l,
-                        o[dt][4 * v4 + 3] * inv_l);
-      }
-    if (g == 0) a.part_lse[pb] = lse2;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int d0 = dt * 32 + 8 * v4 + 4 * g;
+          const f32x16_t& oo = o[qt][dt];
+          *reinterpret_cast<float4*>(a.part_o + pb * D + d0) =
+              make_float4(oo[4 * v4] * inv_l, oo[4 * v4 + 1] * inv_l, oo[4 * v4 + 2] * inv_l,
+                          oo[4 * v4 + 3] * inv_l);
+        }
+      if (g == 0) a.part_lse[pb] = lse2;
+    }
   }
 }
 
@@ -478,8 +563,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
   const int blocks = a.H * a.n_tg * a.n_hc * a.nseg;
-  hipLaunchKernelGGL((k_attn_bf16<D>), dim3(blocks), dim3(kThreads), 0, stream, a);
-  if (ct_status s = check_launch("attention")) return s;
+  if (a.qt == 2)
+    hipLaunchKernelGGL((k_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, stream, a);
+  else if (a.nw == 8)
+    hipLaunchKernelGGL((k_attn_bf16<D, 8, 1>), dim3(blocks), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_attn_bf16<D, 4, 1>), dim3(blocks), dim3(256), 0, stream, a);
+  if (ct_status s = check_launch("attention")) {
+    set_error(std::string(cachetune_last_error()) + " [grid " + std::to_string(blocks) + ", waves " +
+              std::to_string(a.nw) + ", tiles/wave " + std::to_string(a.qt) + ", segments " +
+              std::to_string(a.nseg) + "]");
+    return s;
+  }
   if (a.nseg > 1) {
     const long long waves = (long long)a.n_q * a.Hq;
     hipLaunchKernelGGL((k_attn_merge<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
@@ -492,16 +587,25 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
 
 void attn_plan(AttnArgs* a, int n_cu) {
   const int G = a->group;
-  a->hpb = G < kWaves ? G : kWaves;
-  a->tpb = kWaves / a->hpb;
+  // Block shape: 8 waves with one 32-row tile each (two waves per SIMD); for
+  // tuning, 4 waves with one tile each ("41") or two tiles each ("4").
+  a->nw = 8;
+  a->qt = 1;
+  if (const char* env = getenv("CACHETUNE_ATTN_WAVES")) {
+    const int w = atoi(env);
+    a->nw = (w == 8) ? 8 : 4;
+    a->qt = (w == 8 || w == 41) ? 1 : 2;
+  }
+  a->hpb = G < a->nw ? G : a->nw;
+  a->tpb = a->nw / a->hpb;
   a->n_hc = (G + a->hpb - 1) / a->hpb;
   const int ntiles = (a->n_q + 31) / 32;
-  a->n_tg = (ntiles + a->tpb - 1) / a->tpb;
+  a->n_tg = (ntiles + a->tpb * a->qt - 1) / (a->tpb * a->qt);
   // Segment length: the causal triangle (about units * T / 2 keys of block
-  // work) spread over four blocks per CU, at least 1024 keys, a multiple of
-  // the LDS block.
+  // work) spread over about 2.5 blocks per CU, at least 1024 keys, a
+  // multiple of the LDS block.
   const long long units = (long long)a->H * a->n_tg * a->n_hc;
-  long long s = units * (long long)a->T / (2LL * 4 * (n_cu > 0 ? n_cu : 256));
+  long long s = units * (long long)a->T / (5LL * (n_cu > 0 ? n_cu : 256));
   if (const char* env = getenv("CACHETUNE_ATTN_SEG")) s = atoll(env);
   if (s < 1024) s = 1024;
   s = (s + BK - 1) / BK * BK;

@@ -114,9 +114,11 @@ struct AttnArgs {
   // bf16 path: launch plan (attn_plan) and split-KV partials in the workspace
   int32_t seg_keys;  // keys per segment (multiple of 64)
   int32_t nseg;      // segments covering [0, T)
-  int32_t hpb, tpb;  // query heads and 32-row tiles per block (hpb * tpb <= 8)
+  int32_t nw;        // waves per block (4 or 8)
+  int32_t qt;        // 32-row tiles per wave (1 or 2)
+  int32_t hpb, tpb;  // query heads and 32-row tiles per block (hpb * tpb <= nw)
   int32_t n_hc;      // head chunks per group
-  int32_t n_tg;      // tile groups
+  int32_t n_tg;      // tile groups (tpb * qt tiles each)
   float* part_o;     // [nseg][n_q][Hq][D] normalised partial outputs
   float* part_lse;   // [nseg][n_q][Hq] log2-sum-exp of the partials
 };
