@@ -1,0 +1,84 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/cachetune.h declares, and rejects invalid arguments
+before touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cachetune.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cachetune_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import non_prefix_kv_token_amd as ct
+    if not os.path.exists(ct.LIB_PATH):
+        pytest.skip("library not built")
+    return ct.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("cachetune_score_chunk", "cachetune_select_topr", "cachetune_assemble_rope",
+              "cachetune_recompute_attn"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_symbol_list_matches_header():
+    import non_prefix_kv_token_amd as ct
+    assert sorted(ct.SYMBOLS) == _declared()
+
+
+def test_status_strings(lib):
+    import non_prefix_kv_token_amd as ct
+    for s in (ct.CT_OK, ct.CT_E_INVALID, ct.CT_E_UNSUPPORTED, ct.CT_E_WORKSPACE, ct.CT_E_HIP):
+        assert lib.cachetune_status_string(s)
+    assert lib.cachetune_version() >= 1
+
+
+def test_score_ws_validation(lib):
+    import non_prefix_kv_token_amd as ct
+    n = (C.c_int32 * 2)(2048, 2048)
+    out = C.c_size_t(0)
+    assert lib.cachetune_score_chunk_ws(n, 2, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_OK
+    assert out.value > 0
+    bad = (C.c_int32 * 1)(1)  # chunk shorter than 2 tokens
+    assert lib.cachetune_score_chunk_ws(bad, 1, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_E_INVALID
+    assert b"chunk length" in lib.cachetune_last_error()
+    assert lib.cachetune_score_chunk_ws(n, 2, 32, 8, 128, 3, 2, 0, C.byref(out)) == ct.CT_E_INVALID
+    assert lib.cachetune_score_chunk_ws(n, 2, 32, 3, 7, 1, 16, 0, C.byref(out)) == ct.CT_E_UNSUPPORTED
+
+
+def test_calls_reject_bad_arguments_without_device_work(lib):
+    import non_prefix_kv_token_amd as ct
+    kout = (C.c_int32 * 1)()
+    n = (C.c_int32 * 1)(100)
+    # r outside [0, 1]
+    assert lib.cachetune_select_topr(C.c_void_p(16), n, 1, 3, 2, None, C.c_void_p(16), None, kout,
+                                     None) == ct.CT_E_INVALID
+    # head_dim not supported
+    assert lib.cachetune_assemble_rope(None, 0, None, None, 0, 0, 8, 96, ct.CT_BF16, 10000.0, 0,
+                                       C.c_void_p(16), C.c_void_p(16), 10, None) == ct.CT_E_UNSUPPORTED
+    # misaligned output
+    assert lib.cachetune_assemble_rope(None, 0, None, None, 0, 0, 8, 128, ct.CT_BF16, 10000.0, 0,
+                                       C.c_void_p(18), C.c_void_p(16), 10, None) == ct.CT_E_INVALID
+    # Hq not a multiple of H
+    assert lib.cachetune_recompute_attn(None, None, 0, 6, None, None, 10, 4, 128, ct.CT_BF16, 0.1,
+                                        10000.0, 0, None, None, None, 0, None) == ct.CT_E_INVALID
+    out = C.c_size_t(1)
+    assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 128, ct.CT_BF16, C.byref(out)) == ct.CT_OK
+    assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 100, ct.CT_BF16,
+                                           C.byref(out)) == ct.CT_E_UNSUPPORTED
