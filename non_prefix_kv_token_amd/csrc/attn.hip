@@ -108,6 +108,49 @@ __device__ inline int vt_col(int u) {
   return (u & ~15) + 8 * ((w & 7) >> 2) + (w & 3) + 4 * (w >> 3);
 }
 
+// Per-layer preparation of V for the fp16 PV product: V^T tiles of 64 keys,
+// fp16, keys permuted inside each group of 16 (vt_col), laid out exactly as
+// the attention kernel keeps them in LDS, plus one flag per tile that is set
+// when a value does not fit fp16 (|v| >= 65536, or not finite).  Keys at and
+// beyond T are zero.  One block per (tile, KV head).
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[BK * D];
+  const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int H = a.H, T = a.T;
+  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v);
+  constexpr int CH = BK * D / 8;  // 16-byte chunks per tile
+#pragma unroll
+  for (int c = tid; c < CH; c += 256) {
+    const int key = kb * BK + c / (D / 8), part = c % (D / 8);
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (key < T) w = *reinterpret_cast<const u32x4_t*>(Vg + ((size_t)key * H + h) * D + 8 * part);
+    *reinterpret_cast<u32x4_t*>(&tile[(c / (D / 8)) * D + 8 * part]) = w;
+  }
+  __syncthreads();
+  uint32_t wide = 0u;
+  uint16_t* dst = a.vt16 + ((size_t)h * a.nblk + kb) * D * BK;
+#pragma unroll
+  for (int c = tid; c < CH; c += 256) {
+    const int d = c / (BK / 8), q0 = 8 * (c % (BK / 8));
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int qa = q0 + 2 * e, qb = qa + 1;
+      // key at column q: bits 2 and 3 of its index inside the group swapped
+      const int ua = (qa & ~15) | ((qa & 4) << 1) | ((qa & 8) >> 1) | (qa & 3);
+      const int ub = (qb & ~15) | ((qb & 4) << 1) | ((qb & 8) >> 1) | (qb & 3);
+      const uint32_t xa = tile[ua * D + d], xb = tile[ub * D + d];
+      wide = max(wide, max(xa & 0x7fffu, xb & 0x7fffu));
+      w[e] = pack_f16(__uint_as_float(xa << 16), __uint_as_float(xb << 16));
+    }
+    *reinterpret_cast<u32x4_t*>(dst + (size_t)d * BK + q0) = w;
+  }
+  // 0x4780 is 65536 in bf16: the first magnitude fp16 cannot hold
+  const int any_wide = __syncthreads_or((int)(wide >= 0x4780u));
+  if (tid == 0) a.vflag[h * a.nblk + kb] = any_wide;
+}
+
 // NW waves per block; each wave owns QT tiles of 32 query rows of one query
 // head.  QT = 2 runs one wave per SIMD with the whole register file, so every
 // K / V^T fragment read from LDS feeds two tiles; QT = 1 runs two waves per
@@ -126,8 +169,7 @@ void k_attn_bf16(AttnArgs a) {
   static_assert(KIT >= 1 && BK * KCH == KIT * NT, "K staging split");
   static_assert(DPG >= 4 && DPG % 4 == 0, "V staging split");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VTS];  // V^T: fp16 (bf16 when redone)
-  __shared__ int s_wide[2][NW];  // wave saw a V outside the fp16 range
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[3][D * VTS];  // V^T: fp16 (bf16 when redone)
   __shared__ int s_wmax[NW];
 
   const int H = a.H, G = a.group, T = a.T, Hq = a.Hq, S = a.seg_keys;
@@ -265,36 +307,49 @@ void k_attn_bf16(AttnArgs a) {
     }
   };
 
-  // fp16 == true: V^T as fp16 and the wave's range flag; false: V^T as bf16
-  auto store = [&](int buf, bool fp16) {
+  // main pass: the V^T tile prepared by k_attn_prep, copied as it is
+  constexpr int VIT = D * BK / 8 / NT;  // 16-byte V^T chunks per thread
+  u32x4_t vtreg[VIT];
+  auto load_fast = [&](int kb) {
+    const int k0 = kb * BK;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int item = tid + it * NT;
-      *reinterpret_cast<u32x4_t*>(&Ks[buf][(item / KCH) * KS + 8 * (item % KCH)]) = kreg[it];
+      const int key = k0 + item / KCH, ch = item % KCH;
+      kreg[it] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (key < T) kreg[it] = *reinterpret_cast<const u32x4_t*>(Kg + ((size_t)key * H + kvh) * D + 8 * ch);
+    }
+    const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.vt16 + ((size_t)kvh * a.nblk + kb) * D * BK);
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) vtreg[it] = vt[tid + it * NT];
+  };
+  auto store_fast = [&](int kbuf_i, int buf) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int item = tid + it * NT;
+      *reinterpret_cast<u32x4_t*>(&Ks[kbuf_i][(item / KCH) * KS + 8 * (item % KCH)]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int c = tid + it * NT;
+      *reinterpret_cast<u32x4_t*>(&Vs[buf][(c / (BK / 8)) * VTS + 8 * (c % (BK / 8))]) = vtreg[it];
+    }
+  };
+
+  // fallback pass: V^T transposed here, as bf16
+  auto store = [&](int kbuf_i, int buf) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int item = tid + it * NT;
+      *reinterpret_cast<u32x4_t*>(&Ks[kbuf_i][(item / KCH) * KS + 8 * (item % KCH)]) = kreg[it];
     }
     const int cpos = vt_col(2 * kp);
-    u16x2_t wide = {0, 0};
 #pragma unroll
     for (int i = 0; i < DPG / 2; ++i) {
       const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];  // dims 2i, 2i+1 of keys 2kp, 2kp+1
       const int d0 = dg * DPG + 2 * i;
-      uint32_t lo, hi;
-      if (fp16) {
-        wide = __builtin_elementwise_max(wide, __builtin_bit_cast(u16x2_t, w0 & 0x7fff7fffu));
-        wide = __builtin_elementwise_max(wide, __builtin_bit_cast(u16x2_t, w1 & 0x7fff7fffu));
-        lo = pack_f16(bf16_lo_to_f32(w0), bf16_lo_to_f32(w1));
-        hi = pack_f16(bf16_hi_to_f32(w0), bf16_hi_to_f32(w1));
-      } else {
-        lo = (w0 & 0xffffu) | (w1 << 16);        // dim d0, keys (2kp, 2kp+1)
-        hi = (w0 >> 16) | (w1 & 0xffff0000u);    // dim d0 + 1
-      }
-      *reinterpret_cast<uint32_t*>(&Vs[buf][d0 * VTS + cpos]) = lo;
-      *reinterpret_cast<uint32_t*>(&Vs[buf][(d0 + 1) * VTS + cpos]) = hi;
-    }
-    if (fp16) {
-      // 0x4780 is 65536 in bf16: the first magnitude fp16 cannot hold
-      const int any_wide = __any(max(wide[0], wide[1]) >= 0x4780);
-      if (lane == 0) s_wide[buf][wave] = any_wide;
+      *reinterpret_cast<uint32_t*>(&Vs[buf][d0 * VTS + cpos]) = (w0 & 0xffffu) | (w1 << 16);
+      *reinterpret_cast<uint32_t*>(&Vs[buf][(d0 + 1) * VTS + cpos]) = (w0 >> 16) | (w1 & 0xffff0000u);
     }
   };
 
@@ -381,65 +436,77 @@ void k_attn_bf16(AttnArgs a) {
     for (int v = 0; v < 16; ++v) st[v] = __builtin_amdgcn_exp2f(st[v] - mu);
   };
 
-  // Main pass: P and V^T as fp16.  A block whose V does not fit fp16 stops
-  // it; the segment is then redone below with bf16 V and P as a bf16 pair.
+  // P^T . V^T for one 64-key block (probabilities in st, fp16), row sums from
+  // the rounded probabilities.
   const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-  bool redo = false;
-  load(kb0);
-  store(0, true);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int cur = (kb - kb0) & 1;
-    const bool more = kb + 1 < kb1;
-    if (more) load(kb + 1);
-    __syncthreads();
-    int wide_any = 0;
+  auto pv = [&](const uint16_t* vbuf, f32x16_t (*st)[2]) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) wide_any |= s_wide[cur][w];
-    if (wide_any) {
-      redo = true;  // same decision in every wave of the block
-      break;
-    }
-    const int k0 = kb * BK;
-    if (wave_on && k0 <= wmax) {
-      const uint16_t* kbuf = Ks[cur];
-      const uint16_t* vbuf = Vs[cur];
-      f32x16_t st[QT][2];
-      scores(kbuf, k0, st);
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int qt = 0; qt < QT; ++qt) softmax_tile(qt, st[qt][kt]);
+      // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) softmax_tile(qt, st[qt][kt]);
-        // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        // (the dot product takes the converted pair itself: hipcc reads the
+        // wrong register when it is given a bit-cast element of pw)
+        f16x8_t pf[QT];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          // (the dot product takes the converted pair itself: hipcc reads the
-          // wrong register when it is given a bit-cast element of pw)
-          f16x8_t pf[QT];
+        for (int qt = 0; qt < QT; ++qt) {
+          u32x4_t pw;
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            u32x4_t pw;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const f32x2_t pv = {st[qt][kt][8 * h2 + 2 * h], st[qt][kt][8 * h2 + 2 * h + 1]};
-              const f16x2_t ph = __builtin_convertvector(pv, f16x2_t);
-              l_run[qt] = __builtin_amdgcn_fdot2(ph, ones, l_run[qt], false);
-              pw[h] = __builtin_bit_cast(uint32_t, ph);
-            }
-            pf[qt] = __builtin_bit_cast(f16x8_t, pw);
+          for (int h = 0; h < 4; ++h) {
+            const f32x2_t pv2 = {st[qt][kt][8 * h2 + 2 * h], st[qt][kt][8 * h2 + 2 * h + 1]};
+            const f16x2_t ph = __builtin_convertvector(pv2, f16x2_t);
+            l_run[qt] = __builtin_amdgcn_fdot2(ph, ones, l_run[qt], false);
+            pw[h] = __builtin_bit_cast(uint32_t, ph);
           }
+          pf[qt] = __builtin_bit_cast(f16x8_t, pw);
+        }
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
-                &vbuf[(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
+              &vbuf[(dt * 32 + col) * VTS + 32 * kt + 16 * h2 + 8 * g]);
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-              o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qt], o[qt][dt], 0, 0, 0);
-          }
+          for (int qt = 0; qt < QT; ++qt)
+            o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[qt], o[qt][dt], 0, 0, 0);
         }
       }
     }
-    if (more) store(cur ^ 1, true);
+  };
+
+  // Main pass: P and V^T as fp16.  A segment with a V tile that does not fit
+  // fp16 takes the pass below instead: bf16 V and P as a bf16 pair.
+  // With 8 waves, waves 4-7 (one per SIMD) run half a block behind: they
+  // finish the softmax and PV of the previous block before the scores of the
+  // current one, so each SIMD holds one wave in a matrix phase while the other
+  // is in its vector phase.  V^T therefore has three LDS buffers.
+  const int lag = (NW == 8 && QT == 1) ? (wave >> 2) : 0;
+  // the fp16 path needs every V tile of the segment to fit fp16
+  bool redo = false;
+  for (int kb = kb0; kb < kb1; ++kb) redo |= a.vflag[kvh * a.nblk + kb] != 0;
+  bool pend = false;
+  f32x16_t st[QT][2];
+  if (!redo) {
+    load_fast(kb0);
+    store_fast(0, 0);
   }
+  for (int kb = kb0; kb < kb1 && !redo; ++kb) {
+    const int i = kb - kb0;
+    const int kc = i & 1, vc = i % 3;
+    const bool more = kb + 1 < kb1;
+    if (more) load_fast(kb + 1);
+    __syncthreads();
+    const int k0 = kb * BK;
+    if (lag && pend) pv(Vs[(i + 2) % 3], st);  // the previous block
+    pend = wave_on && k0 <= wmax;
+    if (pend) scores(Ks[kc], k0, st);
+    if (!lag && pend) {
+      pv(Vs[vc], st);
+      pend = false;
+    }
+    if (more) store_fast((i + 1) & 1, (i + 1) % 3);
+  }
+  if (!redo && pend) pv(Vs[(kb1 - 1 - kb0) % 3], st);
 
   if (redo) {
 #pragma unroll
@@ -454,7 +521,7 @@ void k_attn_bf16(AttnArgs a) {
     for (int kb = kb0; kb < kb1; ++kb) {
       __syncthreads();  // previous readers of buffer 0 are done
       load(kb);
-      store(0, false);
+      store(0, 0);
       __syncthreads();
       const int k0 = kb * BK;
       if (wave_on && k0 <= wmax) {
@@ -562,6 +629,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
+  if (ct_status s = check_launch("attention V preparation")) return s;
   const int blocks = a.H * a.n_tg * a.n_hc * a.nseg;
   if (a.qt == 2)
     hipLaunchKernelGGL((k_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, stream, a);
@@ -612,25 +681,40 @@ void attn_plan(AttnArgs* a, int n_cu) {
   if (s > a->T) s = (a->T + BK - 1) / BK * BK;
   a->seg_keys = (int32_t)s;
   a->nseg = (a->T + a->seg_keys - 1) / a->seg_keys;
+  a->nblk = (a->T + BK - 1) / BK;
+}
+
+// Workspace: [partial outputs][partial log2-sum-exp][V^T fp16 tiles][tile flags]
+static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size_t* off_flag) {
+  const size_t rows = a.nseg > 1 ? (size_t)a.nseg * a.n_q * a.Hq : 0;
+  size_t off = align256(rows * a.D * 4);
+  *off_lse = off;
+  off += align256(rows * 4);
+  *off_vt = off;
+  off += align256((size_t)a.H * a.nblk * a.D * BK * 2);
+  *off_flag = off;
+  off += align256((size_t)a.H * a.nblk * 4);
+  return off;
 }
 
 size_t attn_ws_bytes(const AttnArgs& a) {
-  if (a.dtype != CT_BF16 || a.nseg <= 1) return 0;
-  const size_t rows = (size_t)a.nseg * a.n_q * a.Hq;
-  return align256(rows * a.D * 4) + align256(rows * 4);
+  if (a.dtype != CT_BF16) return 0;
+  size_t o1, o2, o3;
+  return ws_layout(a, &o1, &o2, &o3);
 }
 
 ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return CT_OK;
   if (a.dtype == CT_F32) return attn_f32_run(a, stream);
-  const size_t need = attn_ws_bytes(a);
-  if (need > 0) {
-    if (!ws || ws_bytes < need)
-      return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
-    const size_t rows = (size_t)a.nseg * a.n_q * a.Hq;
-    a.part_o = reinterpret_cast<float*>(ws);
-    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(rows * a.D * 4));
-  }
+  size_t off_lse, off_vt, off_flag;
+  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag);
+  if (!ws || ws_bytes < need)
+    return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
+  char* w = reinterpret_cast<char*>(ws);
+  a.part_o = reinterpret_cast<float*>(w);
+  a.part_lse = reinterpret_cast<float*>(w + off_lse);
+  a.vt16 = reinterpret_cast<uint16_t*>(w + off_vt);
+  a.vflag = reinterpret_cast<int32_t*>(w + off_flag);
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
 }
 

@@ -121,6 +121,9 @@ struct AttnArgs {
   int32_t n_tg;      // tile groups (tpb * qt tiles each)
   float* part_o;     // [nseg][n_q][Hq][D] normalised partial outputs
   float* part_lse;   // [nseg][n_q][Hq] log2-sum-exp of the partials
+  int32_t nblk;      // 64-key tiles covering [0, T)
+  uint16_t* vt16;    // [H][nblk][D][64] V^T tiles as fp16 (keys permuted)
+  int32_t* vflag;    // [H][nblk] tile holds a V outside the fp16 range
 };
 void attn_plan(AttnArgs* a, int n_cu);
 size_t attn_ws_bytes(const AttnArgs& a);
