@@ -267,6 +267,70 @@ __global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
   }
 }
 
+// Energy per token from the Gram of one problem (256 threads):
+// coefficients of E * nf^2 = sum_k A_k cos(k phi) + B_k sin(k phi), k < 2kk-1.
+// With weights w_j (1 for DC and the Nyquist bin, 2 otherwise) and
+// RR = G[j][j'], SS = G[kk+j][kk+j'], RS = G[j][kk+j']:
+//   alpha_d = sum_{j-j'=d} w w (RR+SS),  beta_s = sum_{j+j'=s} w w (RR-SS),
+//   gamma_s = 2 sum_{j+j'=s} w w RS,     delta_d = 2 sum_{j-j'=d} w w RS,
+//   A_0 = (alpha_0 + beta_0)/2,  A_k = (2 alpha_k + beta_k)/2,
+//   B_k = (gamma_k - delta_k + delta_{-k})/2.
+// E is then evaluated for every token by a complex Horner scheme in fp64.
+template <int NTH>
+__device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const double* G,
+                            double* coef, char* ws) {
+  const int tid = threadIdx.x;
+  const int kk = d.kk, P2 = 2 * kk, nf = d.nf, N = d.n;
+  const int K2 = 2 * kk - 1;
+  const bool even = (nf % 2) == 0;
+  for (int k = tid; k < K2; k += NTH) {
+    double alpha = 0.0, beta = 0.0, gamma = 0.0, dpos = 0.0, dneg = 0.0;
+    for (int j = 0; j < kk; ++j) {
+      double wj = (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0;
+      int jp = j - k;  // j - j' = k
+      if (jp >= 0) {
+        double wjp = (jp == 0 || (even && 2 * jp == nf)) ? 1.0 : 2.0;
+        double w = wj * wjp;
+        alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
+        dpos += w * G[(size_t)j * P2 + kk + jp];
+      }
+      int jn = j + k;  // j - j' = -k
+      if (k > 0 && jn < kk) {
+        double wjn = (jn == 0 || (even && 2 * jn == nf)) ? 1.0 : 2.0;
+        dneg += wj * wjn * G[(size_t)j * P2 + kk + jn];
+      }
+      int js = k - j;  // j + j' = k
+      if (js >= 0 && js < kk) {
+        double wjs = (js == 0 || (even && 2 * js == nf)) ? 1.0 : 2.0;
+        double w = wj * wjs;
+        beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
+        gamma += w * G[(size_t)j * P2 + kk + js];
+      }
+    }
+    double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
+    double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
+    coef[k] = A;
+    coef[K2 + k] = B;
+  }
+  __syncthreads();
+
+  // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.
+  const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+  double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
+  const double inv = 1.0 / ((double)nf * (double)nf);
+  for (int n = tid; n < N; n += NTH) {
+    double2 z = trig[n];
+    double pr = coef[K2 - 1], pi = -coef[2 * K2 - 1];
+    for (int k = K2 - 2; k >= 0; --k) {
+      double nr = pr * z.x - pi * z.y + coef[k];
+      double ni = pr * z.y + pi * z.x - coef[K2 + k];
+      pr = nr;
+      pi = ni;
+    }
+    E[n] = pr * inv;
+  }
+}
+
 // ---- 2/3. Gram of the band coefficients and energy evaluation ----------------
 // One block per (chunk, layer, K|V) problem (blocks loop over problems); the
 // block's Gram and polynomial coefficients live in its workspace slot.
@@ -329,61 +393,7 @@ __global__ __launch_bounds__(256) void k_gram_eval(ScoreLaunch sl, char* ws, int
       }
     __syncthreads();
 
-    // Coefficients of E * nf^2 = sum_k A_k cos(k phi) + B_k sin(k phi), k < 2kk-1.
-    // With weights w_j (1 for DC and the Nyquist bin, 2 otherwise) and
-    // RR = G[j][j'], SS = G[kk+j][kk+j'], RS = G[j][kk+j']:
-    //   alpha_d = sum_{j-j'=d} w w (RR+SS),  beta_s = sum_{j+j'=s} w w (RR-SS),
-    //   gamma_s = 2 sum_{j+j'=s} w w RS,     delta_d = 2 sum_{j-j'=d} w w RS,
-    //   A_0 = (alpha_0 + beta_0)/2,  A_k = (2 alpha_k + beta_k)/2,
-    //   B_k = (gamma_k - delta_k + delta_{-k})/2.
-    const int K2 = 2 * kk - 1;
-    const bool even = (nf % 2) == 0;
-    for (int k = tid; k < K2; k += 256) {
-      double alpha = 0.0, beta = 0.0, gamma = 0.0, dpos = 0.0, dneg = 0.0;
-      for (int j = 0; j < kk; ++j) {
-        double wj = (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0;
-        int jp = j - k;  // j - j' = k
-        if (jp >= 0) {
-          double wjp = (jp == 0 || (even && 2 * jp == nf)) ? 1.0 : 2.0;
-          double w = wj * wjp;
-          alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
-          dpos += w * G[(size_t)j * P2 + kk + jp];
-        }
-        int jn = j + k;  // j - j' = -k
-        if (k > 0 && jn < kk) {
-          double wjn = (jn == 0 || (even && 2 * jn == nf)) ? 1.0 : 2.0;
-          dneg += wj * wjn * G[(size_t)j * P2 + kk + jn];
-        }
-        int js = k - j;  // j + j' = k
-        if (js >= 0 && js < kk) {
-          double wjs = (js == 0 || (even && 2 * js == nf)) ? 1.0 : 2.0;
-          double w = wj * wjs;
-          beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
-          gamma += w * G[(size_t)j * P2 + kk + js];
-        }
-      }
-      double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
-      double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
-      coef[k] = A;
-      coef[K2 + k] = B;
-    }
-    __syncthreads();
-
-    // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.
-    const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
-    double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
-    const double inv = 1.0 / ((double)nf * (double)nf);
-    for (int n = tid; n < N; n += 256) {
-      double2 z = trig[n];
-      double pr = coef[K2 - 1], pi = -coef[2 * K2 - 1];
-      for (int k = K2 - 2; k >= 0; --k) {
-        double nr = pr * z.x - pi * z.y + coef[k];
-        double ni = pr * z.y + pi * z.x - coef[K2 + k];
-        pr = nr;
-        pi = ni;
-      }
-      E[n] = pr * inv;
-    }
+    poly_energy<256>(d, layer, kv, G, coef, ws);
     __syncthreads();
   }
 }
@@ -409,60 +419,180 @@ __device__ double block_reduce(double v, int op, double* red) {
   return r;
 }
 
-__global__ __launch_bounds__(kFinThreads) void k_finalize(ScoreLaunch sl, char* ws, float* score,
-                                                          float* layer_score) {
+// ---- 2'. Gram on the matrix cores (problems with 2*kk <= 128) ----------------
+// G = Y Y^T over the C channels.  Y (fp32) is split per stage of 64 channels
+// into three bf16 planes Y = Y1 + Y2 + Y3 (exact to 2^-26), and
+//   G = Y1Y1 + Y1Y2 + Y2Y1 + Y1Y3 + Y3Y1 + Y2Y2   (dropped terms < 2^-25 |G|)
+// with bf16 products exact in fp32; accumulation in fp32 over 256 channels,
+// then in fp64.  Only tiles on or above the diagonal are computed; each
+// writes both halves.  Both MFMA operands are "8 channels of one band row",
+// so A and B are read from the same plane rows (no transpose).
+constexpr int kGramCh = 64;            // channels per stage
+constexpr int kGramPS = kGramCh + 8;   // plane row stride (bf16): 144 B
+
+__global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
+  // bf16 planes during the accumulation, then the fp64 Gram and coefficients
+  __shared__ __attribute__((aligned(16))) double lds_g[128 * 128 + 256];
+  typedef uint16_t plane_t[128 * kGramPS];
+  plane_t* pl = reinterpret_cast<plane_t*>(lds_g);
+  static_assert(sizeof(uint16_t) * 3 * 128 * kGramPS <= sizeof(double) * 128 * 128, "plane alias");
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.x;
+  const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int ppad = d.ppad, P2 = 2 * d.kk, nt = ppad / 32;
+  const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
+
+  // upper tiles of the nt x nt tile grid; wave w owns tiles w and w + 8
+  int tI[2] = {0, 0}, tJ[2] = {0, 0};
+  bool own[2] = {false, false};
+  {
+    int u = 0;
+    for (int ti = 0; ti < nt; ++ti)
+      for (int tj = ti; tj < nt; ++tj, ++u) {
+        if (u == wave) { tI[0] = ti; tJ[0] = tj; own[0] = true; }
+        if (u == wave + 8) { tI[1] = ti; tJ[1] = tj; own[1] = true; }
+      }
+  }
+  f32x16_t acc[2];
+  double accd[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { acc[i][v] = 0.f; accd[i][v] = 0.0; }
+
+  for (int c0 = 0; c0 < C; c0 += kGramCh) {
+    __syncthreads();
+    for (int item = tid; item < ppad * (kGramCh / 4); item += 512) {
+      const int r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
+      const float4 v = *reinterpret_cast<const float4*>(Y + (size_t)r * C + c0 + q4);
+      const float x[4] = {v.x, v.y, v.z, v.w};
+      uint32_t h[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b1 = bf16_rne_from_f32_bits(__float_as_uint(x[e]));
+        const float r1 = x[e] - __uint_as_float(b1 << 16);
+        const uint32_t b2 = bf16_rne_from_f32_bits(__float_as_uint(r1));
+        const float r2 = r1 - __uint_as_float(b2 << 16);
+        h[0][e] = b1;
+        h[1][e] = b2;
+        h[2][e] = bf16_rne_from_f32_bits(__float_as_uint(r2));
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<uint2*>(&pl[q][r * kGramPS + q4]) =
+            make_uint2(h[q][0] | (h[q][1] << 16), h[q][2] | (h[q][3] << 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kGramCh / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (!own[i]) continue;
+        const int ra = (tI[i] * 32 + col) * kGramPS + 16 * ks + 8 * g;
+        const int rb = (tJ[i] * 32 + col) * kGramPS + 16 * ks + 8 * g;
+        bf16x8_t a[3], bb[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          a[q] = *reinterpret_cast<const bf16x8_t*>(&pl[q][ra]);
+          bb[q] = *reinterpret_cast<const bf16x8_t*>(&pl[q][rb]);
+        }
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[0], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[1], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[0], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[2], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], bb[0], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[1], acc[i], 0, 0, 0);
+      }
+    }
+    if (((c0 + kGramCh) % 256) == 0 || c0 + kGramCh >= C) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          accd[i][v] += (double)acc[i][v];
+          acc[i][v] = 0.f;
+        }
+    }
+  }
+  __syncthreads();  // planes no longer read: the buffer now holds G [P2][P2]
+  double* Gs = lds_g;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (!own[i]) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = tI[i] * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int c = tJ[i] * 32 + col;
+      if (r < P2 && c < P2) {
+        Gs[r * P2 + c] = accd[i][v];
+        Gs[c * P2 + r] = accd[i][v];
+      }
+    }
+  }
+  __syncthreads();
+  poly_energy<512>(d, layer, kv, Gs, lds_g + 128 * 128, ws);
+}
+
+// ---- 4'. per (chunk, layer): magnitudes and normalisation --------------------
+// s = sqrt(E_K)/2 + sqrt(E_V)/2 per token, normalised within the layer; the
+// result overwrites the E_K row of the layer (read before written by the same
+// thread).  Fixed-order block reductions keep it deterministic.
+__global__ __launch_bounds__(kFinThreads) void k_layer_norm(ScoreLaunch sl, char* ws,
+                                                            float* layer_score) {
   __shared__ double red[kFinThreads];
   const ScoreChunkDesc& d = sl.c[blockIdx.x];
-  const int N = d.n, L = sl.L, tid = threadIdx.x;
-  const double* E = reinterpret_cast<const double*>(ws + d.e_off);
-  double acc[kFinPer];
+  const int l = blockIdx.y, N = d.n, tid = threadIdx.x;
+  double* ek = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(l * 2) * N;
+  const double* ev = ek + N;
+  double s[kFinPer];
+  double part_sum = 0.0, part_max = -INFINITY, part_min = INFINITY;
 #pragma unroll
-  for (int i = 0; i < kFinPer; ++i) acc[i] = 0.0;
-  for (int l = 0; l < L; ++l) {
-    const double* ek = E + (size_t)(l * 2) * N;
-    const double* ev = E + (size_t)(l * 2 + 1) * N;
-    double s[kFinPer];
-    double part_sum = 0.0, part_max = -INFINITY, part_min = INFINITY;
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i) {
-      int n = tid * kFinPer + i;
-      s[i] = 0.0;
-      if (n < N) {
-        s[i] = 0.5 * sqrt(fmax(ek[n], 0.0)) + 0.5 * sqrt(fmax(ev[n], 0.0));
-        part_sum += s[i];
-        part_max = fmax(part_max, s[i]);
-        part_min = fmin(part_min, s[i]);
-      }
+  for (int i = 0; i < kFinPer; ++i) {
+    const int n = tid * kFinPer + i;
+    s[i] = 0.0;
+    if (n < N) {
+      s[i] = 0.5 * sqrt(fmax(ek[n], 0.0)) + 0.5 * sqrt(fmax(ev[n], 0.0));
+      part_sum += s[i];
+      part_max = fmax(part_max, s[i]);
+      part_min = fmin(part_min, s[i]);
     }
-    // normalisation: v = (s - shift) / denom, or the constant `fill`
-    double denom = 1.0, shift = 0.0, fill = -1.0;
-    if (sl.norm == CT_NORM_SUM) {
-      double t = block_reduce(part_sum, 0, red);
-      if (t > 0.0) denom = t; else fill = 1.0 / (double)N;
-    } else if (sl.norm == CT_NORM_MAX) {
-      double mx = block_reduce(part_max, 1, red);
-      if (mx > 0.0) denom = mx; else fill = 0.0;
-    } else if (sl.norm == CT_NORM_MINMAX) {
-      double mx = block_reduce(part_max, 1, red);
-      double mn = block_reduce(part_min, 2, red);
-      if (mx - mn > 0.0) { denom = mx - mn; shift = mn; } else fill = 0.0;
-    }
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i) {
-      int n = tid * kFinPer + i;
-      if (n < N) {
-        double v = fill >= 0.0 ? fill : (s[i] - shift) / denom;
-        if (sl.norm == CT_NORM_NONE) v = s[i];
-        acc[i] += v;
-        if (layer_score) layer_score[(size_t)l * sl.total_tokens + d.tok_off + n] = (float)v;
-      }
-    }
+  }
+  // normalisation: v = (s - shift) / denom, or the constant `fill`
+  double denom = 1.0, shift = 0.0, fill = -1.0;
+  if (sl.norm == CT_NORM_SUM) {
+    const double t = block_reduce(part_sum, 0, red);
+    if (t > 0.0) denom = t; else fill = 1.0 / (double)N;
+  } else if (sl.norm == CT_NORM_MAX) {
+    const double mx = block_reduce(part_max, 1, red);
+    if (mx > 0.0) denom = mx; else fill = 0.0;
+  } else if (sl.norm == CT_NORM_MINMAX) {
+    const double mx = block_reduce(part_max, 1, red);
+    const double mn = block_reduce(part_min, 2, red);
+    if (mx - mn > 0.0) { denom = mx - mn; shift = mn; } else fill = 0.0;
   }
 #pragma unroll
   for (int i = 0; i < kFinPer; ++i) {
-    int n = tid * kFinPer + i;
-    if (n < N) score[d.tok_off + n] = (float)(acc[i] / (double)L);
+    const int n = tid * kFinPer + i;
+    if (n < N) {
+      double v = fill >= 0.0 ? fill : (s[i] - shift) / denom;
+      if (sl.norm == CT_NORM_NONE) v = s[i];
+      ek[n] = v;
+      if (layer_score) layer_score[(size_t)l * sl.total_tokens + d.tok_off + n] = (float)v;
+    }
   }
+}
+
+// ---- 4''. mean over layers, in layer order ------------------------------------
+__global__ __launch_bounds__(256) void k_layer_mean(ScoreLaunch sl, char* ws, float* score) {
+  const ScoreChunkDesc& d = sl.c[blockIdx.y];
+  const int n = blockIdx.x * 256 + threadIdx.x, N = d.n, L = sl.L;
+  if (n >= N) return;
+  const double* e = reinterpret_cast<const double*>(ws + d.e_off);
+  double acc = 0.0;
+  for (int l = 0; l < L; ++l) acc += e[(size_t)(l * 2) * N + n];
+  score[d.tok_off + n] = (float)(acc / (double)L);
 }
 
 }  // namespace
@@ -531,9 +661,12 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   }
   const int64_t slot_bytes = (int64_t)align256(((size_t)max_p2 * max_p2 + 2 * (size_t)max_p2) * 8);
   int64_t probs_max = (int64_t)std::min(n_chunks, kMaxChunksPerLaunch) * L * 2;
-  int64_t n_slots = std::min<int64_t>(probs_max, 1024);
+  // Matrix-core Gram (2kk <= 128) keeps G in LDS and needs no slot; larger
+  // bands take the fp64 path, whose blocks loop over problems and slots.
+  const bool mfma_gram = max_p2 <= 128;
+  int64_t n_slots = mfma_gram ? 0 : std::min<int64_t>(probs_max, 1024);
   const int64_t slot_budget = (int64_t)1 << 30;
-  while (n_slots > 1 && n_slots * slot_bytes > slot_budget) n_slots /= 2;
+  while (!mfma_gram && n_slots > 1 && n_slots * slot_bytes > slot_budget) n_slots /= 2;
   const int64_t slot_off = (int64_t)off;
   off += (size_t)(n_slots * slot_bytes);
   *bytes = align256(off);
@@ -577,14 +710,24 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
       hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
     if (ct_status s = check_launch("band projection")) return s;
 
-    int n_probs = sl.n_chunks * sl.L * 2;
-    int grid = std::min(n_probs, sl.n_slots);
-    hipLaunchKernelGGL(k_gram_eval, dim3(grid), dim3(256), 0, stream, sl, ws, n_probs);
-    if (ct_status s = check_launch("gram/eval")) return s;
+    const int n_probs = sl.n_chunks * sl.L * 2;
+    if (sl.slot_p2 <= 128) {
+      hipLaunchKernelGGL(k_gram_mfma, dim3(n_probs), dim3(512), 0, stream, sl, ws);
+      if (ct_status s = check_launch("gram/energy")) return s;
+    } else {
+      const int grid = std::min(n_probs, sl.n_slots);
+      hipLaunchKernelGGL(k_gram_eval, dim3(grid), dim3(256), 0, stream, sl, ws, n_probs);
+      if (ct_status s = check_launch("gram/eval")) return s;
+    }
 
-    hipLaunchKernelGGL(k_finalize, dim3(sl.n_chunks), dim3(kFinThreads), 0, stream, sl, ws, score,
+    int max_n = 0;
+    for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
+    hipLaunchKernelGGL(k_layer_norm, dim3(sl.n_chunks, sl.L), dim3(kFinThreads), 0, stream, sl, ws,
                        layer_score);
-    if (ct_status s = check_launch("finalize")) return s;
+    if (ct_status s = check_launch("layer normalisation")) return s;
+    hipLaunchKernelGGL(k_layer_mean, dim3((max_n + 255) / 256, sl.n_chunks), dim3(256), 0, stream,
+                       sl, ws, score);
+    if (ct_status s = check_launch("layer mean")) return s;
   }
   return CT_OK;
 }
