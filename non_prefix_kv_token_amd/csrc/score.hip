@@ -331,6 +331,160 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
   }
 }
 
+// bf16 data: the same projection, software-pipelined.  X (the HBM stream) is
+// loaded two 32-token steps ahead into registers; the twiddle slab of the
+// next step is loaded one step ahead and written to the other of two LDS
+// buffers after the current step's MFMAs, so each step has one barrier and
+// no exposed load latency.  NTL = 32-row band tiles per block (the launch's
+// largest; rows a chunk does not have are zero).  The step loop is unrolled
+// by two so that both register and LDS buffers are compile-time.
+template <int NTL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_band_bf16(ScoreLaunch sl, char* ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][3 * 32 * NTL * kTwStride];
+
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.z;
+  const int b = prob / (2 * L);
+  const int layer = (prob / 2) % L;
+  const int kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int pbase = blockIdx.y * 32 * NTL;
+  if (pbase >= d.ppad) return;
+  const int nrows = min(32 * NTL, d.ppad - pbase);  // rows this chunk has in the block
+  const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
+  const int nsteps = (N + 31) / 32;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int cbase = blockIdx.x * 256 + wave * 64;
+  const bool active = cbase < C;
+  const int c0 = cbase + 2 * col;
+
+  // Buffer resources (gfx9 word 3): a load whose VGPR offset is at or past
+  // num_records returns 0, which zero-fills tokens at and beyond N and rows a
+  // chunk does not have.  The whole offset is kept in the VGPR operand (the
+  // scalar offset is 0), so that range check covers every load.
+  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + d.tw_off);
+  const long long plane = (long long)ppad * ntp;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src + (size_t)layer * N * C), 0, N * C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(tw), 0, (int)(3 * plane * 2), 0x00020000);
+  const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;  // inactive lanes read zeros
+
+  f32x16_t acc[NTL][2];
+#pragma unroll
+  for (int i = 0; i < NTL; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][m][v] = 0.f;
+
+  // X of a step: 2 k-steps x 8 tokens x (2 channels in one dword)
+  uint32_t xa[16], xb[16];
+  auto load_x = [&](int step, uint32_t* dst) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        dst[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, xvoff + (step * 32 + 16 * s2 + t) * C * 2, 0, 0);
+  };
+  // twiddle slab of a step: 3 planes x 32*NTL rows x 32 tokens (16-byte chunks)
+  constexpr int TWN = 3 * 32 * NTL * 4;    // chunks per slab
+  constexpr int TWI = (TWN + 255) / 256;   // chunks per thread (the last may be partial)
+  u32x4_t twr[TWI];
+  int twoff[TWI];
+#pragma unroll
+  for (int it = 0; it < TWI; ++it) {
+    const int item = tid + 256 * it;
+    const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
+    // rows this chunk does not have read past the table (zeros)
+    twoff[it] = (item < TWN && r < nrows) ? (int)((q * plane + (long long)(pbase + r) * ntp + 8 * i) * 2)
+                                          : (int)(3 * plane * 2);
+  }
+  auto load_tw = [&](int step) {
+#pragma unroll
+    for (int it = 0; it < TWI; ++it)
+      twr[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tres, twoff[it] + step * 64, 0, 0));
+  };
+  auto store_tw = [&](uint16_t* buf) {
+#pragma unroll
+    for (int it = 0; it < TWI; ++it) {
+      const int item = tid + 256 * it;
+      if (TWN % 256 != 0 && item >= TWN) break;
+      const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
+      *reinterpret_cast<u32x4_t*>(&buf[(q * 32 * NTL + r) * kTwStride + 8 * i]) = twr[it];
+    }
+  };
+  auto compute = [&](const uint16_t* buf, const uint32_t* xs) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4_t bu[2];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t w0 = xs[8 * s2 + 2 * h], w1 = xs[8 * s2 + 2 * h + 1];
+        bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
+        bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bu[0]);
+      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bu[1]);
+      bf16x8_t a[NTL][3];
+#pragma unroll
+      for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          a[pt][q] = *reinterpret_cast<const bf16x8_t*>(
+              &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
+#pragma unroll
+      for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b0, acc[pt][0], 0, 0, 0);
+          acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b1, acc[pt][1], 0, 0, 0);
+        }
+    }
+  };
+
+  load_x(0, xa);
+  if (nsteps > 1) load_x(1, xb);
+  load_tw(0);
+  store_tw(lds[0]);
+  if (nsteps > 1) load_tw(1);
+  for (int step = 0; step < nsteps; step += 2) {
+    // even step: LDS buffer 0, registers xa
+    __syncthreads();
+    if (active) compute(lds[0], xa);
+    if (step + 1 < nsteps) store_tw(lds[1]);
+    if (step + 2 < nsteps) {
+      load_tw(step + 2);
+      load_x(step + 2, xa);
+    }
+    if (step + 1 >= nsteps) break;
+    // odd step: LDS buffer 1, registers xb
+    __syncthreads();
+    if (active) compute(lds[1], xb);
+    if (step + 2 < nsteps) store_tw(lds[0]);
+    if (step + 3 < nsteps) {
+      load_tw(step + 3);
+      load_x(step + 3, xb);
+    }
+  }
+
+  if (!active) return;
+  float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+#pragma unroll
+  for (int pt = 0; pt < NTL; ++pt) {
+    if (pt * 32 >= nrows) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = pbase + pt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
+    }
+  }
+}
+
 // ---- 2/3. Gram of the band coefficients and energy evaluation ----------------
 // One block per (chunk, layer, K|V) problem (blocks loop over problems); the
 // block's Gram and polynomial coefficients live in its workspace slot.
@@ -704,9 +858,15 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
     if (ct_status s = check_launch("twiddle")) return s;
 
     dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
-    if (sl.dtype == CT_BF16)
-      hipLaunchKernelGGL(k_band_fwd<CT_BF16>, gb, dim3(256), 0, stream, sl, ws);
-    else
+    if (sl.dtype == CT_BF16) {
+      // band tiles per block: the launch's largest band, up to 4 (128 rows)
+      const int ntl = sl.max_ppad >= 128 ? 4 : sl.max_ppad / 32;
+      dim3 gq((sl.C + 255) / 256, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+      if (ntl == 4) hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(256), 0, stream, sl, ws);
+      else if (ntl == 3) hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(256), 0, stream, sl, ws);
+      else if (ntl == 2) hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(256), 0, stream, sl, ws);
+      else hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(256), 0, stream, sl, ws);
+    } else
       hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
     if (ct_status s = check_launch("band projection")) return s;
 
