@@ -200,21 +200,11 @@ class Workload:
         self.ct.cachetune_recompute_attn(self.q[l], self.qpos, self.k_asm, self.v_asm, self.scale,
                                          self.theta, out=self.out, ws=self.attn_ws)
 
-    def step(self, ev=None):
-        if ev is not None:
-            ev["s0"].record()
+    def step(self):
         self.score_and_select()
-        if ev is not None:
-            ev["s1"].record()
         for l in range(self.L):
-            if ev is not None:
-                ev["a0"][l].record()
             self.assemble(l)
-            if ev is not None:
-                ev["a1"][l].record()
             self.attend(l)
-            if ev is not None:
-                ev["a2"][l].record()
 
     # ---- algorithmic work -----------------------------------------------------------
     def attn_flops_per_layer(self) -> float:
@@ -297,6 +287,34 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
     }
 
 
+KERNEL_SOURCES = {"attention": "non_prefix_kv_token_amd/csrc/attn.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_llama3-8b-8x2048.md")
+
+
+def source_sha256(rel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a device copy of known size), or None when there is no record
+    for this workload or the kernel source has changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = source_sha256(KERNEL_SOURCES[kernel])
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("traffic-record:"):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split()[1:])
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source_sha256") == sha:
+            return float(kv["fetch_bytes"]) * float(kv["fetch_scale"]) + \
+                float(kv["write_bytes"]) * float(kv["write_scale"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +336,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     w = Workload(args.workload)
+    ct = w.ct
     print(f"[bench] inputs generated in {w.gen_seconds:.1f}s; T={w.T} n_q={w.n_q}", file=sys.stderr,
           flush=True)
 
@@ -334,27 +353,41 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
+    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble",
+             "attention_prep", "attention", "attention_merge"]
+    for n in names:  # drop records of earlier launches
+        ct.cachetune_timing_read(n)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [{"s0": E(), "s1": E(), "a0": [E() for _ in range(w.L)], "a1": [E() for _ in range(w.L)],
-            "a2": [E() for _ in range(w.L)]} for _ in range(args.steps)]
     start, stop = E(), E()
+    ct.cachetune_timing_enable(True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
-        w.step(evs[i])
+    for _ in range(args.steps):
+        w.step()
     stop.record()
     torch.cuda.synchronize()
+    ct.cachetune_timing_enable(False)
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    kt = {n: ct.cachetune_timing_read(n) for n in names}  # name -> (total ms, launches)
 
-    score_ms = np.mean([e["s0"].elapsed_time(e["s1"]) for e in evs])
-    asm_ms = np.mean([e["a0"][l].elapsed_time(e["a1"][l]) for e in evs for l in range(w.L)])
-    attn_ms = np.mean([e["a1"][l].elapsed_time(e["a2"][l]) for e in evs for l in range(w.L)])
+    def per_step(*ns):
+        return sum(kt[n][0] for n in ns) / args.steps
+
+    def per_launch(n):
+        tot, cnt = kt[n]
+        return tot / cnt if cnt else float("nan")
+
     tokens = float(sum(w.ns))
+    score_ms = per_step("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr")
+    asm_ms = per_step("assemble") / w.L
+    attn_call_ms = per_step("attention_prep", "attention", "attention_merge") / w.L
+    attn_kernel_ms = per_launch("attention")
     attn_flops = w.attn_flops_per_layer()
-    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    attn_tflops = attn_flops / (attn_kernel_ms * 1e-3) / 1e12
     score_gbs = w.score_bytes() / (score_ms * 1e-3) / 1e9
     asm_gbs = w.assemble_bytes_per_layer() / (asm_ms * 1e-3) / 1e9
+    traffic = measured_traffic("attention", w.name)
 
     result = {
         "metric": "chunk-KV tokens/s through score->top-r->RoPE-assemble (+ selected-query attention); %HBM peak",
@@ -370,25 +403,35 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded value model: N(0,1) + 3 low-bin sinusoids + 4 x5 spike tokens)",
         "config": {
-            "workload": (f"{len(w.ns)} chunks x {w.ns[0]} tokens, {w.L} layers, {w.Hq} Q / {w.H} KV heads "
-                         f"x {w.D}, {w.dtype}, cutoff {w.alpha[0]}/{w.alpha[1]} of rFFT bins, "
-                         f"r={w.r[0]}/{w.r[1]}, RoPE theta {w.theta:g}, {w.n_sfx}-token suffix"),
+            "workload": (f"{len(w.ns)} chunks x {w.ns[0] if len(set(w.ns)) == 1 else 'ragged'} tokens, "
+                         f"{w.L} layers, {w.Hq} Q / {w.H} KV heads x {w.D}, {w.dtype}, cutoff "
+                         f"{w.alpha[0]}/{w.alpha[1]} of rFFT bins, r={w.r[0]}/{w.r[1]}, RoPE theta "
+                         f"{w.theta:g}, {w.n_sfx}-token suffix"),
             "name": w.name, "T": w.T, "n_q": w.n_q, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "k_attn (selected-query causal GQA attention, per layer)",
+            "kernel": "k_attn_bf16 (selected-query causal GQA attention, one layer)" if w.dtype == "bf16"
+                      else "k_attn (fp32 storage, one layer)",
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch",
+            "launch_ms": attn_kernel_ms,
+            "algorithmic_flops_per_launch": attn_flops,
         },
         "stages": {
             "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
+            "score_kernels_ms": {n: per_step(n) for n in ("twiddle", "band", "gram", "layer_norm",
+                                                           "layer_mean", "topr")},
             "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
             "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS,
-            "attention_ms_per_layer": attn_ms, "attention_TFLOPs": attn_tflops,
+            "attention_call_ms_per_layer": attn_call_ms,
+            "attention_kernels_ms_per_layer": {n: per_step(n) / w.L for n in
+                                               ("attention_prep", "attention", "attention_merge")},
+            "attention_TFLOPs": attn_tflops,
             "attention_flops_per_layer": attn_flops,
             "score_plus_assemble_tokens_per_s": tokens / ((score_ms + asm_ms * w.L) * 1e-3),
         },

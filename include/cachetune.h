@@ -201,6 +201,18 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
 ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
                                       ct_dtype dtype, size_t* bytes);
 
+/* ---- kernel timing (tracing aid) -----------------------------------------
+ * While enabled, each kernel launch of the library is bracketed by a pair of
+ * HIP events on the launch's stream, recorded under the kernel's name:
+ *   "band", "gram", "topr", "assemble", "attention_prep", "attention",
+ *   "attention_merge" (and "twiddle", "layer_norm", "layer_mean").
+ * cachetune_timing_read waits for the events recorded under `kernel`, returns
+ * their summed duration in milliseconds and the number of launches, and
+ * forgets them.  Events of other names are kept.  Thread-safe; the events are
+ * small host objects (no device memory is allocated). */
+ct_status cachetune_timing_enable(int32_t on);
+ct_status cachetune_timing_read(const char* kernel, double* total_ms, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

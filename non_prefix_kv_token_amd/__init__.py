@@ -39,7 +39,8 @@ class CacheTuneError(RuntimeError):
 
 SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version",
            "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
-           "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws"]
+           "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
+           "cachetune_timing_enable", "cachetune_timing_read"]
 
 _lib = None
 
@@ -65,6 +66,8 @@ def lib():
         L.cachetune_recompute_attn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
                                                f64, i32, vp, vp, vp, sz, vp]
         L.cachetune_recompute_attn_ws.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_timing_enable.argtypes = [i32]
+        L.cachetune_timing_read.argtypes = [C.c_char_p, C.POINTER(f64), C.POINTER(i32)]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -210,3 +213,17 @@ def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, styl
                                           _ptr(out), _ptr(lse), _ptr(ws) if need else None,
                                           ws.numel() if need else 0, _stream(stream)))
     return out, lse
+
+
+# ---- kernel timing ---------------------------------------------------------------
+
+def cachetune_timing_enable(on: bool = True):
+    _check(lib().cachetune_timing_enable(1 if on else 0))
+
+
+def cachetune_timing_read(kernel: str):
+    """(total milliseconds, launches) recorded under `kernel` since the last read."""
+    ms = C.c_double(0.0)
+    n = C.c_int32(0)
+    _check(lib().cachetune_timing_read(kernel.encode(), C.byref(ms), C.byref(n)))
+    return ms.value, n.value

@@ -182,7 +182,10 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
 template <int DT, int D>
 ct_status launch(const AsmLaunch& al, void* k_out, void* v_out, hipStream_t stream) {
   dim3 grid((al.max_rows + 3) / 4, al.n_places);
-  hipLaunchKernelGGL((k_assemble<DT, D>), grid, dim3(256), 0, stream, al, k_out, v_out);
+  {
+    TimedLaunch tl_("assemble", stream);
+    hipLaunchKernelGGL((k_assemble<DT, D>), grid, dim3(256), 0, stream, al, k_out, v_out);
+  }
   return check_launch("assemble");
 }
 

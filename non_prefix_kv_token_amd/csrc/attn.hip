@@ -629,15 +629,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
+  {
+    TimedLaunch tl_("attention_prep", stream);
+    hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
+  }
   if (ct_status s = check_launch("attention V preparation")) return s;
   const int blocks = a.H * a.n_tg * a.n_hc * a.nseg;
-  if (a.qt == 2)
-    hipLaunchKernelGGL((k_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, stream, a);
-  else if (a.nw == 8)
-    hipLaunchKernelGGL((k_attn_bf16<D, 8, 1>), dim3(blocks), dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_attn_bf16<D, 4, 1>), dim3(blocks), dim3(256), 0, stream, a);
+  {
+    TimedLaunch tl_("attention", stream);
+    if (a.qt == 2)
+      hipLaunchKernelGGL((k_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, stream, a);
+    else if (a.nw == 8)
+      hipLaunchKernelGGL((k_attn_bf16<D, 8, 1>), dim3(blocks), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_attn_bf16<D, 4, 1>), dim3(blocks), dim3(256), 0, stream, a);
+  }
   if (ct_status s = check_launch("attention")) {
     set_error(std::string(cachetune_last_error()) + " [grid " + std::to_string(blocks) + ", waves " +
               std::to_string(a.nw) + ", tiles/wave " + std::to_string(a.qt) + ", segments " +
@@ -646,7 +652,10 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
   }
   if (a.nseg > 1) {
     const long long waves = (long long)a.n_q * a.Hq;
-    hipLaunchKernelGGL((k_attn_merge<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    {
+      TimedLaunch tl_("attention_merge", stream);
+      hipLaunchKernelGGL((k_attn_merge<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    }
     if (ct_status s = check_launch("attention merge")) return s;
   }
   return CT_OK;

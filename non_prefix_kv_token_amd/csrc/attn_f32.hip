@@ -303,7 +303,10 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
   const int ntiles = (a.n_q + 31) / 32;
   const int units = ntiles * a.group;
   dim3 grid((units + 3) / 4, a.H);
-  hipLaunchKernelGGL((k_attn<DT, D>), grid, dim3(256), 0, stream, a);
+  {
+    TimedLaunch tl_("attention", stream);
+    hipLaunchKernelGGL((k_attn<DT, D>), grid, dim3(256), 0, stream, a);
+  }
   return check_launch("attention");
 }
 

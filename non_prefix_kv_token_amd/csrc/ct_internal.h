@@ -16,6 +16,22 @@ void set_error(const std::string& msg);
 ct_status fail(ct_status s, const std::string& msg);
 ct_status check_launch(const char* what);
 
+// ------------------------------------------------------------ timing
+// Brackets one kernel launch with HIP events when timing is enabled
+// (cachetune_timing_enable); a no-op otherwise.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t stream);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  hipStream_t stream_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+  std::string name_;
+};
+
 // ------------------------------------------------------- shared constants
 constexpr int kMaxChunksPerLaunch = 32;  // descriptors passed by value in kernel arguments
 constexpr int kMaxN = 8192;              // tokens per chunk

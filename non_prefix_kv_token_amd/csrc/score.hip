@@ -854,10 +854,15 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
     for (int i = 0; i < sl.n_chunks; ++i)
       max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
     dim3 gt((max_elems + 255) / 256 < 2048 ? (max_elems + 255) / 256 : 2048, sl.n_chunks);
-    hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
+    {
+      TimedLaunch tl_("twiddle", stream);
+      hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
+    }
     if (ct_status s = check_launch("twiddle")) return s;
 
     dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
+    {
+    TimedLaunch tl_("band", stream);
     if (sl.dtype == CT_BF16) {
       // band tiles per block: the launch's largest band, up to 4 (128 rows)
       const int ntl = sl.max_ppad >= 128 ? 4 : sl.max_ppad / 32;
@@ -868,25 +873,34 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
       else hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(256), 0, stream, sl, ws);
     } else
       hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
+    }
     if (ct_status s = check_launch("band projection")) return s;
 
     const int n_probs = sl.n_chunks * sl.L * 2;
     if (sl.slot_p2 <= 128) {
+      TimedLaunch tl_("gram", stream);
       hipLaunchKernelGGL(k_gram_mfma, dim3(n_probs), dim3(512), 0, stream, sl, ws);
       if (ct_status s = check_launch("gram/energy")) return s;
     } else {
       const int grid = std::min(n_probs, sl.n_slots);
+      TimedLaunch tl_("gram", stream);
       hipLaunchKernelGGL(k_gram_eval, dim3(grid), dim3(256), 0, stream, sl, ws, n_probs);
       if (ct_status s = check_launch("gram/eval")) return s;
     }
 
     int max_n = 0;
     for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
-    hipLaunchKernelGGL(k_layer_norm, dim3(sl.n_chunks, sl.L), dim3(kFinThreads), 0, stream, sl, ws,
-                       layer_score);
+    {
+      TimedLaunch tl_("layer_norm", stream);
+      hipLaunchKernelGGL(k_layer_norm, dim3(sl.n_chunks, sl.L), dim3(kFinThreads), 0, stream, sl, ws,
+                         layer_score);
+    }
     if (ct_status s = check_launch("layer normalisation")) return s;
-    hipLaunchKernelGGL(k_layer_mean, dim3((max_n + 255) / 256, sl.n_chunks), dim3(256), 0, stream,
-                       sl, ws, score);
+    {
+      TimedLaunch tl_("layer_mean", stream);
+      hipLaunchKernelGGL(k_layer_mean, dim3((max_n + 255) / 256, sl.n_chunks), dim3(256), 0, stream,
+                         sl, ws, score);
+    }
     if (ct_status s = check_launch("layer mean")) return s;
   }
   return CT_OK;

@@ -92,8 +92,11 @@ __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* s
 
 ct_status topr_run(const TopRLaunch& tl, const float* score, int32_t* ranking, int32_t* sel,
                    int32_t* comp, hipStream_t stream) {
-  hipLaunchKernelGGL(k_topr, dim3(tl.n_chunks), dim3(kThreads), 0, stream, tl, score, ranking,
+  {
+    TimedLaunch tl_("topr", stream);
+    hipLaunchKernelGGL(k_topr, dim3(tl.n_chunks), dim3(kThreads), 0, stream, tl, score, ranking,
                      sel, comp);
+  }
   return check_launch("top-r");
 }
 
