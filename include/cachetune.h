@@ -201,11 +201,46 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
 ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
                                       ct_dtype dtype, size_t* bytes);
 
+/* ---- host-tier sparse loading (App. B.1 stored ranking, App. B.2) ----------
+ * Offline, when a chunk's cache is generated, its rows are stored in rank
+ * order, so that for any r the reuse complement of a (chunk, layer) is the
+ * contiguous tail [k, n) of that layer and loads with one copy.
+ *
+ * cachetune_rank_order: k_dst[l][j] = k_src[l][ranking[j]] (and likewise V)
+ * for every layer l < L and row j < n.  k_src, v_src, k_dst, v_dst: device
+ * [L][n][H][D], 16-byte aligned, destinations distinct from sources;
+ * ranking: device int32[n] (a permutation of [0, n), as written by
+ * cachetune_select_topr); trusted, not range-checked. */
+ct_status cachetune_rank_order(const void* k_src, const void* v_src, const int32_t* ranking,
+                               int32_t n, int32_t L, int32_t H, int32_t D, ct_dtype dtype,
+                               void* k_dst, void* v_dst, hipStream_t stream);
+
+/* One chunk of the host pool: K and V [L][n][H][D] in rank order (host memory;
+ * pinned with hipHostMalloc for the copies to run asynchronously). */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t n;
+  int32_t L;
+} ct_ranked_chunk;
+
+/* Copies the reuse complement of layer `layer` of every chunk -- rank-ordered
+ * rows [k_per_chunk[b], n_b) -- from the host pool into the device staging
+ * buffers k_stage / v_stage, packed: chunk b's rows start at row
+ * sum_{b' < b} (n_b' - k_b').  Two hipMemcpyAsync per chunk are enqueued on
+ * `stream` (for the staged rows, row j of chunk b holds local row
+ * ranking_b[k_b + j]: pass that tail of the ranking as ct_place.src_rows).
+ * k_per_chunk: host int32[n_chunks]. */
+ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_chunks, int32_t layer,
+                                     int32_t H, int32_t D, ct_dtype dtype,
+                                     const int32_t* k_per_chunk, void* k_stage, void* v_stage,
+                                     hipStream_t stream);
+
 /* ---- kernel timing (tracing aid) -----------------------------------------
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
  *   "band", "gram", "topr", "assemble", "attention_prep", "attention",
- *   "attention_merge" (and "twiddle", "layer_norm", "layer_mean").
+ *   "attention_merge", "rank_order" (and "twiddle", "layer_norm", "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and
  * forgets them.  Events of other names are kept.  Thread-safe; the events are

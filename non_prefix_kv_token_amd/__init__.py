@@ -31,6 +31,10 @@ class ct_place(C.Structure):
                 ("comp", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32), ("offset", C.c_int32)]
 
 
+class ct_ranked_chunk(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n", C.c_int32), ("L", C.c_int32)]
+
+
 class CacheTuneError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{msg} (status {status})")
@@ -40,7 +44,8 @@ class CacheTuneError(RuntimeError):
 SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version",
            "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
            "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
-           "cachetune_timing_enable", "cachetune_timing_read"]
+           "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
+           "cachetune_stage_complement"]
 
 _lib = None
 
@@ -67,6 +72,8 @@ def lib():
                                                f64, i32, vp, vp, vp, sz, vp]
         L.cachetune_recompute_attn_ws.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
         L.cachetune_timing_enable.argtypes = [i32]
+        L.cachetune_rank_order.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.cachetune_stage_complement.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.cachetune_timing_read.argtypes = [C.c_char_p, C.POINTER(f64), C.POINTER(i32)]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
@@ -227,3 +234,32 @@ def cachetune_timing_read(kernel: str):
     n = C.c_int32(0)
     _check(lib().cachetune_timing_read(kernel.encode(), C.byref(ms), C.byref(n)))
     return ms.value, n.value
+
+
+# ---- host tier ---------------------------------------------------------------------
+
+def cachetune_rank_order(k_src, v_src, ranking, k_dst=None, v_dst=None, stream=None):
+    """k_src/v_src [L][n][H][D] device, ranking int32[n] device; returns the
+    rank-ordered copies (device)."""
+    import torch
+    L, n, H, D = (int(x) for x in k_src.shape)
+    if k_dst is None:
+        k_dst = torch.empty_like(k_src)
+    if v_dst is None:
+        v_dst = torch.empty_like(v_src)
+    _check(lib().cachetune_rank_order(_ptr(k_src), _ptr(v_src), _ptr(ranking), n, L, H, D,
+                                      _dtype(k_src), _ptr(k_dst), _ptr(v_dst), _stream(stream)))
+    return k_dst, v_dst
+
+
+def cachetune_stage_complement(chunks, layer, k_per_chunk, k_stage, v_stage, stream=None):
+    """chunks: list of (K, V) rank-ordered host tensors [L][n][H][D] (pinned);
+    copies the complement rows of `layer` into k_stage / v_stage (device)."""
+    arr = (ct_ranked_chunk * len(chunks))()
+    for i, (k, v) in enumerate(chunks):
+        arr[i].k, arr[i].v = k.data_ptr(), v.data_ptr()
+        arr[i].L, arr[i].n = int(k.shape[0]), int(k.shape[1])
+    H, D = int(chunks[0][0].shape[2]), int(chunks[0][0].shape[3])
+    ks = _i32_array(k_per_chunk)
+    _check(lib().cachetune_stage_complement(arr, len(chunks), layer, H, D, _dtype(chunks[0][0]), ks,
+                                            _ptr(k_stage), _ptr(v_stage), _stream(stream)))

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcachetune.so")
-SOURCES = ["abi.hip", "score.hip", "topr.hip", "assemble.hip", "attn.hip", "attn_f32.hip", "timing.hip"]
+SOURCES = ["abi.hip", "score.hip", "topr.hip", "assemble.hip", "attn.hip", "attn_f32.hip", "timing.hip", "hosttier.hip"]
 ARCH = os.environ.get("CACHETUNE_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

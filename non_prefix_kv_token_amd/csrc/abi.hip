@@ -312,4 +312,57 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
   CT_GUARD_END
 }
 
+ct_status cachetune_rank_order(const void* k_src, const void* v_src, const int32_t* ranking,
+                               int32_t n, int32_t L, int32_t H, int32_t D, ct_dtype dtype,
+                               void* k_dst, void* v_dst, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (n < 1 || n > kMaxN || L < 1 || H < 1 || D < 1) return fail(CT_E_INVALID, "bad shape");
+  const long long row_bytes = (long long)H * D * (dtype == CT_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0 || row_bytes > (1LL << 30)) return fail(CT_E_UNSUPPORTED, "H*D*element size must be a multiple of 16 bytes");
+  if (!k_src || !v_src || !ranking || !k_dst || !v_dst) return fail(CT_E_INVALID, "NULL argument");
+  if (!(aligned16(k_src) && aligned16(v_src) && aligned16(k_dst) && aligned16(v_dst)))
+    return fail(CT_E_INVALID, "row buffers must be 16-byte aligned");
+  if (k_src == k_dst || v_src == v_dst || k_src == v_dst || v_src == k_dst)
+    return fail(CT_E_INVALID, "destination must not alias the source");
+  return rank_order_run(k_src, v_src, ranking, n, L, (int32_t)row_bytes, k_dst, v_dst, stream);
+  CT_GUARD_END
+}
+
+ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_chunks, int32_t layer,
+                                     int32_t H, int32_t D, ct_dtype dtype,
+                                     const int32_t* k_per_chunk, void* k_stage, void* v_stage,
+                                     hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (!chunks || !k_per_chunk || n_chunks < 1) return fail(CT_E_INVALID, "NULL argument or no chunks");
+  if (layer < 0 || H < 1 || D < 1) return fail(CT_E_INVALID, "bad shape");
+  const size_t row_bytes = (size_t)H * D * (dtype == CT_BF16 ? 2 : 4);
+  size_t rows = 0;
+  for (int b = 0; b < n_chunks; ++b) {
+    const ct_ranked_chunk& c = chunks[b];
+    if (c.n < 1 || c.n > kMaxN || layer >= c.L) return fail(CT_E_INVALID, "chunk: bad n or layer");
+    if (k_per_chunk[b] < 0 || k_per_chunk[b] > c.n) return fail(CT_E_INVALID, "k outside [0, n]");
+    if (k_per_chunk[b] < c.n && (!c.k || !c.v)) return fail(CT_E_INVALID, "chunk rows are NULL");
+    rows += (size_t)(c.n - k_per_chunk[b]);
+  }
+  if (rows > 0 && (!k_stage || !v_stage)) return fail(CT_E_INVALID, "staging buffers are NULL");
+  size_t at = 0;
+  for (int b = 0; b < n_chunks; ++b) {
+    const ct_ranked_chunk& c = chunks[b];
+    const size_t tail = (size_t)(c.n - k_per_chunk[b]);
+    if (tail == 0) continue;
+    const size_t src = ((size_t)layer * c.n + k_per_chunk[b]) * row_bytes;
+    const size_t dst = at * row_bytes;
+    if (hipMemcpyAsync(reinterpret_cast<char*>(k_stage) + dst, reinterpret_cast<const char*>(c.k) + src,
+                       tail * row_bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(reinterpret_cast<char*>(v_stage) + dst, reinterpret_cast<const char*>(c.v) + src,
+                       tail * row_bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return fail(CT_E_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(hipGetLastError()));
+    at += tail;
+  }
+  return CT_OK;
+  CT_GUARD_END
+}
+
 }  // extern "C"

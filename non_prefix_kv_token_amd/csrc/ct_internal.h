@@ -147,4 +147,8 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream);
 ct_status attn_f32_run(const AttnArgs& a, hipStream_t stream);
 int device_cu_count();
 
+// ------------------------------------------------------------- host tier
+ct_status rank_order_run(const void* k_src, const void* v_src, const int32_t* ranking, int32_t n,
+                         int32_t L, int32_t row_bytes, void* k_dst, void* v_dst, hipStream_t stream);
+
 }  // namespace ct

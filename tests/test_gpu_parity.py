@@ -294,3 +294,75 @@ def test_attention_long_split(orc, syn):
 
 def test_attention_group8_long(orc, syn):
     _attn_case(orc, syn, 3000, 1, 8, 128, 70, "bf16", 500000.0, 0, scale=0.1)
+
+
+# ---- host-tier sparse loading -------------------------------------------------------
+
+@pytest.mark.parametrize("r", [(15, 100), (0, 1), (1, 1)])
+def test_host_tier_matches_device_path(orc, syn, r):
+    """Rank-ordered pinned host pool -> staged complement -> assembly from the
+    packed staging (src_rows = ranking tail) equals the assembly from the
+    device-resident chunks bit for bit, and the oracle's."""
+    ct = need_gpu()
+    ns, L, H, D, theta, layer = [300, 512, 129], 3, 2, 128, 500000.0, 1
+    host = _chunks(syn, ns, L, H, D, "bf16")
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    score, _ = ct.cachetune_score_chunk(dev, L, H, D, alpha=(1, 16))
+    ks, ranking, sel, comp = ct.cachetune_select_topr(score, ns, r=r)
+    pool = []
+    for b, (k, v) in enumerate(dev):
+        off = sum(ns[:b])
+        kr, vr = ct.cachetune_rank_order(k, v, ranking[off:off + ns[b]])
+        pk = torch.empty(kr.shape, dtype=kr.dtype, pin_memory=True)
+        pv = torch.empty(vr.shape, dtype=vr.dtype, pin_memory=True)
+        pk.copy_(kr)
+        pv.copy_(vr)
+        pool.append((pk, pv))
+    torch.cuda.synchronize()
+    rows = sum(n - k for n, k in zip(ns, ks))
+    k_stage = torch.zeros((max(rows, 1), H, D), dtype=torch.bfloat16, device="cuda")
+    v_stage = torch.zeros_like(k_stage)
+    ct.cachetune_stage_complement(pool, layer, ks, k_stage, v_stage)
+    sel_h, comp_h = to_host(sel), to_host(comp)
+    T = sum(ns) + 7
+    offs = [sum(ns[:b]) for b in range(len(ns))]
+    ref = [torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    k_ref = np.zeros((T, H, D), np.uint16)
+    v_ref = np.zeros((T, H, D), np.uint16)
+    pl_dev, pl_host, keep = [], [], []
+    so = co = at = 0
+    for b, n in enumerate(ns):
+        k = ks[b]
+        s_b = sel_h[so:so + k]
+        krec = syn.rows(SEED, syn.K, b, layer, n, H, D, s_b, "bf16", extra_sigma=0.25)
+        vrec = syn.rows(SEED, syn.V, b, layer, n, H, D, s_b, "bf16", extra_sigma=0.25)
+        orc.assemble_chunk(host[b][0][layer], host[b][1][layer], krec, vrec, s_b, offs[b], theta, 0,
+                           k_ref, v_ref)
+        d = dict(sel=sel[so:] if k else None, k_rec=to_dev(krec) if k else None,
+                 v_rec=to_dev(vrec) if k else None)
+        keep.append(d)
+        pl_dev.append(ct.make_place(dev[b][0][layer], dev[b][1][layer], n, k, offs[b],
+                                    comp=comp[co:] if k < n else None, **d))
+        o = sum(ns[:b])
+        pl_host.append(ct.make_place(k_stage[at:] if k < n else None, v_stage[at:] if k < n else None,
+                                     n, k, offs[b], src_rows=ranking[o + k:] if k < n else None, **d))
+        so, co, at = so + k, co + n - k, at + n - k
+    ct.cachetune_assemble_rope(pl_dev, ref[0], ref[1], H, D, theta)
+    ct.cachetune_assemble_rope(pl_host, ref[2], ref[3], H, D, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], ref[2]) and torch.equal(ref[1], ref[3])
+    kg, vg = to_host(ref[2])[:sum(ns)], to_host(ref[3])[:sum(ns)]
+    np.testing.assert_array_equal(vg, v_ref[:sum(ns)])
+    assert ulp_distance_bf16(kg, k_ref[:sum(ns)]).max() <= 1
+
+
+def test_rank_order_is_a_gather(syn):
+    ct = need_gpu()
+    L, n, H, D = 2, 333, 2, 64
+    k = syn.chunk(SEED, syn.K, 3, L, n, H, D, "bf16")
+    v = syn.chunk(SEED, syn.V, 3, L, n, H, D, "bf16")
+    perm = np.random.default_rng(5).permutation(n).astype(np.int32)
+    kd, vd = ct.cachetune_rank_order(to_dev(k), to_dev(v), to_dev(perm))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(kd), k[:, perm])
+    np.testing.assert_array_equal(to_host(vd), v[:, perm])
