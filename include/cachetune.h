@@ -187,7 +187,8 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
  *  out: device [n_q][Hq][D] in `dtype`
  *  lse: device float[n_q][Hq] natural-log sum of exp of the scaled logits, or NULL.
  *  ws/ws_bytes: device workspace of at least cachetune_recompute_attn_ws bytes
- *         (may be NULL when that size is 0), 256-byte aligned; it holds the
+ *         (may be NULL when that size is 0), 256-byte aligned; for bf16 it
+ *         holds the rotated queries as bf16 pairs, V as fp16 tiles, and the
  *         partial results of rows whose keys are split over several segments.
  * D must be 64 or 128; n_q >= 0; T >= 1. */
 ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,

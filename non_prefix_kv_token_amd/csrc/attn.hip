@@ -151,6 +151,79 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
   if (tid == 0) a.vflag[h * a.nblk + kb] = any_wide;
 }
 
+// Per-layer preparation of the queries for the matrix cores: every selected
+// row's query heads rotated at the row's position (the angle's sine and
+// cosine formed once per row in fp64 and shared by all heads), multiplied by
+// softmax_scale * log2(e), and split into a bf16 hi + lo pair.  Stored per
+// (row, query head) as D/8 groups of {8 hi, 8 lo} (32 bytes): the lane that
+// owns dims [8 grp, 8 grp + 8) of a k-step reads both operands with two
+// 16-byte loads.  One block per row.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_qprep(AttnArgs a) {
+  constexpr int NG = D / 8;
+  __shared__ float s_sn[D / 2], s_cs[D / 2];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int pos = min(a.qpos[row], a.T - 1);
+  if (tid < D / 2) rope_sincos(pos, a.inv_freq[tid], &s_sn[tid], &s_cs[tid]);
+  __syncthreads();
+  const float c = a.scale_log2;
+  const bool half = a.style == CT_ROPE_HALF;
+  for (int item = tid; item < a.Hq * NG; item += 256) {
+    const int hq = item / NG, grp = item % NG;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * a.Hq + hq) * D;
+    float y[8];
+    if (half) {  // pairs (j, j + D/2)
+      const bool first = grp < NG / 2;
+      const int j0 = 8 * (first ? grp : grp - NG / 2);
+      const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + j0);
+      const u32x4_t z4 = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + j0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float x = (t & 1) ? bf16_hi_to_f32(x4[t >> 1]) : bf16_lo_to_f32(x4[t >> 1]);
+        const float z = (t & 1) ? bf16_hi_to_f32(z4[t >> 1]) : bf16_lo_to_f32(z4[t >> 1]);
+        const float sn = s_sn[j0 + t], cs = s_cs[j0 + t];
+        y[t] = first ? (x * cs - z * sn) * c : (x * sn + z * cs) * c;
+      }
+    } else {  // pairs (d, d + 1), frequency index d/2
+      const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 8 * grp);
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        const float x = bf16_lo_to_f32(x4[t >> 1]), z = bf16_hi_to_f32(x4[t >> 1]);
+        const int j = (8 * grp + t) >> 1;
+        const float sn = s_sn[j], cs = s_cs[j];
+        y[t] = (x * cs - z * sn) * c;
+        y[t + 1] = (x * sn + z * cs) * c;
+      }
+    }
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t h2[2], l2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        h2[e] = bf16_bits_rne(y[2 * w + e]);
+        l2[e] = bf16_bits_rne(y[2 * w + e] - __uint_as_float(h2[e] << 16));
+      }
+      hi[w] = h2[0] | (h2[1] << 16);
+      lo[w] = l2[0] | (l2[1] << 16);
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.qhl + (((size_t)row * a.Hq + hq) * NG + grp) * 16);
+    dst[0] = hi;
+    dst[1] = lo;
+  }
+}
+
+// Maximum of a lane's 16 logits with the 3-input maximum (no canonicalising
+// moves; NaN propagates).
+__device__ inline float max16(const f32x16_t& s) {
+  auto mx3 = [](float x, float y, float z) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+  };
+  const float m0 = mx3(s[0], s[1], s[2]), m1 = mx3(s[3], s[4], s[5]), m2 = mx3(s[6], s[7], s[8]);
+  const float m3 = mx3(s[9], s[10], s[11]), m4 = mx3(s[12], s[13], s[14]);
+  return __builtin_elementwise_maximum(mx3(mx3(m0, m1, m2), m3, m4), s[15]);
+}
+
 // NW waves per block; each wave owns QT tiles of 32 query rows of one query
 // head.  QT = 2 runs one wave per SIMD with the whole register file, so every
 // K / V^T fragment read from LDS feeds two tiles; QT = 1 runs two waves per
@@ -216,56 +289,20 @@ void k_attn_bf16(AttnArgs a) {
   const int seg_hi = min(seg_lo + S, nkeys);
   const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
-  // ---- rotated, scaled query as bf16 hi + lo (B operand): d = 16*s + 8*g + t
+  // ---- rotated, scaled query as bf16 hi + lo (B operand), from k_attn_qprep:
+  // dims d = 16*s + 8*g + t of k-step s are group 2s + g
   u32x4_t qh[QT][NS], ql[QT][NS];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) { qh[qt][s][w] = 0u; ql[qt][s][w] = 0u; }
-#pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    if (!valid[qt]) continue;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row[qt] * Hq + hq) * D;
-    const float c = a.scale_log2;
-    auto put = [&](int s, int t, float y) {
-      uint32_t hi = bf16_bits_rne(y);
-      uint32_t lo = bf16_bits_rne(y - __uint_as_float(hi << 16));
-      const int w = t >> 1, sh = 16 * (t & 1);
-      qh[qt][s][w] |= hi << sh;
-      ql[qt][s][w] |= lo << sh;
-    };
-    if (a.style == CT_ROPE_HALF) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        a.qhl + ((size_t)(valid[qt] ? row[qt] : 0) * Hq + hq) * D * 2);
 #pragma unroll
-      for (int s = 0; s < NS / 2; ++s) {
-        const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 16 * s + 8 * g);
-        const u32x4_t y4 = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + 16 * s + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int j = 16 * s + 8 * g + t;  // pair (j, j + D/2): steps s and s + NS/2
-          const float x = (t & 1) ? bf16_hi_to_f32(x4[t >> 1]) : bf16_lo_to_f32(x4[t >> 1]);
-          const float y = (t & 1) ? bf16_hi_to_f32(y4[t >> 1]) : bf16_lo_to_f32(y4[t >> 1]);
-          float sn, cs;
-          rope_sincos(pos[qt], a.inv_freq[j], &sn, &cs);
-          put(s, t, (x * cs - y * sn) * c);
-          put(s + NS / 2, t, (x * sn + y * cs) * c);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 16 * s + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const int d = 16 * s + 8 * g + t;  // pair (d, d + 1), frequency index d/2
-          const float x = bf16_lo_to_f32(x4[t >> 1]);
-          const float y = bf16_hi_to_f32(x4[t >> 1]);
-          float sn, cs;
-          rope_sincos(pos[qt], a.inv_freq[d / 2], &sn, &cs);
-          put(s, t, (x * cs - y * sn) * c);
-          put(s, t + 1, (x * sn + y * cs) * c);
-        }
+    for (int s = 0; s < NS; ++s) {
+      qh[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
+      ql[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (valid[qt]) {
+        qh[qt][s] = qp[2 * (2 * s + g)];
+        ql[qt][s] = qp[2 * (2 * s + g) + 1];
       }
     }
   }
@@ -310,14 +347,20 @@ void k_attn_bf16(AttnArgs a) {
   // main pass: the V^T tile prepared by k_attn_prep, copied as it is
   constexpr int VIT = D * BK / 8 / NT;  // 16-byte V^T chunks per thread
   u32x4_t vtreg[VIT];
+  // K rows through a buffer resource based at key k0 of this head whose range
+  // ends at the end of K: rows at and past T read as zero without a branch
+  // (the whole offset is in the VGPR operand, so the range check covers it).
   auto load_fast = [&](int kb) {
     const int k0 = kb * BK;
+    const long long rem = ((long long)(T - k0) * H - kvh) * D * 2;
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Kg + ((size_t)k0 * H + kvh) * D), 0,
+        (int)(rem < 0x7fffffffLL ? rem : 0x7fffffffLL), 0x00020000);
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int item = tid + it * NT;
-      const int key = k0 + item / KCH, ch = item % KCH;
-      kreg[it] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (key < T) kreg[it] = *reinterpret_cast<const u32x4_t*>(Kg + ((size_t)key * H + kvh) * D + 8 * ch);
+      const int voff = ((item / KCH) * H * D + 8 * (item % KCH)) * 2;
+      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kres, voff, 0, 0));
     }
     const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.vt16 + ((size_t)kvh * a.nblk + kb) * D * BK);
 #pragma unroll
@@ -417,10 +460,7 @@ void k_attn_bf16(AttnArgs a) {
   // Online softmax of one 32-key tile of tile qt (16 logits per lane): lazy
   // maximum, probabilities exp2(s - m) in place.
   auto softmax_tile = [&](int qt, f32x16_t& st) {
-    float bm = fmaxf(fmaxf(st[0], st[1]), st[2]);
-#pragma unroll
-    for (int v = 3; v < 15; v += 2) bm = fmaxf(bm, fmaxf(st[v], st[v + 1]));
-    bm = fmaxf(bm, st[15]);
+    const float bm = max16(st);
     if (__any(bm > m_run[qt] + kLazyThr)) {
       const float m_new = fmaxf(m_run[qt], fmaxf(bm, __shfl_xor(bm, 32)));
       const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
@@ -482,14 +522,23 @@ void k_attn_bf16(AttnArgs a) {
   // is in its vector phase.  V^T therefore has three LDS buffers.
   const int lag = (NW == 8 && QT == 1) ? (wave >> 2) : 0;
   // the fp16 path needs every V tile of the segment to fit fp16
-  bool redo = false;
-  for (int kb = kb0; kb < kb1; ++kb) redo |= a.vflag[kvh * a.nblk + kb] != 0;
+  // (the segment's flags are read by the lanes in parallel and combined)
+  bool wide_v = false;
+  for (int kb = kb0 + lane; kb < kb1; kb += 64) wide_v |= a.vflag[kvh * a.nblk + kb] != 0;
+  const bool redo = __any(wide_v);
   bool pend = false;
   f32x16_t st[QT][2];
   if (!redo) {
     load_fast(kb0);
     store_fast(0, 0);
   }
+  // The query operands are complete before the loop: the compiler's wait
+  // counting would otherwise treat them as pending inside the loop and make
+  // every k-block wait for the next block's prefetch.
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qh[qt][s]), "+v"(ql[qt][s]));
   for (int kb = kb0; kb < kb1 && !redo; ++kb) {
     const int i = kb - kb0;
     const int kc = i & 1, vc = i % 3;
@@ -630,6 +679,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
   {
+    TimedLaunch tl_("attention_qprep", stream);
+    hipLaunchKernelGGL((k_attn_qprep<D>), dim3(a.n_q), dim3(256), 0, stream, a);
+  }
+  if (ct_status s = check_launch("attention query preparation")) return s;
+  {
     TimedLaunch tl_("attention_prep", stream);
     hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
   }
@@ -694,7 +748,9 @@ void attn_plan(AttnArgs* a, int n_cu) {
 }
 
 // Workspace: [partial outputs][partial log2-sum-exp][V^T fp16 tiles][tile flags]
-static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size_t* off_flag) {
+// [prepared queries]
+static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size_t* off_flag,
+                        size_t* off_q) {
   const size_t rows = a.nseg > 1 ? (size_t)a.nseg * a.n_q * a.Hq : 0;
   size_t off = align256(rows * a.D * 4);
   *off_lse = off;
@@ -703,20 +759,22 @@ static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size
   off += align256((size_t)a.H * a.nblk * a.D * BK * 2);
   *off_flag = off;
   off += align256((size_t)a.H * a.nblk * 4);
+  *off_q = off;
+  off += align256((size_t)a.n_q * a.Hq * a.D * 4);
   return off;
 }
 
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.dtype != CT_BF16) return 0;
-  size_t o1, o2, o3;
-  return ws_layout(a, &o1, &o2, &o3);
+  size_t o1, o2, o3, o4;
+  return ws_layout(a, &o1, &o2, &o3, &o4);
 }
 
 ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return CT_OK;
   if (a.dtype == CT_F32) return attn_f32_run(a, stream);
-  size_t off_lse, off_vt, off_flag;
-  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag);
+  size_t off_lse, off_vt, off_flag, off_q;
+  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag, &off_q);
   if (!ws || ws_bytes < need)
     return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
   char* w = reinterpret_cast<char*>(ws);
@@ -724,6 +782,7 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   a.part_lse = reinterpret_cast<float*>(w + off_lse);
   a.vt16 = reinterpret_cast<uint16_t*>(w + off_vt);
   a.vflag = reinterpret_cast<int32_t*>(w + off_flag);
+  a.qhl = reinterpret_cast<uint16_t*>(w + off_q);
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
 }
 

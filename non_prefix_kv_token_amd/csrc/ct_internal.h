@@ -140,6 +140,7 @@ struct AttnArgs {
   int32_t nblk;      // 64-key tiles covering [0, T)
   uint16_t* vt16;    // [H][nblk][D][64] V^T tiles as fp16 (keys permuted)
   int32_t* vflag;    // [H][nblk] tile holds a V outside the fp16 range
+  uint16_t* qhl;     // [n_q][Hq][D/8][2][8] rotated, scaled queries as bf16 hi / lo
 };
 void attn_plan(AttnArgs* a, int n_cu);
 size_t attn_ws_bytes(const AttnArgs& a);
