@@ -527,8 +527,8 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble",
-             "attention_prep", "attention", "attention_merge"]
+    attn_names = ("attention_qprep", "attention_prep", "attention_sched", "attention", "attention_merge")
+    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
     for n in names:  # drop records of earlier launches
         ct.cachetune_timing_read(n)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -555,7 +555,7 @@ def main():
     tokens = float(sum(w.ns))
     score_ms = per_step("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr")
     asm_ms = per_step("assemble") / w.L
-    attn_call_ms = per_step("attention_prep", "attention", "attention_merge") / w.L
+    attn_call_ms = per_step(*attn_names) / w.L
     attn_kernel_ms = per_launch("attention")
     attn_flops = w.attn_flops_per_layer()
     attn_tflops = attn_flops / (attn_kernel_ms * 1e-3) / 1e12
@@ -603,8 +603,7 @@ def main():
             "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
             "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS,
             "attention_call_ms_per_layer": attn_call_ms,
-            "attention_kernels_ms_per_layer": {n: per_step(n) / w.L for n in
-                                               ("attention_prep", "attention", "attention_merge")},
+            "attention_kernels_ms_per_layer": {n: per_step(n) / w.L for n in attn_names},
             "attention_TFLOPs": attn_tflops,
             "attention_flops_per_layer": attn_flops,
             "score_plus_assemble_tokens_per_s": tokens / ((score_ms + asm_ms * w.L) * 1e-3),

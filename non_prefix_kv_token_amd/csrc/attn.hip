@@ -244,19 +244,33 @@ void k_attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[3][D * VTS];  // V^T: fp16 (bf16 when redone)
   __shared__ int s_wmax[NW];
+  __shared__ int s_item;
 
   const int H = a.H, G = a.group, T = a.T, Hq = a.Hq, S = a.seg_keys;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 5, col = lane & 31;
 
-  // ---- block -> (KV head, segment, tile group, head chunk)
+  // ---- persistent blocks: block b serves KV head b % H (blocks are dealt
+  // round-robin over the XCDs, so each XCD's L2 holds one head's keys) and
+  // takes that head's work items -- (tile group, segment) pairs in the order
+  // k_attn_sched wrote, longest first, times the head chunks -- from a
+  // counter until none are left.
   const int kvh = blockIdx.x % H;
-  const int rest = blockIdx.x / H;
-  const int per_seg = a.n_tg * a.n_hc;
-  const int seg = rest / per_seg;
-  const int u_ = rest % per_seg;
-  const int tg = a.n_tg - 1 - u_ / a.n_hc;  // latest rows first inside a segment
-  const int hc = u_ % a.n_hc;
+  const int n_work = a.sched_n[0] * a.n_hc;
+  for (;;) {
+  // Lane indices pass through an empty asm once per item: address arithmetic
+  // that depends on them is then formed inside the item, not hoisted out of
+  // this loop, where it would hold registers across the whole kernel.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  __syncthreads();  // the previous item's LDS reads and s_item are done
+  if (tid == 0) s_item = atomicAdd(&a.sched_cnt[kvh], 1);
+  __syncthreads();
+  const int item = s_item;
+  if (item >= n_work) break;
+  const int e_ = a.sched_order[item / a.n_hc];
+  const int tg = e_ / a.nseg, seg = e_ % a.nseg;
+  const int hc = item % a.n_hc;
   const int wt = wave / a.hpb, wh = wave % a.hpb;
   const int tile0 = (tg * a.tpb + wt) * QT;  // first 32-row tile of the wave
   const int hig = hc * a.hpb + wh;           // head inside the group
@@ -285,7 +299,7 @@ void k_attn_bf16(AttnArgs a) {
   for (int w = 0; w < NW; ++w) bmax = max(bmax, s_wmax[w]);
   const int nkeys = bmax + 1;
   const int seg_lo = seg * S;
-  if (seg_lo >= nkeys) return;  // uniform over the block
+  if (seg_lo >= nkeys) continue;  // uniform over the block
   const int seg_hi = min(seg_lo + S, nkeys);
   const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
@@ -607,7 +621,7 @@ void k_attn_bf16(AttnArgs a) {
     }
   }
 
-  if (!wave_on) return;
+  if (!wave_on) continue;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 32);
@@ -642,6 +656,76 @@ void k_attn_bf16(AttnArgs a) {
       if (g == 0) a.part_lse[pb] = lse2;
     }
   }
+  }  // work items
+}
+
+// Work list of the persistent attention blocks (one block of 1024 threads):
+// the key range of each tile group (its rows' largest position), the number
+// of 64-key blocks each (tile group, segment) pair covers, and the pairs that
+// have work, sorted longest first (ties by index): each KV head's blocks take
+// the long items before the short ones, which keeps the tail of the launch
+// short.  Lists longer than kSchedMax pairs keep the natural order (segment
+// by segment, latest rows first) with the empty pairs included.  Also resets
+// the per-head item counters.
+constexpr int kSchedMax = 8192;
+__global__ __launch_bounds__(1024) void k_attn_sched(AttnArgs a) {
+  __shared__ unsigned long long s_key[kSchedMax];
+  __shared__ int s_bmax[kSchedMax];
+  __shared__ int s_n;
+  const int tid = threadIdx.x;
+  const int n_tg = a.n_tg, nseg = a.nseg, S = a.seg_keys;
+  const int n_items = n_tg * nseg;
+  for (int h = tid; h < a.H; h += 1024) a.sched_cnt[h] = 0;
+  if (n_items > kSchedMax) {
+    for (int i = tid; i < n_items; i += 1024) {
+      const int seg = i / n_tg, tg = n_tg - 1 - i % n_tg;
+      a.sched_order[i] = tg * nseg + seg;
+    }
+    if (tid == 0) a.sched_n[0] = n_items;
+    return;
+  }
+  for (int t = tid; t < n_tg; t += 1024) s_bmax[t] = -1;
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  const int rows_per_tg = 32 * a.tpb * a.qt;
+  for (int r = tid; r < a.n_q; r += 1024) atomicMax(&s_bmax[r / rows_per_tg], min(a.qpos[r], a.T - 1));
+  __syncthreads();
+  int N = 1;
+  while (N < n_items) N <<= 1;
+  for (int i = tid; i < N; i += 1024) {
+    unsigned long long key = 0ull;
+    if (i < n_items) {
+      const int tg = i / nseg, seg = i % nseg;
+      const int lo = seg * S, nkeys = s_bmax[tg] + 1;
+      const int work = lo < nkeys ? (min(lo + S, nkeys) + BK - 1) / BK - lo / BK : 0;
+      key = ((unsigned long long)work << 32) | (0xffffffffu - (unsigned)i);
+    }
+    s_key[i] = key;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int k = 2; k <= N; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = s_key[i], y = s_key[l];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            s_key[i] = y;
+            s_key[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < N; i += 1024) {
+    const bool has = (s_key[i] >> 32) != 0;
+    if (has) a.sched_order[i] = (int)(0xffffffffu - (unsigned)(s_key[i] & 0xffffffffu));
+    if (has && (i + 1 == N || (s_key[i + 1] >> 32) == 0)) s_n = i + 1;
+  }
+  __syncthreads();
+  if (tid == 0) a.sched_n[0] = s_n;
 }
 
 // Combine the per-segment results of rows whose keys span several segments:
@@ -688,19 +772,18 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
   }
   if (ct_status s = check_launch("attention V preparation")) return s;
-  const int blocks = a.H * a.n_tg * a.n_hc * a.nseg;
+  {
+    TimedLaunch tl_("attention_sched", stream);
+    hipLaunchKernelGGL(k_attn_sched, dim3(1), dim3(1024), 0, stream, a);
+  }
+  if (ct_status s = check_launch("attention schedule")) return s;
+  const int blocks = a.H * a.blocks_per_head;
   {
     TimedLaunch tl_("attention", stream);
-    if (a.qt == 2)
-      hipLaunchKernelGGL((k_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, stream, a);
-    else if (a.nw == 8)
-      hipLaunchKernelGGL((k_attn_bf16<D, 8, 1>), dim3(blocks), dim3(512), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_attn_bf16<D, 4, 1>), dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_attn_bf16<D, 8, 1>), dim3(blocks), dim3(512), 0, stream, a);
   }
   if (ct_status s = check_launch("attention")) {
-    set_error(std::string(cachetune_last_error()) + " [grid " + std::to_string(blocks) + ", waves " +
-              std::to_string(a.nw) + ", tiles/wave " + std::to_string(a.qt) + ", segments " +
+    set_error(std::string(cachetune_last_error()) + " [grid " + std::to_string(blocks) + ", segments " +
               std::to_string(a.nseg) + "]");
     return s;
   }
@@ -719,15 +802,9 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
 
 void attn_plan(AttnArgs* a, int n_cu) {
   const int G = a->group;
-  // Block shape: 8 waves with one 32-row tile each (two waves per SIMD); for
-  // tuning, 4 waves with one tile each ("41") or two tiles each ("4").
+  // Block shape: 8 waves with one 32-row tile each (two waves per SIMD).
   a->nw = 8;
   a->qt = 1;
-  if (const char* env = getenv("CACHETUNE_ATTN_WAVES")) {
-    const int w = atoi(env);
-    a->nw = (w == 8) ? 8 : 4;
-    a->qt = (w == 8 || w == 41) ? 1 : 2;
-  }
   a->hpb = G < a->nw ? G : a->nw;
   a->tpb = a->nw / a->hpb;
   a->n_hc = (G + a->hpb - 1) / a->hpb;
@@ -745,12 +822,15 @@ void attn_plan(AttnArgs* a, int n_cu) {
   a->seg_keys = (int32_t)s;
   a->nseg = (a->T + a->seg_keys - 1) / a->seg_keys;
   a->nblk = (a->T + BK - 1) / BK;
+  // persistent grid: one block per compute unit, the same number per KV head
+  const int ncu = n_cu > 0 ? n_cu : 256;
+  a->blocks_per_head = ncu / a->H > 0 ? ncu / a->H : 1;
 }
 
 // Workspace: [partial outputs][partial log2-sum-exp][V^T fp16 tiles][tile flags]
-// [prepared queries]
+// [prepared queries][work list, per-head counters, list length]
 static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size_t* off_flag,
-                        size_t* off_q) {
+                        size_t* off_q, size_t* off_sched) {
   const size_t rows = a.nseg > 1 ? (size_t)a.nseg * a.n_q * a.Hq : 0;
   size_t off = align256(rows * a.D * 4);
   *off_lse = off;
@@ -761,20 +841,22 @@ static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size
   off += align256((size_t)a.H * a.nblk * 4);
   *off_q = off;
   off += align256((size_t)a.n_q * a.Hq * a.D * 4);
+  *off_sched = off;
+  off += align256(((size_t)a.n_tg * a.nseg + a.H + 1) * 4);
   return off;
 }
 
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.dtype != CT_BF16) return 0;
-  size_t o1, o2, o3, o4;
-  return ws_layout(a, &o1, &o2, &o3, &o4);
+  size_t o1, o2, o3, o4, o5;
+  return ws_layout(a, &o1, &o2, &o3, &o4, &o5);
 }
 
 ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return CT_OK;
   if (a.dtype == CT_F32) return attn_f32_run(a, stream);
-  size_t off_lse, off_vt, off_flag, off_q;
-  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag, &off_q);
+  size_t off_lse, off_vt, off_flag, off_q, off_sched;
+  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag, &off_q, &off_sched);
   if (!ws || ws_bytes < need)
     return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
   char* w = reinterpret_cast<char*>(ws);
@@ -783,6 +865,9 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   a.vt16 = reinterpret_cast<uint16_t*>(w + off_vt);
   a.vflag = reinterpret_cast<int32_t*>(w + off_flag);
   a.qhl = reinterpret_cast<uint16_t*>(w + off_q);
+  a.sched_order = reinterpret_cast<int32_t*>(w + off_sched);
+  a.sched_cnt = a.sched_order + (size_t)a.n_tg * a.nseg;
+  a.sched_n = a.sched_cnt + a.H;
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
 }
 

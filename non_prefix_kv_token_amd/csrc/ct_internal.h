@@ -130,8 +130,8 @@ struct AttnArgs {
   // bf16 path: launch plan (attn_plan) and split-KV partials in the workspace
   int32_t seg_keys;  // keys per segment (multiple of 64)
   int32_t nseg;      // segments covering [0, T)
-  int32_t nw;        // waves per block (4 or 8)
-  int32_t qt;        // 32-row tiles per wave (1 or 2)
+  int32_t nw;        // waves per block (8)
+  int32_t qt;        // 32-row tiles per wave (1)
   int32_t hpb, tpb;  // query heads and 32-row tiles per block (hpb * tpb <= nw)
   int32_t n_hc;      // head chunks per group
   int32_t n_tg;      // tile groups (tpb * qt tiles each)
@@ -141,6 +141,10 @@ struct AttnArgs {
   uint16_t* vt16;    // [H][nblk][D][64] V^T tiles as fp16 (keys permuted)
   int32_t* vflag;    // [H][nblk] tile holds a V outside the fp16 range
   uint16_t* qhl;     // [n_q][Hq][D/8][2][8] rotated, scaled queries as bf16 hi / lo
+  int32_t blocks_per_head;  // persistent blocks serving each KV head
+  int32_t* sched_order;     // [n_tg * nseg] work items (tg * nseg + seg), longest first
+  int32_t* sched_cnt;       // [H] items taken so far by each head's blocks
+  int32_t* sched_n;         // [1] items in sched_order
 };
 void attn_plan(AttnArgs* a, int n_cu);
 size_t attn_ws_bytes(const AttnArgs& a);
