@@ -19,13 +19,15 @@
 // K/V block in LDS (double-buffered, next block prefetched into registers
 // while the current one is consumed).  Each wave owns 32 query rows of one
 // query head of the group (grouped-query attention: the 4 query heads of a KV
-// head and 2 row tiles for a group of 4).  The causal key range of a block is
-// cut into segments of S keys (split-KV) so that long rows do not serialise
-// the launch; a row whose keys span several segments gets partial results
-// (normalised output and log2-sum-exp) that k_attn_merge combines.  Block ids
-// run fastest over the KV head, so each XCD (blocks are dealt round-robin over
-// the 8 XCDs) serves one KV head and its L2 holds the keys of the segment that
-// its CUs are working on.
+// head and 2 row tiles for a group of 4).  The causal key range of such a
+// tile group is cut into segments of S keys (split-KV) so that long rows do
+// not serialise the launch; a row whose keys span several segments gets
+// partial results (normalised output and log2-sum-exp) that k_attn_merge
+// combines.  The grid is persistent: one block per CU, block b serving KV
+// head b % H (blocks are dealt round-robin over the 8 XCDs, so each XCD's L2
+// holds one head's keys), taking (tile group, segment) items from a per-head
+// counter in the order k_attn_sched computed from the query positions,
+// longest first.
 //
 // Precision.  Logits of these inputs reach the hundreds, so one bf16 rounding
 // of the rotated query would move outputs by O(1): the query (rotated in fp32
@@ -242,7 +244,7 @@ void k_attn_bf16(AttnArgs a) {
   static_assert(KIT >= 1 && BK * KCH == KIT * NT, "K staging split");
   static_assert(DPG >= 4 && DPG % 4 == 0, "V staging split");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[3][D * VTS];  // V^T: fp16 (bf16 when redone)
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VTS];  // V^T: fp16 (bf16 when redone)
   __shared__ int s_wmax[NW];
   __shared__ int s_item;
 
@@ -530,17 +532,11 @@ void k_attn_bf16(AttnArgs a) {
 
   // Main pass: P and V^T as fp16.  A segment with a V tile that does not fit
   // fp16 takes the pass below instead: bf16 V and P as a bf16 pair.
-  // With 8 waves, waves 4-7 (one per SIMD) run half a block behind: they
-  // finish the softmax and PV of the previous block before the scores of the
-  // current one, so each SIMD holds one wave in a matrix phase while the other
-  // is in its vector phase.  V^T therefore has three LDS buffers.
-  const int lag = (NW == 8 && QT == 1) ? (wave >> 2) : 0;
   // the fp16 path needs every V tile of the segment to fit fp16
   // (the segment's flags are read by the lanes in parallel and combined)
   bool wide_v = false;
   for (int kb = kb0 + lane; kb < kb1; kb += 64) wide_v |= a.vflag[kvh * a.nblk + kb] != 0;
   const bool redo = __any(wide_v);
-  bool pend = false;
   f32x16_t st[QT][2];
   if (!redo) {
     load_fast(kb0);
@@ -554,22 +550,22 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qh[qt][s]), "+v"(ql[qt][s]));
   for (int kb = kb0; kb < kb1 && !redo; ++kb) {
-    const int i = kb - kb0;
-    const int kc = i & 1, vc = i % 3;
+    const int c = (kb - kb0) & 1;
     const bool more = kb + 1 < kb1;
     if (more) load_fast(kb + 1);
     __syncthreads();
     const int k0 = kb * BK;
-    if (lag && pend) pv(Vs[(i + 2) % 3], st);  // the previous block
-    pend = wave_on && k0 <= wmax;
-    if (pend) scores(Ks[kc], k0, st);
-    if (!lag && pend) {
-      pv(Vs[vc], st);
-      pend = false;
+    if (wave_on && k0 <= wmax) {
+      // The score products run at raised wave priority: of the two waves
+      // sharing a SIMD, the one in its matrix phase gets the issue slots, and
+      // the other drifts into the complementary (softmax) phase.
+      __builtin_amdgcn_s_setprio(2);
+      scores(Ks[c], k0, st);
+      __builtin_amdgcn_s_setprio(0);
+      pv(Vs[c], st);
     }
-    if (more) store_fast((i + 1) & 1, (i + 1) % 3);
+    if (more) store_fast(c ^ 1, c ^ 1);
   }
-  if (!redo && pend) pv(Vs[(kb1 - 1 - kb0) % 3], st);
 
   if (redo) {
 #pragma unroll
