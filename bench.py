@@ -527,7 +527,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    attn_names = ("attention_qprep", "attention_prep", "attention_sched", "attention", "attention_merge")
+    attn_names = ("attention_setup", "attention", "attention_merge")
     names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
     for n in names:  # drop records of earlier launches
         ct.cachetune_timing_read(n)

@@ -110,24 +110,28 @@ __device__ inline int vt_col(int u) {
   return (u & ~15) + 8 * ((w & 7) >> 2) + (w & 3) + 4 * (w >> 3);
 }
 
-// Per-layer preparation of V for the fp16 PV product: V^T tiles of 64 keys,
-// fp16, keys permuted inside each group of 16 (vt_col), laid out exactly as
-// the attention kernel keeps them in LDS, plus one flag per tile that is set
-// when a value does not fit fp16 (|v| >= 65536, or not finite).  Keys at and
-// beyond T are zero.  One block per (tile, KV head).
+// Preparation of V for the fp16 PV product, one (64-key tile, KV head) per
+// call: V^T tiles of 64 keys, fp16, keys permuted inside each group of 16
+// (vt_col), laid out exactly as the attention kernel keeps them in LDS, plus
+// one flag per tile that is set when a value does not fit fp16 (|v| >= 65536,
+// or not finite).  Keys at and beyond T are zero.  The tile passes through
+// LDS with rows padded by one 32-bit word, so that the column reads of the
+// transpose fall in distinct banks.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[BK * D];
-  const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+__device__ void prep_v_tile(const AttnArgs& a, int kb, int h, uint16_t* tile) {
+  constexpr int TS = D + 2;       // padded row (16-bit elements)
+  constexpr int CH = BK * D / 8;  // 16-byte chunks per tile
+  const int tid = threadIdx.x;
   const int H = a.H, T = a.T;
   const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v);
-  constexpr int CH = BK * D / 8;  // 16-byte chunks per tile
 #pragma unroll
   for (int c = tid; c < CH; c += 256) {
     const int key = kb * BK + c / (D / 8), part = c % (D / 8);
     u32x4_t w = {0u, 0u, 0u, 0u};
     if (key < T) w = *reinterpret_cast<const u32x4_t*>(Vg + ((size_t)key * H + h) * D + 8 * part);
-    *reinterpret_cast<u32x4_t*>(&tile[(c / (D / 8)) * D + 8 * part]) = w;
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[(c / (D / 8)) * TS + 8 * part]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = w[i];  // 4-byte aligned only (padded rows)
   }
   __syncthreads();
   uint32_t wide = 0u;
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
       // key at column q: bits 2 and 3 of its index inside the group swapped
       const int ua = (qa & ~15) | ((qa & 4) << 1) | ((qa & 8) >> 1) | (qa & 3);
       const int ub = (qb & ~15) | ((qb & 4) << 1) | ((qb & 8) >> 1) | (qb & 3);
-      const uint32_t xa = tile[ua * D + d], xb = tile[ub * D + d];
+      const uint32_t xa = tile[ua * TS + d], xb = tile[ub * TS + d];
       wide = max(wide, max(xa & 0x7fffu, xb & 0x7fffu));
       w[e] = pack_f16(__uint_as_float(xa << 16), __uint_as_float(xb << 16));
     }
@@ -159,12 +163,11 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
 // softmax_scale * log2(e), and split into a bf16 hi + lo pair.  Stored per
 // (row, query head) as D/8 groups of {8 hi, 8 lo} (32 bytes): the lane that
 // owns dims [8 grp, 8 grp + 8) of a k-step reads both operands with two
-// 16-byte loads.  One block per row.
+// 16-byte loads.  One row per call.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_qprep(AttnArgs a) {
+__device__ void prep_q_row(const AttnArgs& a, int row, float* s_sn, float* s_cs) {
   constexpr int NG = D / 8;
-  __shared__ float s_sn[D / 2], s_cs[D / 2];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int pos = min(a.qpos[row], a.T - 1);
   if (tid < D / 2) rope_sincos(pos, a.inv_freq[tid], &s_sn[tid], &s_cs[tid]);
   __syncthreads();
@@ -655,40 +658,52 @@ void k_attn_bf16(AttnArgs a) {
   }  // work items
 }
 
-// Work list of the persistent attention blocks (one block of 1024 threads):
-// the key range of each tile group (its rows' largest position), the number
-// of 64-key blocks each (tile group, segment) pair covers, and the pairs that
-// have work, sorted longest first (ties by index): each KV head's blocks take
-// the long items before the short ones, which keeps the tail of the launch
-// short.  Lists longer than kSchedMax pairs keep the natural order (segment
-// by segment, latest rows first) with the empty pairs included.  Also resets
-// the per-head item counters.
-constexpr int kSchedMax = 8192;
-__global__ __launch_bounds__(1024) void k_attn_sched(AttnArgs a) {
-  __shared__ unsigned long long s_key[kSchedMax];
-  __shared__ int s_bmax[kSchedMax];
-  __shared__ int s_n;
+// Work list of the persistent attention blocks (one block): the key range
+// of each tile group (its rows' largest position), the number of 64-key
+// blocks each (tile group, segment) pair covers, and the pairs that have
+// work, sorted longest first: each KV head's blocks take the long items
+// before the short ones, which keeps the tail of the launch short.  Lists
+// longer than kSchedMax pairs keep the natural order (segment by segment,
+// latest rows first) with the empty pairs included.  Also resets the
+// per-head item counters.
+constexpr int kSchedMax = 2048;
+__device__ void build_schedule(const AttnArgs& a, char* smem) {
+  unsigned long long* s_key = reinterpret_cast<unsigned long long*>(smem);
+  int* s_bmax = reinterpret_cast<int*>(smem + kSchedMax * 8);
+  int* s_n = s_bmax + kSchedMax;
   const int tid = threadIdx.x;
   const int n_tg = a.n_tg, nseg = a.nseg, S = a.seg_keys;
   const int n_items = n_tg * nseg;
-  for (int h = tid; h < a.H; h += 1024) a.sched_cnt[h] = 0;
+  for (int h = tid; h < a.H; h += 256) a.sched_cnt[h] = 0;
   if (n_items > kSchedMax) {
-    for (int i = tid; i < n_items; i += 1024) {
+    for (int i = tid; i < n_items; i += 256) {
       const int seg = i / n_tg, tg = n_tg - 1 - i % n_tg;
       a.sched_order[i] = tg * nseg + seg;
     }
     if (tid == 0) a.sched_n[0] = n_items;
     return;
   }
-  for (int t = tid; t < n_tg; t += 1024) s_bmax[t] = -1;
-  if (tid == 0) s_n = 0;
+  for (int t = tid; t < n_tg; t += 256) s_bmax[t] = -1;
+  if (tid == 0) *s_n = 0;
   __syncthreads();
   const int rows_per_tg = 32 * a.tpb * a.qt;
-  for (int r = tid; r < a.n_q; r += 1024) atomicMax(&s_bmax[r / rows_per_tg], min(a.qpos[r], a.T - 1));
+  for (int r0 = 0; r0 < a.n_q; r0 += 256 * 8) {
+    int p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // eight loads in flight per thread
+      const int r = r0 + u * 256 + tid;
+      p[u] = r < a.n_q ? a.qpos[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * 256 + tid;
+      if (r < a.n_q) atomicMax(&s_bmax[r / rows_per_tg], min(p[u], a.T - 1));
+    }
+  }
   __syncthreads();
   int N = 1;
   while (N < n_items) N <<= 1;
-  for (int i = tid; i < N; i += 1024) {
+  for (int i = tid; i < N; i += 256) {
     unsigned long long key = 0ull;
     if (i < n_items) {
       const int tg = i / nseg, seg = i % nseg;
@@ -702,7 +717,7 @@ __global__ __launch_bounds__(1024) void k_attn_sched(AttnArgs a) {
   // bitonic sort, descending
   for (int k = 2; k <= N; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += 1024) {
+      for (int i = tid; i < N; i += 256) {
         const int l = i ^ j;
         if (l > i) {
           const unsigned long long x = s_key[i], y = s_key[l];
@@ -715,13 +730,32 @@ __global__ __launch_bounds__(1024) void k_attn_sched(AttnArgs a) {
       }
       __syncthreads();
     }
-  for (int i = tid; i < N; i += 1024) {
+  for (int i = tid; i < N; i += 256) {
     const bool has = (s_key[i] >> 32) != 0;
     if (has) a.sched_order[i] = (int)(0xffffffffu - (unsigned)(s_key[i] & 0xffffffffu));
-    if (has && (i + 1 == N || (s_key[i + 1] >> 32) == 0)) s_n = i + 1;
+    if (has && (i + 1 == N || (s_key[i + 1] >> 32) == 0)) *s_n = i + 1;
   }
   __syncthreads();
-  if (tid == 0) a.sched_n[0] = s_n;
+  if (tid == 0) a.sched_n[0] = *s_n;
+}
+
+// Per-layer set-up of the attention, one launch: block 0 builds the work
+// list, then one block per (64-key V tile, KV head) and one per query row.
+template <int D>
+constexpr int setup_lds_bytes() {
+  return BK * (D + 2) * 2 > kSchedMax * 12 + 4 ? BK * (D + 2) * 2 : kSchedMax * 12 + 4;
+}
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[setup_lds_bytes<D>()];
+  const int nv = a.nblk * a.H;
+  const int b = (int)blockIdx.x - 1;
+  if (b < 0)
+    build_schedule(a, smem);
+  else if (b < nv)
+    prep_v_tile<D>(a, b % a.nblk, b / a.nblk, reinterpret_cast<uint16_t*>(smem));
+  else
+    prep_q_row<D>(a, b - nv, reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + D / 2);
 }
 
 // Combine the per-segment results of rows whose keys span several segments:
@@ -759,20 +793,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
   {
-    TimedLaunch tl_("attention_qprep", stream);
-    hipLaunchKernelGGL((k_attn_qprep<D>), dim3(a.n_q), dim3(256), 0, stream, a);
+    TimedLaunch tl_("attention_setup", stream);
+    hipLaunchKernelGGL((k_attn_setup<D>), dim3(1 + a.nblk * a.H + a.n_q), dim3(256), 0, stream, a);
   }
-  if (ct_status s = check_launch("attention query preparation")) return s;
-  {
-    TimedLaunch tl_("attention_prep", stream);
-    hipLaunchKernelGGL((k_attn_prep<D>), dim3(a.nblk, a.H), dim3(256), 0, stream, a);
-  }
-  if (ct_status s = check_launch("attention V preparation")) return s;
-  {
-    TimedLaunch tl_("attention_sched", stream);
-    hipLaunchKernelGGL(k_attn_sched, dim3(1), dim3(1024), 0, stream, a);
-  }
-  if (ct_status s = check_launch("attention schedule")) return s;
+  if (ct_status s = check_launch("attention set-up")) return s;
   const int blocks = a.H * a.blocks_per_head;
   {
     TimedLaunch tl_("attention", stream);
@@ -807,10 +831,12 @@ void attn_plan(AttnArgs* a, int n_cu) {
   const int ntiles = (a->n_q + 31) / 32;
   a->n_tg = (ntiles + a->tpb * a->qt - 1) / (a->tpb * a->qt);
   // Segment length: the causal triangle (about units * T / 2 keys of block
-  // work) spread over about 2.5 blocks per CU, at least 1024 keys, a
-  // multiple of the LDS block.
+  // work) spread over about 1.8 items per CU (longer items mean fewer
+  // partial results and merges; with the longest-first order of k_attn_sched
+  // this keeps the tail short), at least 1024 keys, a multiple of the LDS
+  // block.
   const long long units = (long long)a->H * a->n_tg * a->n_hc;
-  long long s = units * (long long)a->T / (5LL * (n_cu > 0 ? n_cu : 256));
+  long long s = units * (long long)a->T * 5 / (18LL * (n_cu > 0 ? n_cu : 256));
   if (const char* env = getenv("CACHETUNE_ATTN_SEG")) s = atoll(env);
   if (s < 1024) s = 1024;
   s = (s + BK - 1) / BK * BK;
