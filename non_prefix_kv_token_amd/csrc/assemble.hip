@@ -99,9 +99,11 @@ template <> struct Vec8<CT_F32> {
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, void* v_out) {
   constexpr int CPH = D / 16;  // 8-pair chunks per head
+  // sine and cosine of the row's D/2 rotation angles, shared by its heads
+  __shared__ double s_sc[4][D / 2][2];
   const AsmPlace& pl = al.p[blockIdx.y];
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = blockIdx.x * 4 + wv;
   if (r >= pl.n) return;
   const int H = al.H;
 
@@ -134,6 +136,11 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
   const size_t src_base = (size_t)srow * H * D;
   const size_t dst_base = (size_t)gpos * H * D;
   const bool half = al.style == CT_ROPE_HALF;
+  // one angle per lane (frequency index j), then read back by every head
+  // (the wave's own LDS slice: no barrier beyond the wave)
+  for (int j = lane; j < D / 2; j += 64) sincos_pos(gpos, al.inv_freq[j], &s_sc[wv][j][0], &s_sc[wv][j][1]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   for (int item = lane; item < H * CPH; item += 64) {
     const int h = item / CPH, c = item % CPH;
@@ -150,8 +157,7 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       // pair t of this lane: frequency index 8c + t
-      double sn, cs;
-      sincos_pos(gpos, al.inv_freq[8 * c + t], &sn, &cs);
+      const double sn = s_sc[wv][8 * c + t][0], cs = s_sc[wv][8 * c + t][1];
       double x0, x1;
       if (half) {
         x0 = xa.get(t);
