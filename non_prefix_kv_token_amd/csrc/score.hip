@@ -339,7 +339,7 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // largest; rows a chunk does not have are zero).  The step loop is unrolled
 // by two so that both register and LDS buffers are compile-time.
 template <int NTL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_band_bf16(ScoreLaunch sl, char* ws) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][3 * 32 * NTL * kTwStride];
 
@@ -357,7 +357,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, col = lane & 31;
-  const int cbase = blockIdx.x * 256 + wave * 64;
+  const int cbase = blockIdx.x * 512 + wave * 64;
   const bool active = cbase < C;
   const int c0 = cbase + 2 * col;
 
@@ -393,12 +393,12 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
   };
   // twiddle slab of a step: 3 planes x 32*NTL rows x 32 tokens (16-byte chunks)
   constexpr int TWN = 3 * 32 * NTL * 4;    // chunks per slab
-  constexpr int TWI = (TWN + 255) / 256;   // chunks per thread (the last may be partial)
+  constexpr int TWI = (TWN + 511) / 512;   // chunks per thread (the last may be partial)
   u32x4_t twr[TWI];
   int twoff[TWI];
 #pragma unroll
   for (int it = 0; it < TWI; ++it) {
-    const int item = tid + 256 * it;
+    const int item = tid + 512 * it;
     const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
     // rows this chunk does not have read past the table (zeros)
     twoff[it] = (item < TWN && r < nrows) ? (int)((q * plane + (long long)(pbase + r) * ntp + 8 * i) * 2)
@@ -412,8 +412,8 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
   auto store_tw = [&](uint16_t* buf) {
 #pragma unroll
     for (int it = 0; it < TWI; ++it) {
-      const int item = tid + 256 * it;
-      if (TWN % 256 != 0 && item >= TWN) break;
+      const int item = tid + 512 * it;
+      if (TWN % 512 != 0 && item >= TWN) break;
       const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
       *reinterpret_cast<u32x4_t*>(&buf[(q * 32 * NTL + r) * kTwStride + 8 * i]) = twr[it];
     }
@@ -438,12 +438,14 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
           a[pt][q] = *reinterpret_cast<const bf16x8_t*>(
               &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
 #pragma unroll
-      for (int pt = 0; pt < NTL; ++pt)
+      for (int pt = 0; pt < NTL; ++pt) {
+        if (pt * 32 >= nrows) break;  // the band ends inside this block: no products of padding
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
           acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b0, acc[pt][0], 0, 0, 0);
           acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b1, acc[pt][1], 0, 0, 0);
         }
+      }
     }
   };
 
@@ -864,13 +866,23 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
     {
     TimedLaunch tl_("band", stream);
     if (sl.dtype == CT_BF16) {
-      // band tiles per block: the launch's largest band, up to 4 (128 rows)
-      const int ntl = sl.max_ppad >= 128 ? 4 : sl.max_ppad / 32;
-      dim3 gq((sl.C + 255) / 256, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
-      if (ntl == 4) hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(256), 0, stream, sl, ws);
-      else if (ntl == 3) hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(256), 0, stream, sl, ws);
-      else if (ntl == 2) hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(256), 0, stream, sl, ws);
-      else hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(256), 0, stream, sl, ws);
+      // Band tiles per block: the whole of the launch's largest band when it
+      // has at most 5 tiles (160 rows), else that band split evenly over the
+      // fewest blocks of at most 5 tiles.  Each block streams X from HBM
+      // once, so more blocks per band means more reads of X.
+      const int tiles = sl.max_ppad / 32;
+      const int nyb = (tiles + 4) / 5;
+      const int ntl = (tiles + nyb - 1) / nyb;
+      // 8 waves x 64 channels per block: every twiddle slab staged in LDS
+      // serves 512 channels (the slabs, not X, are most of the L2 traffic)
+      dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+      switch (ntl) {
+        case 5: hipLaunchKernelGGL(k_band_bf16<5>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 4: hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 3: hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 2: hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(512), 0, stream, sl, ws); break;
+        default: hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(512), 0, stream, sl, ws); break;
+      }
     } else
       hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
     }
