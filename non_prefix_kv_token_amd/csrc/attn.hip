@@ -26,7 +26,7 @@
 // combines.  The grid is persistent: one block per CU, block b serving KV
 // head b % H (blocks are dealt round-robin over the 8 XCDs, so each XCD's L2
 // holds one head's keys), taking (tile group, segment) items from a per-head
-// counter in the order k_attn_sched computed from the query positions,
+// counter in the order the set-up launch computed from the query positions,
 // longest first.
 //
 // Precision.  Logits of these inputs reach the hundreds, so one bf16 rounding
@@ -764,6 +764,8 @@ __global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   constexpr int PER = D / 64;
+  constexpr int U = 4;  // segments whose loads are in flight together
+  typedef float fv_t __attribute__((ext_vector_type(PER)));
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= a.n_q * a.Hq) return;
   const int row = w / a.Hq, hq = w % a.Hq;
@@ -771,17 +773,33 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int S = a.seg_keys;
   if (pos < S) return;
   const int ns = pos / S + 1;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[((size_t)s * a.n_q + row) * a.Hq + hq]);
-  float wsum = 0.f, acc[PER];
+  // online combination over groups of U segments: running maximum M, weight
+  // sum and weighted output
+  float M = -INFINITY, wsum = 0.f;
+  fv_t acc = {};
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float ls[U];
+    fv_t os[U];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t pb = ((size_t)s * a.n_q + row) * a.Hq + hq;
-    const float wgt = __builtin_amdgcn_exp2f(a.part_lse[pb] - M);
-    wsum += wgt;
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      const size_t pb = ((size_t)min(s, ns - 1) * a.n_q + row) * a.Hq + hq;
+      ls[u] = s < ns ? a.part_lse[pb] : -INFINITY;
+      os[u] = *reinterpret_cast<const fv_t*>(a.part_o + pb * D + lane * PER);
+    }
+    float mg = M;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += wgt * a.part_o[pb * D + lane * PER + i];
+    for (int u = 0; u < U; ++u) mg = fmaxf(mg, ls[u]);
+    const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mg);
+    wsum *= c;
+    acc *= c;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = ls[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u] - mg);
+      wsum += wgt;
+      acc += wgt * os[u];
+    }
+    M = mg;
   }
   const float inv = 1.f / wsum;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.Hq + hq) * D + lane * PER;
