@@ -498,11 +498,32 @@ void k_attn_bf16(AttnArgs a) {
   // P^T . V^T for one 64-key block (probabilities in st, fp16), row sums from
   // the rounded probabilities.
   const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // One lazy-maximum decision covers the whole 64-key block, so that the
+  // exponentials of the second 32-key tile and the products of the first sit
+  // in one scheduling region (no branch between them) and can interleave.
   auto pv = [&](const uint16_t* vbuf, f32x16_t (*st)[2]) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float bm = __builtin_elementwise_maximum(max16(st[qt][0]), max16(st[qt][1]));
+      if (__any(bm > m_run[qt] + kLazyThr)) {
+        const float m_new = fmaxf(m_run[qt], fmaxf(bm, __shfl_xor(bm, 32)));
+        const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[qt][i][v] *= alpha;
+        l_run[qt] *= alpha;
+        m_run[qt] = m_new;
+      }
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) softmax_tile(qt, st[qt][kt]);
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[qt][kt][v] = __builtin_amdgcn_exp2f(st[qt][kt][v] - mu);
+      }
       // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
