@@ -246,8 +246,11 @@ void k_attn_bf16(AttnArgs a) {
   constexpr int DPG = D / NDG;       // V dims per thread (2 keys x DPG dims)
   static_assert(KIT >= 1 && BK * KCH == KIT * NT, "K staging split");
   static_assert(DPG >= 4 && DPG % 4 == 0, "V staging split");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VTS];  // V^T: fp16 (bf16 when redone)
+  // K and V^T rings of four 64-key blocks: blocks are staged two ahead, so
+  // one barrier every other block orders both the writes before their reads
+  // and the reads before the slot is written again.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[4][BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[4][D * VTS];  // V^T: fp16 (bf16 when redone)
   __shared__ int s_wmax[NW];
   __shared__ int s_item;
 
@@ -565,6 +568,10 @@ void k_attn_bf16(AttnArgs a) {
   if (!redo) {
     load_fast(kb0);
     store_fast(0, 0);
+    if (kb0 + 1 < kb1) {
+      load_fast(kb0 + 1);
+      store_fast(1, 1);
+    }
   }
   // The query operands are complete before the loop: the compiler's wait
   // counting would otherwise treat them as pending inside the loop and make
@@ -574,10 +581,14 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qh[qt][s]), "+v"(ql[qt][s]));
   for (int kb = kb0; kb < kb1 && !redo; ++kb) {
-    const int c = (kb - kb0) & 1;
-    const bool more = kb + 1 < kb1;
-    if (more) load_fast(kb + 1);
-    __syncthreads();
+    const int i = kb - kb0, c = i & 3;
+    const bool more = kb + 2 < kb1;
+    // Block kb + 2 goes to slot (i + 2) & 3, last read at block i - 2.  A
+    // barrier at the start of every even block lies between each store
+    // (block i) and its reads (block i + 2), and between the reads of a slot
+    // (block i - 2) and its next store (block i).
+    if ((i & 1) == 0) __syncthreads();
+    if (more) load_fast(kb + 2);
     const int k0 = kb * BK;
     if (wave_on && k0 <= wmax) {
       // The score products run at raised wave priority: of the two waves
@@ -588,7 +599,7 @@ void k_attn_bf16(AttnArgs a) {
       __builtin_amdgcn_s_setprio(0);
       pv(Vs[c], st);
     }
-    if (more) store_fast(c ^ 1, c ^ 1);
+    if (more) store_fast((i + 2) & 3, (i + 2) & 3);
   }
 
   if (redo) {
@@ -871,9 +882,9 @@ void attn_plan(AttnArgs* a, int n_cu) {
   a->n_tg = (ntiles + a->tpb * a->qt - 1) / (a->tpb * a->qt);
   // Segment length: the causal triangle (about units * T / 2 keys of block
   // work) spread over about 1.8 items per CU (longer items mean fewer
-  // partial results and merges; with the longest-first order of k_attn_sched
-  // this keeps the tail short), at least 1024 keys, a multiple of the LDS
-  // block.
+  // partial results and merges; with the longest-first order of the work
+  // list this keeps the tail short), at least 1024 keys, a multiple of the
+  // LDS block.
   const long long units = (long long)a->H * a->n_tg * a->n_hc;
   long long s = units * (long long)a->T * 5 / (18LL * (n_cu > 0 ? n_cu : 256));
   if (const char* env = getenv("CACHETUNE_ATTN_SEG")) s = atoll(env);
