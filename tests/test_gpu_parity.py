@@ -296,6 +296,31 @@ def test_attention_group8_long(orc, syn):
     _attn_case(orc, syn, 3000, 1, 8, 128, 70, "bf16", 500000.0, 0, scale=0.1)
 
 
+def test_attention_many_items_natural_order(orc, syn, monkeypatch):
+    """More (tile group, segment) items than the set-up launch sorts (54 tile
+    groups x 40 segments of 1024 keys = 2160): the work list keeps its natural
+    order, empty items included, and every row still gets all its segments
+    merged.  Sampled rows across the context, all query heads."""
+    monkeypatch.setenv("CACHETUNE_ATTN_SEG", "1024")
+    ct = need_gpu()
+    T, H, Hq, D, n_q = 40000, 1, 4, 128, 3400
+    rng = np.random.default_rng(T + n_q)
+    k = syn.rows(SEED, syn.K, 0, 1, T, H, D, np.arange(T), "bf16")
+    v = syn.rows(SEED, syn.V, 0, 1, T, H, D, np.arange(T), "bf16")
+    qpos = np.sort(rng.choice(np.arange(1, T - 1), n_q - 2, replace=False))
+    qpos = np.concatenate([[0], qpos, [T - 1]]).astype(np.int32)
+    q = syn.rows(SEED, syn.Q, 0, 1, T, Hq, D, qpos, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    out, lse = ct.cachetune_recompute_attn(to_dev(q), to_dev(qpos), to_dev(k), to_dev(v), scale, 500000.0, 0,
+                                           want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, n_q - 2, n_q - 1], rng.choice(n_q, 12, replace=False)]))
+    ref, lref = orc.attention(q, qpos, k, v, scale, 500000.0, 0, rows=rows)
+    og, lg = widen(to_host(out))[rows], to_host(lse).astype(np.float64)[rows]
+    assert (np.abs(og - ref) <= 2e-2 + half_ulp_bf16(ref)).all(), np.abs(og - ref).max()
+    assert np.abs(lg - lref).max() <= 2e-2 * np.maximum(1.0, np.abs(lref)).max()
+
+
 # ---- host-tier sparse loading -------------------------------------------------------
 
 @pytest.mark.parametrize("r", [(15, 100), (0, 1), (1, 1)])
