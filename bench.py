@@ -374,16 +374,17 @@ def host_tier(args):
     copy_stream = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    for r in r_list:
-        ks = [(r[0] * N) // r[1] for _ in ns]
-        kmax = max(ks)
+    def setup(k_per_chunk):
+        """Per-ratio state (staging buffers, recomputed rows, queries, places);
+        returns (request, rows staged per layer, n_q, release)."""
+        ks = list(k_per_chunk)
         rows = sum(N - k for k in ks)
         k_stage = [torch.empty((rows, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
         v_stage = [torch.empty_like(k_stage[0]) for _ in range(2)]
         # selected rows: the first k of each ranking; recomputed rows are the cached
         # rows plus seeded noise, in ascending local order
         sel_list, rec = [], []
-        gen.manual_seed(seed + r[0])
+        gen.manual_seed(seed + ks[0])
         for b in range(nb):
             head = rank_h[offs[b]:offs[b] + ks[b]]
             order = np.argsort(head)
@@ -423,6 +424,7 @@ def host_tier(args):
         # (also across requests)
         ev_free = [torch.cuda.Event(), torch.cuda.Event()]
         used = [False, False]
+        state = [k_stage, v_stage, rec, qs, ws, out, places]
 
         def request():
             ev_ready = [torch.cuda.Event() for _ in range(L)]
@@ -441,22 +443,64 @@ def host_tier(args):
                 ct.cachetune_recompute_attn(qs[l], qpos_d, k_asm, v_asm, scale, theta, out=out, ws=ws,
                                             stream=comp)
 
+        def release():
+            state.clear()
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+        return request, rows, n_q, release
+
+    def measure(request, steps):
+        """Mean ms per request after one untimed request."""
         request()
         torch.cuda.synchronize()
         a, z = E(), E()
         comp.synchronize()
         a.record(comp)
-        for _ in range(args.steps):
+        for _ in range(steps):
             request()
         z.record(comp)
         torch.cuda.synchronize()
-        ms = a.elapsed_time(z) / args.steps
+        return a.elapsed_time(z) / steps
+
+    for r in r_list:
+        ks = [(r[0] * N) // r[1] for _ in ns]
+        request, rows, n_q, release = setup(ks)
+        ms = measure(request, args.steps)
+        release()
         h2d = 2.0 * rows * H * D * 2 * L
         results.append({"r": f"{r[0]}/{r[1]}", "k": ks[0], "n_q": n_q, "ms_per_request": ms,
                         "h2d_bytes": h2d, "h2d_GBs_effective": h2d / (ms * 1e-3) / 1e9})
         print(f"[bench] r={r[0]}/{r[1]} {ms:.1f} ms per request", file=sys.stderr, flush=True)
-        del k_stage, v_stage, rec, qs, ws, out, places
-        torch.cuda.empty_cache()
+
+    calibration = None
+    if args.calibrate:
+        # App. C.1: per-token costs from two profiling probes -- at r = 5 % the
+        # request is bound by the complement transfer, at r = 30 % by the
+        # recomputed rows' work -- then App. C.2's warm-started golden-section
+        # search on the measured request time, with and without the 15 % floor.
+        tok = float(T_c) * L
+        t_i = results[0]["ms_per_request"] / (tok * (1.0 - 0.05))
+        t_c = results[-1]["ms_per_request"] / (tok * 0.30)
+        calibration = {"t_c_us_per_token_layer": t_c * 1e3, "t_i_us_per_token_layer": t_i * 1e3,
+                       "warm_start": t_i / (t_c + t_i), "eps": 0.01, "half_width": 0.1, "runs": []}
+        for r_min in (0.15, 0.02):
+            probes = []
+
+            def cost(r):
+                k = int(math.floor(r * N))
+                request, _, _, release = setup([k] * nb)
+                ms = measure(request, max(2, args.steps // 2))
+                release()
+                probes.append([r, k, ms])
+                print(f"[bench] calibration probe r={r:.4f} (k={k}) {ms:.1f} ms", file=sys.stderr, flush=True)
+                return ms
+
+            r_star, n_probes = ct.cachetune_calibrate_ratio(t_c, t_i, cost, r_min=r_min, r_max=1.0,
+                                                            half_width=0.1, eps=0.01)
+            calibration["runs"].append({"r_min": r_min, "r_star": r_star, "probes": probes,
+                                        "n_probes": n_probes})
+            print(f"[bench] calibrated r* = {r_star:.4f} (r_min {r_min})", file=sys.stderr, flush=True)
 
     # pinned host -> device copy bandwidth for reference
     src = pool[0][0]
@@ -482,6 +526,7 @@ def host_tier(args):
                                "host pool in rank order, r swept", "T": T},
         "per_r": results, "r_star": best["r"], "pinned_h2d_GBs": copy_gbs,
         "r_min_quality_bound": "15/100",
+        **({"calibration": calibration} if calibration else {}),
     }), flush=True)
 
 def main():
@@ -493,6 +538,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-tier", action="store_true",
                     help="run the 32 x 2048 host-tier pipeline with an r sweep instead")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="with --host-tier: also run the warm-started golden-section search for r")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()

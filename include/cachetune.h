@@ -240,7 +240,7 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
 /* ---- kernel timing (tracing aid) -----------------------------------------
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
- *   "band", "gram", "topr", "assemble", "attention_prep", "attention",
+ *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
  *   "attention_merge", "rank_order" (and "twiddle", "layer_norm", "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and
@@ -248,6 +248,32 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
  * small host objects (no device memory is allocated). */
 ct_status cachetune_timing_enable(int32_t on);
 ct_status cachetune_timing_read(const char* kernel, double* total_ms, int32_t* launches);
+
+/* ---- hardware-aware recomputation ratio -----------------------------------
+ * App. C.1 (cost model) and App. C.2 (warm-started golden-section search):
+ * host logic over a caller-supplied cost measurement; no device work.
+ *
+ * Warm start: r0 = t_i / (t_c + t_i), clamped to [r_min, r_max] -- the ratio at
+ * which a layer's recomputation of r*N tokens (t_c per token) and its loading
+ * of the other (1 - r)*N (t_i per token) take equal time.
+ * Search: on [a, b] = [max(r_min, r0 - half_width), min(r_max, r0 + half_width)],
+ * golden-section steps with phi = (sqrt(5) - 1)/2: probes x1 = b - phi(b - a)
+ * and x2 = a + phi(b - a); the side with the lower cost is kept (ties keep
+ * [a, x2]) and its inner probe is reused, so each step makes one new call.
+ * When b - a < eps the midpoint of [a, b] is returned.
+ *  t_c, t_i: per-token costs (any common unit, >= 0, not both 0).
+ *  cost: host callback, cost(r, user) = the measured objective at ratio r
+ *        (e.g. mean time to first token over a calibration set); it is called
+ *        2 + (number of steps) times, in order, on the calling thread.
+ *  r_out: host double, the calibrated ratio.  n_probes: host int32 (or NULL),
+ *        the number of cost calls made.
+ * Errors: CT_E_INVALID for a negative or non-finite t_c or t_i, both zero,
+ * r_min > r_max, a range outside [0, 1], half_width <= 0, eps <= 0, a NULL
+ * callback or output, or a cost that is not finite (the search stops there). */
+typedef double (*ct_cost_fn)(double r, void* user);
+ct_status cachetune_calibrate_ratio(double t_c, double t_i, double r_min, double r_max,
+                                    double half_width, double eps, ct_cost_fn cost, void* user,
+                                    double* r_out, int32_t* n_probes);
 
 #ifdef __cplusplus
 }

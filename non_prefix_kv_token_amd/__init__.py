@@ -45,7 +45,10 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
            "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
-           "cachetune_stage_complement"]
+           "cachetune_stage_complement", "cachetune_calibrate_ratio"]
+
+# cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
+COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
 
 _lib = None
 
@@ -75,6 +78,8 @@ def lib():
         L.cachetune_rank_order.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.cachetune_stage_complement.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.cachetune_timing_read.argtypes = [C.c_char_p, C.POINTER(f64), C.POINTER(i32)]
+        L.cachetune_calibrate_ratio.argtypes = [f64, f64, f64, f64, f64, f64, COST_FN, vp,
+                                                C.POINTER(f64), C.POINTER(i32)]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -226,6 +231,32 @@ def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, styl
 
 def cachetune_timing_enable(on: bool = True):
     _check(lib().cachetune_timing_enable(1 if on else 0))
+
+
+def cachetune_calibrate_ratio(t_c, t_i, cost, r_min=0.15, r_max=1.0, half_width=0.1, eps=0.01):
+    """Warm-started golden-section search for the recomputation ratio (host
+    logic in the library).  cost(r) -> float is called for each probe, in
+    order; returns (r, number of probes).  An exception raised by `cost` stops
+    the search and is re-raised here."""
+    err = []
+
+    def cb(r, _user):
+        try:
+            return float(cost(r))
+        except BaseException as e:  # handed back after the library returns
+            err.append(e)
+            return float("nan")
+
+    fn = COST_FN(cb)
+    r_out = C.c_double(0.0)
+    n = C.c_int32(0)
+    st = lib().cachetune_calibrate_ratio(float(t_c), float(t_i), float(r_min), float(r_max),
+                                         float(half_width), float(eps), fn, None, C.byref(r_out),
+                                         C.byref(n))
+    if err:
+        raise err[0]
+    _check(st)
+    return r_out.value, n.value
 
 
 def cachetune_timing_read(kernel: str):

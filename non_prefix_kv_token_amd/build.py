@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcachetune.so")
-SOURCES = ["abi.hip", "score.hip", "topr.hip", "assemble.hip", "attn.hip", "attn_f32.hip", "timing.hip", "hosttier.hip"]
+SOURCES = ["abi.hip", "score.hip", "topr.hip", "assemble.hip", "attn.hip", "attn_f32.hip", "timing.hip", "hosttier.hip",
+           "calibrate.cpp"]
 ARCH = os.environ.get("CACHETUNE_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -25,7 +26,7 @@ FLAGS = [
 
 
 def _compile(src: str, out_dir: str) -> str:
-    obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -215,3 +215,50 @@ def attention(q_pre, qpos, k, v, scale, theta, style=ROPE_HALF, rows=None):
     if rc != 0:
         raise ValueError("orc_attention rejected its arguments")
     return out, lse
+
+
+# ---- hardware-aware recomputation ratio (App. C.1, App. C.2) ----------------
+
+def warm_start_ratio(t_c: float, t_i: float, r_min: float, r_max: float) -> float:
+    """App. C.1: per layer, recomputing r*N tokens costs r*N*t_c and loading the
+    other (1 - r)*N costs (1 - r)*N*t_i; the two are equal at
+    r = t_i / (t_c + t_i).  Clamped to the allowed range."""
+    r = t_i / (t_c + t_i)
+    return min(max(r, r_min), r_max)
+
+
+def calibrate_ratio(t_c, t_i, cost, r_min=0.15, r_max=1.0, half_width=0.1, eps=0.01):
+    """App. C.2, warm-started golden-section search, written out step by step.
+    The interval around the warm start is [r0 - half_width, r0 + half_width]
+    cut to [r_min, r_max].  Each step compares the costs at the two inner
+    points x1 = b - phi (b - a) and x2 = a + phi (b - a), keeps the side with
+    the lower cost (the lower side [a, x2] on a tie), and reuses the inner point
+    that stays inside, so only one new cost is measured per step.  Once the
+    width is below eps, the midpoint is the ratio.
+
+    Returns (r, probes, widths): the probes in call order as (r, cost) pairs,
+    and the interval width before each step and at the end."""
+    phi = (5.0 ** 0.5 - 1.0) / 2.0
+    r0 = warm_start_ratio(t_c, t_i, r_min, r_max)
+    a, b = max(r_min, r0 - half_width), min(r_max, r0 + half_width)
+    probes = []
+
+    def f(r):
+        v = float(cost(r))
+        probes.append((r, v))
+        return v
+
+    x1, x2 = b - phi * (b - a), a + phi * (b - a)
+    f1, f2 = f(x1), f(x2)
+    widths = [b - a]
+    while b - a >= eps:
+        if f1 <= f2:
+            b, x2, f2 = x2, x1, f1
+            x1 = b - phi * (b - a)
+            f1 = f(x1)
+        else:
+            a, x1, f1 = x1, x2, f2
+            x2 = a + phi * (b - a)
+            f2 = f(x2)
+        widths.append(b - a)
+    return 0.5 * (a + b), probes, widths

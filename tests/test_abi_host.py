@@ -82,3 +82,40 @@ def test_calls_reject_bad_arguments_without_device_work(lib):
     assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 128, ct.CT_BF16, C.byref(out)) == ct.CT_OK
     assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 100, ct.CT_BF16,
                                            C.byref(out)) == ct.CT_E_UNSUPPORTED
+
+
+# ---- hardware-aware ratio search: host logic, callable without a GPU ---------------------
+
+@pytest.mark.parametrize("case", [
+    dict(t_c=1.0, t_i=0.25, c=0.23, r_min=0.0, half_width=0.1, eps=0.01),
+    dict(t_c=0.6, t_i=0.09, c=0.10, r_min=0.15, half_width=0.1, eps=0.005),   # optimum below the floor
+    dict(t_c=1.0, t_i=1.0, c=0.62, r_min=0.0, half_width=0.2, eps=1e-4),
+])
+def test_calibrate_ratio_matches_oracle(lib, orc, case):
+    """The library's search makes the oracle's probes, in the same order, and
+    returns the oracle's ratio."""
+    import non_prefix_kv_token_amd as ct
+    c = case["c"]
+    cost = lambda r: (r - c) ** 2 + 0.1 * abs(r - c)  # noqa: E731
+    kw = dict(r_min=case["r_min"], half_width=case["half_width"], eps=case["eps"])
+    seen = []
+    r_lib, n = ct.cachetune_calibrate_ratio(case["t_c"], case["t_i"], lambda r: (seen.append(r), cost(r))[1],
+                                            **kw)
+    r_orc, probes, _ = orc.calibrate_ratio(case["t_c"], case["t_i"], cost, **kw)
+    assert n == len(probes) == len(seen)
+    assert max(abs(x - p[0]) for x, p in zip(seen, probes)) <= 1e-12
+    assert abs(r_lib - r_orc) <= 1e-12
+
+
+def test_calibrate_ratio_rejects_bad_arguments(lib):
+    import non_prefix_kv_token_amd as ct
+    good = lambda r: r  # noqa: E731
+    for kw in [dict(t_c=-1.0, t_i=1.0), dict(t_c=0.0, t_i=0.0), dict(t_c=1.0, t_i=1.0, r_min=0.6, r_max=0.5),
+               dict(t_c=1.0, t_i=1.0, r_max=1.5), dict(t_c=1.0, t_i=1.0, eps=0.0),
+               dict(t_c=1.0, t_i=1.0, half_width=-0.1), dict(t_c=float("nan"), t_i=1.0)]:
+        with pytest.raises(RuntimeError):
+            ct.cachetune_calibrate_ratio(cost=good, **kw)
+    with pytest.raises(RuntimeError):   # a non-finite measurement stops the search
+        ct.cachetune_calibrate_ratio(1.0, 1.0, lambda r: float("nan"))
+    with pytest.raises(ZeroDivisionError):   # the callback's own exception comes back
+        ct.cachetune_calibrate_ratio(1.0, 1.0, lambda r: 1 / 0)
