@@ -141,6 +141,27 @@ ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_
                                 ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- scoring variants the pages compare (§5.4, App. E.2, App. E.4) ----------
+ *   CT_SCORE_LOWPASS  the score of cachetune_score_chunk.
+ *   CT_SCORE_L2       the same joint K/V magnitudes, layer normalisation and
+ *                     layer mean without the frequency analysis: a = L2 norm
+ *                     of K over the token's H*D channels, b the same for V
+ *                     (the alpha = 1 score of App. E.4, which keeps every bin;
+ *                     alpha_num / alpha_den and fftlen are ignored).
+ * Random selection needs no score of its own: cachetune_select_topr over
+ * caller-supplied seeded uniform scores selects a uniformly random set.
+ * Arguments, layouts and errors are those of cachetune_score_chunk(_ws); an
+ * unknown variant is CT_E_INVALID. */
+typedef enum { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1 } ct_score_variant;
+ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                     int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
+                                     ct_fftlen fftlen, ct_score_variant variant, size_t* bytes);
+ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                  int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
+                                  ct_fftlen fftlen, ct_norm norm, ct_score_variant variant,
+                                  float* score, float* layer_score, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* ---- selection (App. B.1) -------------------------------------------------
  * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].
  * Ranking order: higher score first, equal scores by lower local index (the
@@ -241,7 +262,8 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
  *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
- *   "attention_merge", "rank_order" (and "twiddle", "layer_norm", "layer_mean").
+ *   "attention_merge", "rank_order", "energy_l2" (and "twiddle", "layer_norm",
+ *   "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and
  * forgets them.  Events of other names are kept.  Thread-safe; the events are

@@ -19,6 +19,7 @@ CT_F32, CT_BF16 = 0, 1
 CT_NORM_SUM, CT_NORM_MAX, CT_NORM_MINMAX, CT_NORM_NONE = 0, 1, 2, 3
 CT_ROPE_HALF, CT_ROPE_INTERLEAVED = 0, 1
 CT_FFT_EXACT_N, CT_FFT_ZEROPAD_POW2 = 0, 1
+CT_SCORE_LOWPASS, CT_SCORE_L2 = 0, 1
 
 
 class ct_chunk(C.Structure):
@@ -45,7 +46,8 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_score_chunk_ws", "cachetune_score_chunk", "cachetune_select_topr",
            "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
-           "cachetune_stage_complement", "cachetune_calibrate_ratio"]
+           "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
+           "cachetune_score_variant"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -80,6 +82,10 @@ def lib():
         L.cachetune_timing_read.argtypes = [C.c_char_p, C.POINTER(f64), C.POINTER(i32)]
         L.cachetune_calibrate_ratio.argtypes = [f64, f64, f64, f64, f64, f64, COST_FN, vp,
                                                 C.POINTER(f64), C.POINTER(i32)]
+        L.cachetune_score_variant_ws.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                 C.POINTER(sz)]
+        L.cachetune_score_variant.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                              vp, vp, vp, sz, vp]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -118,18 +124,22 @@ def _i32_array(vals):
 
 # ---- scoring -----------------------------------------------------------------
 
-def cachetune_score_chunk_ws(n_per_chunk, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N) -> int:
+def cachetune_score_chunk_ws(n_per_chunk, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N,
+                             variant=CT_SCORE_LOWPASS) -> int:
     arr = _i32_array(n_per_chunk)
     out = C.c_size_t(0)
-    _check(lib().cachetune_score_chunk_ws(arr, len(n_per_chunk), L, H, D, alpha[0], alpha[1],
-                                          fftlen, C.byref(out)))
+    _check(lib().cachetune_score_variant_ws(arr, len(n_per_chunk), L, H, D, alpha[0], alpha[1],
+                                            fftlen, variant, C.byref(out)))
     return out.value
 
 
 def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N, norm=CT_NORM_SUM,
-                          score=None, layer_score=None, ws=None, want_layers=False, stream=None):
+                          score=None, layer_score=None, ws=None, want_layers=False, stream=None,
+                          variant=CT_SCORE_LOWPASS):
     """chunks: list of (K, V) device tensors [L][n][H][D].  Returns (score,
-    layer_score) fp32 device tensors (layer_score None unless requested)."""
+    layer_score) fp32 device tensors (layer_score None unless requested).
+    variant: CT_SCORE_LOWPASS (the method) or CT_SCORE_L2 (magnitudes without
+    the frequency analysis); the latter goes through cachetune_score_variant."""
     import torch
     dev = chunks[0][0].device
     ns = [int(k.shape[1]) for k, _ in chunks]
@@ -138,15 +148,20 @@ def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N,
         score = torch.empty(total, dtype=torch.float32, device=dev)
     if want_layers and layer_score is None:
         layer_score = torch.empty((L, total), dtype=torch.float32, device=dev)
-    need = cachetune_score_chunk_ws(ns, L, H, D, alpha, fftlen)
+    need = cachetune_score_chunk_ws(ns, L, H, D, alpha, fftlen, variant)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     arr = (ct_chunk * len(chunks))()
     for i, (k, v) in enumerate(chunks):
         arr[i].k, arr[i].v, arr[i].n = k.data_ptr(), v.data_ptr(), int(k.shape[1])
-    _check(lib().cachetune_score_chunk(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
-                                       alpha[1], fftlen, norm, _ptr(score), _ptr(layer_score),
-                                       _ptr(ws), ws.numel(), _stream(stream)))
+    if variant == CT_SCORE_LOWPASS:
+        _check(lib().cachetune_score_chunk(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
+                                           alpha[1], fftlen, norm, _ptr(score), _ptr(layer_score),
+                                           _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(lib().cachetune_score_variant(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
+                                             alpha[1], fftlen, norm, variant, _ptr(score),
+                                             _ptr(layer_score), _ptr(ws), ws.numel(), _stream(stream)))
     return score, layer_score
 
 

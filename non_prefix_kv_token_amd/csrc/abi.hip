@@ -96,22 +96,49 @@ static ct_status check_score_shapes(const int32_t* n_per_chunk, int32_t n_chunks
   return CT_OK;
 }
 
+ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                     int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
+                                     ct_fftlen fftlen, ct_score_variant variant, size_t* bytes) {
+  CT_GUARD_BEGIN
+  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2) return fail(CT_E_INVALID, "unknown variant");
+  if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
+    alpha_num = alpha_den = 1;
+    fftlen = CT_FFT_EXACT_N;
+  }
+  if (ct_status s = check_score_shapes(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen))
+    return s;
+  return score_plan(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen, bytes, nullptr,
+                    variant);
+  CT_GUARD_END
+}
+
 ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                    int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                    ct_fftlen fftlen, size_t* bytes) {
-  CT_GUARD_BEGIN
-  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
-  if (ct_status s = check_score_shapes(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen))
-    return s;
-  return score_plan(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen, bytes, nullptr);
-  CT_GUARD_END
+  return cachetune_score_variant_ws(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen,
+                                    CT_SCORE_LOWPASS, bytes);
 }
 
 ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
                                 int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
                                 ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  return cachetune_score_variant(chunks, n_chunks, L, H, D, dtype, alpha_num, alpha_den, fftlen, norm,
+                                 CT_SCORE_LOWPASS, score, layer_score, ws, ws_bytes, stream);
+}
+
+ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                  int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
+                                  ct_fftlen fftlen, ct_norm norm, ct_score_variant variant,
+                                  float* score, float* layer_score, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   CT_GUARD_BEGIN
+  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2) return fail(CT_E_INVALID, "unknown variant");
+  if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
+    alpha_num = alpha_den = 1;
+    fftlen = CT_FFT_EXACT_N;
+  }
   if (!chunks) return fail(CT_E_INVALID, "chunks is NULL");
   if (n_chunks < 1 || n_chunks > 4096) return fail(CT_E_INVALID, "n_chunks must be in [1, 4096]");
   if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
@@ -127,7 +154,7 @@ ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_
   size_t need = 0;
   std::vector<ScoreLaunch> launches;
   if (ct_status s = score_plan(ns.data(), n_chunks, L, H, D, alpha_num, alpha_den, fftlen, &need,
-                               &launches))
+                               &launches, variant))
     return s;
   if (!ws || ws_bytes < need)
     return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");

@@ -74,11 +74,12 @@ struct ScoreLaunch {
   int64_t slot_off;    // byte offset of the Gram slots
   int64_t slot_bytes;  // bytes per slot
   int64_t total_tokens;
+  int32_t variant;     // ct_score_variant
 };
 
 ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
                      int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
-                     std::vector<ScoreLaunch>* launches);
+                     std::vector<ScoreLaunch>* launches, int32_t variant = CT_SCORE_LOWPASS);
 ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
                     float* layer_score, hipStream_t stream);
 

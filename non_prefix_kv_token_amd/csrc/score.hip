@@ -691,6 +691,50 @@ __global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
   poly_energy<512>(d, layer, kv, Gs, lds_g + 128 * 128, ws);
 }
 
+// ---- L2 variant: energies without the frequency analysis ----------------------
+// E[n] = sum_c x_c[n]^2 over the token's H*D channels (the alpha = 1 energies,
+// App. E.4), written where the band path writes its low-pass energies, so the
+// same layer normalisation and mean follow.  One wave per token row; each lane
+// sums C/64 squares in fp64 (exact products), then a fixed-order wave
+// reduction (deterministic).
+template <int DT>
+__global__ __launch_bounds__(256) void k_energy_l2(ScoreLaunch sl, char* ws) {
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.y;
+  const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d.n) return;
+  const size_t base = ((size_t)layer * d.n + row) * C;
+  double e = 0.0;
+  if (DT == CT_BF16) {
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k) + base;
+    for (int c = 8 * lane; c < C; c += 8 * 64) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(x + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double lo = (double)__uint_as_float(w[i] << 16), hi = (double)__uint_as_float(w[i] & 0xffff0000u);
+        e = fma(lo, lo, e);
+        e = fma(hi, hi, e);
+      }
+    }
+  } else {
+    const float* x = reinterpret_cast<const float*>(kv ? d.v : d.k) + base;
+    for (int c = 4 * lane; c < C; c += 4 * 64) {
+      const float4 w = *reinterpret_cast<const float4*>(x + c);
+      e = fma((double)w.x, (double)w.x, e);
+      e = fma((double)w.y, (double)w.y, e);
+      e = fma((double)w.z, (double)w.z, e);
+      e = fma((double)w.w, (double)w.w, e);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+  if (lane == 0) reinterpret_cast<double*>(ws + d.e_off)[(size_t)(layer * 2 + kv) * d.n + row] = e;
+}
+
+
 // ---- 4'. per (chunk, layer): magnitudes and normalisation --------------------
 // s = sqrt(E_K)/2 + sqrt(E_V)/2 per token, normalised within the layer; the
 // result overwrites the E_K row of the layer (read before written by the same
@@ -772,8 +816,9 @@ int kkeep(int nf, int a_num, int a_den) {
 
 ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
                      int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
-                     std::vector<ScoreLaunch>* launches) {
+                     std::vector<ScoreLaunch>* launches, int32_t variant) {
   const int C = H * D;
+  const bool band = variant == CT_SCORE_LOWPASS;  // the L2 variant needs only the energies
   size_t off = 0;
   struct Tab { int nf, kk, ntp; int64_t tw, trig; };
   std::vector<Tab> tabs;
@@ -791,6 +836,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
     d.tok_off = tok;
     tok += d.n;
     if (2 * d.kk > max_p2) max_p2 = 2 * d.kk;
+    if (!band) continue;
     int found = -1;
     for (size_t t = 0; t < tabs.size(); ++t)
       if (tabs[t].nf == d.nf && tabs[t].kk == d.kk && tabs[t].ntp == d.ntok_pad) found = (int)t;
@@ -807,7 +853,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
     d.tw_off = tabs[found].tw;
     d.trig_off = tabs[found].trig;
   }
-  for (int b = 0; b < n_chunks; ++b) {
+  for (int b = 0; b < n_chunks && band; ++b) {
     desc[b].y_off = (int64_t)off;
     off = align256(off + (size_t)L * 2 * desc[b].ppad * C * 4);
   }
@@ -820,7 +866,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   // Matrix-core Gram (2kk <= 128) keeps G in LDS and needs no slot; larger
   // bands take the fp64 path, whose blocks loop over problems and slots.
   const bool mfma_gram = max_p2 <= 128;
-  int64_t n_slots = mfma_gram ? 0 : std::min<int64_t>(probs_max, 1024);
+  int64_t n_slots = (mfma_gram || !band) ? 0 : std::min<int64_t>(probs_max, 1024);
   const int64_t slot_budget = (int64_t)1 << 30;
   while (!mfma_gram && n_slots > 1 && n_slots * slot_bytes > slot_budget) n_slots /= 2;
   const int64_t slot_off = (int64_t)off;
@@ -838,6 +884,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
       sl.slot_p2 = max_p2;
       sl.slot_off = slot_off;
       sl.slot_bytes = slot_bytes;
+      sl.variant = variant;
       sl.max_ppad = 0;
       for (int i = 0; i < sl.n_chunks; ++i) {
         sl.c[i] = desc[b0 + i];
@@ -849,9 +896,43 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   return CT_OK;
 }
 
+// Energies -> per-layer scores -> layer mean.
+static ct_status score_finish(const ScoreLaunch& sl, char* ws, float* score, float* layer_score,
+                              hipStream_t stream) {
+  int max_n = 0;
+  for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
+  {
+    TimedLaunch tl_("layer_norm", stream);
+    hipLaunchKernelGGL(k_layer_norm, dim3(sl.n_chunks, sl.L), dim3(kFinThreads), 0, stream, sl, ws,
+                       layer_score);
+  }
+  if (ct_status s = check_launch("layer normalisation")) return s;
+  {
+    TimedLaunch tl_("layer_mean", stream);
+    hipLaunchKernelGGL(k_layer_mean, dim3((max_n + 255) / 256, sl.n_chunks), dim3(256), 0, stream,
+                       sl, ws, score);
+  }
+  return check_launch("layer mean");
+}
+
 ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
                     float* layer_score, hipStream_t stream) {
   for (const ScoreLaunch& sl : launches) {
+    if (sl.variant == CT_SCORE_L2) {
+      int max_n = 0;
+      for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
+      dim3 ge((max_n + 3) / 4, sl.n_chunks * sl.L * 2);
+      {
+        TimedLaunch tl_("energy_l2", stream);
+        if (sl.dtype == CT_BF16)
+          hipLaunchKernelGGL(k_energy_l2<CT_BF16>, ge, dim3(256), 0, stream, sl, ws);
+        else
+          hipLaunchKernelGGL(k_energy_l2<CT_F32>, ge, dim3(256), 0, stream, sl, ws);
+      }
+      if (ct_status s = check_launch("L2 energies")) return s;
+      if (ct_status s = score_finish(sl, ws, score, layer_score, stream)) return s;
+      continue;
+    }
     int max_elems = 0;
     for (int i = 0; i < sl.n_chunks; ++i)
       max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
@@ -900,20 +981,7 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
       if (ct_status s = check_launch("gram/eval")) return s;
     }
 
-    int max_n = 0;
-    for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
-    {
-      TimedLaunch tl_("layer_norm", stream);
-      hipLaunchKernelGGL(k_layer_norm, dim3(sl.n_chunks, sl.L), dim3(kFinThreads), 0, stream, sl, ws,
-                         layer_score);
-    }
-    if (ct_status s = check_launch("layer normalisation")) return s;
-    {
-      TimedLaunch tl_("layer_mean", stream);
-      hipLaunchKernelGGL(k_layer_mean, dim3((max_n + 255) / 256, sl.n_chunks), dim3(256), 0, stream,
-                         sl, ws, score);
-    }
-    if (ct_status s = check_launch("layer mean")) return s;
+    if (ct_status s = score_finish(sl, ws, score, layer_score, stream)) return s;
   }
   return CT_OK;
 }

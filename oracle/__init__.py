@@ -145,6 +145,21 @@ def score_chunk(K: np.ndarray, V: np.ndarray, a_num: int, a_den: int,
     return (score, ls) if layers else score
 
 
+def score_l2(K: np.ndarray, V: np.ndarray, norm: int = NORM_SUM, layers: bool = False):
+    """§5.4 L2-norm selection score: joint K/V magnitudes of the stored rows,
+    per-layer normalisation and layer mean, no frequency analysis."""
+    assert K.shape == V.shape and K.ndim == 4 and K.dtype == V.dtype
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    L_, N, H, D = K.shape
+    score = np.zeros(N)
+    ls = np.zeros((L_, N)) if layers else None
+    rc = lib().orc_score_l2(_p(K), _p(V), _dtype_code(K), L_, N, H, D, norm, _p(ls), _p(score))
+    if rc != 0:
+        raise ValueError("orc_score_l2 rejected its arguments")
+    return (score, ls) if layers else score
+
+
 def topr(score: np.ndarray, k: int):
     s = np.ascontiguousarray(score, dtype=np.float64)
     n = s.shape[0]

@@ -478,3 +478,33 @@ int orc_attention(const void* q_pre, const int* qpos, int Hq, const void* k,
   }
   return 0;
 }
+
+/* ---- scoring without the frequency analysis (§5.4 "L2-norm selection") ----
+ * The same joint K/V magnitudes, per-layer normalisation and layer mean as
+ * orc_score_chunk, on the stored K and V themselves: a = ||K_l[n]||_2 over the
+ * H*D channels, b = ||V_l[n]||_2, s = a/2 + b/2. */
+int orc_score_l2(const void* K, const void* V, int dtype, int L, int N, int H, int D, int norm,
+                 double* layer_score, double* score) {
+  if (L < 1 || N < 1 || H < 1 || D < 1) return -1;
+  int C = H * D;
+  double* sl = malloc(sizeof(double) * N);
+  for (int n = 0; n < N; ++n) score[n] = 0.0;
+  for (int l = 0; l < L; ++l) {
+    for (int n = 0; n < N; ++n) {
+      size_t base = ((size_t)l * N + n) * C;
+      double ek = 0.0, ev = 0.0;
+      for (int ch = 0; ch < C; ++ch) {
+        double k = load_elem(K, dtype, base + ch), v = load_elem(V, dtype, base + ch);
+        ek += k * k;
+        ev += v * v;
+      }
+      sl[n] = 0.5 * sqrt(ek) + 0.5 * sqrt(ev);
+    }
+    normalise(sl, N, norm);
+    if (layer_score) memcpy(layer_score + (size_t)l * N, sl, sizeof(double) * N);
+    for (int n = 0; n < N; ++n) score[n] += sl[n];
+  }
+  for (int n = 0; n < N; ++n) score[n] /= (double)L;
+  free(sl);
+  return 0;
+}

@@ -142,6 +142,46 @@ def test_topr_many_chunks(orc):
     _topr_exact(orc, scores, (15, 100))
 
 
+@pytest.mark.parametrize("ns,L,H,D,dtype", [([300, 2048, 7], 2, 8, 128, "bf16"), ([512, 65], 3, 2, 64, "f32")])
+def test_score_variant_l2(orc, syn, ns, L, H, D, dtype):
+    """§5.4 L2-norm selection: joint K/V magnitudes without the frequency
+    analysis, per-layer scores and the layer mean, against the oracle; then the
+    index sets it selects."""
+    ct = need_gpu()
+    host = _chunks(syn, ns, L, H, D, dtype)
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    for norm in (ct.CT_NORM_SUM, ct.CT_NORM_MINMAX):
+        s_gpu, ls_gpu = ct.cachetune_score_chunk(dev, L, H, D, norm=norm, want_layers=True,
+                                                 variant=ct.CT_SCORE_L2)
+        torch.cuda.synchronize()
+        s_gpu, ls_gpu = to_host(s_gpu), to_host(ls_gpu)
+        s_orc, ls_orc = [], []
+        for k, v in host:
+            s, ls = orc.score_l2(k, v, norm, layers=True)
+            s_orc.append(s)
+            ls_orc.append(ls)
+        s_orc, ls_orc = np.concatenate(s_orc), np.concatenate(ls_orc, axis=1)
+        _rel_close(s_gpu, s_orc, floor=1e-6 * np.abs(s_orc).max())
+        _rel_close(ls_gpu, ls_orc, floor=1e-6 * np.abs(ls_orc).max())
+    ks, _, sel, _ = ct.cachetune_select_topr(to_dev(s_gpu), ns, r=(15, 100))
+    torch.cuda.synchronize()
+    sel = to_host(sel)
+    o = so = 0
+    for n, k in zip(ns, ks):
+        _, want, _ = orc.topr(s_orc[o:o + n], k)
+        check_index_sets(sel[so:so + k], want, s_orc[o:o + n], k)
+        o, so = o + n, so + k
+
+
+def test_random_selection(orc, syn):
+    """§5.4 random selection: top-r over seeded uniform scores (drawn by the
+    input generator and passed in) is a uniformly random set of k tokens per
+    chunk; GPU and oracle select the same set."""
+    ns = [2048, 512, 1000]
+    scores = [syn.uniform_ints(SEED, 77 + b, n, 0, 1 << 24).astype(np.float32) for b, n in enumerate(ns)]
+    _topr_exact(orc, scores, (15, 100))
+
+
 @pytest.mark.parametrize("ns,L,H,D,alpha", [([512, 2048, 999], 2, 2, 64, (1, 16)),
                                             ([2048], 3, 8, 128, (1, 16))])
 def test_index_sets_end_to_end(orc, syn, ns, L, H, D, alpha):

@@ -197,3 +197,37 @@ def test_reordering_changes_only_mapping(orc, syn):
     # the same chunks scored in another order give identical per-chunk results
     np.testing.assert_array_equal(orc.score_chunk(*b, 1, 16), sb)
     np.testing.assert_array_equal(orc.score_chunk(*a, 1, 16), sa)
+
+
+# ---- §5.4 L2-norm selection score ------------------------------------------------------
+
+def test_l2_score_hand_case(orc):
+    # one layer, two tokens, H = D = 1: a = |k|, b = |v|, s = a/2 + b/2, sum-normalised
+    K = np.array([[[[3.0]], [[0.0]]]], np.float32)
+    V = np.array([[[[-4.0]], [[1.0]]]], np.float32)
+    s = orc.score_l2(K, V)
+    assert np.allclose(s, [3.5 / 4.0, 0.5 / 4.0], rtol=0, atol=1e-15)
+
+
+def test_l2_score_equals_alpha_one_score(orc):
+    # App. E.4: keeping every bin reconstructs the stored rows, so the
+    # frequency-guided score at alpha = 1 is the L2 score (two independent code
+    # paths: direct DFT and inverse vs plain norms)
+    rng = np.random.default_rng(11)
+    for N in (7, 16, 33):
+        K = rng.standard_normal((3, N, 2, 4)).astype(np.float32)
+        V = rng.standard_normal((3, N, 2, 4)).astype(np.float32)
+        for norm in (orc.NORM_SUM, orc.NORM_MAX, orc.NORM_MINMAX, orc.NORM_NONE):
+            a = orc.score_l2(K, V, norm)
+            b = orc.score_chunk(K, V, 1, 1, norm=norm)
+            assert np.allclose(a, b, rtol=1e-12, atol=1e-15)
+
+
+def test_l2_score_scale_and_layer_permutation(orc):
+    rng = np.random.default_rng(12)
+    K = rng.standard_normal((4, 20, 2, 4)).astype(np.float32)
+    V = rng.standard_normal((4, 20, 2, 4)).astype(np.float32)
+    s = orc.score_l2(K, V)
+    assert np.isclose(s.sum(), 1.0, rtol=1e-12)
+    assert np.allclose(orc.score_l2(4.0 * K, 4.0 * V), s, rtol=1e-12)   # exact power-of-two scale
+    assert np.allclose(orc.score_l2(K[::-1].copy(), V[::-1].copy()), s, rtol=1e-12)
