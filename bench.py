@@ -529,6 +529,36 @@ def host_tier(args):
         **({"calibration": calibration} if calibration else {}),
     }), flush=True)
 
+def score_variants(w, args):
+    """Scoring time per variant on the workload's chunks (all layers): the
+    method's low-pass score and §5.4's L2-norm score.  One JSON line."""
+    import torch
+    ct = w.ct
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {}
+    for name, variant in (("lowpass", ct.CT_SCORE_LOWPASS), ("l2", ct.CT_SCORE_L2)):
+        need = ct.cachetune_score_chunk_ws(w.ns, w.L, w.H, w.D, w.alpha, variant=variant)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        run = lambda: ct.cachetune_score_chunk(w.chunks, w.L, w.H, w.D, alpha=w.alpha, score=w.score,  # noqa: E731
+                                               ws=ws, variant=variant)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        a, z = E(), E()
+        a.record()
+        for _ in range(args.steps):
+            run()
+        z.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(z) / args.steps
+        gbs = w.score_bytes() / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "GBs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "workspace_bytes": need}
+        print(f"[bench] score variant {name}: {ms:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "chunk scoring time per variant (all chunks, all layers)",
+                      "unit": "ms", "config": {"workload": w.name}, "variants": out,
+                      "bytes_read": w.score_bytes()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -542,6 +572,8 @@ def main():
                     help="with --host-tier: also run the warm-started golden-section search for r")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--score-variants", action="store_true",
+                    help="time the scoring variants (low-pass, L2-norm) on the workload instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -560,6 +592,10 @@ def main():
     ct = w.ct
     print(f"[bench] inputs generated in {w.gen_seconds:.1f}s; T={w.T} n_q={w.n_q}", file=sys.stderr,
           flush=True)
+
+    if args.score_variants:
+        score_variants(w, args)
+        return
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
