@@ -52,6 +52,8 @@ def lib():
         L.orc_round_bf16.restype = C.c_uint16
         L.orc_rfft.argtypes = [vp, i32, vp, vp]
         L.orc_lowpass.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.orc_highpass.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.orc_score_highpass.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_topr.argtypes = [vp, i32, i32, vp, vp, vp]
         L.orc_offsets.argtypes = [vp, vp, i32, i32, vp]
@@ -127,6 +129,14 @@ def lowpass(x: np.ndarray, a_num: int, a_den: int, mode: int = FFT_EXACT_N) -> n
     return out
 
 
+def highpass(x: np.ndarray, a_num: int, a_den: int, mode: int = FFT_EXACT_N) -> np.ndarray:
+    """High-frequency reconstruction: the bins at and above the low-pass cutoff."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    lib().orc_highpass(_p(x), x.shape[0], a_num, a_den, mode, _p(out))
+    return out
+
+
 # ---- scoring / selection ------------------------------------------------
 
 def score_chunk(K: np.ndarray, V: np.ndarray, a_num: int, a_den: int,
@@ -157,6 +167,23 @@ def score_l2(K: np.ndarray, V: np.ndarray, norm: int = NORM_SUM, layers: bool = 
     rc = lib().orc_score_l2(_p(K), _p(V), _dtype_code(K), L_, N, H, D, norm, _p(ls), _p(score))
     if rc != 0:
         raise ValueError("orc_score_l2 rejected its arguments")
+    return (score, ls) if layers else score
+
+
+def score_highpass(K: np.ndarray, V: np.ndarray, a_num: int, a_den: int,
+                   mode: int = FFT_EXACT_N, norm: int = NORM_SUM, layers: bool = False):
+    """Sec. 5.4 and App. E.2 (Table 3) high-frequency-guided selection score: the scoring of
+    score_chunk applied to the high-frequency reconstruction (bins >= cutoff)."""
+    assert K.shape == V.shape and K.ndim == 4 and K.dtype == V.dtype
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    L_, N, H, D = K.shape
+    score = np.zeros(N)
+    ls = np.zeros((L_, N)) if layers else None
+    rc = lib().orc_score_highpass(_p(K), _p(V), _dtype_code(K), L_, N, H, D, a_num, a_den,
+                                  mode, norm, _p(ls), _p(score))
+    if rc != 0:
+        raise ValueError("orc_score_highpass rejected its arguments")
     return (score, ls) if layers else score
 
 

@@ -508,3 +508,105 @@ int orc_score_l2(const void* K, const void* V, int dtype, int L, int N, int H, i
   free(sl);
   return 0;
 }
+
+/* ---- high-frequency-guided selection (Sec. 5.4, Table 3, Figure 1) ---- */
+
+/* Inverse real transform with output length n_len (irfft(n=n_len) convention,
+ * as inverse_lowpass) of the bins j in [j0, nb) alone: every bin below the
+ * cutoff j0 is treated as zero. */
+static void inverse_highband(const double* re, const double* im, int n_len, int j0, int nb,
+                             const double* c, const double* s, double* out) {
+  for (int n = 0; n < n_len; ++n) {
+    double acc = 0.0;
+    for (int j = j0; j < nb; ++j) {
+      long long m = ((long long)j * n) % n_len;
+      int edge = (j == 0) || ((n_len % 2 == 0) && j == n_len / 2);
+      double term = re[j] * c[m];
+      if (!edge) term = 2.0 * (term - im[j] * s[m]);
+      acc += term;
+    }
+    out[n] = acc / (double)n_len;
+  }
+}
+
+/* High-frequency reconstruction of one real sequence of n tokens: rFFT over
+ * the transform length, keep the bins at and above the low-pass cutoff (the
+ * bins the low-pass view discards), inverse transform, positions [0, n). */
+void orc_highpass(const double* x, int n, int a_num, int a_den, int fftlen_mode, double* out) {
+  int nf = orc_fft_len(n, fftlen_mode);
+  int nb = orc_nbins(nf);
+  int kk = orc_kkeep(nb, a_num, a_den);
+  double* c = malloc(sizeof(double) * nf);
+  double* s = malloc(sizeof(double) * nf);
+  double* xp = calloc(nf, sizeof(double));
+  double* re = malloc(sizeof(double) * nb);
+  double* im = malloc(sizeof(double) * nb);
+  double* rec = malloc(sizeof(double) * nf);
+  memcpy(xp, x, sizeof(double) * n);
+  trig_table(nf, c, s);
+  dft_bins(xp, nf, nb, c, s, re, im);
+  inverse_highband(re, im, nf, kk, nb, c, s, rec);
+  memcpy(out, rec, sizeof(double) * n);
+  free(c); free(s); free(xp); free(re); free(im); free(rec);
+}
+
+/* Importance score of the high-frequency-guided strategy the pages compare
+ * against: the same joint K/V magnitudes, per-layer normalisation and layer
+ * mean as orc_score_chunk, taken of the high-frequency reconstruction (bins
+ * at and above the cutoff kk) instead of the low-frequency one.  Reading: the
+ * cutoff is the low-pass one for the same alpha, so the two views split the
+ * spectrum between them. */
+int orc_score_highpass(const void* K, const void* V, int dtype, int L, int N, int H, int D,
+                       int a_num, int a_den, int fftlen_mode, int norm, double* layer_score,
+                       double* score) {
+  if (L < 1 || N < 1 || H < 1 || D < 1 || a_den <= 0 || a_num <= 0) return -1;
+  int C = H * D;
+  int nf = orc_fft_len(N, fftlen_mode);
+  int nb = orc_nbins(nf);
+  int kk = orc_kkeep(nb, a_num, a_den);
+  double* c = malloc(sizeof(double) * nf);
+  double* s = malloc(sizeof(double) * nf);
+  trig_table(nf, c, s);
+  double* mag[2];
+  mag[0] = malloc(sizeof(double) * N);
+  mag[1] = malloc(sizeof(double) * N);
+  double* sl = malloc(sizeof(double) * N);
+  double* rec = malloc(sizeof(double) * (size_t)C * N);
+  for (int n = 0; n < N; ++n) score[n] = 0.0;
+  for (int l = 0; l < L; ++l) {
+    size_t off = (size_t)l * N * C;
+    for (int t = 0; t < 2; ++t) {
+      const void* x = t ? V : K;
+#pragma omp parallel
+      {
+        double* seq = calloc(nf, sizeof(double));
+        double* re = malloc(sizeof(double) * nb);
+        double* im = malloc(sizeof(double) * nb);
+        double* out = malloc(sizeof(double) * nf);
+#pragma omp for schedule(static)
+        for (int ch = 0; ch < C; ++ch) {
+          for (int n = 0; n < N; ++n) seq[n] = load_elem(x, dtype, off + (size_t)n * C + ch);
+          dft_bins(seq, nf, nb, c, s, re, im);
+          inverse_highband(re, im, nf, kk, nb, c, s, out);
+          memcpy(rec + (size_t)ch * N, out, sizeof(double) * N);
+        }
+        free(seq); free(re); free(im); free(out);
+      }
+      for (int n = 0; n < N; ++n) {
+        double e = 0.0;
+        for (int ch = 0; ch < C; ++ch) {
+          double v = rec[(size_t)ch * N + n];
+          e += v * v;
+        }
+        mag[t][n] = sqrt(e);
+      }
+    }
+    for (int n = 0; n < N; ++n) sl[n] = 0.5 * mag[0][n] + 0.5 * mag[1][n];
+    normalise(sl, N, norm);
+    if (layer_score) memcpy(layer_score + (size_t)l * N, sl, sizeof(double) * N);
+    for (int n = 0; n < N; ++n) score[n] += sl[n];
+  }
+  for (int n = 0; n < N; ++n) score[n] /= (double)L;
+  free(c); free(s); free(mag[0]); free(mag[1]); free(sl); free(rec);
+  return 0;
+}

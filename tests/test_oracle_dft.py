@@ -163,3 +163,67 @@ def test_brute_force_projector_matrix(orc, n):
         P = (F @ F.conj().T).real / n
         x = RNG.standard_normal(n)
         np.testing.assert_allclose(orc.lowpass(x, kk_target, nb), P @ x, atol=1e-12)
+
+
+# ---- high-frequency view (Sec. 5.4, App. E.2 Table 3) ---------------------------------
+
+def np_highpass(x, kk, nf=None):
+    n = x.shape[0]
+    nf = n if nf is None else nf
+    F = np.fft.rfft(np.concatenate([x, np.zeros(nf - n)]))
+    F[:kk] = 0
+    return np.fft.irfft(F, n=nf)[:n]
+
+
+@pytest.mark.parametrize("n,a_num,a_den", [(64, 1, 16), (65, 1, 16), (100, 1, 2), (513, 1, 32),
+                                           (16, 3, 7), (9, 1, 100)])
+def test_highpass_matches_numpy(orc, n, a_num, a_den):
+    x = RNG.standard_normal(n)
+    kk = max(1, (a_num * (n // 2 + 1)) // a_den)
+    np.testing.assert_allclose(orc.highpass(x, a_num, a_den), np_highpass(x, kk), atol=1e-11)
+
+
+@pytest.mark.parametrize("n,a_num,a_den", [(100, 1, 16), (600, 1, 32), (33, 1, 2)])
+def test_highpass_zeropad_matches_numpy(orc, n, a_num, a_den):
+    x = RNG.standard_normal(n)
+    nf = 1 << (n - 1).bit_length()
+    kk = max(1, (a_num * (nf // 2 + 1)) // a_den)
+    got = orc.highpass(x, a_num, a_den, orc.FFT_ZEROPAD_POW2)
+    np.testing.assert_allclose(got, np_highpass(x, kk, nf), atol=1e-11)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("n", [5, 32, 77, 300])
+def test_low_plus_high_is_signal(orc, n, mode):
+    # the two views split the spectrum, so they add up to the signal at every
+    # stored position (also with zero padding: the padded tail is cut after)
+    x = RNG.standard_normal(n)
+    for a in ((1, 16), (1, 2), (3, 7)):
+        np.testing.assert_allclose(orc.lowpass(x, *a, mode) + orc.highpass(x, *a, mode), x, atol=1e-11)
+
+
+def test_highpass_cosine_pass_and_stop(orc):
+    n, a_num, a_den = 2048, 1, 16  # cutoff at bin 64
+    t = np.arange(n)
+    below = 1.3 * np.cos(2 * np.pi * 63 * t / n + 0.2)
+    above = 0.8 * np.cos(2 * np.pi * 64 * t / n + 1.1)
+    nyq = np.where(t % 2 == 0, 2.5, -2.5)  # the Nyquist bin, real by construction
+    np.testing.assert_allclose(orc.highpass(below, a_num, a_den), 0.0, atol=1e-11)
+    np.testing.assert_allclose(orc.highpass(above, a_num, a_den), above, atol=1e-11)
+    np.testing.assert_allclose(orc.highpass(nyq, a_num, a_den), nyq, atol=1e-11)
+
+
+def test_highpass_parseval_and_empty_band(orc):
+    n = 90
+    x = RNG.standard_normal(n)
+    kk = (1 * (n // 2 + 1)) // 4
+    F = np.fft.rfft(x)
+    w = np.full(n // 2 + 1, 2.0)
+    w[0] = 1.0
+    w[-1] = 1.0  # n even: Nyquist counted once
+    want = (w[kk:] * np.abs(F[kk:]) ** 2).sum() / n
+    assert np.isclose((orc.highpass(x, 1, 4) ** 2).sum(), want, rtol=1e-11)
+    # alpha = 1 keeps every bin in the low view: nothing is left above it
+    np.testing.assert_allclose(orc.highpass(x, 1, 1), 0.0, atol=1e-12)
+    # the DC bin is always in the low view: the high view has zero mean
+    assert abs(orc.highpass(x, 1, 1000).sum()) < 1e-10

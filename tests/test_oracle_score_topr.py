@@ -231,3 +231,75 @@ def test_l2_score_scale_and_layer_permutation(orc):
     assert np.isclose(s.sum(), 1.0, rtol=1e-12)
     assert np.allclose(orc.score_l2(4.0 * K, 4.0 * V), s, rtol=1e-12)   # exact power-of-two scale
     assert np.allclose(orc.score_l2(K[::-1].copy(), V[::-1].copy()), s, rtol=1e-12)
+
+
+# ---- Sec. 5.4 / App. E.2 high-frequency-guided selection score -----------------------
+
+def test_highpass_score_matches_numpy_pipeline(orc, syn):
+    """The high-frequency score rebuilt from numpy's rfft/irfft."""
+    K, V = _kv(syn, L=2, N=70, H=2, D=4)
+    L, N = K.shape[:2]
+    kk = orc.kkeep(N // 2 + 1, 1, 4)
+
+    def mags(X):
+        x = orc.widen(X).reshape(L, N, -1)
+        F = np.fft.rfft(x, axis=1)
+        F[:, :kk, :] = 0
+        r = np.fft.irfft(F, n=N, axis=1)
+        return np.sqrt((r ** 2).sum(-1))
+
+    s = 0.5 * mags(K) + 0.5 * mags(V)
+    for norm, want in ((orc.NORM_SUM, (s / s.sum(axis=1, keepdims=True)).mean(axis=0)),
+                       (orc.NORM_NONE, s.mean(axis=0))):
+        np.testing.assert_allclose(orc.score_highpass(K, V, 1, 4, norm=norm), want, rtol=1e-10)
+
+
+def test_highpass_score_zeropad_matches_numpy(orc, syn):
+    K, V = _kv(syn, L=1, N=50, H=1, D=4, dtype="f32")
+    L, N = K.shape[:2]
+    nf = 64
+    kk = orc.kkeep(nf // 2 + 1, 1, 8)
+
+    def mags(X):
+        x = np.concatenate([orc.widen(X).reshape(L, N, -1), np.zeros((L, nf - N, 4))], axis=1)
+        F = np.fft.rfft(x, axis=1)
+        F[:, :kk, :] = 0
+        r = np.fft.irfft(F, n=nf, axis=1)[:, :N]
+        return np.sqrt((r ** 2).sum(-1))
+
+    s = 0.5 * mags(K) + 0.5 * mags(V)
+    got = orc.score_highpass(K, V, 1, 8, mode=orc.FFT_ZEROPAD_POW2, norm=orc.NORM_MAX)
+    np.testing.assert_allclose(got, (s / s.max(axis=1, keepdims=True)).mean(axis=0), rtol=1e-10)
+
+
+def test_highpass_score_of_high_band_content_is_l2(orc):
+    # rows built from bins at or above the cutoff pass unchanged, so the
+    # high-frequency score equals the L2 score; the low-frequency score of the
+    # same rows sees only the float32 rounding of the stored rows
+    L, N, H, D = 2, 64, 2, 3
+    t = np.arange(N)
+    rng = np.random.default_rng(21)
+    K = np.zeros((L, N, H, D))
+    V = np.zeros((L, N, H, D))
+    for X in (K, V):
+        for l in range(L):
+            for h in range(H):
+                for d in range(D):
+                    f = rng.integers(4, N // 2 + 1)  # cutoff for alpha 1/8, N = 64: bin 4
+                    X[l, :, h, d] = rng.uniform(0.5, 2.0) * np.cos(2 * np.pi * f * t / N + rng.uniform(0, 6))
+    K, V = K.astype(np.float32), V.astype(np.float32)
+    assert orc.kkeep(N // 2 + 1, 1, 8) == 4
+    # float32 storage rounds the rows: compare against the rows as stored
+    np.testing.assert_allclose(orc.score_highpass(K, V, 1, 8), orc.score_l2(K, V), rtol=1e-6)
+    assert orc.score_chunk(K, V, 1, 8, norm=orc.NORM_NONE).max() < 1e-6
+
+
+def test_highpass_score_hand_case(orc):
+    # N = 2, one channel, exact length: bins 0 (mean) and 1 (Nyquist, half the
+    # difference); alpha 1/2 keeps bin 0 low, so the high view is
+    # x - mean = (+-d/2): magnitudes |k0-k1|/2 at both tokens
+    K = np.array([[[[3.0]], [[1.0]]]], np.float32)
+    V = np.array([[[[-2.0]], [[2.0]]]], np.float32)
+    s = orc.score_highpass(K, V, 1, 2, norm=orc.NORM_NONE)
+    assert orc.kkeep(2, 1, 2) == 1
+    np.testing.assert_allclose(s, [0.5 * 1.0 + 0.5 * 2.0] * 2, atol=1e-14)
