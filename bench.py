@@ -531,12 +531,15 @@ def host_tier(args):
 
 def score_variants(w, args):
     """Scoring time per variant on the workload's chunks (all layers): the
-    method's low-pass score and §5.4's L2-norm score.  One JSON line."""
+    method's low-pass score and the L2-norm and high-frequency-guided scores
+    of Sec. 5.4, with the per-kernel times of each.  One JSON line."""
     import torch
     ct = w.ct
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = {}
-    for name, variant in (("lowpass", ct.CT_SCORE_LOWPASS), ("l2", ct.CT_SCORE_L2)):
+    names = ("twiddle", "band", "gram", "energy_l2", "highpass", "layer_norm", "layer_mean")
+    for name, variant in (("lowpass", ct.CT_SCORE_LOWPASS), ("l2", ct.CT_SCORE_L2),
+                          ("highpass", ct.CT_SCORE_HIGHPASS)):
         need = ct.cachetune_score_chunk_ws(w.ns, w.L, w.H, w.D, w.alpha, variant=variant)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
         run = lambda: ct.cachetune_score_chunk(w.chunks, w.L, w.H, w.D, alpha=w.alpha, score=w.score,  # noqa: E731
@@ -551,8 +554,15 @@ def score_variants(w, args):
         z.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(z) / args.steps
+        for n in names:
+            ct.cachetune_timing_read(n)  # drop what earlier runs recorded
+        ct.cachetune_timing_enable(True)
+        run()
+        ct.cachetune_timing_enable(False)
+        kern = {n: round(ct.cachetune_timing_read(n)[0], 4) for n in names}
         gbs = w.score_bytes() / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GBs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "workspace_bytes": need}
+        out[name] = {"ms": ms, "GBs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "workspace_bytes": need,
+                     "kernel_ms": {n: t for n, t in kern.items() if t > 0}}
         print(f"[bench] score variant {name}: {ms:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
     print(json.dumps({"metric": "chunk scoring time per variant (all chunks, all layers)",
                       "unit": "ms", "config": {"workload": w.name}, "variants": out,
@@ -573,7 +583,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--score-variants", action="store_true",
-                    help="time the scoring variants (low-pass, L2-norm) on the workload instead")
+                    help="time the scoring variants (low-pass, L2-norm, high-frequency) on the workload instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "

@@ -148,11 +148,17 @@ ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_
  *                     of K over the token's H*D channels, b the same for V
  *                     (the alpha = 1 score of App. E.4, which keeps every bin;
  *                     alpha_num / alpha_den and fftlen are ignored).
+ *   CT_SCORE_HIGHPASS the high-frequency-guided strategy of Sec. 5.4 and
+ *                     App. E.2 (Table 3, Figure 1): the same magnitudes of
+ *                     the reconstruction from the bins at and above the
+ *                     low-pass cutoff (bins >= kk for the same alpha and
+ *                     fftlen), i.e. of x - xlow at the stored positions.
+ *                     Needs the workspace of the low-pass score.
  * Random selection needs no score of its own: cachetune_select_topr over
  * caller-supplied seeded uniform scores selects a uniformly random set.
  * Arguments, layouts and errors are those of cachetune_score_chunk(_ws); an
  * unknown variant is CT_E_INVALID. */
-typedef enum { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1 } ct_score_variant;
+typedef enum { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1, CT_SCORE_HIGHPASS = 2 } ct_score_variant;
 ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                      int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                      ct_fftlen fftlen, ct_score_variant variant, size_t* bytes);
@@ -262,7 +268,7 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
  *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
- *   "attention_merge", "rank_order", "energy_l2" (and "twiddle", "layer_norm",
+ *   "attention_merge", "rank_order", "energy_l2", "highpass" (and "twiddle", "layer_norm",
  *   "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and

@@ -19,7 +19,7 @@ CT_F32, CT_BF16 = 0, 1
 CT_NORM_SUM, CT_NORM_MAX, CT_NORM_MINMAX, CT_NORM_NONE = 0, 1, 2, 3
 CT_ROPE_HALF, CT_ROPE_INTERLEAVED = 0, 1
 CT_FFT_EXACT_N, CT_FFT_ZEROPAD_POW2 = 0, 1
-CT_SCORE_LOWPASS, CT_SCORE_L2 = 0, 1
+CT_SCORE_LOWPASS, CT_SCORE_L2, CT_SCORE_HIGHPASS = 0, 1, 2
 
 
 class ct_chunk(C.Structure):
@@ -138,8 +138,9 @@ def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N,
                           variant=CT_SCORE_LOWPASS):
     """chunks: list of (K, V) device tensors [L][n][H][D].  Returns (score,
     layer_score) fp32 device tensors (layer_score None unless requested).
-    variant: CT_SCORE_LOWPASS (the method) or CT_SCORE_L2 (magnitudes without
-    the frequency analysis); the latter goes through cachetune_score_variant."""
+    variant: CT_SCORE_LOWPASS (the method), CT_SCORE_L2 (magnitudes without
+    the frequency analysis) or CT_SCORE_HIGHPASS (magnitudes of the bins at
+    and above the cutoff); the last two go through cachetune_score_variant."""
     import torch
     dev = chunks[0][0].device
     ns = [int(k.shape[1]) for k, _ in chunks]

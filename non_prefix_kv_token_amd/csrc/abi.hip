@@ -101,7 +101,8 @@ ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunk
                                      ct_fftlen fftlen, ct_score_variant variant, size_t* bytes) {
   CT_GUARD_BEGIN
   if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
-  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2) return fail(CT_E_INVALID, "unknown variant");
+  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2 && variant != CT_SCORE_HIGHPASS)
+    return fail(CT_E_INVALID, "unknown variant");
   if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
     alpha_num = alpha_den = 1;
     fftlen = CT_FFT_EXACT_N;
@@ -134,7 +135,8 @@ ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int3
                                   float* score, float* layer_score, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   CT_GUARD_BEGIN
-  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2) return fail(CT_E_INVALID, "unknown variant");
+  if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2 && variant != CT_SCORE_HIGHPASS)
+    return fail(CT_E_INVALID, "unknown variant");
   if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
     alpha_num = alpha_den = 1;
     fftlen = CT_FFT_EXACT_N;

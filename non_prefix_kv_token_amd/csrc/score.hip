@@ -735,6 +735,192 @@ __global__ __launch_bounds__(256) void k_energy_l2(ScoreLaunch sl, char* ws) {
 }
 
 
+// ---- high-frequency view: energies of x - xlow ----------------------------------
+// At the stored positions n < N the inverse transform of every bin returns the
+// row itself, so the bins at and above the cutoff reconstruct x - xlow there,
+// and (Sec. 5.4, App. E.2: the high-frequency-guided strategy)
+//     E_high[n] = |x[n]|^2 - 2 <x[n], xlow[n]> + E_low[n].
+// E_low comes from the band path above.  The cross term is
+//     <x[n], xlow[n]> = (1/nf) sum_p w_p t_p(n) Z[p][n],   Z = Y X^T,
+// with t_p the twiddle row p, w_p the bin weight (1 for DC and Nyquist, else
+// 2), and Z the band coefficients contracted with the stored row over the
+// channels, on the matrix cores: Y (fp32) in three bf16 planes as the Gram
+// takes it, bf16 X exact (three products), fp32 X in three planes too (six).
+// One wave per 32 tokens, 8 waves per block; a 64-channel stage of the Y
+// planes is shared in LDS, the next stage's Y and X are loaded during the
+// current stage's products; the band is taken 128 rows at a time.  Z is
+// accumulated in fp32 over the channels, the sums over p and the energies in
+// fp64.  The result overwrites E_low (read first by the same lane).
+template <int DT>
+__global__ __launch_bounds__(512) void k_highpass(ScoreLaunch sl, char* ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t pl[3][128 * kGramPS];
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.y;
+  const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int N = d.n, kk = d.kk, P2 = 2 * kk, ppad = d.ppad, nf = d.nf;
+  const int t0 = blockIdx.x * 256;
+  if (t0 >= N) return;  // block-uniform
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
+  const int n = t0 + wave * 32 + col;
+  const int nrow = min(n, N - 1);  // lanes past N read a valid row; their results are dropped
+  const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+  const size_t xoff = ((size_t)layer * N + nrow) * C + 8 * g;
+  const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+  constexpr int XW = DT == CT_BF16 ? 4 : 8;  // dwords of X per lane per 16-channel step
+
+  double etot = 0.0, cross = 0.0;
+  uint32_t xr[4][XW];
+  float4 yr[4];
+  auto load_x = [&](int c0) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (DT == CT_BF16) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint16_t*>(kv ? d.v : d.k) + xoff + c0 + 16 * ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[ks][i] = v[i];
+      } else {
+        const float* p = reinterpret_cast<const float*>(kv ? d.v : d.k) + xoff + c0 + 16 * ks;
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(p);
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { xr[ks][i] = v0[i]; xr[ks][XW / 2 + i] = v1[i]; }
+      }
+    }
+  };
+  // Y rows [pg, pg + 128) x channels [c0, c0 + 64): 16 floats per thread
+  auto load_y = [&](int pg, int c0) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 512 * it, r = item >> 4, q4 = 4 * (item & 15);
+      yr[it] = pg + r < ppad ? *reinterpret_cast<const float4*>(Y + (size_t)(pg + r) * C + c0 + q4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_y = [&]() {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 512 * it, r = item >> 4, q4 = 4 * (item & 15);
+      const float x[4] = {yr[it].x, yr[it].y, yr[it].z, yr[it].w};
+      uint32_t h[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b1 = bf16_rne_from_f32_bits(__float_as_uint(x[e]));
+        const float r1 = x[e] - __uint_as_float(b1 << 16);
+        const uint32_t b2 = bf16_rne_from_f32_bits(__float_as_uint(r1));
+        const float r2 = r1 - __uint_as_float(b2 << 16);
+        h[0][e] = b1;
+        h[1][e] = b2;
+        h[2][e] = bf16_rne_from_f32_bits(__float_as_uint(r2));
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<uint2*>(&pl[q][r * kGramPS + q4]) =
+            make_uint2(h[q][0] | (h[q][1] << 16), h[q][2] | (h[q][3] << 16));
+    }
+  };
+
+  for (int pg = 0; pg < ppad; pg += 128) {
+    const int nt = min(4, (ppad - pg) / 32);  // block-uniform
+    f32x16_t acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    load_x(0);
+    load_y(pg, 0);
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      __syncthreads();  // the previous stage's planes are no longer read
+      store_y();
+      __syncthreads();
+      uint32_t xs[4][XW];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < XW; ++i) xs[ks][i] = xr[ks][i];
+      if (c0 + 64 < C) {
+        load_x(c0 + 64);
+        load_y(pg, c0 + 64);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8_t bx[3];
+        if (DT == CT_BF16) {
+          u32x4_t u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[i] = xs[ks][i];
+          bx[0] = __builtin_bit_cast(bf16x8_t, u);
+          if (pg == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const double lo = (double)__uint_as_float(xs[ks][i] << 16);
+              const double hi = (double)__uint_as_float(xs[ks][i] & 0xffff0000u);
+              etot = fma(lo, lo, etot);
+              etot = fma(hi, hi, etot);
+            }
+          }
+        } else {
+          u32x4_t u[3];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(xs[ks][e]);
+            const uint32_t b1 = bf16_rne_from_f32_bits(xs[ks][e]);
+            const float r1 = x - __uint_as_float(b1 << 16);
+            const uint32_t b2 = bf16_rne_from_f32_bits(__float_as_uint(r1));
+            const float r2 = r1 - __uint_as_float(b2 << 16);
+            const uint32_t b3 = bf16_rne_from_f32_bits(__float_as_uint(r2));
+            const int w = e >> 1, sh = 16 * (e & 1);
+            if (sh == 0) { u[0][w] = b1; u[1][w] = b2; u[2][w] = b3; }
+            else { u[0][w] |= b1 << 16; u[1][w] |= b2 << 16; u[2][w] |= b3 << 16; }
+            if (pg == 0) etot = fma((double)x, (double)x, etot);
+          }
+#pragma unroll
+          for (int q = 0; q < 3; ++q) bx[q] = __builtin_bit_cast(bf16x8_t, u[q]);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          if (pt >= nt) break;
+          const int ra = (pt * 32 + col) * kGramPS + 16 * ks + 8 * g;
+          bf16x8_t a[3];
+#pragma unroll
+          for (int q = 0; q < 3; ++q) a[q] = *reinterpret_cast<const bf16x8_t*>(&pl[q][ra]);
+          acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bx[0], acc[pt], 0, 0, 0);
+          acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bx[0], acc[pt], 0, 0, 0);
+          acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], bx[0], acc[pt], 0, 0, 0);
+          if (DT != CT_BF16) {
+            acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bx[1], acc[pt], 0, 0, 0);
+            acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bx[1], acc[pt], 0, 0, 0);
+            acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bx[2], acc[pt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // cross term of this band slice: lane holds Z[p][n] for 16 rows p per tile
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      if (pt >= nt) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int p = pg + pt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (p < P2) {
+          const int j = p < kk ? p : p - kk;
+          const uint32_t m = ((uint32_t)j * (uint32_t)nrow) % (uint32_t)nf;
+          const double2 cs = trig[m];
+          const double w = (j == 0 || 2 * j == nf) ? 1.0 : 2.0;
+          cross = fma(w * (p < kk ? cs.x : cs.y), (double)acc[pt][v], cross);
+        }
+      }
+    }
+  }
+  cross += __shfl_xor(cross, 32);
+  etot += __shfl_xor(etot, 32);
+  if (g == 0 && n < N) {
+    double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
+    E[n] = etot - 2.0 * cross / (double)nf + E[n];
+  }
+}
+
 // ---- 4'. per (chunk, layer): magnitudes and normalisation --------------------
 // s = sqrt(E_K)/2 + sqrt(E_V)/2 per token, normalised within the layer; the
 // result overwrites the E_K row of the layer (read before written by the same
@@ -818,7 +1004,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
                      int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
                      std::vector<ScoreLaunch>* launches, int32_t variant) {
   const int C = H * D;
-  const bool band = variant == CT_SCORE_LOWPASS;  // the L2 variant needs only the energies
+  const bool band = variant != CT_SCORE_L2;  // the L2 variant needs only the energies
   size_t off = 0;
   struct Tab { int nf, kk, ntp; int64_t tw, trig; };
   std::vector<Tab> tabs;
@@ -979,6 +1165,18 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
       TimedLaunch tl_("gram", stream);
       hipLaunchKernelGGL(k_gram_eval, dim3(grid), dim3(256), 0, stream, sl, ws, n_probs);
       if (ct_status s = check_launch("gram/eval")) return s;
+    }
+
+    if (sl.variant == CT_SCORE_HIGHPASS) {
+      int max_n = 0;
+      for (int i = 0; i < sl.n_chunks; ++i) max_n = std::max(max_n, sl.c[i].n);
+      TimedLaunch tl_("highpass", stream);
+      dim3 gh((max_n + 255) / 256, n_probs);
+      if (sl.dtype == CT_BF16)
+        hipLaunchKernelGGL(k_highpass<CT_BF16>, gh, dim3(512), 0, stream, sl, ws);
+      else
+        hipLaunchKernelGGL(k_highpass<CT_F32>, gh, dim3(512), 0, stream, sl, ws);
+      if (ct_status s = check_launch("high-frequency energies")) return s;
     }
 
     if (ct_status s = score_finish(sl, ws, score, layer_score, stream)) return s;

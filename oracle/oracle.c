@@ -518,12 +518,14 @@ static void inverse_highband(const double* re, const double* im, int n_len, int 
                              const double* c, const double* s, double* out) {
   for (int n = 0; n < n_len; ++n) {
     double acc = 0.0;
+    int m = (int)(((long long)j0 * n) % n_len); /* (j * n) mod n_len, advanced exactly */
     for (int j = j0; j < nb; ++j) {
-      long long m = ((long long)j * n) % n_len;
       int edge = (j == 0) || ((n_len % 2 == 0) && j == n_len / 2);
       double term = re[j] * c[m];
       if (!edge) term = 2.0 * (term - im[j] * s[m]);
       acc += term;
+      m += n;
+      if (m >= n_len) m -= n_len;
     }
     out[n] = acc / (double)n_len;
   }

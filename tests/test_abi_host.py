@@ -119,3 +119,19 @@ def test_calibrate_ratio_rejects_bad_arguments(lib):
         ct.cachetune_calibrate_ratio(1.0, 1.0, lambda r: float("nan"))
     with pytest.raises(ZeroDivisionError):   # the callback's own exception comes back
         ct.cachetune_calibrate_ratio(1.0, 1.0, lambda r: 1 / 0)
+
+
+def test_score_variant_ws(lib):
+    import non_prefix_kv_token_amd as ct
+    n = (C.c_int32 * 2)(2048, 700)
+    sz = {}
+    for v in (ct.CT_SCORE_LOWPASS, ct.CT_SCORE_L2, ct.CT_SCORE_HIGHPASS):
+        out = C.c_size_t(0)
+        assert lib.cachetune_score_variant_ws(n, 2, 4, 8, 128, 1, 16, 0, v, C.byref(out)) == ct.CT_OK
+        sz[v] = out.value
+    # the high-frequency view runs the band path first: same workspace; L2 needs only energies
+    assert sz[ct.CT_SCORE_HIGHPASS] == sz[ct.CT_SCORE_LOWPASS]
+    assert 0 < sz[ct.CT_SCORE_L2] < sz[ct.CT_SCORE_LOWPASS]
+    out = C.c_size_t(0)
+    assert lib.cachetune_score_variant_ws(n, 2, 4, 8, 128, 1, 16, 0, 3, C.byref(out)) == ct.CT_E_INVALID
+    assert b"unknown variant" in lib.cachetune_last_error()

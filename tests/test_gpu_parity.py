@@ -173,6 +173,41 @@ def test_score_variant_l2(orc, syn, ns, L, H, D, dtype):
         o, so = o + n, so + k
 
 
+@pytest.mark.parametrize("ns,L,H,D,dtype,alpha,fftlen", [
+    ([300, 2048, 7], 1, 2, 64, "bf16", (1, 16), 0),
+    ([2048], 1, 8, 128, "bf16", (1, 16), 0),       # the per-chunk shape of the 8 x 2048 workload
+    ([513, 65], 2, 1, 64, "f32", (1, 2), 1),       # zero padding; a band of 512 rows (4 slices)
+])
+def test_score_variant_highpass(orc, syn, ns, L, H, D, dtype, alpha, fftlen):
+    """Sec. 5.4 / App. E.2 high-frequency-guided selection: magnitudes of the
+    bins at and above the cutoff, per-layer scores and the layer mean against
+    the oracle's explicit high-band reconstruction; then the index sets."""
+    ct = need_gpu()
+    host = _chunks(syn, ns, L, H, D, dtype)
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    for norm in (ct.CT_NORM_SUM, ct.CT_NORM_NONE):
+        s_gpu, ls_gpu = ct.cachetune_score_chunk(dev, L, H, D, alpha=alpha, fftlen=fftlen, norm=norm,
+                                                 want_layers=True, variant=ct.CT_SCORE_HIGHPASS)
+        torch.cuda.synchronize()
+        s_gpu, ls_gpu = to_host(s_gpu), to_host(ls_gpu)
+        s_orc, ls_orc = [], []
+        for k, v in host:
+            s, ls = orc.score_highpass(k, v, *alpha, mode=fftlen, norm=norm, layers=True)
+            s_orc.append(s)
+            ls_orc.append(ls)
+        s_orc, ls_orc = np.concatenate(s_orc), np.concatenate(ls_orc, axis=1)
+        _rel_close(s_gpu, s_orc, floor=1e-6 * np.abs(s_orc).max())
+        _rel_close(ls_gpu, ls_orc, floor=1e-6 * np.abs(ls_orc).max())
+    ks, _, sel, _ = ct.cachetune_select_topr(to_dev(s_gpu), ns, r=(15, 100))
+    torch.cuda.synchronize()
+    sel = to_host(sel)
+    o = so = 0
+    for n, k in zip(ns, ks):
+        _, want, _ = orc.topr(s_orc[o:o + n], k)
+        check_index_sets(sel[so:so + k], want, s_orc[o:o + n], k)
+        o, so = o + n, so + k
+
+
 def test_random_selection(orc, syn):
     """§5.4 random selection: top-r over seeded uniform scores (drawn by the
     input generator and passed in) is a uniformly random set of k tokens per
