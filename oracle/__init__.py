@@ -53,6 +53,7 @@ def lib():
         L.orc_rfft.argtypes = [vp, i32, vp, vp]
         L.orc_lowpass.argtypes = [vp, i32, i32, i32, i32, vp]
         L.orc_highpass.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.orc_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_score_highpass.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_topr.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -168,6 +169,21 @@ def score_l2(K: np.ndarray, V: np.ndarray, norm: int = NORM_SUM, layers: bool = 
     if rc != 0:
         raise ValueError("orc_score_l2 rejected its arguments")
     return (score, ls) if layers else score
+
+
+def band_energy(X: np.ndarray, n_bands: int, mode: int = FFT_EXACT_N):
+    """App. E.1 energy fractions of one tensor [L][N][H][D] over n_bands equal
+    bands of its rFFT bins along the tokens (channels summed).  Returns
+    (fraction [L][n_bands], total [L])."""
+    assert X.ndim == 4
+    X = np.ascontiguousarray(X)
+    L_, N, H, D = X.shape
+    fr = np.zeros((L_, n_bands))
+    tot = np.zeros(L_)
+    rc = lib().orc_band_energy(_p(X), _dtype_code(X), L_, N, H, D, mode, n_bands, _p(fr), _p(tot))
+    if rc != 0:
+        raise ValueError("orc_band_energy rejected its arguments")
+    return fr, tot
 
 
 def score_highpass(K: np.ndarray, V: np.ndarray, a_num: int, a_den: int,

@@ -612,3 +612,58 @@ int orc_score_highpass(const void* K, const void* V, int dtype, int L, int N, in
   free(c); free(s); free(mag[0]); free(mag[1]); free(sl); free(rec);
   return 0;
 }
+
+/* ---- frequency-band energy fractions (App. E.1, Figure 9) ---- */
+
+/* Energy of one real tensor X ([L][N][H][D], storage dtype) per band of rFFT
+ * bins, taken along the tokens of each channel and summed over the H*D
+ * channels.  Bin j of a length-nf transform carries w_j |X_j|^2 / nf with w_j
+ * = 1 at DC and Nyquist, else 2 (the two-sided spectrum folded; by Parseval
+ * the bins sum to the energy of the sequence).  Reading: "bands" are n_bands
+ * equal parts of the bin range [0, nb), bin j in band floor(j * n_bands / nb).
+ * fraction [L][n_bands] = band energy / total; total [L] (may be NULL).
+ * Returns 0, or -1 on bad arguments (n_bands outside [1, nb]). */
+int orc_band_energy(const void* X, int dtype, int L, int N, int H, int D, int fftlen_mode,
+                    int n_bands, double* fraction, double* total) {
+  if (L < 1 || N < 1 || H < 1 || D < 1) return -1;
+  int C = H * D;
+  int nf = orc_fft_len(N, fftlen_mode);
+  int nb = orc_nbins(nf);
+  if (n_bands < 1 || n_bands > nb) return -1;
+  double* c = malloc(sizeof(double) * nf);
+  double* s = malloc(sizeof(double) * nf);
+  trig_table(nf, c, s);
+  double* ebin = malloc(sizeof(double) * (size_t)C * nb); /* [channel][bin] */
+  for (int l = 0; l < L; ++l) {
+    size_t off = (size_t)l * N * C;
+#pragma omp parallel
+    {
+      double* seq = calloc(nf, sizeof(double));
+      double* re = malloc(sizeof(double) * nb);
+      double* im = malloc(sizeof(double) * nb);
+#pragma omp for schedule(static)
+      for (int ch = 0; ch < C; ++ch) {
+        for (int n = 0; n < N; ++n) seq[n] = load_elem(X, dtype, off + (size_t)n * C + ch);
+        dft_bins(seq, nf, nb, c, s, re, im);
+        for (int j = 0; j < nb; ++j) {
+          int edge = (j == 0) || ((nf % 2 == 0) && j == nf / 2);
+          ebin[(size_t)ch * nb + j] = (edge ? 1.0 : 2.0) * (re[j] * re[j] + im[j] * im[j]) / nf;
+        }
+      }
+      free(seq); free(re); free(im);
+    }
+    double* fr = fraction + (size_t)l * n_bands;
+    for (int b = 0; b < n_bands; ++b) fr[b] = 0.0;
+    double tot = 0.0;
+    for (int j = 0; j < nb; ++j) {
+      double e = 0.0;
+      for (int ch = 0; ch < C; ++ch) e += ebin[(size_t)ch * nb + j];
+      fr[(int)(((long long)j * n_bands) / nb)] += e;
+      tot += e;
+    }
+    for (int b = 0; b < n_bands; ++b) fr[b] = tot > 0.0 ? fr[b] / tot : 0.0;
+    if (total) total[l] = tot;
+  }
+  free(c); free(s); free(ebin);
+  return 0;
+}

@@ -227,3 +227,57 @@ def test_highpass_parseval_and_empty_band(orc):
     np.testing.assert_allclose(orc.highpass(x, 1, 1), 0.0, atol=1e-12)
     # the DC bin is always in the low view: the high view has zero mean
     assert abs(orc.highpass(x, 1, 1000).sum()) < 1e-10
+
+
+# ---- App. E.1 band energy fractions ----------------------------------------------------
+
+def _np_band(x, n_bands, nf):
+    # x [L][N][C] float64 -> fractions [L][n_bands], totals [L] from numpy's rfft
+    L, N, C = x.shape
+    xp = np.concatenate([x, np.zeros((L, nf - N, C))], axis=1)
+    F = np.fft.rfft(xp, axis=1)
+    nb = nf // 2 + 1
+    w = np.full(nb, 2.0)
+    w[0] = 1.0
+    if nf % 2 == 0:
+        w[-1] = 1.0
+    e = (w[None, :, None] * np.abs(F) ** 2 / nf).sum(-1)  # [L][nb]
+    band = (np.arange(nb) * n_bands) // nb
+    fr = np.stack([np.bincount(band, weights=e[l], minlength=n_bands) for l in range(L)])
+    tot = e.sum(-1)
+    return fr / tot[:, None], tot
+
+
+@pytest.mark.parametrize("N,mode,n_bands", [(64, 0, 10), (77, 0, 5), (100, 1, 8), (33, 1, 17), (9, 0, 5)])
+def test_band_energy_matches_numpy(orc, N, mode, n_bands):
+    X = RNG.standard_normal((2, N, 2, 3)).astype(np.float32)
+    fr, tot = orc.band_energy(X, n_bands, mode)
+    nf = N if mode == 0 else 1 << (N - 1).bit_length()
+    want_fr, want_tot = _np_band(X.astype(np.float64).reshape(2, N, 6), n_bands, nf)
+    np.testing.assert_allclose(fr, want_fr, atol=1e-12)
+    np.testing.assert_allclose(tot, want_tot, rtol=1e-11)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_band_energy_parseval_and_sum(orc, mode):
+    # Parseval: the bins carry the energy of the stored sequence (zero padding adds none)
+    X = RNG.standard_normal((3, 50, 1, 4)).astype(np.float32)
+    fr, tot = orc.band_energy(X, 7, mode)
+    np.testing.assert_allclose(tot, (X.astype(np.float64) ** 2).sum(axis=(1, 2, 3)), rtol=1e-12)
+    np.testing.assert_allclose(fr.sum(axis=1), 1.0, atol=1e-13)
+    assert (fr >= 0).all()
+
+
+def test_band_energy_single_bins(orc):
+    N, nb, n_bands = 40, 21, 4   # bands of bins: [0,6) [6,11) [11,16) [16,21)
+    t = np.arange(N)
+    for f, band in ((0, 0), (5, 0), (6, 1), (10, 1), (11, 2), (15, 2), (16, 3), (20, 3)):
+        x = np.cos(2 * np.pi * f * t / N + (0.0 if f in (0, 20) else 0.7))
+        X = np.tile(x[None, :, None, None], (1, 1, 1, 2)).astype(np.float64).astype(np.float32)
+        fr, _ = orc.band_energy(X, n_bands)
+        assert fr[0, band] > 1.0 - 1e-6, (f, fr)
+    # constant rows: all energy at DC; n_bands = nb puts each bin in a band of its own
+    fr, tot = orc.band_energy(np.full((1, N, 1, 1), 3.0, np.float32), nb)
+    assert fr[0, 0] == pytest.approx(1.0, abs=1e-14) and tot[0] == pytest.approx(9.0 * N, rel=1e-14)
+    with pytest.raises(ValueError):
+        orc.band_energy(np.zeros((1, N, 1, 1), np.float32), nb + 1)
