@@ -569,6 +569,34 @@ def score_variants(w, args):
                       "bytes_read": w.score_bytes()}), flush=True)
 
 
+def band_energy(w, args, n_bands=10):
+    """App. E.1 on the workload's chunks: time of the band-energy pass and the
+    energy fraction of each tenth of the rFFT bins (mean over chunks and
+    layers) for K and V.  One JSON line."""
+    import torch
+    ct = w.ct
+    need = ct.cachetune_band_energy_ws(w.ns, w.L, w.H, w.D)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    run = lambda: ct.cachetune_band_energy(w.chunks, w.L, w.H, w.D, n_bands, ws=ws)  # noqa: E731
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        fr, tot = run()
+    z.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(z) / args.steps
+    mean = fr.mean(dim=(0, 1)).cpu().numpy()  # [2][n_bands]
+    print(f"[bench] band energy: {ms:.3f} ms", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "band energy fractions (all chunks, all layers)", "unit": "ms",
+                      "value": ms, "config": {"workload": w.name, "n_bands": n_bands},
+                      "workspace_bytes": need,
+                      "fraction_K": [round(float(x), 5) for x in mean[0]],
+                      "fraction_V": [round(float(x), 5) for x in mean[1]]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -582,6 +610,8 @@ def main():
                     help="with --host-tier: also run the warm-started golden-section search for r")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--band-energy", action="store_true",
+                    help="time the band energy fractions of the workload's chunks instead")
     ap.add_argument("--score-variants", action="store_true",
                     help="time the scoring variants (low-pass, L2-norm, high-frequency) on the workload instead")
     args = ap.parse_args()
@@ -605,6 +635,9 @@ def main():
 
     if args.score_variants:
         score_variants(w, args)
+        return
+    if args.band_energy:
+        band_energy(w, args)
         return
 
     if args.copy_calib:

@@ -168,6 +168,30 @@ ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int3
                                   float* score, float* layer_score, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* ---- frequency-band energy fractions (App. E.1, Figure 9) ------------------
+ * For every chunk, layer and tensor (K, V): the rFFT of each channel along the
+ * tokens (transform length per fftlen, as cachetune_score_chunk), bin j
+ * carrying w_j |X_j|^2 / nf summed over the H*D channels (w_j = 1 at DC and
+ * Nyquist, else 2; the bins sum to the energy of the stored rows), grouped
+ * into n_bands equal bands of the bin range [0, nb): bin j in band
+ * floor(j * n_bands / nb).
+ *  chunks, L, H, D, dtype, fftlen: as cachetune_score_chunk
+ *  n_bands:  in [1, 1024] and at most the bin count nb of every chunk
+ *  fraction: device double[n_chunks][L][2][n_bands] (2: K then V), band
+ *            energy over the total (0 when the total is 0)
+ *  total:    device double[n_chunks][L][2] total energies, or NULL
+ *  ws:       device workspace of cachetune_band_energy_ws bytes, 256-aligned:
+ *            the coefficients of every bin, L*2*2*nb*H*D*4 bytes per chunk
+ *            (about 545 MB for 32 layers of 2048 tokens and 8 x 128 channels)
+ * Deterministic (fixed-order fp64 sums).  Errors as cachetune_score_chunk;
+ * n_bands out of range is CT_E_INVALID.  Asynchronous on `stream`. */
+ct_status cachetune_band_energy_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                  int32_t H, int32_t D, ct_fftlen fftlen, size_t* bytes);
+ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                int32_t D, ct_dtype dtype, ct_fftlen fftlen, int32_t n_bands,
+                                double* fraction, double* total, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* ---- selection (App. B.1) -------------------------------------------------
  * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].
  * Ranking order: higher score first, equal scores by lower local index (the
@@ -268,8 +292,8 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
  *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
- *   "attention_merge", "rank_order", "energy_l2", "highpass" (and "twiddle", "layer_norm",
- *   "layer_mean").
+ *   "attention_merge", "rank_order", "energy_l2", "highpass", "bin_energy"
+ *   (and "twiddle", "layer_norm", "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and
  * forgets them.  Events of other names are kept.  Thread-safe; the events are

@@ -47,7 +47,7 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
-           "cachetune_score_variant"]
+           "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -86,6 +86,8 @@ def lib():
                                                  C.POINTER(sz)]
         L.cachetune_score_variant.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                               vp, vp, vp, sz, vp]
+        L.cachetune_band_energy_ws.argtypes = [vp, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -164,6 +166,34 @@ def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N,
                                              alpha[1], fftlen, norm, variant, _ptr(score),
                                              _ptr(layer_score), _ptr(ws), ws.numel(), _stream(stream)))
     return score, layer_score
+
+
+def cachetune_band_energy_ws(n_per_chunk, L, H, D, fftlen=CT_FFT_EXACT_N) -> int:
+    arr = _i32_array(n_per_chunk)
+    out = C.c_size_t(0)
+    _check(lib().cachetune_band_energy_ws(arr, len(n_per_chunk), L, H, D, fftlen, C.byref(out)))
+    return out.value
+
+
+def cachetune_band_energy(chunks, L, H, D, n_bands, fftlen=CT_FFT_EXACT_N, ws=None, stream=None):
+    """App. E.1 band energy fractions.  chunks: list of (K, V) device tensors
+    [L][n][H][D].  Returns (fraction [n_chunks][L][2][n_bands], total
+    [n_chunks][L][2]) float64 device tensors."""
+    import torch
+    dev = chunks[0][0].device
+    ns = [int(k.shape[1]) for k, _ in chunks]
+    need = cachetune_band_energy_ws(ns, L, H, D, fftlen)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    fraction = torch.empty((len(chunks), L, 2, n_bands), dtype=torch.float64, device=dev)
+    total = torch.empty((len(chunks), L, 2), dtype=torch.float64, device=dev)
+    arr = (ct_chunk * len(chunks))()
+    for i, (k, v) in enumerate(chunks):
+        arr[i].k, arr[i].v, arr[i].n = k.data_ptr(), v.data_ptr(), int(k.shape[1])
+    _check(lib().cachetune_band_energy(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), fftlen, n_bands,
+                                       _ptr(fraction), _ptr(total), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+    return fraction, total
 
 
 # ---- selection ----------------------------------------------------------------

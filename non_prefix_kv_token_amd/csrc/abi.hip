@@ -176,6 +176,56 @@ ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int3
   CT_GUARD_END
 }
 
+ct_status cachetune_band_energy_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+                                  int32_t H, int32_t D, ct_fftlen fftlen, size_t* bytes) {
+  CT_GUARD_BEGIN
+  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  if (ct_status s = check_score_shapes(n_per_chunk, n_chunks, L, H, D, 1, 1, fftlen)) return s;
+  return score_plan(n_per_chunk, n_chunks, L, H, D, 1, 1, fftlen, bytes, nullptr, kVariantBandEnergy);
+  CT_GUARD_END
+}
+
+ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+                                int32_t D, ct_dtype dtype, ct_fftlen fftlen, int32_t n_bands,
+                                double* fraction, double* total, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!chunks) return fail(CT_E_INVALID, "chunks is NULL");
+  if (n_chunks < 1 || n_chunks > 4096) return fail(CT_E_INVALID, "n_chunks must be in [1, 4096]");
+  if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
+  if (!fraction) return fail(CT_E_INVALID, "fraction is NULL");
+  std::vector<int32_t> ns(n_chunks);
+  for (int b = 0; b < n_chunks; ++b) {
+    if (!chunks[b].k || !chunks[b].v) return fail(CT_E_INVALID, "chunk K or V pointer is NULL");
+    ns[b] = chunks[b].n;
+  }
+  if (ct_status s = check_score_shapes(ns.data(), n_chunks, L, H, D, 1, 1, fftlen)) return s;
+  if (n_bands < 1 || n_bands > 1024) return fail(CT_E_INVALID, "n_bands must be in [1, 1024]");
+  for (int b = 0; b < n_chunks; ++b)
+    if (n_bands > fft_len(ns[b], fftlen) / 2 + 1)
+      return fail(CT_E_INVALID, "n_bands above the bin count of a chunk");
+  size_t need = 0;
+  std::vector<ScoreLaunch> launches;
+  if (ct_status s = score_plan(ns.data(), n_chunks, L, H, D, 1, 1, fftlen, &need, &launches,
+                               kVariantBandEnergy))
+    return s;
+  if (!ws || ws_bytes < need)
+    return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  int b0 = 0;
+  for (ScoreLaunch& sl : launches) {
+    sl.dtype = dtype;
+    for (int i = 0; i < sl.n_chunks; ++i) {
+      sl.c[i].k = chunks[b0 + i].k;
+      sl.c[i].v = chunks[b0 + i].v;
+    }
+    b0 += sl.n_chunks;
+  }
+  return band_energy_run(launches, reinterpret_cast<char*>(ws), n_bands, fraction, total, stream);
+  CT_GUARD_END
+}
+
 ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
                                 int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
                                 int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {

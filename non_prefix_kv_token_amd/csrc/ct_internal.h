@@ -82,6 +82,11 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
                      std::vector<ScoreLaunch>* launches, int32_t variant = CT_SCORE_LOWPASS);
 ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
                     float* layer_score, hipStream_t stream);
+// Band projection of every bin (plan with alpha = 1 and this variant: no Gram
+// slots), then the energy fractions of n_bands equal bands of the bins.
+constexpr int32_t kVariantBandEnergy = 100;
+ct_status band_energy_run(const std::vector<ScoreLaunch>& launches, char* ws, int n_bands,
+                          double* fraction, double* total, hipStream_t stream);
 
 // ------------------------------------------------------------- selection
 struct TopRChunk {

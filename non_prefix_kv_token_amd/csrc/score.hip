@@ -921,6 +921,71 @@ __global__ __launch_bounds__(512) void k_highpass(ScoreLaunch sl, char* ws) {
   }
 }
 
+// ---- App. E.1: energy fractions of frequency bands ------------------------------
+// With every bin kept (kk = nb), Y holds R_j and S_j of all bins for all
+// channels.  Bin j carries e_j = w_j (|R_j|^2 + |S_j|^2) / nf summed over the
+// channels (w_j = 1 at DC and Nyquist, else 2), and the bins sum to the
+// energy of the stored sequence (Parseval).  Band b of n_bands holds the bins
+// j with floor(j * n_bands / nb) = b.  One block per problem: each wave sums
+// the squares of a cos row and its sin row in fp64 (fixed order), the bins
+// go to LDS, then each band and the total are summed in bin order.
+constexpr int kMaxBins = kMaxN / 2 + 1;
+constexpr int kMaxBands = 1024;
+
+__global__ __launch_bounds__(512) void k_bin_energy(ScoreLaunch sl, char* ws, int n_bands,
+                                                    double* fraction, double* total) {
+  __shared__ double ebin[kMaxBins];
+  __shared__ double eband[kMaxBands];
+  __shared__ double etot;
+  const int L = sl.L, C = sl.C;
+  const int prob = blockIdx.x;
+  const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int nb = d.kk, nf = d.nf;
+  const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * d.ppad) * C;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int j = wave; j < nb; j += 8) {
+    const float* rc = Y + (size_t)j * C;
+    const float* rs = Y + (size_t)(nb + j) * C;
+    double e = 0.0;
+    for (int c = 4 * lane; c < C; c += 256) {
+      const float4 a = *reinterpret_cast<const float4*>(rc + c);
+      const float4 q = *reinterpret_cast<const float4*>(rs + c);
+      e = fma((double)a.x, (double)a.x, e);
+      e = fma((double)a.y, (double)a.y, e);
+      e = fma((double)a.z, (double)a.z, e);
+      e = fma((double)a.w, (double)a.w, e);
+      e = fma((double)q.x, (double)q.x, e);
+      e = fma((double)q.y, (double)q.y, e);
+      e = fma((double)q.z, (double)q.z, e);
+      e = fma((double)q.w, (double)q.w, e);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+    if (lane == 0) ebin[j] = ((j == 0 || 2 * j == nf) ? 1.0 : 2.0) * e / (double)nf;
+  }
+  __syncthreads();
+  for (int bd = tid; bd < n_bands; bd += 512) {
+    // first bin of band bd: the least j with j * n_bands >= bd * nb
+    const int j0 = (int)(((long long)bd * nb + n_bands - 1) / n_bands);
+    const int j1 = (int)(((long long)(bd + 1) * nb + n_bands - 1) / n_bands);
+    double e = 0.0;
+    for (int j = j0; j < j1; ++j) e += ebin[j];
+    eband[bd] = e;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int bd = 0; bd < n_bands; ++bd) t += eband[bd];
+    etot = t;
+  }
+  __syncthreads();
+  const size_t row = (size_t)(b * L + layer) * 2 + kv;
+  for (int bd = tid; bd < n_bands; bd += 512)
+    fraction[row * n_bands + bd] = etot > 0.0 ? eband[bd] / etot : 0.0;
+  if (tid == 0 && total) total[row] = etot;
+}
+
 // ---- 4'. per (chunk, layer): magnitudes and normalisation --------------------
 // s = sqrt(E_K)/2 + sqrt(E_V)/2 per token, normalised within the layer; the
 // result overwrites the E_K row of the layer (read before written by the same
@@ -1052,7 +1117,8 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   // Matrix-core Gram (2kk <= 128) keeps G in LDS and needs no slot; larger
   // bands take the fp64 path, whose blocks loop over problems and slots.
   const bool mfma_gram = max_p2 <= 128;
-  int64_t n_slots = (mfma_gram || !band) ? 0 : std::min<int64_t>(probs_max, 1024);
+  const bool gram = band && variant != kVariantBandEnergy;
+  int64_t n_slots = (mfma_gram || !gram) ? 0 : std::min<int64_t>(probs_max, 1024);
   const int64_t slot_budget = (int64_t)1 << 30;
   while (!mfma_gram && n_slots > 1 && n_slots * slot_bytes > slot_budget) n_slots /= 2;
   const int64_t slot_off = (int64_t)off;
@@ -1079,6 +1145,46 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
       launches->push_back(sl);
     }
   }
+  return CT_OK;
+}
+
+// Twiddle planes and the band projection Y of every problem of a launch.
+static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t stream) {
+  int max_elems = 0;
+  for (int i = 0; i < sl.n_chunks; ++i)
+    max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
+  dim3 gt((max_elems + 255) / 256 < 2048 ? (max_elems + 255) / 256 : 2048, sl.n_chunks);
+  {
+    TimedLaunch tl_("twiddle", stream);
+    hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
+  }
+  if (ct_status s = check_launch("twiddle")) return s;
+
+  dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
+  {
+    TimedLaunch tl_("band", stream);
+    if (sl.dtype == CT_BF16) {
+      // Band tiles per block: the whole of the launch's largest band when it
+      // has at most 5 tiles (160 rows), else that band split evenly over the
+      // fewest blocks of at most 5 tiles.  Each block streams X from HBM
+      // once, so more blocks per band means more reads of X.
+      const int tiles = sl.max_ppad / 32;
+      const int nyb = (tiles + 4) / 5;
+      const int ntl = (tiles + nyb - 1) / nyb;
+      // 8 waves x 64 channels per block: every twiddle slab staged in LDS
+      // serves 512 channels (the slabs, not X, are most of the L2 traffic)
+      dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+      switch (ntl) {
+        case 5: hipLaunchKernelGGL(k_band_bf16<5>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 4: hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 3: hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 2: hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(512), 0, stream, sl, ws); break;
+        default: hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(512), 0, stream, sl, ws); break;
+      }
+    } else
+      hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
+  }
+  if (ct_status s = check_launch("band projection")) return s;
   return CT_OK;
 }
 
@@ -1119,41 +1225,7 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
       if (ct_status s = score_finish(sl, ws, score, layer_score, stream)) return s;
       continue;
     }
-    int max_elems = 0;
-    for (int i = 0; i < sl.n_chunks; ++i)
-      max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
-    dim3 gt((max_elems + 255) / 256 < 2048 ? (max_elems + 255) / 256 : 2048, sl.n_chunks);
-    {
-      TimedLaunch tl_("twiddle", stream);
-      hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
-    }
-    if (ct_status s = check_launch("twiddle")) return s;
-
-    dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
-    {
-    TimedLaunch tl_("band", stream);
-    if (sl.dtype == CT_BF16) {
-      // Band tiles per block: the whole of the launch's largest band when it
-      // has at most 5 tiles (160 rows), else that band split evenly over the
-      // fewest blocks of at most 5 tiles.  Each block streams X from HBM
-      // once, so more blocks per band means more reads of X.
-      const int tiles = sl.max_ppad / 32;
-      const int nyb = (tiles + 4) / 5;
-      const int ntl = (tiles + nyb - 1) / nyb;
-      // 8 waves x 64 channels per block: every twiddle slab staged in LDS
-      // serves 512 channels (the slabs, not X, are most of the L2 traffic)
-      dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
-      switch (ntl) {
-        case 5: hipLaunchKernelGGL(k_band_bf16<5>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 4: hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 3: hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 2: hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(512), 0, stream, sl, ws); break;
-        default: hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(512), 0, stream, sl, ws); break;
-      }
-    } else
-      hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
-    }
-    if (ct_status s = check_launch("band projection")) return s;
+    if (ct_status s = band_project(sl, ws, stream)) return s;
 
     const int n_probs = sl.n_chunks * sl.L * 2;
     if (sl.slot_p2 <= 128) {
@@ -1180,6 +1252,24 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
     }
 
     if (ct_status s = score_finish(sl, ws, score, layer_score, stream)) return s;
+  }
+  return CT_OK;
+}
+
+ct_status band_energy_run(const std::vector<ScoreLaunch>& launches, char* ws, int n_bands,
+                          double* fraction, double* total, hipStream_t stream) {
+  if (n_bands < 1 || n_bands > kMaxBands) return fail(CT_E_INVALID, "n_bands out of range");
+  size_t done = 0;  // (chunk, layer, K|V) rows written by earlier launches
+  for (const ScoreLaunch& sl : launches) {
+    if (ct_status s = band_project(sl, ws, stream)) return s;
+    const int n_probs = sl.n_chunks * sl.L * 2;
+    {
+      TimedLaunch tl_("bin_energy", stream);
+      hipLaunchKernelGGL(k_bin_energy, dim3(n_probs), dim3(512), 0, stream, sl, ws, n_bands,
+                         fraction + done * n_bands, total ? total + done : nullptr);
+    }
+    if (ct_status s = check_launch("band energies")) return s;
+    done += (size_t)n_probs;
   }
   return CT_OK;
 }

@@ -135,3 +135,23 @@ def test_score_variant_ws(lib):
     out = C.c_size_t(0)
     assert lib.cachetune_score_variant_ws(n, 2, 4, 8, 128, 1, 16, 0, 3, C.byref(out)) == ct.CT_E_INVALID
     assert b"unknown variant" in lib.cachetune_last_error()
+
+
+def test_band_energy_validation(lib):
+    import non_prefix_kv_token_amd as ct
+    n = (C.c_int32 * 2)(2048, 9)
+    out = C.c_size_t(0)
+    assert lib.cachetune_band_energy_ws(n, 2, 4, 8, 128, 0, C.byref(out)) == ct.CT_OK
+    # every bin's coefficients: 4 layers x 2 tensors x padded 2*nb rows x 1024 channels x 4 bytes
+    assert out.value >= 4 * 2 * (2080 + 32) * 1024 * 4
+    arr = (ct.ct_chunk * 2)()
+    for i, m in enumerate((2048, 9)):  # pointers are only checked for NULL before device work
+        arr[i].k, arr[i].v, arr[i].n = 256, 512, m
+    fake = C.c_void_p(1024)
+    for nb in (0, 6, 2000):  # 9 tokens have 5 bins
+        assert lib.cachetune_band_energy(arr, 2, 4, 8, 128, ct.CT_BF16, 0, nb, fake, None, fake,
+                                         1 << 40, None) == ct.CT_E_INVALID
+    assert lib.cachetune_band_energy(arr, 2, 4, 8, 128, ct.CT_BF16, 0, 5, None, None, fake,
+                                     1 << 40, None) == ct.CT_E_INVALID
+    assert lib.cachetune_band_energy(arr, 2, 4, 8, 128, ct.CT_BF16, 0, 5, fake, None, None,
+                                     0, None) == ct.CT_E_WORKSPACE

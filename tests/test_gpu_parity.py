@@ -208,6 +208,27 @@ def test_score_variant_highpass(orc, syn, ns, L, H, D, dtype, alpha, fftlen):
         o, so = o + n, so + k
 
 
+@pytest.mark.parametrize("ns,L,H,D,dtype,fftlen,n_bands", [
+    ([300, 64, 9], 2, 2, 64, "bf16", 0, 5),
+    ([2048], 1, 8, 128, "bf16", 0, 10),            # the per-chunk shape of the 8 x 2048 workload
+    ([513, 100], 1, 1, 64, "f32", 1, 10),         # zero padding to 1024 and 128
+])
+def test_band_energy(orc, syn, ns, L, H, D, dtype, fftlen, n_bands):
+    """App. E.1 energy fractions of equal bands of rFFT bins, for K and V of
+    every chunk and layer, and the totals, against the oracle."""
+    ct = need_gpu()
+    host = _chunks(syn, ns, L, H, D, dtype)
+    dev = [(to_dev(k), to_dev(v)) for k, v in host]
+    fr, tot = ct.cachetune_band_energy(dev, L, H, D, n_bands, fftlen=fftlen)
+    torch.cuda.synchronize()
+    fr, tot = to_host(fr), to_host(tot)
+    for b, (k, v) in enumerate(host):
+        for t, X in enumerate((k, v)):
+            want_fr, want_tot = orc.band_energy(X, n_bands, fftlen)
+            np.testing.assert_allclose(fr[b, :, t], want_fr, rtol=1e-4, atol=1e-7)
+            np.testing.assert_allclose(tot[b, :, t], want_tot, rtol=1e-5)
+
+
 def test_random_selection(orc, syn):
     """§5.4 random selection: top-r over seeded uniform scores (drawn by the
     input generator and passed in) is a uniformly random set of k tokens per
