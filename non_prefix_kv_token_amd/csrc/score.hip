@@ -338,7 +338,10 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // no exposed load latency.  NTL = 32-row band tiles per block (the launch's
 // largest; rows a chunk does not have are zero).  The step loop is unrolled
 // by two so that both register and LDS buffers are compile-time.
-template <int NTL>
+// FULL: every chunk's padded band is a whole number of blocks of 32*NTL rows,
+// so no block holds padding tiles and the tile loop carries no per-tile test
+// (the branches would break up the matrix-core issue).
+template <int NTL, bool FULL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_band_bf16(ScoreLaunch sl, char* ws) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][3 * 32 * NTL * kTwStride];
@@ -439,7 +442,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
               &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
 #pragma unroll
       for (int pt = 0; pt < NTL; ++pt) {
-        if (pt * 32 >= nrows) break;  // the band ends inside this block: no products of padding
+        if (!FULL && pt * 32 >= nrows) break;  // the band ends inside this block: no products of padding
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
           acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b0, acc[pt][0], 0, 0, 0);
@@ -618,11 +621,26 @@ __global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) { acc[i][v] = 0.f; accd[i][v] = 0.0; }
 
+  // Y of the next stage is loaded into registers during the current stage's
+  // products (ppad <= 128 rows x 16 float4 = at most 4 per thread).
+  constexpr int kPf = 128 * (kGramCh / 4) / 512;
+  float4 pf[kPf];
+  auto load_stage = [&](int c0) {
+#pragma unroll
+    for (int it = 0; it < kPf; ++it) {
+      const int item = tid + 512 * it, r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
+      if (item < ppad * (kGramCh / 4)) pf[it] = *reinterpret_cast<const float4*>(Y + (size_t)r * C + c0 + q4);
+    }
+  };
+  load_stage(0);
   for (int c0 = 0; c0 < C; c0 += kGramCh) {
     __syncthreads();
-    for (int item = tid; item < ppad * (kGramCh / 4); item += 512) {
+#pragma unroll
+    for (int it = 0; it < kPf; ++it) {
+      const int item = tid + 512 * it;
+      if (item >= ppad * (kGramCh / 4)) break;
       const int r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
-      const float4 v = *reinterpret_cast<const float4*>(Y + (size_t)r * C + c0 + q4);
+      const float4 v = pf[it];
       const float x[4] = {v.x, v.y, v.z, v.w};
       uint32_t h[3][4];
 #pragma unroll
@@ -641,6 +659,7 @@ __global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
             make_uint2(h[q][0] | (h[q][1] << 16), h[q][2] | (h[q][3] << 16));
     }
     __syncthreads();
+    if (c0 + kGramCh < C) load_stage(c0 + kGramCh);
 #pragma unroll
     for (int ks = 0; ks < kGramCh / 16; ++ks) {
 #pragma unroll
@@ -1174,13 +1193,21 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
       // 8 waves x 64 channels per block: every twiddle slab staged in LDS
       // serves 512 channels (the slabs, not X, are most of the L2 traffic)
       dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+      bool full = true;
+      for (int i = 0; i < sl.n_chunks; ++i) full = full && sl.c[i].ppad % (32 * ntl) == 0;
+#define CT_BAND(N)                                                                   \
+  if (full)                                                                          \
+    hipLaunchKernelGGL((k_band_bf16<N, true>), gq, dim3(512), 0, stream, sl, ws);    \
+  else                                                                               \
+    hipLaunchKernelGGL((k_band_bf16<N, false>), gq, dim3(512), 0, stream, sl, ws);
       switch (ntl) {
-        case 5: hipLaunchKernelGGL(k_band_bf16<5>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 4: hipLaunchKernelGGL(k_band_bf16<4>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 3: hipLaunchKernelGGL(k_band_bf16<3>, gq, dim3(512), 0, stream, sl, ws); break;
-        case 2: hipLaunchKernelGGL(k_band_bf16<2>, gq, dim3(512), 0, stream, sl, ws); break;
-        default: hipLaunchKernelGGL(k_band_bf16<1>, gq, dim3(512), 0, stream, sl, ws); break;
+        case 5: CT_BAND(5) break;
+        case 4: CT_BAND(4) break;
+        case 3: CT_BAND(3) break;
+        case 2: CT_BAND(2) break;
+        default: CT_BAND(1) break;
       }
+#undef CT_BAND
     } else
       hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
   }
