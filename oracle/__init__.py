@@ -53,6 +53,7 @@ def lib():
         L.orc_rfft.argtypes = [vp, i32, vp, vp]
         L.orc_lowpass.argtypes = [vp, i32, i32, i32, i32, vp]
         L.orc_highpass.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.orc_round_bf16_array.argtypes = [vp, C.c_longlong, vp]
         L.orc_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_score_highpass.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.orc_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
@@ -320,3 +321,85 @@ def calibrate_ratio(t_c, t_i, cost, r_min=0.15, r_max=1.0, half_width=0.1, eps=0
             f2 = f(x2)
         widths.append(b - a)
     return 0.5 * (a + b), probes, widths
+
+
+# ---- the rest of the selective-recompute layer (synthetic weights) ---------------
+# The recomputed rows (Sec. 4.1, App. B.2: the selected tokens and the uncached
+# suffix run through each layer in the new context) pass through a decoder layer
+# of the models the pages evaluate (Sec. 5.1: Llama-3-8B and relatives): pre-norm
+# RMSNorm, bias-free Q/K/V projections, RoPE at the global position and causal
+# GQA attention over the assembled layer, output projection plus residual,
+# RMSNorm, the gated MLP silu(gate) * up, down projection plus residual.  Plain
+# fp64 definitions; numpy's matmul is the library primitive for the products.
+
+def bf16_bits(x) -> np.ndarray:
+    """Vectorised RNE rounding of float64 values to bf16 bit patterns."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().orc_round_bf16_array(_p(a), a.size, _p(out))
+    return out
+
+
+def rmsnorm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * np.asarray(gain, np.float64)
+
+
+def linear(x: np.ndarray, w: np.ndarray, residual: np.ndarray | None = None) -> np.ndarray:
+    """x [m][k] times w [n][k] transposed (a bias-free projection), plus the
+    residual [m][n] when given."""
+    y = np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+    return y if residual is None else y + np.asarray(residual, np.float64)
+
+
+def silu_mul(gu: np.ndarray) -> np.ndarray:
+    """gu [m][2f] holds gate (columns [0, f)) and up ([f, 2f)): silu(gate) * up
+    with silu(g) = g / (1 + exp(-g))."""
+    gu = np.asarray(gu, np.float64)
+    f = gu.shape[-1] // 2
+    g, u = gu[..., :f], gu[..., f:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def recompute_layer(h, w, chunks, sel, offsets, sfx_start, qpos, H, Hq, D, theta, eps,
+                    style=ROPE_HALF):
+    """One layer for the n_q recomputed rows, in bf16 storage as the GPU path
+    keeps it: every stored intermediate (normalised rows, q, k, v, attention
+    output, h1, gate/up, MLP input, output) is rounded to bf16 where it is
+    stored; arithmetic between stores is fp64.
+
+    h: [n_q][d] float64 holding bf16 values, rows in qpos order (the selected
+    rows of each chunk in placement order, then the suffix).  w: dict of float64
+    arrays holding bf16 values: g1, g2 [d]; wq [Hq*D][d]; wk, wv [H*D][d];
+    wo [d][Hq*D]; wgu [2f][d]; wd [d][f].  chunks: list of (K, V) cached
+    [n][H][D] bf16 bit arrays of this layer; sel: per chunk the selected local
+    indices (ascending); offsets: per chunk its global start; sfx_start: global
+    position of the first suffix row.  Returns h2 [n_q][d] float64 (bf16 values)
+    and the intermediates in a dict."""
+    r = lambda a: widen(bf16_bits(a))  # noqa: E731  (stored as bf16)
+    n_q = h.shape[0]
+    x1 = r(rmsnorm(h, w["g1"], eps))
+    q = r(linear(x1, w["wq"]))
+    kr = r(linear(x1, w["wk"]))
+    vr = r(linear(x1, w["wv"]))
+    T = sfx_start + (n_q - sum(len(s) for s in sel))
+    k_asm = np.zeros((T, H, D), np.uint16)
+    v_asm = np.zeros((T, H, D), np.uint16)
+    kb = bf16_bits(kr).reshape(n_q, H, D)
+    vb = bf16_bits(vr).reshape(n_q, H, D)
+    row = 0
+    for (K, V), s, off in zip(chunks, sel, offsets):
+        k = len(s)
+        assemble_chunk(K, V, kb[row:row + k], vb[row:row + k], s, off, theta, style, k_asm, v_asm)
+        row += k
+    assemble_rows(kb[row:], vb[row:], sfx_start, theta, style, k_asm, v_asm)
+    qb = bf16_bits(q).reshape(n_q, Hq, D)
+    o, _ = attention(qb, qpos, k_asm, v_asm, 1.0 / np.sqrt(D), theta, style)
+    o = r(o.reshape(n_q, Hq * D))
+    h1 = r(linear(o, w["wo"], h))
+    x2 = r(rmsnorm(h1, w["g2"], eps))
+    gu = r(linear(x2, w["wgu"]))
+    a = r(silu_mul(gu))
+    h2 = r(linear(a, w["wd"], h1))
+    return h2, dict(x1=x1, q=q, k=kr, v=vr, k_asm=k_asm, v_asm=v_asm, o=o, h1=h1, x2=x2, gu=gu, a=a)

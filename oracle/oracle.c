@@ -667,3 +667,10 @@ int orc_band_energy(const void* X, int dtype, int L, int N, int H, int D, int ff
   free(c); free(s); free(ebin);
   return 0;
 }
+
+/* ---- storage rounding of whole arrays (used by the layer oracle) ---- */
+
+/* out[i] = bf16 bit pattern of v[i], rounded to nearest even (orc_round_bf16). */
+void orc_round_bf16_array(const double* v, long long n, uint16_t* out) {
+  for (long long i = 0; i < n; ++i) out[i] = orc_round_bf16(v[i]);
+}
