@@ -192,6 +192,38 @@ ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_
                                 double* fraction, double* total, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* ---- the rest of the selective-recompute layer (Sec. 4.1, App. B.2) --------
+ * The selected tokens and the uncached suffix run through every layer in the
+ * new context.  Besides assembly and attention, a layer of the models the
+ * pages evaluate (Sec. 5.1, Llama-3-8B-shaped) normalises their hidden rows,
+ * projects them to q / k / v (bias-free), projects the attention output back
+ * with a residual, and applies the gated MLP (silu(gate) * up, down projection,
+ * residual).  All tensors are bf16, row-major, device memory owned by the
+ * caller; every output element is rounded once to bf16.
+ *
+ * cachetune_rmsnorm: out[r][c] = x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * gain[c]
+ *   (fp32 arithmetic).  x, out: [rows][dim]; gain: [dim]; dim a multiple of 8
+ *   in [8, 65536]; 16-byte aligned.  out may equal x.
+ * cachetune_silu_mul: out[r][j] = silu(gu[r][j]) * gu[r][ff + j] with
+ *   silu(g) = g / (1 + exp(-g)) (fp32).  gate_up: [rows][2 ff]; out: [rows][ff];
+ *   ff a multiple of 8; 16-byte aligned.
+ * cachetune_linear: out[i][j] = sum_k x[i][k] w[j][k] (+ residual[i][j]) with
+ *   fp32 accumulation (hipBLASLt; the library keeps one handle per device,
+ *   created on the first call there).  x: [m][k]; w: [n][k] (the usual
+ *   [out][in] weight layout); residual: [m][n] or NULL (may equal out);
+ *   out: [m][n].  n, k multiples of 8; 16-byte aligned.  ws: device workspace
+ *   of cachetune_linear_ws bytes, 256-aligned, not shared by concurrent calls.
+ * Errors: CT_E_INVALID (shapes, NULL, alignment), CT_E_UNSUPPORTED (dtype other
+ * than bf16), CT_E_WORKSPACE, CT_E_HIP.  Asynchronous on `stream`. */
+ct_status cachetune_rmsnorm(const void* x, const void* gain, int32_t rows, int32_t dim, float eps,
+                            ct_dtype dtype, void* out, hipStream_t stream);
+ct_status cachetune_silu_mul(const void* gate_up, int32_t rows, int32_t ff, ct_dtype dtype, void* out,
+                             hipStream_t stream);
+ct_status cachetune_linear_ws(size_t* bytes);
+ct_status cachetune_linear(const void* x, const void* w, const void* residual, int32_t m, int32_t n,
+                           int32_t k, ct_dtype dtype, void* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* ---- selection (App. B.1) -------------------------------------------------
  * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].
  * Ranking order: higher score first, equal scores by lower local index (the
@@ -292,8 +324,8 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
  *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
- *   "attention_merge", "rank_order", "energy_l2", "highpass", "bin_energy"
- *   (and "twiddle", "layer_norm", "layer_mean").
+ *   "attention_merge", "rank_order", "energy_l2", "highpass", "bin_energy",
+ *   "rmsnorm", "silu_mul", "linear" (and "twiddle", "layer_norm", "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns
  * their summed duration in milliseconds and the number of launches, and
  * forgets them.  Events of other names are kept.  Thread-safe; the events are

@@ -47,7 +47,8 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_assemble_rope", "cachetune_recompute_attn", "cachetune_recompute_attn_ws",
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
-           "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy"]
+           "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
+           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear_ws", "cachetune_linear"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -88,6 +89,10 @@ def lib():
                                               vp, vp, vp, sz, vp]
         L.cachetune_band_energy_ws.argtypes = [vp, i32, i32, i32, i32, i32, C.POINTER(sz)]
         L.cachetune_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.cachetune_rmsnorm.argtypes = [vp, vp, i32, i32, f32, i32, vp, vp]
+        L.cachetune_silu_mul.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.cachetune_linear_ws.argtypes = [C.POINTER(sz)]
+        L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -194,6 +199,50 @@ def cachetune_band_energy(chunks, L, H, D, n_bands, fftlen=CT_FFT_EXACT_N, ws=No
                                        _ptr(fraction), _ptr(total), _ptr(ws), ws.numel(),
                                        _stream(stream)))
     return fraction, total
+
+
+# ---- the rest of the selective-recompute layer --------------------------------------
+
+def cachetune_rmsnorm(x, gain, eps=1e-5, out=None, stream=None):
+    """x: [rows][dim] bf16 device tensor; gain [dim].  Returns out (bf16)."""
+    import torch
+    out = torch.empty_like(x) if out is None else out
+    rows, dim = int(x.shape[0]), int(x.shape[-1])
+    _check(lib().cachetune_rmsnorm(_ptr(x), _ptr(gain), rows, dim, float(eps), _dtype(x), _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def cachetune_silu_mul(gate_up, out=None, stream=None):
+    """gate_up: [rows][2 ff] bf16.  Returns silu(gate) * up, [rows][ff]."""
+    import torch
+    rows, ff = int(gate_up.shape[0]), int(gate_up.shape[1]) // 2
+    if out is None:
+        out = torch.empty((rows, ff), dtype=gate_up.dtype, device=gate_up.device)
+    _check(lib().cachetune_silu_mul(_ptr(gate_up), rows, ff, _dtype(gate_up), _ptr(out), _stream(stream)))
+    return out
+
+
+def cachetune_linear_ws() -> int:
+    out = C.c_size_t(0)
+    _check(lib().cachetune_linear_ws(C.byref(out)))
+    return out.value
+
+
+def cachetune_linear(x, w, residual=None, out=None, ws=None, stream=None):
+    """x: [m][k], w: [n][k] bf16 device tensors; residual [m][n] or None.
+    Returns x w^T (+ residual) as [m][n] bf16."""
+    import torch
+    m, k = int(x.shape[0]), int(x.shape[1])
+    n = int(w.shape[0])
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    need = cachetune_linear_ws()
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().cachetune_linear(_ptr(x), _ptr(w), _ptr(residual), m, n, k, _dtype(x), _ptr(out),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 # ---- selection ----------------------------------------------------------------

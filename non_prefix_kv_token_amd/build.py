@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcachetune.so")
 SOURCES = ["abi.hip", "score.hip", "topr.hip", "assemble.hip", "attn.hip", "attn_f32.hip", "timing.hip", "hosttier.hip",
-           "calibrate.cpp"]
+           "calibrate.cpp", "layer.hip"]
 ARCH = os.environ.get("CACHETUNE_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, out_dir), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

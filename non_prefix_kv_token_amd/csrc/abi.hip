@@ -226,6 +226,58 @@ ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_
   CT_GUARD_END
 }
 
+ct_status cachetune_rmsnorm(const void* x, const void* gain, int32_t rows, int32_t dim, float eps,
+                            ct_dtype dtype, void* out, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (dtype != CT_BF16) return fail(CT_E_UNSUPPORTED, "rmsnorm takes bf16 rows");
+  if (rows < 0) return fail(CT_E_INVALID, "rows must be non-negative");
+  if (dim < 8 || dim % 8 != 0 || dim > 65536) return fail(CT_E_INVALID, "dim must be a multiple of 8 in [8, 65536]");
+  if (!(eps >= 0.0f)) return fail(CT_E_INVALID, "eps must be non-negative");
+  if (rows > 0 && (!x || !gain || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if (rows > 0 && (!aligned16(x) || !aligned16(gain) || !aligned16(out)))
+    return fail(CT_E_INVALID, "rows and gain must be 16-byte aligned");
+  return rmsnorm_run(x, gain, rows, dim, eps, out, stream);
+  CT_GUARD_END
+}
+
+ct_status cachetune_silu_mul(const void* gate_up, int32_t rows, int32_t ff, ct_dtype dtype, void* out,
+                             hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (dtype != CT_BF16) return fail(CT_E_UNSUPPORTED, "silu_mul takes bf16 rows");
+  if (rows < 0) return fail(CT_E_INVALID, "rows must be non-negative");
+  if (ff < 8 || ff % 8 != 0) return fail(CT_E_INVALID, "ff must be a positive multiple of 8");
+  if (rows > 0 && (!gate_up || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if (rows > 0 && (!aligned16(gate_up) || !aligned16(out)))
+    return fail(CT_E_INVALID, "rows must be 16-byte aligned");
+  return silu_mul_run(gate_up, rows, ff, out, stream);
+  CT_GUARD_END
+}
+
+ct_status cachetune_linear_ws(size_t* bytes) {
+  CT_GUARD_BEGIN
+  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  *bytes = kLinearWs;
+  return CT_OK;
+  CT_GUARD_END
+}
+
+ct_status cachetune_linear(const void* x, const void* w, const void* residual, int32_t m, int32_t n,
+                           int32_t k, ct_dtype dtype, void* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (dtype != CT_BF16) return fail(CT_E_UNSUPPORTED, "linear takes bf16 operands");
+  if (m < 0 || n < 1 || k < 1) return fail(CT_E_INVALID, "m must be non-negative, n and k positive");
+  if (n % 8 != 0 || k % 8 != 0) return fail(CT_E_INVALID, "n and k must be multiples of 8");
+  if (m > 0 && (!x || !w || !out)) return fail(CT_E_INVALID, "NULL argument");
+  if (m > 0 && (!aligned16(x) || !aligned16(w) || !aligned16(out) || (residual && !aligned16(residual))))
+    return fail(CT_E_INVALID, "operands must be 16-byte aligned");
+  if (!ws || ws_bytes < kLinearWs)
+    return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(kLinearWs) + " bytes required");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  return linear_run(x, w, residual, m, n, k, out, ws, kLinearWs, stream);
+  CT_GUARD_END
+}
+
 ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
                                 int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
                                 int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {
