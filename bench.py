@@ -597,6 +597,136 @@ def band_energy(w, args, n_bands=10):
                       "fraction_V": [round(float(x), 5) for x in mean[1]]}), flush=True)
 
 
+class RecomputeLayers:
+    """The whole request with the rest of the selective-recompute layer: the
+    selected rows and the suffix run through every layer (RMSNorm, q/k/v
+    projections feeding the assembly and the attention, output projection with
+    residual, RMSNorm, gated MLP with residual).  Synthetic Llama-3-8B-shaped
+    weights (hidden Hq*D, MLP width d_ff, N(0, 1/fan_in) entries, gains
+    N(1, 0.1^2)), one set shared by all layers: each layer still streams the
+    whole weight set from HBM, as distinct weights would."""
+
+    def __init__(self, w: "Workload", d_ff: int = 14336, seed: int = 20260601):
+        import torch
+        import synth as syn
+        self.w, self.ct = w, w.ct
+        H, Hq, D = w.H, w.Hq, w.D
+        self.d, self.f = Hq * D, d_ff
+        d, f, n_q = self.d, d_ff, w.n_q
+        t0 = time.time()
+        gen = lambda stream, shape, sigma, mean=0.0: _dev(syn.normal(seed, stream, shape, "bf16", mean, sigma))  # noqa: E731
+        self.g1, self.g2 = gen(1, (d,), 0.1, 1.0), gen(2, (d,), 0.1, 1.0)
+        self.wq = gen(3, (Hq * D, d), d ** -0.5)
+        self.wk = gen(4, (H * D, d), d ** -0.5)
+        self.wv = gen(5, (H * D, d), d ** -0.5)
+        self.wo = gen(6, (d, Hq * D), (Hq * D) ** -0.5)
+        self.wgu = gen(7, (2 * f, d), d ** -0.5)
+        self.wd = gen(8, (d, f), f ** -0.5)
+        self.h0 = gen(9, (n_q, d), 1.0)
+        self.gen_seconds = time.time() - t0
+        bf = torch.bfloat16
+        self.h = torch.empty((n_q, d), dtype=bf, device="cuda")
+        self.h1 = torch.empty_like(self.h)
+        self.x = torch.empty_like(self.h)
+        self.q = torch.empty((n_q, Hq * D), dtype=bf, device="cuda")
+        self.kr = torch.empty((n_q, H * D), dtype=bf, device="cuda")
+        self.vr = torch.empty((n_q, H * D), dtype=bf, device="cuda")
+        self.gu = torch.empty((n_q, 2 * f), dtype=bf, device="cuda")
+        self.a = torch.empty((n_q, f), dtype=bf, device="cuda")
+        self.lin_ws = torch.empty(self.ct.cachetune_linear_ws(), dtype=torch.uint8, device="cuda")
+        # rows of each chunk's selected tokens in qpos order (chunk ranges are disjoint)
+        self.row0 = [int(np.searchsorted(w.qpos_host, w.offsets[b])) for b in range(len(w.ns))]
+        self._places = {}
+
+    def places(self, l):
+        if l not in self._places:
+            w, ct, H, D = self.w, self.ct, self.w.H, self.w.D
+            out = []
+            for b, n in enumerate(w.ns):
+                k, v = w.chunks[b]
+                r0, kb = self.row0[b], w.ks[b]
+                out.append(ct.make_place(k[l], v[l], n, kb, int(w.offsets[b]), sel=w.sel[w.sel_off[b]:],
+                                         comp=w.comp[w.comp_off[b]:],
+                                         k_rec=self.kr[r0:r0 + kb].view(kb, H, D),
+                                         v_rec=self.vr[r0:r0 + kb].view(kb, H, D)))
+            self._places[l] = out
+        return self._places[l]
+
+    def layer(self, l):
+        w, ct = self.w, self.ct
+        n_q, H, Hq, D = w.n_q, w.H, w.Hq, w.D
+        lin = lambda x, wt, out, res=None: ct.cachetune_linear(x, wt, residual=res, out=out, ws=self.lin_ws)  # noqa: E731
+        ct.cachetune_rmsnorm(self.h, self.g1, 1e-5, out=self.x)
+        lin(self.x, self.wq, self.q)
+        lin(self.x, self.wk, self.kr)
+        lin(self.x, self.wv, self.vr)
+        s0 = n_q - w.n_sfx
+        ct.cachetune_assemble_rope(self.places(l), w.k_asm, w.v_asm, H, D, w.theta,
+                                   k_sfx=self.kr[s0:].view(w.n_sfx, H, D), v_sfx=self.vr[s0:].view(w.n_sfx, H, D),
+                                   n_sfx=w.n_sfx, sfx_offset=w.T_c)
+        ct.cachetune_recompute_attn(self.q.view(n_q, Hq, D), w.qpos, w.k_asm, w.v_asm, w.scale, w.theta,
+                                    out=w.out, ws=w.attn_ws)
+        lin(w.out.view(n_q, Hq * D), self.wo, self.h1, self.h)
+        ct.cachetune_rmsnorm(self.h1, self.g2, 1e-5, out=self.x)
+        lin(self.x, self.wgu, self.gu)
+        ct.cachetune_silu_mul(self.gu, out=self.a)
+        lin(self.a, self.wd, self.h, self.h1)
+
+    def step(self):
+        self.h.copy_(self.h0)
+        self.w.score_and_select()
+        for l in range(self.w.L):
+            self.layer(l)
+
+    def gemm_flops_per_layer(self) -> float:
+        w = self.w
+        d, f, n_q = self.d, self.f, w.n_q
+        return 2.0 * n_q * d * (w.Hq * w.D + 2 * w.H * w.D) + 2.0 * n_q * w.Hq * w.D * d + 2.0 * n_q * d * 2 * f \
+            + 2.0 * n_q * f * d
+
+
+def recompute_layers(w, args):
+    """Time the request with the full recompute layer (one JSON line)."""
+    import torch
+    ct = w.ct
+    m = RecomputeLayers(w)
+    print(f"[bench] recompute layers: weights generated in {m.gen_seconds:.1f}s", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        m.step()
+    torch.cuda.synchronize()
+    names = ["linear", "rmsnorm", "silu_mul", "assemble", "attention_setup", "attention", "attention_merge",
+             "twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"]
+    for n in names:
+        ct.cachetune_timing_read(n)
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ct.cachetune_timing_enable(True)
+    a.record()
+    for _ in range(args.steps):
+        m.step()
+    z.record()
+    torch.cuda.synchronize()
+    ct.cachetune_timing_enable(False)
+    ms = a.elapsed_time(z) / args.steps
+    kt = {n: ct.cachetune_timing_read(n) for n in names}
+    per = {n: round(t / args.steps, 4) for n, (t, c) in kt.items() if c}
+    lin_ms = kt["linear"][0] / args.steps
+    gflop = m.gemm_flops_per_layer() * w.L / 1e9
+    tflops = gflop / lin_ms
+    toks = sum(w.ns) / (ms * 1e-3)
+    print(f"[bench] recompute layers: {ms:.2f} ms/request, projections {lin_ms:.2f} ms "
+          f"({tflops:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "request time with the full selective-recompute layer (score, top-r, per layer: norm, "
+                  "q/k/v, assembly, attention, o-proj, MLP)",
+        "value": ms, "unit": "ms", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "chunk_tokens_per_s": toks,
+        "config": {"workload": w.name, "hidden": m.d, "d_ff": m.f, "n_rows": w.n_q, "layers": w.L,
+                   "weights": "synthetic N(0, 1/fan_in), shared by the layers"},
+        "projections": {"ms": lin_ms, "gflop": gflop, "tflops": tflops,
+                        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS},
+        "kernel_ms_per_request": per}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -610,6 +740,8 @@ def main():
                     help="with --host-tier: also run the warm-started golden-section search for r")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--recompute-layers", action="store_true",
+                    help="time the request with the full recompute layer (synthetic weights) instead")
     ap.add_argument("--band-energy", action="store_true",
                     help="time the band energy fractions of the workload's chunks instead")
     ap.add_argument("--score-variants", action="store_true",
@@ -638,6 +770,9 @@ def main():
         return
     if args.band_energy:
         band_energy(w, args)
+        return
+    if args.recompute_layers:
+        recompute_layers(w, args)
         return
 
     if args.copy_calib:

@@ -44,6 +44,7 @@ def lib():
         L.synth_chunk.argtypes = [u64, i32, i32, i32, i32, i32, i32, i32, i32, vp]
         L.synth_uniform_ints.argtypes = [u64, i32, i32, i32, i32, vp]
         L.synth_permutation.argtypes = [u64, i32, i32, vp]
+        L.synth_normal.argtypes = [u64, i32, C.c_longlong, f64, f64, i32, vp]
         _lib = L
     return _lib
 
@@ -100,4 +101,13 @@ def uniform_ints(seed: int, stream: int, n: int, lo: int, hi: int) -> np.ndarray
 def permutation(seed: int, stream: int, n: int) -> np.ndarray:
     out = np.zeros(n, np.int32)
     lib().synth_permutation(seed, stream, n, out.ctypes.data_as(C.c_void_p))
+    return out
+
+
+def normal(seed: int, stream: int, shape, dtype: str, mean: float = 0.0, sigma: float = 1.0) -> np.ndarray:
+    """i.i.d. N(mean, sigma^2) values of one stream, stored in dtype (weights,
+    gains and hidden rows of the recompute layer)."""
+    out = np.empty(shape, dtype=_np(dtype))
+    lib().synth_normal(seed, stream, out.size, float(mean), float(sigma), _code(dtype),
+                       out.ctypes.data_as(C.c_void_p))
     return out

@@ -28,7 +28,7 @@
 #define SY_BF16 1
 
 enum { TAG_SIN = 11, TAG_NOISE = 12, TAG_SPIKE = 13, TAG_EXTRA = 14, TAG_INTS = 15,
-       TAG_PERM = 16 };
+       TAG_PERM = 16, TAG_NORMAL = 17 };
 
 static inline uint64_t sm64(uint64_t z) {
   z += 0x9E3779B97F4A7C15ULL;
@@ -207,4 +207,15 @@ void synth_permutation(uint64_t seed, int stream, int n, int* out) {
     if (j > i) j = i;
     int t = out[i]; out[i] = out[j]; out[j] = t;
   }
+}
+
+/* n i.i.d. N(mean, sigma^2) values of stream `stream` (element i from the
+ * counter-based hash of (seed, stream, i)), stored in dtype.  Synthetic
+ * weights, gains and hidden rows of the recompute layer. */
+void synth_normal(uint64_t seed, int stream, long long n, double mean, double sigma, int dtype,
+                  void* out) {
+#pragma omp parallel for schedule(static)
+  for (long long i = 0; i < n; ++i)
+    put(out, dtype, (size_t)i, mean + sigma * normal_from(hkey(seed, TAG_NORMAL, (uint64_t)stream,
+                                                                (uint64_t)i, 0, 0, 0)));
 }

@@ -67,3 +67,15 @@ def test_lengths_and_orders(syn):
     assert n.min() >= 512 and n.max() <= 4096 and len(set(n.tolist())) > 50
     p = syn.permutation(20260523, 0, 16)
     assert sorted(p.tolist()) == list(range(16)) and p.tolist() != list(range(16))
+
+
+def test_normal_stream(syn):
+    a = syn.normal(5, 2, (300, 40), "f32", mean=1.0, sigma=0.5)
+    b = syn.normal(5, 2, (300, 40), "f32", mean=1.0, sigma=0.5)
+    np.testing.assert_array_equal(a, b)  # counter-based: same seed and stream, same values
+    assert not np.array_equal(a, syn.normal(5, 3, (300, 40), "f32", mean=1.0, sigma=0.5))
+    assert abs(a.mean() - 1.0) < 0.01 and abs(a.std() - 0.5) < 0.01
+    h = syn.normal(5, 2, (300, 40), "bf16", mean=1.0, sigma=0.5)
+    assert h.dtype == np.uint16
+    w = (h.astype(np.uint32) << 16).view(np.float32)
+    assert np.abs(w - a).max() <= 2.0 ** -8 * np.abs(a).max()
