@@ -633,7 +633,6 @@ class RecomputeLayers:
         self.vr = torch.empty((n_q, H * D), dtype=bf, device="cuda")
         self.gu = torch.empty((n_q, 2 * f), dtype=bf, device="cuda")
         self.a = torch.empty((n_q, f), dtype=bf, device="cuda")
-        self.lin_ws = torch.empty(self.ct.cachetune_linear_ws(), dtype=torch.uint8, device="cuda")
         # rows of each chunk's selected tokens in qpos order (chunk ranges are disjoint)
         self.row0 = [int(np.searchsorted(w.qpos_host, w.offsets[b])) for b in range(len(w.ns))]
         self._places = {}
@@ -655,7 +654,7 @@ class RecomputeLayers:
     def layer(self, l):
         w, ct = self.w, self.ct
         n_q, H, Hq, D = w.n_q, w.H, w.Hq, w.D
-        lin = lambda x, wt, out, res=None: ct.cachetune_linear(x, wt, residual=res, out=out, ws=self.lin_ws)  # noqa: E731
+        lin = lambda x, wt, out, res=None: ct.cachetune_linear(x, wt, residual=res, out=out)  # noqa: E731
         ct.cachetune_rmsnorm(self.h, self.g1, 1e-5, out=self.x)
         lin(self.x, self.wq, self.q)
         lin(self.x, self.wk, self.kr)

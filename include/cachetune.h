@@ -207,22 +207,19 @@ ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_
  * cachetune_silu_mul: out[r][j] = silu(gu[r][j]) * gu[r][ff + j] with
  *   silu(g) = g / (1 + exp(-g)) (fp32).  gate_up: [rows][2 ff]; out: [rows][ff];
  *   ff a multiple of 8; 16-byte aligned.
- * cachetune_linear: out[i][j] = sum_k x[i][k] w[j][k] (+ residual[i][j]) with
- *   fp32 accumulation (hipBLASLt; the library keeps one handle per device,
- *   created on the first call there).  x: [m][k]; w: [n][k] (the usual
- *   [out][in] weight layout); residual: [m][n] or NULL (may equal out);
- *   out: [m][n].  n, k multiples of 8; 16-byte aligned.  ws: device workspace
- *   of cachetune_linear_ws bytes, 256-aligned, not shared by concurrent calls.
+ * cachetune_linear: out[i][j] = sum_k x[i][k] w[j][k] (+ residual[i][j]) on the
+ *   matrix cores (bf16 products, fp32 accumulation, the residual added before
+ *   the one rounding).  x: [m][k]; w: [n][k] (the usual [out][in] weight
+ *   layout); residual: [m][n] or NULL (may equal out); out: [m][n].  n, k
+ *   multiples of 8, k below 4 194 304; 16-byte aligned.  No workspace.
  * Errors: CT_E_INVALID (shapes, NULL, alignment), CT_E_UNSUPPORTED (dtype other
- * than bf16), CT_E_WORKSPACE, CT_E_HIP.  Asynchronous on `stream`. */
+ * than bf16, sizes past the stated limits), CT_E_HIP.  Asynchronous on `stream`. */
 ct_status cachetune_rmsnorm(const void* x, const void* gain, int32_t rows, int32_t dim, float eps,
                             ct_dtype dtype, void* out, hipStream_t stream);
 ct_status cachetune_silu_mul(const void* gate_up, int32_t rows, int32_t ff, ct_dtype dtype, void* out,
                              hipStream_t stream);
-ct_status cachetune_linear_ws(size_t* bytes);
 ct_status cachetune_linear(const void* x, const void* w, const void* residual, int32_t m, int32_t n,
-                           int32_t k, ct_dtype dtype, void* out, void* ws, size_t ws_bytes,
-                           hipStream_t stream);
+                           int32_t k, ct_dtype dtype, void* out, hipStream_t stream);
 
 /* ---- selection (App. B.1) -------------------------------------------------
  * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].

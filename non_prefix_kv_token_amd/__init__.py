@@ -48,7 +48,7 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
-           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear_ws", "cachetune_linear"]
+           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -91,8 +91,7 @@ def lib():
         L.cachetune_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.cachetune_rmsnorm.argtypes = [vp, vp, i32, i32, f32, i32, vp, vp]
         L.cachetune_silu_mul.argtypes = [vp, i32, i32, i32, vp, vp]
-        L.cachetune_linear_ws.argtypes = [C.POINTER(sz)]
-        L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -223,13 +222,7 @@ def cachetune_silu_mul(gate_up, out=None, stream=None):
     return out
 
 
-def cachetune_linear_ws() -> int:
-    out = C.c_size_t(0)
-    _check(lib().cachetune_linear_ws(C.byref(out)))
-    return out.value
-
-
-def cachetune_linear(x, w, residual=None, out=None, ws=None, stream=None):
+def cachetune_linear(x, w, residual=None, out=None, stream=None):
     """x: [m][k], w: [n][k] bf16 device tensors; residual [m][n] or None.
     Returns x w^T (+ residual) as [m][n] bf16."""
     import torch
@@ -237,11 +230,8 @@ def cachetune_linear(x, w, residual=None, out=None, ws=None, stream=None):
     n = int(w.shape[0])
     if out is None:
         out = torch.empty((m, n), dtype=x.dtype, device=x.device)
-    need = cachetune_linear_ws()
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(lib().cachetune_linear(_ptr(x), _ptr(w), _ptr(residual), m, n, k, _dtype(x), _ptr(out),
-                                  _ptr(ws), ws.numel(), _stream(stream)))
+                                  _stream(stream)))
     return out
 
 

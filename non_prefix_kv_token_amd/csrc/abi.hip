@@ -253,28 +253,18 @@ ct_status cachetune_silu_mul(const void* gate_up, int32_t rows, int32_t ff, ct_d
   CT_GUARD_END
 }
 
-ct_status cachetune_linear_ws(size_t* bytes) {
-  CT_GUARD_BEGIN
-  if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
-  *bytes = kLinearWs;
-  return CT_OK;
-  CT_GUARD_END
-}
-
 ct_status cachetune_linear(const void* x, const void* w, const void* residual, int32_t m, int32_t n,
-                           int32_t k, ct_dtype dtype, void* out, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
+                           int32_t k, ct_dtype dtype, void* out, hipStream_t stream) {
   CT_GUARD_BEGIN
   if (dtype != CT_BF16) return fail(CT_E_UNSUPPORTED, "linear takes bf16 operands");
   if (m < 0 || n < 1 || k < 1) return fail(CT_E_INVALID, "m must be non-negative, n and k positive");
   if (n % 8 != 0 || k % 8 != 0) return fail(CT_E_INVALID, "n and k must be multiples of 8");
+  if ((long long)k * 256 * 2 >= (1LL << 31)) return fail(CT_E_UNSUPPORTED, "k above 4 194 303");
   if (m > 0 && (!x || !w || !out)) return fail(CT_E_INVALID, "NULL argument");
   if (m > 0 && (!aligned16(x) || !aligned16(w) || !aligned16(out) || (residual && !aligned16(residual))))
     return fail(CT_E_INVALID, "operands must be 16-byte aligned");
-  if (!ws || ws_bytes < kLinearWs)
-    return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(kLinearWs) + " bytes required");
-  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
-  return linear_run(x, w, residual, m, n, k, out, ws, kLinearWs, stream);
+  if ((long long)(m + 127) / 128 > 65535) return fail(CT_E_UNSUPPORTED, "m above 8 388 480");
+  return linear_run(x, w, residual, m, n, k, out, stream);
   CT_GUARD_END
 }
 

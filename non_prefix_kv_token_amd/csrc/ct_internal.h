@@ -163,8 +163,7 @@ ct_status rmsnorm_run(const void* x, const void* g, int rows, int dim, float eps
                       hipStream_t stream);
 ct_status silu_mul_run(const void* gu, int rows, int ff, void* out, hipStream_t stream);
 ct_status linear_run(const void* x, const void* w, const void* residual, int m, int n, int k, void* out,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
-constexpr size_t kLinearWs = size_t(32) << 20;  // hipBLASLt workspace offered per call
+                     hipStream_t stream);
 
 // ------------------------------------------------------------- host tier
 ct_status rank_order_run(const void* k_src, const void* v_src, const int32_t* ranking, int32_t n,

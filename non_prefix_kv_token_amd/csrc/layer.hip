@@ -5,16 +5,9 @@
 // hidden rows, projects them to q / k / v, projects the attention output back
 // with a residual, and applies the gated MLP of the models of Sec. 5.1.
 //
-// RMSNorm and the gated activation are HBM-bound row kernels written here.
-// The projections are plain bf16 GEMMs with fp32 accumulation; they go to
-// hipBLASLt (one handle per device, created on first use and kept until the
-// process ends), with the residual folded in as D = X W^T + R (beta = 1).
-#include <hipblaslt/hipblaslt.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
-
+// RMSNorm and the gated activation are HBM-bound row kernels; the projections
+// are bf16 GEMMs on the matrix cores with the residual added before the single
+// rounding of each output.
 #include "ct_internal.h"
 
 namespace ct {
@@ -89,64 +82,123 @@ __global__ __launch_bounds__(256) void k_silu_mul(const uint16_t* gu, int rows, 
   *reinterpret_cast<u32x4_t*>(out + m * ff + j) = o;
 }
 
-// ---- projections on hipBLASLt ---------------------------------------------------
-// Row-major Y[m][n] = X[m][k] W[n][k]^T (+ R[m][n]) is, in hipBLASLt's
-// column-major terms, Y^T (n x m) = op_T(W as k x n) * (X as k x m): a "TN"
-// product with leading dimensions k, k and n.
-struct Plan {
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
-  size_t ws_need = 0;
-};
+// ---- projections on the matrix cores ---------------------------------------------
+// out[m][n] = sum_k x[m][k] w[n][k] (+ res[m][n]), bf16 operands (products exact
+// in fp32), fp32 accumulation, one rounding to bf16 at the end (after the
+// residual is added).  Block tile 128 (m) x 256 (n), four waves of 64 x 128
+// (2 x 4 tiles of v_mfma_f32_32x32x16_bf16), k in stages of 32: each stage's
+// x and w slabs are loaded into registers one stage ahead with buffer loads
+// (rows past m or n and k past K read as zeros), written to the other of two
+// padded LDS buffers after the current stage's products, one barrier per stage.
+constexpr int kGBM = 128, kGBN = 256, kGBK = 32;
+constexpr int kGLD = kGBK + 8;  // LDS row stride in bf16 (80 bytes: conflict-free 16-byte reads)
 
-std::mutex g_blas_mu;
-hipblasLtHandle_t g_handle[64] = {};
-std::map<std::tuple<int, int, int, int, size_t>, Plan> g_plans[64];
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-ct_status blas_fail(hipblasStatus_t st, const char* what) {
-  return fail(CT_E_HIP, std::string("hipBLASLt ") + what + " failed (status " + std::to_string((int)st) + ")");
-}
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                 const uint16_t* res, uint16_t* out, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kGBM * kGLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kGBN * kGLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
+  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+  const int mrows = min(kGBM, M - m0), nrows = min(kGBN, N - n0);
+  // resources start at the block's first row; a load at or past num_records reads 0
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + (size_t)m0 * K), 0, mrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w + (size_t)n0 * K), 0, nrows * K * 2, 0x00020000);
+  const int xlim = mrows * K * 2, wlim = nrows * K * 2;
+  // staging: the x slab is 128 rows x 4 vectors of 8, the w slab 256 x 4
+  int xo[2], wo[4], xl[2], wl[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + 256 * i, r = v >> 2, q = v & 3;
+    xo[i] = (r * K + 8 * q) * 2;
+    xl[i] = r * kGLD + 8 * q;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = tid + 256 * i, r = v >> 2, q = v & 3;
+    wo[i] = (r * K + 8 * q) * 2;
+    wl[i] = r * kGLD + 8 * q;
+  }
+  u32x4_t xs[2], ws[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = (tid + 256 * i) & 3;
+      const int off = k0 + 8 * q < K ? xo[i] + k0 * 2 : xlim;  // k past K: zeros
+      xs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = (tid + 256 * i) & 3;
+      const int off = k0 + 8 * q < K ? wo[i] + k0 * 2 : wlim;
+      ws[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(&sa[buf][xl[i]]) = xs[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&sb[buf][wl[i]]) = ws[i];
+  };
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kGBK / 16; ++ks) {
+      bf16x8_t a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][(wm + 32 * i + col) * kGLD + 16 * ks + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(wn + 32 * j + col) * kGLD + 16 * ks + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
 
-ct_status get_plan(int dev, int m, int n, int k, size_t ws_bytes, const Plan** out) {
-  std::lock_guard<std::mutex> lock(g_blas_mu);
-  if (!g_handle[dev]) {
-    hipblasStatus_t st = hipblasLtCreate(&g_handle[dev]);
-    if (st != HIPBLAS_STATUS_SUCCESS) {
-      g_handle[dev] = nullptr;
-      return blas_fail(st, "handle creation");
+  const int nk = (K + kGBK - 1) / kGBK;
+  load(0);
+  store(0);
+  if (nk > 1) load(kGBK);
+  for (int s = 0; s < nk; ++s) {
+    __syncthreads();
+    compute(s & 1);
+    if (s + 1 < nk) {
+      store((s + 1) & 1);
+      if (s + 2 < nk) load((s + 2) * kGBK);
     }
   }
-  auto key = std::make_tuple(m, n, k, 0, ws_bytes);
-  auto it = g_plans[dev].find(key);
-  if (it != g_plans[dev].end()) {
-    *out = &it->second;
-    return CT_OK;
-  }
-  Plan p;
-  hipblasStatus_t st = hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F);
-  if (st != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "descriptor");
-  const hipblasOperation_t tA = HIPBLAS_OP_T, tB = HIPBLAS_OP_N;
-  hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &tA, sizeof(tA));
-  hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tB, sizeof(tB));
-  if ((st = hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, k, n, k)) != HIPBLAS_STATUS_SUCCESS ||
-      (st = hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, k, m, k)) != HIPBLAS_STATUS_SUCCESS ||
-      (st = hipblasLtMatrixLayoutCreate(&p.c, HIP_R_16BF, n, m, n)) != HIPBLAS_STATUS_SUCCESS)
-    return blas_fail(st, "layout");
-  hipblasLtMatmulPreference_t pref = nullptr;
-  if ((st = hipblasLtMatmulPreferenceCreate(&pref)) != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "preference");
-  const uint64_t cap = ws_bytes;
-  hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
-  hipblasLtMatmulHeuristicResult_t res[1];
-  int got = 0;
-  st = hipblasLtMatmulAlgoGetHeuristic(g_handle[dev], p.op, p.a, p.b, p.c, p.c, pref, 1, res, &got);
-  hipblasLtMatmulPreferenceDestroy(pref);
-  if (st != HIPBLAS_STATUS_SUCCESS || got < 1) return blas_fail(st, "algorithm selection");
-  p.algo = res[0].algo;
-  p.ws_need = res[0].workspaceSize;
-  auto ins = g_plans[dev].emplace(key, p);
-  *out = &ins.first->second;
-  return CT_OK;
+
+  // lane holds n = n0 + wn + 32 j + col and m = m0 + wm + 32 i + 8 (v / 4) + 4 g + v % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 32 * j + col;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m >= M) continue;
+        float val = acc[i][j][v];
+        if (res) val += __uint_as_float(((uint32_t)res[(size_t)m * N + n]) << 16);
+        out[(size_t)m * N + n] = (uint16_t)bf16_rne(val);
+      }
+    }
 }
 
 }  // namespace
@@ -171,18 +223,13 @@ ct_status silu_mul_run(const void* gu, int rows, int ff, void* out, hipStream_t 
 }
 
 ct_status linear_run(const void* x, const void* w, const void* residual, int m, int n, int k, void* out,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
+                     hipStream_t stream) {
   if (m == 0) return CT_OK;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(CT_E_HIP, "no current device");
-  const Plan* p = nullptr;
-  if (ct_status s = get_plan(dev, m, n, k, ws_bytes, &p)) return s;
-  const float alpha = 1.0f, beta = residual ? 1.0f : 0.0f;
   TimedLaunch tl_("linear", stream);
-  hipblasStatus_t st = hipblasLtMatmul(g_handle[dev], p->op, &alpha, w, p->a, x, p->b, &beta,
-                                       residual ? residual : out, p->c, out, p->c, &p->algo, ws,
-                                       ws_bytes, stream);
-  if (st != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "matmul");
+  dim3 grid((n + kGBN - 1) / kGBN, (m + kGBM - 1) / kGBM);
+  hipLaunchKernelGGL(k_gemm_bf16, grid, dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(x),
+                     reinterpret_cast<const uint16_t*>(w), reinterpret_cast<const uint16_t*>(residual),
+                     reinterpret_cast<uint16_t*>(out), m, n, k);
   return check_launch("linear");
 }
 

@@ -166,11 +166,8 @@ def test_layer_calls_reject_bad_arguments(lib):
     assert lib.cachetune_rmsnorm(C.c_void_p(4098), fake, 4, 64, C.c_float(1e-5), ct.CT_BF16, fake,
                                  None) == ct.CT_E_INVALID
     assert lib.cachetune_silu_mul(fake, 3, 12, ct.CT_BF16, fake, None) == ct.CT_E_INVALID
-    out = C.c_size_t(0)
-    assert lib.cachetune_linear_ws(C.byref(out)) == ct.CT_OK and out.value >= 1 << 20
-    assert lib.cachetune_linear(fake, fake, None, 4, 12, 64, ct.CT_BF16, fake, fake, out.value,
+    assert lib.cachetune_linear(fake, fake, None, 4, 12, 64, ct.CT_BF16, fake, None) == ct.CT_E_INVALID
+    assert lib.cachetune_linear(fake, fake, None, 4, 16, 64, ct.CT_F32, fake, None) == ct.CT_E_UNSUPPORTED
+    assert lib.cachetune_linear(None, fake, None, 4, 16, 64, ct.CT_BF16, fake, None) == ct.CT_E_INVALID
+    assert lib.cachetune_linear(fake, fake, C.c_void_p(4100), 4, 16, 64, ct.CT_BF16, fake,
                                 None) == ct.CT_E_INVALID
-    assert lib.cachetune_linear(fake, fake, None, 4, 16, 64, ct.CT_BF16, fake, None, 0,
-                                None) == ct.CT_E_WORKSPACE
-    assert lib.cachetune_linear(fake, fake, None, 4, 16, 64, ct.CT_F32, fake, fake, out.value,
-                                None) == ct.CT_E_UNSUPPORTED

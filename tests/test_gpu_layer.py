@@ -53,16 +53,18 @@ def test_silu_mul(orc, rows, ff):
 
 
 @pytest.mark.parametrize("m,n,k,res", [(77, 256, 512, True), (3, 8, 8, False), (130, 1024, 4096, False),
-                                       (2584, 1024, 4096, True)])
-def test_linear(orc, m, n, k, res):
+                                       (2584, 1024, 4096, True), (200, 264, 40, True),
+                                       # the 8 x 2048 workload's gate/up and down projections
+                                       (2584, 28672, 4096, False), (2584, 4096, 14336, True)])
+def test_linear(orc, syn, m, n, k, res):
     """Bias-free projection with fp32 accumulation: each output within half a
     bf16 ulp of the exact sum plus 2^-16 of sum_k |x_k w_k| (fp32 accumulation
     error, with room over its random-walk size and under its worst case
     k 2^-24).  Large shapes are checked on sampled rows."""
     ct = need_gpu()
     rng = np.random.default_rng(m + n + k)
-    x = _bf16(orc, rng.standard_normal((m, k)))
-    w = _bf16(orc, rng.standard_normal((n, k)) / math.sqrt(k))
+    x = syn.normal(m + n, 1, (m, k), "bf16")
+    w = syn.normal(m + n, 2, (n, k), "bf16", sigma=1.0 / math.sqrt(k))
     r = _bf16(orc, rng.standard_normal((m, n))) if res else None
     out = ct.cachetune_linear(to_dev(x), to_dev(w), to_dev(r) if res else None)
     torch.cuda.synchronize()
