@@ -616,9 +616,8 @@ class RecomputeLayers:
         t0 = time.time()
         gen = lambda stream, shape, sigma, mean=0.0: _dev(syn.normal(seed, stream, shape, "bf16", mean, sigma))  # noqa: E731
         self.g1, self.g2 = gen(1, (d,), 0.1, 1.0), gen(2, (d,), 0.1, 1.0)
-        self.wq = gen(3, (Hq * D, d), d ** -0.5)
-        self.wk = gen(4, (H * D, d), d ** -0.5)
-        self.wv = gen(5, (H * D, d), d ** -0.5)
+        # q, k and v weights stacked by rows for the fused projection
+        self.wqkv = gen(3, ((Hq + 2 * H) * D, d), d ** -0.5)
         self.wo = gen(6, (d, Hq * D), (Hq * D) ** -0.5)
         self.wgu = gen(7, (2 * f, d), d ** -0.5)
         self.wd = gen(8, (d, f), f ** -0.5)
@@ -656,9 +655,7 @@ class RecomputeLayers:
         n_q, H, Hq, D = w.n_q, w.H, w.Hq, w.D
         lin = lambda x, wt, out, res=None: ct.cachetune_linear(x, wt, residual=res, out=out)  # noqa: E731
         ct.cachetune_rmsnorm(self.h, self.g1, 1e-5, out=self.x)
-        lin(self.x, self.wq, self.q)
-        lin(self.x, self.wk, self.kr)
-        lin(self.x, self.wv, self.vr)
+        ct.cachetune_qkv_proj(self.x, self.wqkv, Hq * D, H * D, q=self.q, k=self.kr, v=self.vr)
         s0 = n_q - w.n_sfx
         ct.cachetune_assemble_rope(self.places(l), w.k_asm, w.v_asm, H, D, w.theta,
                                    k_sfx=self.kr[s0:].view(w.n_sfx, H, D), v_sfx=self.vr[s0:].view(w.n_sfx, H, D),

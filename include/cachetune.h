@@ -212,6 +212,11 @@ ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_
  *   the one rounding).  x: [m][k]; w: [n][k] (the usual [out][in] weight
  *   layout); residual: [m][n] or NULL (may equal out); out: [m][n].  n, k
  *   multiples of 8, k below 4 194 304; 16-byte aligned.  No workspace.
+ * cachetune_qkv_proj: the fused q / k / v projection of the rows: one product
+ *   with w_qkv = [wq; wk; wv] ([nq + 2 nkv][d], the three weights stacked by
+ *   rows), its output columns split into q_out [m][nq], k_out [m][nkv] and
+ *   v_out [m][nkv] (each a plain row-major buffer, as the assembly and the
+ *   attention take them).  Arithmetic as cachetune_linear, no residual.
  * Errors: CT_E_INVALID (shapes, NULL, alignment), CT_E_UNSUPPORTED (dtype other
  * than bf16, sizes past the stated limits), CT_E_HIP.  Asynchronous on `stream`. */
 ct_status cachetune_rmsnorm(const void* x, const void* gain, int32_t rows, int32_t dim, float eps,
@@ -220,6 +225,9 @@ ct_status cachetune_silu_mul(const void* gate_up, int32_t rows, int32_t ff, ct_d
                              hipStream_t stream);
 ct_status cachetune_linear(const void* x, const void* w, const void* residual, int32_t m, int32_t n,
                            int32_t k, ct_dtype dtype, void* out, hipStream_t stream);
+ct_status cachetune_qkv_proj(const void* x, const void* w_qkv, int32_t m, int32_t d, int32_t nq,
+                             int32_t nkv, ct_dtype dtype, void* q_out, void* k_out, void* v_out,
+                             hipStream_t stream);
 
 /* ---- selection (App. B.1) -------------------------------------------------
  * Per chunk of n scores: k = floor(r * n) with r = r_num / r_den in [0, 1].

@@ -48,7 +48,7 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
-           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear"]
+           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -92,6 +92,7 @@ def lib():
         L.cachetune_rmsnorm.argtypes = [vp, vp, i32, i32, f32, i32, vp, vp]
         L.cachetune_silu_mul.argtypes = [vp, i32, i32, i32, vp, vp]
         L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        L.cachetune_qkv_proj.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in SYMBOLS[3:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -233,6 +234,20 @@ def cachetune_linear(x, w, residual=None, out=None, stream=None):
     _check(lib().cachetune_linear(_ptr(x), _ptr(w), _ptr(residual), m, n, k, _dtype(x), _ptr(out),
                                   _stream(stream)))
     return out
+
+
+def cachetune_qkv_proj(x, w_qkv, nq, nkv, q=None, k=None, v=None, stream=None):
+    """x: [m][d]; w_qkv: [nq + 2 nkv][d] (wq, wk, wv stacked).  Returns the
+    q [m][nq], k [m][nkv], v [m][nkv] bf16 tensors."""
+    import torch
+    m, d = int(x.shape[0]), int(x.shape[1])
+    mk = lambda n: torch.empty((m, n), dtype=x.dtype, device=x.device)  # noqa: E731
+    q = mk(nq) if q is None else q
+    k = mk(nkv) if k is None else k
+    v = mk(nkv) if v is None else v
+    _check(lib().cachetune_qkv_proj(_ptr(x), _ptr(w_qkv), m, d, nq, nkv, _dtype(x), _ptr(q), _ptr(k), _ptr(v),
+                                    _stream(stream)))
+    return q, k, v
 
 
 # ---- selection ----------------------------------------------------------------

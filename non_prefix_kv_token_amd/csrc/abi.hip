@@ -268,6 +268,23 @@ ct_status cachetune_linear(const void* x, const void* w, const void* residual, i
   CT_GUARD_END
 }
 
+ct_status cachetune_qkv_proj(const void* x, const void* w_qkv, int32_t m, int32_t d, int32_t nq,
+                             int32_t nkv, ct_dtype dtype, void* q_out, void* k_out, void* v_out,
+                             hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (dtype != CT_BF16) return fail(CT_E_UNSUPPORTED, "qkv_proj takes bf16 operands");
+  if (m < 0 || d < 1 || nq < 1 || nkv < 1) return fail(CT_E_INVALID, "m must be non-negative, d, nq, nkv positive");
+  if (d % 8 != 0 || nq % 8 != 0 || nkv % 8 != 0) return fail(CT_E_INVALID, "d, nq and nkv must be multiples of 8");
+  if ((long long)d * 256 * 2 >= (1LL << 31)) return fail(CT_E_UNSUPPORTED, "d above 4 194 303");
+  if ((long long)nq + 2LL * nkv > (1LL << 30)) return fail(CT_E_UNSUPPORTED, "nq + 2 nkv too large");
+  if ((long long)(m + 127) / 128 > 65535) return fail(CT_E_UNSUPPORTED, "m above 8 388 480");
+  if (m > 0 && (!x || !w_qkv || !q_out || !k_out || !v_out)) return fail(CT_E_INVALID, "NULL argument");
+  if (m > 0 && (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out)))
+    return fail(CT_E_INVALID, "operands must be 16-byte aligned");
+  return qkv_run(x, w_qkv, m, d, nq, nkv, q_out, k_out, v_out, stream);
+  CT_GUARD_END
+}
+
 ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
                                 int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
                                 int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {

@@ -164,6 +164,8 @@ ct_status rmsnorm_run(const void* x, const void* g, int rows, int dim, float eps
 ct_status silu_mul_run(const void* gu, int rows, int ff, void* out, hipStream_t stream);
 ct_status linear_run(const void* x, const void* w, const void* residual, int m, int n, int k, void* out,
                      hipStream_t stream);
+ct_status qkv_run(const void* x, const void* w_qkv, int m, int d, int nq, int nkv, void* q, void* k, void* v,
+                  hipStream_t stream);
 
 // ------------------------------------------------------------- host tier
 ct_status rank_order_run(const void* k_src, const void* v_src, const int32_t* ranking, int32_t n,

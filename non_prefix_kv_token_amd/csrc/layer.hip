@@ -85,120 +85,138 @@ __global__ __launch_bounds__(256) void k_silu_mul(const uint16_t* gu, int rows, 
 // ---- projections on the matrix cores ---------------------------------------------
 // out[m][n] = sum_k x[m][k] w[n][k] (+ res[m][n]), bf16 operands (products exact
 // in fp32), fp32 accumulation, one rounding to bf16 at the end (after the
-// residual is added).  Block tile 128 (m) x 256 (n), four waves of 64 x 128
-// (2 x 4 tiles of v_mfma_f32_32x32x16_bf16), k in stages of 32: each stage's
-// x and w slabs are loaded into registers one stage ahead with buffer loads
-// (rows past m or n and k past K read as zeros), written to the other of two
-// padded LDS buffers after the current stage's products, one barrier per stage.
-constexpr int kGBM = 128, kGBN = 256, kGBK = 32;
-constexpr int kGLD = kGBK + 8;  // LDS row stride in bf16 (80 bytes: conflict-free 16-byte reads)
+// residual is added).  A block computes a BM x BN tile with WGM x WGN waves,
+// each a (BM / WGM) x (BN / WGN) tile of v_mfma_f32_32x32x16_bf16 tiles; k
+// advances in stages of 32.  Each stage's x and w slabs are loaded into
+// registers one stage ahead with buffer loads (rows past m or n and k past K
+// read as zeros) and written to the other of two LDS buffers after the current
+// stage's products: one barrier per stage.  An LDS row is 32 k (four 16-byte
+// chunks); chunk c of row r sits at chunk c ^ ((r / 4) % 4), so that both the
+// row-major slab writes and the operand reads (one row per lane) hit 16
+// distinct 4-bank groups per 16 lanes.  The output columns may be split over
+// three destinations (q | k | v of the fused projection): columns [0, n1) go
+// to out0 (row length n1), [n1, n2) to out1, [n2, N) to out2.
+constexpr int kGBK = 32;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int BM, int BN, int WGM, int WGN, int PF>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                 const uint16_t* res, uint16_t* out, int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kGBM * kGLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kGBN * kGLD];
+                 const uint16_t* res, uint16_t* out0, uint16_t* out1, uint16_t* out2, int n1, int n2,
+                 int M, int N, int K) {
+  constexpr int NT = 64 * WGM * WGN;                        // threads
+  constexpr int TI = BM / WGM / 32, TJ = BN / WGN / 32;     // MFMA tiles per wave
+  constexpr int NX = BM * 4 / NT, NW = BN * 4 / NT;         // 16-byte vectors per thread and stage
+  static_assert(NX * NT == BM * 4 && NW * NT == BN * 4, "slab split");
+  static_assert(PF == 1, "prefetch depth");
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * kGBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * kGBK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
-  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  const int mrows = min(kGBM, M - m0), nrows = min(kGBN, N - n0);
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
+  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
   // resources start at the block's first row; a load at or past num_records reads 0
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x + (size_t)m0 * K), 0, mrows * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(w + (size_t)n0 * K), 0, nrows * K * 2, 0x00020000);
   const int xlim = mrows * K * 2, wlim = nrows * K * 2;
-  // staging: the x slab is 128 rows x 4 vectors of 8, the w slab 256 x 4
-  int xo[2], wo[4], xl[2], wl[4];
+  int xo[NX], wo[NW], xl[NX], wl[NW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int v = tid + 256 * i, r = v >> 2, q = v & 3;
+  for (int i = 0; i < NX; ++i) {
+    const int v = tid + NT * i, r = v >> 2, q = v & 3;
     xo[i] = (r * K + 8 * q) * 2;
-    xl[i] = r * kGLD + 8 * q;
+    xl[i] = r * kGBK + 8 * (q ^ ((r >> 2) & 3));
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + 256 * i, r = v >> 2, q = v & 3;
+  for (int i = 0; i < NW; ++i) {
+    const int v = tid + NT * i, r = v >> 2, q = v & 3;
     wo[i] = (r * K + 8 * q) * 2;
-    wl[i] = r * kGLD + 8 * q;
+    wl[i] = r * kGBK + 8 * (q ^ ((r >> 2) & 3));
   }
-  u32x4_t xs[2], ws[4];
-  auto load = [&](int k0) {
+  const int q8 = 8 * (tid & 3);  // k offset of this thread's vectors within a stage (NT is a multiple of 4)
+  u32x4_t xs0[NX], ws0[NW];
+  auto load = [&](int k0, u32x4_t* xs, u32x4_t* ws) {
+    const bool in = k0 + q8 < K;  // k past K: zeros
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = (tid + 256 * i) & 3;
-      const int off = k0 + 8 * q < K ? xo[i] + k0 * 2 : xlim;  // k past K: zeros
-      xs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
+    for (int i = 0; i < NX; ++i)
+      xs[i] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(xr, in ? xo[i] + k0 * 2 : xlim, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = (tid + 256 * i) & 3;
-      const int off = k0 + 8 * q < K ? wo[i] + k0 * 2 : wlim;
-      ws[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
-    }
+    for (int i = 0; i < NW; ++i)
+      ws[i] = __builtin_bit_cast(u32x4_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(wr, in ? wo[i] + k0 * 2 : wlim, 0, 0));
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const u32x4_t* xs, const u32x4_t* ws) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(&sa[buf][xl[i]]) = xs[i];
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4_t*>(&sa[buf][xl[i]]) = xs[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&sb[buf][wl[i]]) = ws[i];
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4_t*>(&sb[buf][wl[i]]) = ws[i];
   };
-  f32x16_t acc[2][4];
+  f32x16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int sw = (col >> 2) & 3;  // rows read by this lane are col mod 32
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kGBK / 16; ++ks) {
-      bf16x8_t a[2], b[4];
+      bf16x8_t a[TI], b[TJ];
+      const int ch = 8 * ((2 * ks + g) ^ sw);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][(wm + 32 * i + col) * kGLD + 16 * ks + 8 * g]);
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][(wm + 32 * i + col) * kGBK + ch]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(wn + 32 * j + col) * kGLD + 16 * ks + 8 * g]);
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(wn + 32 * j + col) * kGBK + ch]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   };
 
   const int nk = (K + kGBK - 1) / kGBK;
-  load(0);
-  store(0);
-  if (nk > 1) load(kGBK);
+  load(0, xs0, ws0);
+  store(0, xs0, ws0);
+  if (nk > 1) load(kGBK, xs0, ws0);
   for (int s = 0; s < nk; ++s) {
     __syncthreads();
     compute(s & 1);
     if (s + 1 < nk) {
-      store((s + 1) & 1);
-      if (s + 2 < nk) load((s + 2) * kGBK);
+      store((s + 1) & 1, xs0, ws0);
+      if (s + 2 < nk) load((s + 2) * kGBK, xs0, ws0);
     }
   }
 
   // lane holds n = n0 + wn + 32 j + col and m = m0 + wm + 32 i + 8 (v / 4) + 4 g + v % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < TJ; ++j) {
+    const int n = n0 + wn + 32 * j + col;
+    if (n >= N) continue;
+    uint16_t* dst = out0;
+    int ld = n1, c = n;
+    if (n >= n2) {
+      dst = out2; ld = N - n2; c = n - n2;
+    } else if (n >= n1) {
+      dst = out1; ld = n2 - n1; c = n - n1;
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + 32 * j + col;
-      if (n >= N) continue;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
         if (m >= M) continue;
         float val = acc[i][j][v];
         if (res) val += __uint_as_float(((uint32_t)res[(size_t)m * N + n]) << 16);
-        out[(size_t)m * N + n] = (uint16_t)bf16_rne(val);
+        dst[(size_t)m * ld + c] = (uint16_t)bf16_rne(val);
       }
-    }
+  }
 }
 
 }  // namespace
@@ -222,15 +240,45 @@ ct_status silu_mul_run(const void* gu, int rows, int ff, void* out, hipStream_t 
   return check_launch("silu_mul");
 }
 
-ct_status linear_run(const void* x, const void* w, const void* residual, int m, int n, int k, void* out,
-                     hipStream_t stream) {
+template <int BM, int BN, int WGM, int WGN, int PF>
+static void gemm_go(const void* x, const void* w, const void* residual, void* out0, void* out1, void* out2,
+                    int n1, int n2, int m, int n, int k, hipStream_t stream) {
+  dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, PF>), grid, dim3(64 * WGM * WGN), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                     reinterpret_cast<const uint16_t*>(residual), reinterpret_cast<uint16_t*>(out0),
+                     reinterpret_cast<uint16_t*>(out1), reinterpret_cast<uint16_t*>(out2), n1, n2, m, n, k);
+}
+
+// Tile choice by waves of blocks: a 256 x 256 block (8 waves, one per CU)
+// moves half the LDS bytes per product of a 128 x 256 block (4 waves, two per
+// CU), and one round of small blocks was measured at about 1.15 rounds of big
+// ones; the configuration with the fewer (weighted) rounds is taken, so a
+// product whose big-block count just passes a multiple of the CU count (the
+// fused q/k/v projection of 2584 rows: 264 blocks) uses small blocks.
+static ct_status gemm_launch(const void* x, const void* w, const void* residual, void* out0, void* out1,
+                             void* out2, int n1, int n2, int m, int n, int k, hipStream_t stream) {
   if (m == 0) return CT_OK;
   TimedLaunch tl_("linear", stream);
-  dim3 grid((n + kGBN - 1) / kGBN, (m + kGBM - 1) / kGBM);
-  hipLaunchKernelGGL(k_gemm_bf16, grid, dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(x),
-                     reinterpret_cast<const uint16_t*>(w), reinterpret_cast<const uint16_t*>(residual),
-                     reinterpret_cast<uint16_t*>(out), m, n, k);
+  const long long ncu = device_cu_count();
+  const long long big = (long long)((m + 255) / 256) * ((n + 255) / 256);
+  const long long small = (long long)((m + 127) / 128) * ((n + 255) / 256);
+  const double r_big = (double)((big + ncu - 1) / ncu), r_small = 1.15 * (double)((small + 2 * ncu - 1) / (2 * ncu));
+  if (r_big <= r_small)
+    gemm_go<256, 256, 4, 2, 1>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
+  else
+    gemm_go<128, 256, 2, 2, 1>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
   return check_launch("linear");
+}
+
+ct_status linear_run(const void* x, const void* w, const void* residual, int m, int n, int k, void* out,
+                     hipStream_t stream) {
+  return gemm_launch(x, w, residual, out, out, out, n, n, m, n, k, stream);
+}
+
+ct_status qkv_run(const void* x, const void* w_qkv, int m, int d, int nq, int nkv, void* q, void* k, void* v,
+                  hipStream_t stream) {
+  return gemm_launch(x, w_qkv, nullptr, q, k, v, nq, nq + nkv, m, nq + 2 * nkv, d, stream);
 }
 
 }  // namespace ct

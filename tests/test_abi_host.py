@@ -171,3 +171,5 @@ def test_layer_calls_reject_bad_arguments(lib):
     assert lib.cachetune_linear(None, fake, None, 4, 16, 64, ct.CT_BF16, fake, None) == ct.CT_E_INVALID
     assert lib.cachetune_linear(fake, fake, C.c_void_p(4100), 4, 16, 64, ct.CT_BF16, fake,
                                 None) == ct.CT_E_INVALID
+    assert lib.cachetune_qkv_proj(fake, fake, 4, 64, 12, 8, ct.CT_BF16, fake, fake, fake, None) == ct.CT_E_INVALID
+    assert lib.cachetune_qkv_proj(fake, fake, 4, 64, 16, 8, ct.CT_BF16, fake, None, fake, None) == ct.CT_E_INVALID

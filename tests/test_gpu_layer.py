@@ -76,6 +76,24 @@ def test_linear(orc, syn, m, n, k, res):
     _within_rounding(got[rows], exact, slack)
 
 
+@pytest.mark.parametrize("m,d,nq,nkv", [(2584, 4096, 4096, 1024), (45, 256, 256, 128), (3, 64, 16, 8)])
+def test_qkv_proj(orc, syn, m, d, nq, nkv):
+    """Fused q / k / v projection: one product with the stacked weights, its
+    columns split over three buffers; each against the oracle's projection."""
+    ct = need_gpu()
+    x = syn.normal(m + d, 3, (m, d), "bf16")
+    w = syn.normal(m + d, 4, (nq + 2 * nkv, d), "bf16", sigma=1.0 / math.sqrt(d))
+    q, k, v = ct.cachetune_qkv_proj(to_dev(x), to_dev(w), nq, nkv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(m)
+    rows = np.arange(m) if m <= 64 else np.sort(rng.choice(m, 48, replace=False))
+    xs = widen(x[rows])
+    for got, lo, hi in ((q, 0, nq), (k, nq, nq + nkv), (v, nq + nkv, nq + 2 * nkv)):
+        ws_ = widen(w[lo:hi])
+        exact = orc.linear(xs, ws_)
+        _within_rounding(to_host(got)[rows], exact, 2.0 ** -16 * (np.abs(xs) @ np.abs(ws_).T))
+
+
 def test_linear_in_place_residual(orc):
     ct = need_gpu()
     rng = np.random.default_rng(2)
