@@ -322,7 +322,12 @@ def host_tier(args):
     layer, the complement rows of the next layer are copied host -> device on a
     side stream while the compute stream assembles the current layer from the
     staging buffer and runs the selected-query attention.  Prints one JSON
-    line with the request time per r and the r that minimises it."""
+    line with the request time per r and the r that minimises it.  With
+    --full-layer every layer also runs the rest of the recompute layer on the
+    selected and suffix rows (RMSNorm, fused q/k/v projection whose k and v
+    rows feed the assembly, output projection, gated MLP; synthetic
+    Llama-3-8B-shaped weights shared by the layers), so the recompute cost t_c
+    of the calibration is that of the full layer."""
     import torch
     import non_prefix_kv_token_amd as ct
     import synth as syn
@@ -370,6 +375,15 @@ def host_tier(args):
     k_asm = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
     v_asm = torch.empty_like(k_asm)
     gen = torch.Generator(device="cuda")
+    full = args.full_layer
+    d_model, d_ff, wseed = Hq * D, 14336, 20260601
+    if full:
+        wgen = lambda stream, shape, sigma, mean=0.0: _dev(syn.normal(wseed, stream, shape, "bf16", mean, sigma))  # noqa: E731
+        g1, g2 = wgen(1, (d_model,), 0.1, 1.0), wgen(2, (d_model,), 0.1, 1.0)
+        wqkv = wgen(3, ((Hq + 2 * H) * D, d_model), d_model ** -0.5)
+        wo = wgen(6, (d_model, Hq * D), (Hq * D) ** -0.5)
+        wgu = wgen(7, (2 * d_ff, d_model), d_model ** -0.5)
+        wd = wgen(8, (d_model, d_ff), d_ff ** -0.5)
     results = []
     copy_stream = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
@@ -389,6 +403,8 @@ def host_tier(args):
             head = rank_h[offs[b]:offs[b] + ks[b]]
             order = np.argsort(head)
             sel_list.append(np.sort(head).astype(np.int32))
+            if full:
+                continue  # recomputed rows come from the layer's own projection
             perm = torch.from_numpy(order).cuda()
             lr = []
             for l in range(L):
@@ -403,7 +419,22 @@ def host_tier(args):
                                       [np.arange(T_c, T)])).astype(np.int32)
         n_q = len(qpos)
         qpos_d = _dev(qpos)
-        qs = [(2.0 * torch.randn((n_q, Hq, D), generator=gen, device="cuda")).bfloat16() for _ in range(L)]
+        if full:
+            bf = torch.bfloat16
+            mk = lambda n: torch.empty((n_q, n), dtype=bf, device="cuda")  # noqa: E731
+            h0 = _dev(syn.normal(wseed, 9, (n_q, d_model), "bf16"))
+            hb, h1b, xb = mk(d_model), mk(d_model), mk(d_model)
+            qb, krb, vrb = mk(Hq * D), mk(H * D), mk(H * D)
+            gub, ab = mk(2 * d_ff), mk(d_ff)
+            row0 = [int(np.searchsorted(qpos, offs[b])) for b in range(nb)]
+            rec = [[(krb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D), vrb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D))
+                    for _ in range(L)] for b in range(nb)]
+            qs = [qb.view(n_q, Hq, D)] * L
+            s0 = n_q - n_sfx
+            sfx_l = [(krb[s0:].view(n_sfx, H, D), vrb[s0:].view(n_sfx, H, D))] * L
+        else:
+            qs = [(2.0 * torch.randn((n_q, Hq, D), generator=gen, device="cuda")).bfloat16() for _ in range(L)]
+            sfx_l = sfx
         ws = torch.empty(max(256, ct.cachetune_recompute_attn_ws(n_q, Hq, T, H, D)), dtype=torch.uint8,
                          device="cuda")
         out = torch.empty((n_q, Hq, D), dtype=torch.bfloat16, device="cuda")
@@ -425,9 +456,14 @@ def host_tier(args):
         ev_free = [torch.cuda.Event(), torch.cuda.Event()]
         used = [False, False]
         state = [k_stage, v_stage, rec, qs, ws, out, places]
+        if full:
+            state += [h0, hb, h1b, xb, qb, krb, vrb, gub, ab]
 
         def request():
             ev_ready = [torch.cuda.Event() for _ in range(L)]
+            if full:
+                with torch.cuda.stream(comp):
+                    hb.copy_(h0)
             for l in range(L):
                 with torch.cuda.stream(copy_stream):
                     if used[l % 2]:
@@ -435,13 +471,22 @@ def host_tier(args):
                     ct.cachetune_stage_complement([(p[0], p[1]) for p in pool], l, ks, k_stage[l % 2],
                                                   v_stage[l % 2], stream=copy_stream)
                     ev_ready[l].record(copy_stream)
+                if full:  # the layer's own k / v rows for the selected and suffix tokens
+                    ct.cachetune_rmsnorm(hb, g1, 1e-5, out=xb, stream=comp)
+                    ct.cachetune_qkv_proj(xb, wqkv, Hq * D, H * D, q=qb, k=krb, v=vrb, stream=comp)
                 comp.wait_event(ev_ready[l])
-                ct.cachetune_assemble_rope(places[l], k_asm, v_asm, H, D, theta, k_sfx=sfx[l][0],
-                                           v_sfx=sfx[l][1], n_sfx=n_sfx, sfx_offset=T_c, stream=comp)
+                ct.cachetune_assemble_rope(places[l], k_asm, v_asm, H, D, theta, k_sfx=sfx_l[l][0],
+                                           v_sfx=sfx_l[l][1], n_sfx=n_sfx, sfx_offset=T_c, stream=comp)
                 ev_free[l % 2].record(comp)
                 used[l % 2] = True
                 ct.cachetune_recompute_attn(qs[l], qpos_d, k_asm, v_asm, scale, theta, out=out, ws=ws,
                                             stream=comp)
+                if full:
+                    ct.cachetune_linear(out.view(n_q, Hq * D), wo, residual=hb, out=h1b, stream=comp)
+                    ct.cachetune_rmsnorm(h1b, g2, 1e-5, out=xb, stream=comp)
+                    ct.cachetune_linear(xb, wgu, out=gub, stream=comp)
+                    ct.cachetune_silu_mul(gub, out=ab, stream=comp)
+                    ct.cachetune_linear(ab, wd, residual=h1b, out=hb, stream=comp)
 
         def release():
             state.clear()
@@ -451,7 +496,9 @@ def host_tier(args):
         return request, rows, n_q, release
 
     def measure(request, steps):
-        """Mean ms per request after one untimed request."""
+        """Mean ms per request after two untimed requests (the first request of
+        a ratio also pays for its buffers' first use)."""
+        request()
         request()
         torch.cuda.synchronize()
         a, z = E(), E()
@@ -520,10 +567,14 @@ def host_tier(args):
                   "selected-query attention, all layers",
         "unit": "ms per request", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
         "dtype": "bf16",
-        "data": "synthetic chunk K/V (seeded value model) in pinned host memory; recomputed rows = cached "
-                "rows + seeded N(0, 0.25^2); queries seeded N(0, 4)",
+        "data": ("synthetic chunk K/V (seeded value model) in pinned host memory; selected and suffix rows "
+                 "carry seeded N(0, 1) hidden states through synthetic layer weights") if full else
+                ("synthetic chunk K/V (seeded value model) in pinned host memory; recomputed rows = cached "
+                 "rows + seeded N(0, 0.25^2); queries seeded N(0, 4)"),
         "config": {"workload": "32 chunks x 2048 tokens, 32 layers, 32 Q / 8 KV heads x 128, bf16, "
-                               "host pool in rank order, r swept", "T": T},
+                               "host pool in rank order, r swept", "T": T,
+                   "recompute": ("full layer: RMSNorm, q/k/v, o-proj, gated MLP (hidden 4096, MLP 14336, "
+                                 "synthetic weights)") if full else "attention only"},
         "per_r": results, "r_star": best["r"], "pinned_h2d_GBs": copy_gbs,
         "r_min_quality_bound": "15/100",
         **({"calibration": calibration} if calibration else {}),
@@ -732,6 +783,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-tier", action="store_true",
                     help="run the 32 x 2048 host-tier pipeline with an r sweep instead")
+    ap.add_argument("--full-layer", action="store_true",
+                    help="with --host-tier: run the full recompute layer on the selected rows in every layer")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --host-tier: also run the warm-started golden-section search for r")
     ap.add_argument("--copy-calib", action="store_true",
