@@ -33,11 +33,26 @@ def _rows(path_or_dir: str, pattern: str):
     return out
 
 
+def short_name(name: str) -> str:
+    """Kernel name without its parameter list (the first '(' outside template
+    brackets)."""
+    name = name.replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
 def kernel_stats_table(stats_csv: str) -> str:
     rows = _rows(stats_csv, "*kernel_stats.csv")
     lines = ["| Kernel | Calls | Average (us) | Total (ms) | Share |", "|---|---:|---:|---:|---:|"]
     for r in rows:
-        name = r["Name"].replace("(anonymous namespace)::", "").split("(ct::")[0]
+        name = short_name(r["Name"])
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
     return "\n".join(lines)
