@@ -215,6 +215,18 @@ class Workload:
         esz = 2 if self.dtype == "bf16" else 4
         return float(sum(self.ns)) * self.L * 2 * self.H * self.D * esz  # one read of K and V
 
+    def band_mfma_flops(self) -> float:
+        """Matrix-core flops the band projection issues per step: per (chunk,
+        layer, K|V), the padded band rows x the padded tokens x the channels x 2,
+        three twiddle planes (bf16 data) or six products (fp32 data)."""
+        flops = 0.0
+        for n in self.ns:
+            nb = n // 2 + 1
+            kk = min(nb, max(1, (self.alpha[0] * nb) // self.alpha[1]))
+            ppad = -(-2 * kk // 32) * 32
+            flops += self.L * 2 * ppad * (-(-n // 32) * 32) * self.H * self.D * 2 * (3 if self.dtype == "bf16" else 6)
+        return flops
+
     def assemble_bytes_per_layer(self) -> float:
         esz = 2 if self.dtype == "bf16" else 4
         row = self.H * self.D * esz
@@ -272,10 +284,17 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
     t_attn = t_attn_sample / frac * L
     t_step = t_score + t_topr + t_asm_layer * L + t_attn
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": sum(w.ns) / t_step,
         "unit": "chunk-KV tokens/s",
         "cores": threads,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": (f"score: 1 chunk x {budget_layers} of {L} layers, scaled x{L // budget_layers} layers "
                    f"x{len(w.ns)} chunks; top-r: all chunks; assembly: layer 0, scaled x{L}; "
@@ -872,6 +891,22 @@ def main():
     score_gbs = w.score_bytes() / (score_ms * 1e-3) / 1e9
     asm_gbs = w.assemble_bytes_per_layer() / (asm_ms * 1e-3) / 1e9
     traffic = measured_traffic("attention", w.name)
+    # reference: a plain 1 GiB device-to-device copy (read + write), the
+    # bandwidth a streaming kernel can reach on this part
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ca, cz = E(), E()
+    ca.record()
+    for _ in range(5):
+        dst.copy_(src)
+    cz.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2.0 * (1 << 30) / (ca.elapsed_time(cz) * 1e-3) / 1e9
+    del src, dst
+    band_ms = per_step("band")
+    band_tflops = w.band_mfma_flops() / (band_ms * 1e-3) / 1e12 if band_ms > 0 else float("nan")
 
     result = {
         "metric": "chunk-KV tokens/s through score->top-r->RoPE-assemble (+ selected-query attention); %HBM peak",
@@ -907,11 +942,14 @@ def main():
             "algorithmic_flops_per_launch": attn_flops,
         },
         "stages": {
+            "copy_GBs": copy_gbs,
             "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
+            "score_frac_copy": score_gbs / copy_gbs,
+            "band_mfma_TFLOPs_issued": band_tflops, "band_frac_bf16_peak": band_tflops / PEAK_BF16_TFLOPS,
             "score_kernels_ms": {n: per_step(n) for n in ("twiddle", "band", "gram", "layer_norm",
                                                            "layer_mean", "topr")},
             "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
-            "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS,
+            "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS, "assemble_frac_copy": asm_gbs / copy_gbs,
             "attention_call_ms_per_layer": attn_call_ms,
             "attention_kernels_ms_per_layer": {n: per_step(n) / w.L for n in attn_names},
             "attention_TFLOPs": attn_tflops,

@@ -87,32 +87,35 @@ __global__ __launch_bounds__(256) void k_silu_mul(const uint16_t* gu, int rows, 
 // in fp32), fp32 accumulation, one rounding to bf16 at the end (after the
 // residual is added).  A block computes a BM x BN tile with WGM x WGN waves,
 // each a (BM / WGM) x (BN / WGN) tile of v_mfma_f32_32x32x16_bf16 tiles; k
-// advances in stages of 32.  Each stage's x and w slabs are loaded into
+// advances in stages of BK (32 or 64).  Each stage's x and w slabs are loaded into
 // registers one stage ahead with buffer loads (rows past m or n and k past K
 // read as zeros) and written to the other of two LDS buffers after the current
-// stage's products: one barrier per stage.  An LDS row is 32 k (four 16-byte
-// chunks); chunk c of row r sits at chunk c ^ ((r / 4) % 4), so that both the
-// row-major slab writes and the operand reads (one row per lane) hit 16
-// distinct 4-bank groups per 16 lanes.  The output columns may be split over
+// stage's products: one barrier per stage.  An LDS row is BK k (BK / 8
+// 16-byte chunks); chunk c of row r sits at chunk c ^ ((r / R) % (BK / 8)),
+// R = 128 / BK rows per pass over the 64 banks, so that both the row-major
+// slab writes and the operand reads (one row per lane) hit 16 distinct 4-bank
+// groups per 16 lanes.  The output columns may be split over
 // three destinations (q | k | v of the fused projection): columns [0, n1) go
 // to out0 (row length n1), [n1, n2) to out1, [n2, N) to out2.
-constexpr int kGBK = 32;
-
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int WGM, int WGN, int PF>
-__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int BM, int BN, int WGM, int WGN, int BK>
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu((BM / WGM) * (BN / WGN) > 64 * 128 ? 1 : 2,
+                                   (BM / WGM) * (BN / WGN) > 64 * 128 ? 1 : 2)))
 void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                  const uint16_t* res, uint16_t* out0, uint16_t* out1, uint16_t* out2, int n1, int n2,
                  int M, int N, int K) {
   constexpr int NT = 64 * WGM * WGN;                        // threads
   constexpr int TI = BM / WGM / 32, TJ = BN / WGN / 32;     // MFMA tiles per wave
-  constexpr int NX = BM * 4 / NT, NW = BN * 4 / NT;         // 16-byte vectors per thread and stage
-  static_assert(NX * NT == BM * 4 && NW * NT == BN * 4, "slab split");
-  static_assert(PF == 1, "prefetch depth");
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * kGBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * kGBK];
+  constexpr int CPR = BK / 8;                               // 16-byte chunks per LDS row
+  constexpr int RPC = 128 / BK;                             // LDS rows per 64-bank cycle
+  constexpr int NX = BM * CPR / NT, NW = BN * CPR / NT;     // 16-byte vectors per thread and stage
+  static_assert(NX * NT == BM * CPR && NW * NT == BN * CPR && NT % CPR == 0, "slab split");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * BK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
@@ -126,17 +129,17 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   int xo[NX], wo[NW], xl[NX], wl[NW];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
-    const int v = tid + NT * i, r = v >> 2, q = v & 3;
+    const int v = tid + NT * i, r = v / CPR, q = v % CPR;
     xo[i] = (r * K + 8 * q) * 2;
-    xl[i] = r * kGBK + 8 * (q ^ ((r >> 2) & 3));
+    xl[i] = r * BK + 8 * (q ^ ((r / RPC) % CPR));
   }
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int v = tid + NT * i, r = v >> 2, q = v & 3;
+    const int v = tid + NT * i, r = v / CPR, q = v % CPR;
     wo[i] = (r * K + 8 * q) * 2;
-    wl[i] = r * kGBK + 8 * (q ^ ((r >> 2) & 3));
+    wl[i] = r * BK + 8 * (q ^ ((r / RPC) % CPR));
   }
-  const int q8 = 8 * (tid & 3);  // k offset of this thread's vectors within a stage (NT is a multiple of 4)
+  const int q8 = 8 * (tid % CPR);  // k offset of this thread's vectors within a stage
   u32x4_t xs0[NX], ws0[NW];
   auto load = [&](int k0, u32x4_t* xs, u32x4_t* ws) {
     const bool in = k0 + q8 < K;  // k past K: zeros
@@ -162,18 +165,18 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  const int sw = (col >> 2) & 3;  // rows read by this lane are col mod 32
+  const int sw = (col / RPC) % CPR;  // rows read by this lane are col mod 32
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kGBK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8_t a[TI], b[TJ];
       const int ch = 8 * ((2 * ks + g) ^ sw);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][(wm + 32 * i + col) * kGBK + ch]);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][(wm + 32 * i + col) * BK + ch]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(wn + 32 * j + col) * kGBK + ch]);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(wn + 32 * j + col) * BK + ch]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -181,16 +184,16 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     }
   };
 
-  const int nk = (K + kGBK - 1) / kGBK;
+  const int nk = (K + BK - 1) / BK;
   load(0, xs0, ws0);
   store(0, xs0, ws0);
-  if (nk > 1) load(kGBK, xs0, ws0);
+  if (nk > 1) load(BK, xs0, ws0);
   for (int s = 0; s < nk; ++s) {
     __syncthreads();
     compute(s & 1);
     if (s + 1 < nk) {
       store((s + 1) & 1, xs0, ws0);
-      if (s + 2 < nk) load((s + 2) * kGBK, xs0, ws0);
+      if (s + 2 < nk) load((s + 2) * BK, xs0, ws0);
     }
   }
 
@@ -240,11 +243,11 @@ ct_status silu_mul_run(const void* gu, int rows, int ff, void* out, hipStream_t 
   return check_launch("silu_mul");
 }
 
-template <int BM, int BN, int WGM, int WGN, int PF>
+template <int BM, int BN, int WGM, int WGN, int BK>
 static void gemm_go(const void* x, const void* w, const void* residual, void* out0, void* out1, void* out2,
                     int n1, int n2, int m, int n, int k, hipStream_t stream) {
   dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, PF>), grid, dim3(64 * WGM * WGN), 0, stream,
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, BK>), grid, dim3(64 * WGM * WGN), 0, stream,
                      reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
                      reinterpret_cast<const uint16_t*>(residual), reinterpret_cast<uint16_t*>(out0),
                      reinterpret_cast<uint16_t*>(out1), reinterpret_cast<uint16_t*>(out2), n1, n2, m, n, k);
@@ -265,9 +268,9 @@ static ct_status gemm_launch(const void* x, const void* w, const void* residual,
   const long long small = (long long)((m + 127) / 128) * ((n + 255) / 256);
   const double r_big = (double)((big + ncu - 1) / ncu), r_small = 1.15 * (double)((small + 2 * ncu - 1) / (2 * ncu));
   if (r_big <= r_small)
-    gemm_go<256, 256, 4, 2, 1>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
+    gemm_go<256, 256, 4, 2, 32>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
   else
-    gemm_go<128, 256, 2, 2, 1>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
+    gemm_go<128, 256, 2, 2, 32>(x, w, residual, out0, out1, out2, n1, n2, m, n, k, stream);
   return check_launch("linear");
 }
 
