@@ -800,6 +800,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3-8b-8x2048", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager step only (no HIP-graph replay)")
     ap.add_argument("--host-tier", action="store_true",
                     help="run the 32 x 2048 host-tier pipeline with an r sweep instead")
     ap.add_argument("--full-layer", action="store_true",
@@ -871,7 +873,35 @@ def main():
     torch.cuda.synchronize()
     ct.cachetune_timing_enable(False)
     ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
+    ms_step_eager = ms_total / args.steps
+    ms_step, launch = ms_step_eager, "eager"
+    if not args.no_graph:
+        # the same step captured once in a HIP graph and replayed: the kernels
+        # and their arguments are those of the eager step, without the per-call
+        # launch cost (timing events are off while capturing)
+        try:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                w.step()
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                w.step()
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(args.steps):
+                graph.replay()
+            stop.record()
+            torch.cuda.synchronize()
+            ms_step, launch = start.elapsed_time(stop) / args.steps, "hip-graph"
+            del graph
+        except RuntimeError as e:  # capture unsupported here: keep the eager figure
+            print(f"[bench] graph capture failed ({e}); reporting the eager step", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
     kt = {n: ct.cachetune_timing_read(n) for n in names}  # name -> (total ms, launches)
 
     def per_step(*ns):
@@ -916,6 +946,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_eager": ms_step_eager,
+        "launch": launch,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -1,0 +1,79 @@
+"""HIP-graph replay of the hot path: the step captured once (scoring, top-r,
+per layer assembly and attention, through the C ABI on torch's capture
+stream) and replayed several times, with eager work and synchronisations in
+between, gives bit-identical results to the eager step every time."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+SEED = 20260611
+
+
+def test_step_graph_replays_match_eager(syn):
+    ct = need_gpu()
+    ns, L, H, Hq, D, theta, n_sfx = [512, 300], 2, 2, 8, 64, 500000.0, 16
+    chunks = [(to_dev(syn.chunk(SEED, syn.K, b, L, n, H, D, "bf16")), to_dev(syn.chunk(SEED, syn.V, b, L, n, H, D, "bf16")))
+              for b, n in enumerate(ns)]
+    offs = [0, ns[0]]
+    T_c = sum(ns)
+    T = T_c + n_sfx
+    ks = [(15 * n) // 100 for n in ns]
+    score = torch.empty(T_c, dtype=torch.float32, device="cuda")
+    sel = torch.empty(sum(ks), dtype=torch.int32, device="cuda")
+    comp = torch.empty(T_c - sum(ks), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ct.cachetune_score_chunk_ws(ns, L, H, D, (1, 16)), dtype=torch.uint8, device="cuda")
+    rec = [[(to_dev(syn.rows(SEED, syn.K, b, l, n, H, D, np.arange(ks[b]), "bf16")),
+             to_dev(syn.rows(SEED, syn.V, b, l, n, H, D, np.arange(ks[b]), "bf16"))) for b, n in enumerate(ns)]
+           for l in range(L)]
+    sfx = [(to_dev(syn.rows(SEED, syn.K, syn.SUFFIX_CHUNK, l, n_sfx, H, D, np.arange(n_sfx), "bf16")),
+            to_dev(syn.rows(SEED, syn.V, syn.SUFFIX_CHUNK, l, n_sfx, H, D, np.arange(n_sfx), "bf16"))) for l in range(L)]
+    n_q = 40
+    qpos = to_dev(np.sort(np.random.default_rng(1).choice(T, n_q, replace=False)).astype(np.int32))
+    q = [to_dev(syn.rows(SEED, syn.Q, 0, l, T, Hq, D, np.arange(n_q), "bf16")) for l in range(L)]
+    k_asm = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    v_asm = torch.empty_like(k_asm)
+    out = [torch.empty((n_q, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    attn_ws = torch.empty(max(256, ct.cachetune_recompute_attn_ws(n_q, Hq, T, H, D)), dtype=torch.uint8,
+                          device="cuda")
+    so, co = [0, ks[0]], [0, ns[0] - ks[0]]
+    places = [[ct.make_place(chunks[b][0][l], chunks[b][1][l], n, ks[b], offs[b], sel=sel[so[b]:],
+                             comp=comp[co[b]:], k_rec=rec[l][b][0], v_rec=rec[l][b][1])
+               for b, n in enumerate(ns)] for l in range(L)]
+
+    def step():
+        ct.cachetune_score_chunk(chunks, L, H, D, score=score, ws=ws)
+        ct.cachetune_select_topr(score, ns, r=(15, 100), sel=sel, comp=comp, want_ranking=False)
+        for l in range(L):
+            ct.cachetune_assemble_rope(places[l], k_asm, v_asm, H, D, theta, k_sfx=sfx[l][0], v_sfx=sfx[l][1],
+                                       n_sfx=n_sfx, sfx_offset=T_c)
+            ct.cachetune_recompute_attn(q[l], qpos, k_asm, v_asm, 1.0 / math.sqrt(D), theta, out=out[l],
+                                        ws=attn_ws)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (score, sel, comp, k_asm, v_asm, *out)]
+
+    step()
+    want = snapshot()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        step()
+    for rep in range(3):
+        for t in (score, k_asm, v_asm, *out):  # clobber the outputs with eager work between replays
+            t.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
