@@ -51,7 +51,7 @@ def _dev(a):
 class Workload:
     """Device-resident inputs and buffers of one request."""
 
-    def __init__(self, name: str, layers: int | None = None):
+    def __init__(self, name: str, layers: int | None = None, r: tuple | None = None):
         import torch
         import non_prefix_kv_token_amd as ct
         import synth as syn
@@ -62,7 +62,7 @@ class Workload:
         self.ct = ct
         ns, self.L = cfg["ns"], cfg["L"] if layers is None else layers
         self.H, self.Hq, self.D = cfg["H"], cfg["Hq"], cfg["D"]
-        self.theta, self.alpha, self.r = cfg["theta"], cfg["alpha"], cfg["r"]
+        self.theta, self.alpha, self.r = cfg["theta"], cfg["alpha"], (cfg["r"] if r is None else tuple(r))
         self.dtype = cfg["dtype"]
         self.ns = ns
         seed = cfg["seed"]
@@ -639,6 +639,53 @@ def score_variants(w, args):
                       "bytes_read": w.score_bytes()}), flush=True)
 
 
+def r_sweep(args):
+    """The device-resident step at each r of {5, 10, 15, 20, 30}% (one chunk
+    order, the stored ranking cut at each r): per-stage chunk-KV tokens/s and
+    the attention kernel's fraction of the bf16 MFMA peak.  One JSON line."""
+    import torch
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = []
+    attn_names = ("attention_setup", "attention", "attention_merge")
+    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
+    for r in [(5, 100), (10, 100), (15, 100), (20, 100), (30, 100)]:
+        w = Workload(args.workload, r=r)
+        ct = w.ct
+        for _ in range(args.warmup):
+            w.step()
+        torch.cuda.synchronize()
+        for n in names:
+            ct.cachetune_timing_read(n)
+        a, z = E(), E()
+        ct.cachetune_timing_enable(True)
+        a.record()
+        for _ in range(args.steps):
+            w.step()
+        z.record()
+        torch.cuda.synchronize()
+        ct.cachetune_timing_enable(False)
+        ms = a.elapsed_time(z) / args.steps
+        kt = {n: ct.cachetune_timing_read(n)[0] / args.steps for n in names}
+        tokens = float(sum(w.ns))
+        score_ms = sum(kt[n] for n in ("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"))
+        asm_ms = kt["assemble"]
+        attn_ms = sum(kt[n] for n in attn_names)
+        attn_tf = w.attn_flops_per_layer() * w.L / (kt["attention"] * 1e-3) / 1e12
+        out.append({"r": f"{r[0]}/{r[1]}", "n_q": w.n_q, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                    "score_tokens_per_s": tokens / (score_ms * 1e-3),
+                    "assemble_tokens_per_s": tokens / (asm_ms * 1e-3),
+                    "attention_tokens_per_s": tokens / (attn_ms * 1e-3),
+                    "assemble_frac_hbm": w.assemble_bytes_per_layer() * w.L / (asm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    "attention_TFLOPs": attn_tf, "attention_frac_bf16_peak": attn_tf / PEAK_BF16_TFLOPS})
+        print(f"[bench] r={r[0]}/{r[1]}: {ms:.2f} ms per step, attention {attn_tf:.0f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "per-stage chunk-KV tokens/s and attention MFMA fraction across r",
+                      "unit": "chunk-KV tokens/s", "config": {"workload": args.workload}, "per_r": out}),
+          flush=True)
+
+
 def band_energy(w, args, n_bands=10):
     """App. E.1 on the workload's chunks: time of the band-energy pass and the
     energy fraction of each tenth of the rFFT bins (mean over chunks and
@@ -812,6 +859,8 @@ def main():
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--recompute-layers", action="store_true",
                     help="time the request with the full recompute layer (synthetic weights) instead")
+    ap.add_argument("--r-sweep", action="store_true",
+                    help="run the step at r in {5,10,15,20,30}%% and report per-stage rates instead")
     ap.add_argument("--band-energy", action="store_true",
                     help="time the band energy fractions of the workload's chunks instead")
     ap.add_argument("--score-variants", action="store_true",
@@ -828,6 +877,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.host_tier:
         host_tier(args)
+        return
+    if args.r_sweep:
+        r_sweep(args)
         return
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     w = Workload(args.workload)
