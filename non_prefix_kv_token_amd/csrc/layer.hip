@@ -88,9 +88,10 @@ __global__ __launch_bounds__(256) void k_silu_mul(const uint16_t* gu, int rows, 
 // residual is added).  A block computes a BM x BN tile with WGM x WGN waves,
 // each a (BM / WGM) x (BN / WGN) tile of v_mfma_f32_32x32x16_bf16 tiles; k
 // advances in stages of BK (32 or 64).  Each stage's x and w slabs are loaded into
-// registers one stage ahead with buffer loads (rows past m or n and k past K
-// read as zeros) and written to the other of two LDS buffers after the current
-// stage's products: one barrier per stage.  An LDS row is BK k (BK / 8
+// registers two stages ahead (two register sets, alternating) with buffer
+// loads (rows past m or n and k past K read as zeros) and written to the other
+// of two LDS buffers after the current stage's products: one barrier per
+// stage, and two stages of products to cover each load's latency.  An LDS row is BK k (BK / 8
 // 16-byte chunks); chunk c of row r sits at chunk c ^ ((r / R) % (BK / 8)),
 // R = 128 / BK rows per pass over the 64 banks, so that both the row-major
 // slab writes and the operand reads (one row per lane) hit 16 distinct 4-bank
@@ -140,7 +141,7 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     wl[i] = r * BK + 8 * (q ^ ((r / RPC) % CPR));
   }
   const int q8 = 8 * (tid % CPR);  // k offset of this thread's vectors within a stage
-  u32x4_t xs0[NX], ws0[NW];
+  u32x4_t xa[NX], wa[NW], xb[NX], wb[NW];
   auto load = [&](int k0, u32x4_t* xs, u32x4_t* ws) {
     const bool in = k0 + q8 < K;  // k past K: zeros
 #pragma unroll
@@ -185,16 +186,27 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   };
 
   const int nk = (K + BK - 1) / BK;
-  load(0, xs0, ws0);
-  store(0, xs0, ws0);
-  if (nk > 1) load(BK, xs0, ws0);
-  for (int s = 0; s < nk; ++s) {
+  // stages two ahead in registers (sets a and b alternate), two LDS buffers
+  load(0, xa, wa);
+  store(0, xa, wa);
+  if (nk > 1) load(BK, xa, wa);
+  if (nk > 2) load(2 * BK, xb, wb);
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
     __syncthreads();
-    compute(s & 1);
-    if (s + 1 < nk) {
-      store((s + 1) & 1, xs0, ws0);
-      if (s + 2 < nk) load((s + 2) * BK, xs0, ws0);
+    compute(0);
+    store(1, xa, wa);
+    if (s + 3 < nk) load((s + 3) * BK, xa, wa);
+    __syncthreads();
+    compute(1);
+    if (s + 2 < nk) {
+      store(0, xb, wb);
+      if (s + 4 < nk) load((s + 4) * BK, xb, wb);
     }
+  }
+  if (s < nk) {
+    __syncthreads();
+    compute(0);
   }
 
   // lane holds n = n0 + wn + 32 j + col and m = m0 + wm + 32 i + 8 (v / 4) + 4 g + v % 4
