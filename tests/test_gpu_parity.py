@@ -52,6 +52,7 @@ def _rel_close(got, want, rtol=1e-4, floor=0.0):
     ([96, 257], 2, 1, 64, (1, 2)),                  # the paper's default alpha
     ([130, 77], 1, 1, 64, (1, 1)),                  # alpha = 1: every bin (odd N, Nyquist)
     ([600, 4096], 1, 1, 64, (1, 32)),               # 1/32 cutoff, shortest/longest lengths
+    ([2, 8192, 3], 1, 1, 64, (1, 16)),              # the smallest and largest chunk lengths
 ])
 def test_score_parity_bf16(orc, syn, ns, L, H, D, alpha):
     s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
@@ -487,3 +488,33 @@ def test_rank_order_is_a_gather(syn):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_host(kd), k[:, perm])
     np.testing.assert_array_equal(to_host(vd), v[:, perm])
+
+
+def test_assembly_and_attention_deterministic(syn):
+    """Two runs of the assembly and of the attention (persistent grid, work
+    items taken from atomic counters in whatever order the blocks arrive) give
+    bit-identical outputs: every item's arithmetic is independent of the block
+    that runs it and the split-KV merge has a fixed order."""
+    ct = need_gpu()
+    T, H, Hq, D, theta = 9000, 8, 32, 128, 500000.0
+    k = to_dev(syn.rows(SEED, syn.K, 0, 1, T, H, D, np.arange(T), "bf16"))
+    v = to_dev(syn.rows(SEED, syn.V, 0, 1, T, H, D, np.arange(T), "bf16"))
+    rng = np.random.default_rng(5)
+    qpos = np.sort(rng.choice(T, 700, replace=False)).astype(np.int32)
+    q = to_dev(syn.rows(SEED, syn.Q, 0, 1, T, Hq, D, qpos, "bf16"))
+    n = T // 2
+    sel = np.sort(rng.choice(n, 100, replace=False)).astype(np.int32)
+    comp = np.setdiff1d(np.arange(n, dtype=np.int32), sel).astype(np.int32)
+    keep = dict(sel=to_dev(sel), comp=to_dev(comp), k_rec=k[:100].contiguous(), v_rec=v[:100].contiguous())
+    all2 = to_dev(np.arange(T - n, dtype=np.int32))
+    places = [ct.make_place(k[:n], v[:n], n, 100, 0, **keep), ct.make_place(k[n:], v[n:], T - n, 0, n, comp=all2)]
+    outs = []
+    for _ in range(2):
+        ka = torch.empty_like(k)
+        va = torch.empty_like(v)
+        ct.cachetune_assemble_rope(places, ka, va, H, D, theta)
+        o, lse = ct.cachetune_recompute_attn(q, to_dev(qpos), ka, va, 1.0 / np.sqrt(D), theta, want_lse=True)
+        torch.cuda.synchronize()
+        outs.append((ka.clone(), va.clone(), o.clone(), lse.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
