@@ -218,13 +218,14 @@ class Workload:
     def band_mfma_flops(self) -> float:
         """Matrix-core flops the band projection issues per step: per (chunk,
         layer, K|V), the padded band rows x the padded tokens x the channels x 2,
-        three twiddle planes (bf16 data) or six products (fp32 data)."""
+        two fp16 twiddle planes (bf16 data that fit fp16; a problem that does
+        not is redone with three bf16 planes) or six products (fp32 data)."""
         flops = 0.0
         for n in self.ns:
             nb = n // 2 + 1
             kk = min(nb, max(1, (self.alpha[0] * nb) // self.alpha[1]))
             ppad = -(-2 * kk // 32) * 32
-            flops += self.L * 2 * ppad * (-(-n // 32) * 32) * self.H * self.D * 2 * (3 if self.dtype == "bf16" else 6)
+            flops += self.L * 2 * ppad * (-(-n // 32) * 32) * self.H * self.D * 2 * (2 if self.dtype == "bf16" else 6)
         return flops
 
     def assemble_bytes_per_layer(self) -> float:
@@ -630,7 +631,7 @@ def score_variants(w, args):
     ct = w.ct
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = {}
-    names = ("twiddle", "band", "gram", "energy_l2", "highpass", "layer_norm", "layer_mean")
+    names = ("twiddle", "band", "band_redo", "gram", "energy_l2", "highpass", "layer_norm", "layer_mean")
     for name, variant in (("lowpass", ct.CT_SCORE_LOWPASS), ("l2", ct.CT_SCORE_L2),
                           ("highpass", ct.CT_SCORE_HIGHPASS)):
         need = ct.cachetune_score_chunk_ws(w.ns, w.L, w.H, w.D, w.alpha, variant=variant)
@@ -670,7 +671,7 @@ def r_sweep(args):
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = []
     attn_names = ("attention_setup", "attention", "attention_merge")
-    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
+    names = ["twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
     for r in [(5, 100), (10, 100), (15, 100), (20, 100), (30, 100)]:
         w = Workload(args.workload, r=r)
         ct = w.ct
@@ -690,7 +691,7 @@ def r_sweep(args):
         ms = a.elapsed_time(z) / args.steps
         kt = {n: ct.cachetune_timing_read(n)[0] / args.steps for n in names}
         tokens = float(sum(w.ns))
-        score_ms = sum(kt[n] for n in ("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"))
+        score_ms = sum(kt[n] for n in ("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr"))
         asm_ms = kt["assemble"]
         attn_ms = sum(kt[n] for n in attn_names)
         attn_tf = w.attn_flops_per_layer() * w.L / (kt["attention"] * 1e-3) / 1e12
@@ -831,7 +832,7 @@ def recompute_layers(w, args):
         m.step()
     torch.cuda.synchronize()
     names = ["linear", "rmsnorm", "silu_mul", "assemble", "attention_setup", "attention", "attention_merge",
-             "twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"]
+             "twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr"]
     for n in names:
         ct.cachetune_timing_read(n)
     a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -934,7 +935,7 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     attn_names = ("attention_setup", "attention", "attention_merge")
-    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
+    names = ["twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
     for n in names:  # drop records of earlier launches
         ct.cachetune_timing_read(n)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -987,7 +988,7 @@ def main():
         return tot / cnt if cnt else float("nan")
 
     tokens = float(sum(w.ns))
-    score_ms = per_step("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr")
+    score_ms = per_step("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr")
     asm_ms = per_step("assemble") / w.L
     attn_call_ms = per_step(*attn_names) / w.L
     attn_kernel_ms = per_launch("attention")
@@ -1053,7 +1054,7 @@ def main():
             "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
             "score_frac_copy": score_gbs / copy_gbs,
             "band_mfma_TFLOPs_issued": band_tflops, "band_frac_bf16_peak": band_tflops / PEAK_BF16_TFLOPS,
-            "score_kernels_ms": {n: per_step(n) for n in ("twiddle", "band", "gram", "layer_norm",
+            "score_kernels_ms": {n: per_step(n) for n in ("twiddle", "band", "band_redo", "gram", "layer_norm",
                                                            "layer_mean", "topr")},
             "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
             "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS, "assemble_frac_copy": asm_gbs / copy_gbs,

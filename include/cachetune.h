@@ -328,7 +328,7 @@ ct_status cachetune_stage_complement(const ct_ranked_chunk* chunks, int32_t n_ch
 /* ---- kernel timing (tracing aid) -----------------------------------------
  * While enabled, each kernel launch of the library is bracketed by a pair of
  * HIP events on the launch's stream, recorded under the kernel's name:
- *   "band", "gram", "topr", "assemble", "attention_setup", "attention",
+ *   "band", "band_redo", "gram", "topr", "assemble", "attention_setup", "attention",
  *   "attention_merge", "rank_order", "energy_l2", "highpass", "bin_energy",
  *   "rmsnorm", "silu_mul", "linear" (and "twiddle", "layer_norm", "layer_mean").
  * cachetune_timing_read waits for the events recorded under `kernel`, returns

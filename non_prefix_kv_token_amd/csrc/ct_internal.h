@@ -56,6 +56,8 @@ struct ScoreChunkDesc {
   int32_t ntok_pad;  // twiddle table row length (multiple of 32, >= n)
   int32_t tw_owner;  // 1: this chunk writes the shared twiddle table
   int64_t tw_off;    // bf16 twiddle planes [3][ppad][ntok_pad]
+  int64_t tw16_off;  // fp16 twiddle planes [2][ppad][ntok_pad]
+  int64_t flag_off;  // int32 [L][2]: 1 when the problem's X does not fit fp16
   int64_t trig_off;  // fp64 (cos, sin) of 2*pi*m/nf, m < nf
   int64_t y_off;     // fp32 band coefficients [L][2][ppad][C]
   int64_t e_off;     // fp64 low-pass energies [L][2][n]

@@ -8,10 +8,12 @@
 // is computed exactly (up to rounding) without forming xlow:
 //  1. band projection on the matrix cores: Y = [cos | sin](j*n) . X, i.e. the
 //     real and imaginary parts R_j, S_j (j < kk) of the retained bins for all
-//     channels at once.  The twiddles are split into three bf16 planes
-//     (t = t1 + t2 + t3 to ~2^-24), bf16 data are exact, products are exact in
-//     fp32, so one pass of three bf16 MFMAs gives fp32-accurate coefficients;
-//     fp32 data are split the same way (six MFMAs).
+//     channels at once.  bf16 data enter the fp16 matrix cores, where they
+//     are exact below 65536, against the twiddles as an fp16 hi + lo pair
+//     (t = t1 + t2 to 2^-24): two MFMAs give fp32-accurate coefficients.  A
+//     problem holding a larger or non-finite value is redone with the
+//     twiddles as three bf16 planes (t1 + t2 + t3 to ~2^-25) against the bf16
+//     data (three MFMAs); fp32 data are split the same way (six MFMAs).
 //  2. the channel Gram G = Y Y^T (fp64);
 //  3. E[n] as a trigonometric polynomial of degree 2(kk-1) in phi = 2*pi*n/nf,
 //     whose coefficients are diagonal and anti-diagonal sums of G; evaluated
@@ -46,6 +48,24 @@ __device__ inline double f64_from_bf16(uint16_t h) {
   return (double)__uint_as_float(((uint32_t)h) << 16);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Round a double to fp16 with a single rounding (round-to-odd to binary32,
+// then round to nearest even).
+__device__ inline _Float16 f16_from_f64(double d) {
+  float f = __double2float_rz(d);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != d) u |= 1u;
+  return (_Float16)__uint_as_float(u);
+}
+
+__device__ inline uint32_t pack_f16(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
 // cos and sin of 2*pi*m/nf (0 <= m < nf): quarter turns are taken out exactly
 // so that multiples of pi/2 give exact 0 and +-1.
 __device__ inline void turn_sincos(long long m, int nf, double* s, double* c) {
@@ -66,12 +86,18 @@ __device__ inline void turn_sincos(long long m, int nf, double* s, double* c) {
 
 // ---- 1a. twiddle planes ----------------------------------------------------
 // Row p < kk holds cos(2*pi*p*n/nf); row kk + j holds sin(2*pi*j*n/nf);
-// rows >= 2kk are zero.  Each value is stored as three bf16 planes.
+// rows >= 2kk are zero.  Each value is stored as three bf16 planes and as an
+// fp16 pair.  Also clears the chunk's fp16-range flags.
 __global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl, char* ws) {
   const ScoreChunkDesc& d = sl.c[blockIdx.y];
+  if (blockIdx.x == 0 && sl.dtype == CT_BF16) {
+    int* flag = reinterpret_cast<int*>(ws + d.flag_off);
+    for (int i = threadIdx.x; i < 2 * sl.L; i += blockDim.x) flag[i] = 0;
+  }
   if (!d.tw_owner) return;
   const int ppad = d.ppad, ntp = d.ntok_pad, kk = d.kk, nf = d.nf;
   uint16_t* tw = reinterpret_cast<uint16_t*>(ws + d.tw_off);
+  _Float16* tw16 = reinterpret_cast<_Float16*>(ws + d.tw16_off);
   const long long plane = (long long)ppad * ntp;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < plane;
        e += (long long)gridDim.x * blockDim.x) {
@@ -91,6 +117,11 @@ __global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl, char* ws) {
     tw[e] = t1;
     tw[plane + e] = t2;
     tw[2 * plane + e] = t3;
+    if (sl.dtype == CT_BF16) {
+      const _Float16 h1 = f16_from_f64(v);
+      tw16[e] = h1;
+      tw16[plane + e] = f16_from_f64(v - (double)h1);
+    }
   }
   double2* trig = reinterpret_cast<double2*>(ws + d.trig_off);
   for (long long m = (long long)blockIdx.x * blockDim.x + threadIdx.x; m < nf;
@@ -341,10 +372,15 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // FULL: every chunk's padded band is a whole number of blocks of 32*NTL rows,
 // so no block holds padding tiles and the tile loop carries no per-tile test
 // (the branches would break up the matrix-core issue).
-template <int NTL, bool FULL>
+// F16: X converted to fp16 in registers against the fp16 twiddle pair (two
+// MFMAs per tile and k-step); a block that meets |x| >= 65536 or a non-finite
+// value raises the problem's flag.  Otherwise X stays bf16 against the three
+// bf16 planes (three MFMAs); with redo set, only flagged problems run.
+template <int NTL, bool FULL, bool F16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_band_bf16(ScoreLaunch sl, char* ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][3 * 32 * NTL * kTwStride];
+void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
+  constexpr int NPL = F16 ? 2 : 3;  // twiddle planes
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][NPL * 32 * NTL * kTwStride];
 
   const int L = sl.L, C = sl.C;
   const int prob = blockIdx.z;
@@ -352,6 +388,8 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
   const int layer = (prob / 2) % L;
   const int kv = prob % 2;
   const ScoreChunkDesc& d = sl.c[b];
+  int* flag = reinterpret_cast<int*>(ws + d.flag_off) + layer * 2 + kv;
+  if (!F16 && redo && *flag == 0) return;
   const int pbase = blockIdx.y * 32 * NTL;
   if (pbase >= d.ppad) return;
   const int nrows = min(32 * NTL, d.ppad - pbase);  // rows this chunk has in the block
@@ -368,13 +406,13 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
   // num_records returns 0, which zero-fills tokens at and beyond N and rows a
   // chunk does not have.  The whole offset is kept in the VGPR operand (the
   // scalar offset is 0), so that range check covers every load.
-  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + d.tw_off);
+  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + (F16 ? d.tw16_off : d.tw_off));
   const long long plane = (long long)ppad * ntp;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(src + (size_t)layer * N * C), 0, N * C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(tw), 0, (int)(3 * plane * 2), 0x00020000);
+      const_cast<uint16_t*>(tw), 0, (int)(NPL * plane * 2), 0x00020000);
   const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;  // inactive lanes read zeros
 
   f32x16_t acc[NTL][2];
@@ -394,8 +432,8 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
       for (int t = 0; t < 8; ++t)
         dst[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, xvoff + (step * 32 + 16 * s2 + t) * C * 2, 0, 0);
   };
-  // twiddle slab of a step: 3 planes x 32*NTL rows x 32 tokens (16-byte chunks)
-  constexpr int TWN = 3 * 32 * NTL * 4;    // chunks per slab
+  // twiddle slab of a step: NPL planes x 32*NTL rows x 32 tokens (16-byte chunks)
+  constexpr int TWN = NPL * 32 * NTL * 4;  // chunks per slab
   constexpr int TWI = (TWN + 511) / 512;   // chunks per thread (the last may be partial)
   u32x4_t twr[TWI];
   int twoff[TWI];
@@ -405,7 +443,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
     const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
     // rows this chunk does not have read past the table (zeros)
     twoff[it] = (item < TWN && r < nrows) ? (int)((q * plane + (long long)(pbase + r) * ntp + 8 * i) * 2)
-                                          : (int)(3 * plane * 2);
+                                          : (int)(NPL * plane * 2);
   }
   auto load_tw = [&](int step) {
 #pragma unroll
@@ -421,6 +459,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
       *reinterpret_cast<u32x4_t*>(&buf[(q * 32 * NTL + r) * kTwStride + 8 * i]) = twr[it];
     }
   };
+  float xmax = 0.f;  // F16: largest |x| met (NaN is not counted: it stays NaN in fp16)
   auto compute = [&](const uint16_t* buf, const uint32_t* xs) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -428,25 +467,34 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const uint32_t w0 = xs[8 * s2 + 2 * h], w1 = xs[8 * s2 + 2 * h + 1];
-        bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
-        bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+        if constexpr (F16) {
+          // bf16 -> fp32 is exact; fp32 -> fp16 is exact below 65536
+          const float a0 = __uint_as_float(w0 << 16), a1 = __uint_as_float(w1 << 16);
+          const float c0_ = __uint_as_float(w0 & 0xffff0000u), c1_ = __uint_as_float(w1 & 0xffff0000u);
+          xmax = __builtin_fmaxf(xmax, __builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
+          xmax = __builtin_fmaxf(xmax, __builtin_fmaxf(__builtin_fabsf(c0_), __builtin_fabsf(c1_)));
+          bu[0][h] = pack_f16(a0, a1);
+          bu[1][h] = pack_f16(c0_, c1_);
+        } else {
+          bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
+          bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+        }
       }
-      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bu[0]);
-      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bu[1]);
-      bf16x8_t a[NTL][3];
-#pragma unroll
-      for (int pt = 0; pt < NTL; ++pt)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          a[pt][q] = *reinterpret_cast<const bf16x8_t*>(
-              &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
 #pragma unroll
       for (int pt = 0; pt < NTL; ++pt) {
         if (!FULL && pt * 32 >= nrows) break;  // the band ends inside this block: no products of padding
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b0, acc[pt][0], 0, 0, 0);
-          acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pt][q], b1, acc[pt][1], 0, 0, 0);
+        for (int q = 0; q < NPL; ++q) {
+          const uint16_t* ap = &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g];
+          if constexpr (F16) {
+            const f16x8_t a = *reinterpret_cast<const f16x8_t*>(ap);
+            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
+            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
+          } else {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ap);
+            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
+            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
+          }
         }
       }
     }
@@ -477,6 +525,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
     }
   }
 
+  if (F16 && __any(!(xmax < 65536.f)) && lane == 0) *flag = 1;  // (inactive lanes hold 0)
   if (!active) return;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
 #pragma unroll
@@ -1090,7 +1139,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   const int C = H * D;
   const bool band = variant != CT_SCORE_L2;  // the L2 variant needs only the energies
   size_t off = 0;
-  struct Tab { int nf, kk, ntp; int64_t tw, trig; };
+  struct Tab { int nf, kk, ntp; int64_t tw, tw16, trig; };
   std::vector<Tab> tabs;
   std::vector<ScoreChunkDesc> desc(n_chunks);
   int max_p2 = 0;
@@ -1111,9 +1160,11 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
     for (size_t t = 0; t < tabs.size(); ++t)
       if (tabs[t].nf == d.nf && tabs[t].kk == d.kk && tabs[t].ntp == d.ntok_pad) found = (int)t;
     if (found < 0) {
-      Tab t{d.nf, d.kk, d.ntok_pad, 0, 0};
+      Tab t{d.nf, d.kk, d.ntok_pad, 0, 0, 0};
       t.tw = (int64_t)off;
       off = align256(off + (size_t)3 * d.ppad * d.ntok_pad * 2);
+      t.tw16 = (int64_t)off;
+      off = align256(off + (size_t)2 * d.ppad * d.ntok_pad * 2);
       t.trig = (int64_t)off;
       off = align256(off + (size_t)d.nf * 16);
       tabs.push_back(t);
@@ -1121,7 +1172,12 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
       found = (int)tabs.size() - 1;
     }
     d.tw_off = tabs[found].tw;
+    d.tw16_off = tabs[found].tw16;
     d.trig_off = tabs[found].trig;
+  }
+  for (int b = 0; b < n_chunks && band; ++b) {
+    desc[b].flag_off = (int64_t)off;
+    off = align256(off + (size_t)L * 2 * 4);
   }
   for (int b = 0; b < n_chunks && band; ++b) {
     desc[b].y_off = (int64_t)off;
@@ -1180,36 +1236,57 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
   if (ct_status s = check_launch("twiddle")) return s;
 
   dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
-  {
-    TimedLaunch tl_("band", stream);
-    if (sl.dtype == CT_BF16) {
-      // Band tiles per block: the whole of the launch's largest band when it
-      // has at most 5 tiles (160 rows), else that band split evenly over the
-      // fewest blocks of at most 5 tiles.  Each block streams X from HBM
-      // once, so more blocks per band means more reads of X.
-      const int tiles = sl.max_ppad / 32;
-      const int nyb = (tiles + 4) / 5;
-      const int ntl = (tiles + nyb - 1) / nyb;
-      // 8 waves x 64 channels per block: every twiddle slab staged in LDS
-      // serves 512 channels (the slabs, not X, are most of the L2 traffic)
-      dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
-      bool full = true;
-      for (int i = 0; i < sl.n_chunks; ++i) full = full && sl.c[i].ppad % (32 * ntl) == 0;
-#define CT_BAND(N)                                                                   \
-  if (full)                                                                          \
-    hipLaunchKernelGGL((k_band_bf16<N, true>), gq, dim3(512), 0, stream, sl, ws);    \
-  else                                                                               \
-    hipLaunchKernelGGL((k_band_bf16<N, false>), gq, dim3(512), 0, stream, sl, ws);
-      switch (ntl) {
-        case 5: CT_BAND(5) break;
-        case 4: CT_BAND(4) break;
-        case 3: CT_BAND(3) break;
-        case 2: CT_BAND(2) break;
-        default: CT_BAND(1) break;
-      }
+  if (sl.dtype == CT_BF16) {
+    // Band tiles per block: the whole of the launch's largest band when it
+    // has at most 5 tiles (160 rows), else that band split evenly over the
+    // fewest blocks of at most 5 tiles.  Each block streams X from HBM
+    // once, so more blocks per band means more reads of X.
+    // The fp16 kernel with 5 tiles and padding tiles runs out of registers:
+    // such launches take at most 4 tiles per block.
+    const int tiles = sl.max_ppad / 32;
+    auto tiles_per_block = [&](int cap) {
+      const int nyb = (tiles + cap - 1) / cap;
+      return (tiles + nyb - 1) / nyb;
+    };
+    auto whole = [&](int ntl) {
+      bool f = true;
+      for (int i = 0; i < sl.n_chunks; ++i) f = f && sl.c[i].ppad % (32 * ntl) == 0;
+      return f;
+    };
+    int ntl = tiles_per_block(5);
+    if (ntl == 5 && !whole(5)) ntl = tiles_per_block(4);
+    const bool full = whole(ntl);
+    // 8 waves x 64 channels per block: every twiddle slab staged in LDS
+    // serves 512 channels (the slabs, not X, are most of the L2 traffic)
+    dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+#define CT_BAND(N, F16, REDO)                                                                   \
+  if (full)                                                                                     \
+    hipLaunchKernelGGL((k_band_bf16<N, true, F16>), gq, dim3(512), 0, stream, sl, ws, REDO);    \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_band_bf16<N, false, F16>), gq, dim3(512), 0, stream, sl, ws, REDO);
+#define CT_BAND_NTL(F16, REDO)            \
+  switch (ntl) {                          \
+    case 5: CT_BAND(5, F16, REDO) break;  \
+    case 4: CT_BAND(4, F16, REDO) break;  \
+    case 3: CT_BAND(3, F16, REDO) break;  \
+    case 2: CT_BAND(2, F16, REDO) break;  \
+    default: CT_BAND(1, F16, REDO) break; \
+  }
+    {
+      TimedLaunch tl_("band", stream);
+      CT_BAND_NTL(true, 0)
+    }
+    if (ct_status s = check_launch("band projection")) return s;
+    {
+      // problems whose X does not fit fp16: the three-plane bf16 pass
+      TimedLaunch tl_("band_redo", stream);
+      CT_BAND_NTL(false, 1)
+    }
+#undef CT_BAND_NTL
 #undef CT_BAND
-    } else
-      hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
+  } else {
+    TimedLaunch tl_("band", stream);
+    hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
   }
   if (ct_status s = check_launch("band projection")) return s;
   return CT_OK;

@@ -23,9 +23,11 @@ def _chunks(syn, ns, L, H, D, dtype, seed=SEED):
             for b, n in enumerate(ns)]
 
 
-def _score_both(orc, syn, ns, L, H, D, dtype, alpha, mode=0, norm=0):
+def _score_both(orc, syn, ns, L, H, D, dtype, alpha, mode=0, norm=0, edit=None):
     ct = need_gpu()
     host = _chunks(syn, ns, L, H, D, dtype)
+    if edit is not None:
+        edit(host)
     dev = [(to_dev(k), to_dev(v)) for k, v in host]
     s_gpu, ls_gpu = ct.cachetune_score_chunk(dev, L, H, D, alpha=alpha, fftlen=mode, norm=norm,
                                              want_layers=True)
@@ -56,6 +58,31 @@ def _rel_close(got, want, rtol=1e-4, floor=0.0):
 ])
 def test_score_parity_bf16(orc, syn, ns, L, H, D, alpha):
     s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
+    _rel_close(s_gpu, s_orc)
+    _rel_close(ls_gpu, ls_orc)
+
+
+def _bf16_scaled(bits, factor):
+    """bf16 bits times a power of two (exact)."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_score_parity_bf16_wide_values(orc, syn):
+    """bf16 data beyond the fp16 range: the (chunk, layer, K|V) problems that
+    hold |x| >= 65536 are redone with the three bf16 twiddle planes, the others
+    stay on the fp16 pair.  Whole problems are scaled by powers of two, which
+    leaves each problem's conditioning as it was: chunk 1 layer 1 K reaches
+    75264 and chunk 0 layer 0 V 113664 (redone); chunk 0 layer 1 K reaches
+    55552 (fp16, near the top of its range)."""
+    def edit(host):
+        host[1][0][1] = _bf16_scaled(host[1][0][1], 2.0 ** 11)
+        host[0][1][0] = _bf16_scaled(host[0][1][0], 2.0 ** 12)
+        host[0][0][1] = _bf16_scaled(host[0][0][1], 2.0 ** 11)
+        wide = lambda a: float(np.abs((a.astype(np.uint32) << 16).view(np.float32)).max())
+        assert wide(host[1][0][1]) >= 65536 and wide(host[0][1][0]) >= 65536
+        assert 32768 <= wide(host[0][0][1]) < 65536
+    s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, [300, 2048], 2, 2, 64, "bf16", (1, 16), edit=edit)
     _rel_close(s_gpu, s_orc)
     _rel_close(ls_gpu, ls_orc)
 
