@@ -277,7 +277,8 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
  *  ws/ws_bytes: device workspace of at least cachetune_recompute_attn_ws bytes
  *         (may be NULL when that size is 0), 256-byte aligned; for bf16 it
  *         holds the rotated queries as bf16 pairs, V as fp16 tiles, and the
- *         partial results of rows whose keys are split over several segments.
+ *         partial results of rows whose keys are split over several segments
+ *         (fp16, or fp32 for a segment whose V exceeds the fp16 range).
  * D must be 64 or 128; n_q >= 0; T >= 1. */
 ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                    int32_t Hq, const void* k, const void* v, int32_t T,

@@ -673,6 +673,9 @@ void k_attn_bf16(AttnArgs a) {
         }
       if (a.lse && g == 0) a.lse[(size_t)row[qt] * Hq + hq] = 0.6931471805599453f * lse2;
     } else {
+      // A partial is a convex combination of V rows: with every V of the
+      // segment inside the fp16 range it is stored as fp16 (half the bytes
+      // for this kernel and the merge), else as fp32.
       const size_t pb = (((size_t)seg * a.n_q + row[qt]) * Hq + hq);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -680,11 +683,19 @@ void k_attn_bf16(AttnArgs a) {
         for (int v4 = 0; v4 < 4; ++v4) {
           const int d0 = dt * 32 + 8 * v4 + 4 * g;
           const f32x16_t& oo = o[qt][dt];
-          *reinterpret_cast<float4*>(a.part_o + pb * D + d0) =
-              make_float4(oo[4 * v4] * inv_l, oo[4 * v4 + 1] * inv_l, oo[4 * v4 + 2] * inv_l,
-                          oo[4 * v4 + 3] * inv_l);
+          if (!redo)
+            *reinterpret_cast<u32x2_t*>(a.part_o16 + pb * D + d0) =
+                (u32x2_t){pack_f16(oo[4 * v4] * inv_l, oo[4 * v4 + 1] * inv_l),
+                          pack_f16(oo[4 * v4 + 2] * inv_l, oo[4 * v4 + 3] * inv_l)};
+          else
+            *reinterpret_cast<float4*>(a.part_o + pb * D + d0) =
+                make_float4(oo[4 * v4] * inv_l, oo[4 * v4 + 1] * inv_l, oo[4 * v4 + 2] * inv_l,
+                            oo[4 * v4 + 3] * inv_l);
         }
-      if (g == 0) a.part_lse[pb] = lse2;
+      if (g == 0) {
+        a.part_lse[pb] = lse2;
+        a.part_fmt[pb] = redo ? 1 : 0;
+      }
     }
   }
   }  // work items
@@ -792,15 +803,22 @@ __global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
 
 // Combine the per-segment results of rows whose keys span several segments:
 // out = sum_s 2^(lse2_s - M) o_s / sum_s 2^(lse2_s - M).  One wave per
-// (row, query head); rows in segment 0 only were written by k_attn_bf16.
+// (row, group of kMergeHeads query heads), 16 lanes per head holding D/16
+// dims each (16-byte fp16 loads); rows in segment 0 only were written by
+// k_attn_bf16.  Lanes work independently (no cross-lane operations).
+constexpr int kMergeHeads = 4;
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 16;
   constexpr int U = 4;  // segments whose loads are in flight together
   typedef float fv_t __attribute__((ext_vector_type(PER)));
+  typedef _Float16 hv_t __attribute__((ext_vector_type(PER)));
+  const int hgroups = (a.Hq + kMergeHeads - 1) / kMergeHeads;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (w >= a.n_q * a.Hq) return;
-  const int row = w / a.Hq, hq = w % a.Hq;
+  if (w >= a.n_q * hgroups) return;
+  const int row = w / hgroups, hq = (w % hgroups) * kMergeHeads + lane / 16;
+  const int dl = (lane % 16) * PER;  // this lane's first dim
+  if (hq >= a.Hq) return;
   const int pos = min(a.qpos[row], a.T - 1);
   const int S = a.seg_keys;
   if (pos < S) return;
@@ -812,12 +830,33 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int s0 = 0; s0 < ns; s0 += U) {
     float ls[U];
     fv_t os[U];
+    hv_t hs[U];
+    int fm[U];
+    // the fp16 record is loaded with the format and the lse (one round
+    // trip); a record stored as fp32 (wide V, rare) is loaded after
+    // (segments past the row's last read its last record, with weight 0:
+    // every load is unconditional)
+    int any_fp32 = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
       const size_t pb = ((size_t)min(s, ns - 1) * a.n_q + row) * a.Hq + hq;
-      ls[u] = s < ns ? a.part_lse[pb] : -INFINITY;
-      os[u] = *reinterpret_cast<const fv_t*>(a.part_o + pb * D + lane * PER);
+      const float lv = a.part_lse[pb];
+      ls[u] = s < ns ? lv : -INFINITY;
+      fm[u] = a.part_fmt[pb];
+      hs[u] = *reinterpret_cast<const hv_t*>(a.part_o16 + pb * D + dl);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      os[u] = __builtin_convertvector(hs[u], fv_t);
+      any_fp32 |= fm[u];
+    }
+    if (any_fp32) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t pb = ((size_t)min(s0 + u, ns - 1) * a.n_q + row) * a.Hq + hq;
+        if (fm[u]) os[u] = *reinterpret_cast<const fv_t*>(a.part_o + pb * D + dl);
+      }
     }
     float mg = M;
 #pragma unroll
@@ -834,10 +873,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     M = mg;
   }
   const float inv = 1.f / wsum;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.Hq + hq) * D + lane * PER;
+  typedef uint32_t uv_t __attribute__((ext_vector_type(PER / 2)));
+  uv_t ov;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) out[i] = (uint16_t)bf16_bits_rne(acc[i] * inv);
-  if (a.lse && lane == 0) a.lse[(size_t)row * a.Hq + hq] = 0.6931471805599453f * (M + __log2f(wsum));
+  for (int i = 0; i < PER / 2; ++i)
+    ov[i] = bf16_bits_rne(acc[2 * i] * inv) | (bf16_bits_rne(acc[2 * i + 1] * inv) << 16);
+  *reinterpret_cast<uv_t*>(reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.Hq + hq) * D + dl) = ov;
+  if (a.lse && lane % 16 == 0) a.lse[(size_t)row * a.Hq + hq] = 0.6931471805599453f * (M + __log2f(wsum));
 }
 
 template <int D>
@@ -858,7 +900,7 @@ ct_status launch(const AttnArgs& a, hipStream_t stream) {
     return s;
   }
   if (a.nseg > 1) {
-    const long long waves = (long long)a.n_q * a.Hq;
+    const long long waves = (long long)a.n_q * ((a.Hq + kMergeHeads - 1) / kMergeHeads);
     {
       TimedLaunch tl_("attention_merge", stream);
       hipLaunchKernelGGL((k_attn_merge<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
@@ -899,45 +941,52 @@ void attn_plan(AttnArgs* a, int n_cu) {
   a->blocks_per_head = ncu / a->H > 0 ? ncu / a->H : 1;
 }
 
-// Workspace: [partial outputs][partial log2-sum-exp][V^T fp16 tiles][tile flags]
-// [prepared queries][work list, per-head counters, list length]
-static size_t ws_layout(const AttnArgs& a, size_t* off_lse, size_t* off_vt, size_t* off_flag,
-                        size_t* off_q, size_t* off_sched) {
+// Workspace: [partial outputs fp32][partial outputs fp16][record formats]
+// [partial log2-sum-exp][V^T fp16 tiles][tile flags][prepared queries]
+// [work list, per-head counters, list length]
+struct AttnWs { size_t o16, fmt, lse, vt, flag, q, sched, total; };
+static AttnWs ws_layout(const AttnArgs& a) {
+  AttnWs w{};
   const size_t rows = a.nseg > 1 ? (size_t)a.nseg * a.n_q * a.Hq : 0;
   size_t off = align256(rows * a.D * 4);
-  *off_lse = off;
+  w.o16 = off;
+  off += align256(rows * a.D * 2);
+  w.fmt = off;
+  off += align256(rows);
+  w.lse = off;
   off += align256(rows * 4);
-  *off_vt = off;
+  w.vt = off;
   off += align256((size_t)a.H * a.nblk * a.D * BK * 2);
-  *off_flag = off;
+  w.flag = off;
   off += align256((size_t)a.H * a.nblk * 4);
-  *off_q = off;
+  w.q = off;
   off += align256((size_t)a.n_q * a.Hq * a.D * 4);
-  *off_sched = off;
+  w.sched = off;
   off += align256(((size_t)a.n_tg * a.nseg + a.H + 1) * 4);
-  return off;
+  w.total = off;
+  return w;
 }
 
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.dtype != CT_BF16) return 0;
-  size_t o1, o2, o3, o4, o5;
-  return ws_layout(a, &o1, &o2, &o3, &o4, &o5);
+  return ws_layout(a).total;
 }
 
 ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return CT_OK;
   if (a.dtype == CT_F32) return attn_f32_run(a, stream);
-  size_t off_lse, off_vt, off_flag, off_q, off_sched;
-  const size_t need = ws_layout(a, &off_lse, &off_vt, &off_flag, &off_q, &off_sched);
-  if (!ws || ws_bytes < need)
-    return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(need) + " bytes required");
+  const AttnWs L = ws_layout(a);
+  if (!ws || ws_bytes < L.total)
+    return fail(CT_E_WORKSPACE, "attention workspace of " + std::to_string(L.total) + " bytes required");
   char* w = reinterpret_cast<char*>(ws);
   a.part_o = reinterpret_cast<float*>(w);
-  a.part_lse = reinterpret_cast<float*>(w + off_lse);
-  a.vt16 = reinterpret_cast<uint16_t*>(w + off_vt);
-  a.vflag = reinterpret_cast<int32_t*>(w + off_flag);
-  a.qhl = reinterpret_cast<uint16_t*>(w + off_q);
-  a.sched_order = reinterpret_cast<int32_t*>(w + off_sched);
+  a.part_o16 = reinterpret_cast<uint16_t*>(w + L.o16);
+  a.part_fmt = reinterpret_cast<uint8_t*>(w + L.fmt);
+  a.part_lse = reinterpret_cast<float*>(w + L.lse);
+  a.vt16 = reinterpret_cast<uint16_t*>(w + L.vt);
+  a.vflag = reinterpret_cast<int32_t*>(w + L.flag);
+  a.qhl = reinterpret_cast<uint16_t*>(w + L.q);
+  a.sched_order = reinterpret_cast<int32_t*>(w + L.sched);
   a.sched_cnt = a.sched_order + (size_t)a.n_tg * a.nseg;
   a.sched_n = a.sched_cnt + a.H;
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);

@@ -143,7 +143,9 @@ struct AttnArgs {
   int32_t hpb, tpb;  // query heads and 32-row tiles per block (hpb * tpb <= nw)
   int32_t n_hc;      // head chunks per group
   int32_t n_tg;      // tile groups (tpb * qt tiles each)
-  float* part_o;     // [nseg][n_q][Hq][D] normalised partial outputs
+  float* part_o;     // [nseg][n_q][Hq][D] normalised partial outputs, fp32 (segments with wide V)
+  uint16_t* part_o16;  // [nseg][n_q][Hq][D] the same as fp16 (every other segment)
+  uint8_t* part_fmt;   // [nseg][n_q][Hq] 1: the record is in part_o, 0: in part_o16
   float* part_lse;   // [nseg][n_q][Hq] log2-sum-exp of the partials
   int32_t nblk;      // 64-key tiles covering [0, T)
   uint16_t* vt16;    // [H][nblk][D][64] V^T tiles as fp16 (keys permuted)
