@@ -48,6 +48,7 @@ namespace ct {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -157,65 +158,21 @@ __device__ void prep_v_tile(const AttnArgs& a, int kb, int h, uint16_t* tile) {
   if (tid == 0) a.vflag[h * a.nblk + kb] = any_wide;
 }
 
-// Per-layer preparation of the queries for the matrix cores: every selected
-// row's query heads rotated at the row's position (the angle's sine and
-// cosine formed once per row in fp64 and shared by all heads), multiplied by
-// softmax_scale * log2(e), and split into a bf16 hi + lo pair.  Stored per
-// (row, query head) as D/8 groups of {8 hi, 8 lo} (32 bytes): the lane that
-// owns dims [8 grp, 8 grp + 8) of a k-step reads both operands with two
-// 16-byte loads.  One row per call.
+// Per-layer preparation of the query rotation: the sine and cosine of every
+// selected row's RoPE angles (position times each frequency), reduced and
+// evaluated in fp64 and stored as fp32 pairs, once per row for all its query
+// heads.  The attention kernel rotates the bf16 queries with them.  Rows
+// row0 .. row0 + 256/(D/2) - 1 per call.
 template <int D>
-__device__ void prep_q_row(const AttnArgs& a, int row, float* s_sn, float* s_cs) {
-  constexpr int NG = D / 8;
-  const int tid = threadIdx.x;
+__device__ void prep_q_rows(const AttnArgs& a, int row0) {
+  constexpr int RPB = 256 / (D / 2);
+  const int row = row0 + threadIdx.x / (D / 2), j = threadIdx.x % (D / 2);
+  if (row >= a.n_q) return;
   const int pos = min(a.qpos[row], a.T - 1);
-  if (tid < D / 2) rope_sincos(pos, a.inv_freq[tid], &s_sn[tid], &s_cs[tid]);
-  __syncthreads();
-  const float c = a.scale_log2;
-  const bool half = a.style == CT_ROPE_HALF;
-  for (int item = tid; item < a.Hq * NG; item += 256) {
-    const int hq = item / NG, grp = item % NG;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * a.Hq + hq) * D;
-    float y[8];
-    if (half) {  // pairs (j, j + D/2)
-      const bool first = grp < NG / 2;
-      const int j0 = 8 * (first ? grp : grp - NG / 2);
-      const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + j0);
-      const u32x4_t z4 = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + j0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float x = (t & 1) ? bf16_hi_to_f32(x4[t >> 1]) : bf16_lo_to_f32(x4[t >> 1]);
-        const float z = (t & 1) ? bf16_hi_to_f32(z4[t >> 1]) : bf16_lo_to_f32(z4[t >> 1]);
-        const float sn = s_sn[j0 + t], cs = s_cs[j0 + t];
-        y[t] = first ? (x * cs - z * sn) * c : (x * sn + z * cs) * c;
-      }
-    } else {  // pairs (d, d + 1), frequency index d/2
-      const u32x4_t x4 = *reinterpret_cast<const u32x4_t*>(qp + 8 * grp);
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const float x = bf16_lo_to_f32(x4[t >> 1]), z = bf16_hi_to_f32(x4[t >> 1]);
-        const int j = (8 * grp + t) >> 1;
-        const float sn = s_sn[j], cs = s_cs[j];
-        y[t] = (x * cs - z * sn) * c;
-        y[t + 1] = (x * sn + z * cs) * c;
-      }
-    }
-    u32x4_t hi, lo;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t h2[2], l2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        h2[e] = bf16_bits_rne(y[2 * w + e]);
-        l2[e] = bf16_bits_rne(y[2 * w + e] - __uint_as_float(h2[e] << 16));
-      }
-      hi[w] = h2[0] | (h2[1] << 16);
-      lo[w] = l2[0] | (l2[1] << 16);
-    }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.qhl + (((size_t)row * a.Hq + hq) * NG + grp) * 16);
-    dst[0] = hi;
-    dst[1] = lo;
-  }
+  float sn, cs;
+  rope_sincos(pos, a.inv_freq[j], &sn, &cs);
+  *reinterpret_cast<float2*>(a.qsc + (size_t)row * D + 2 * j) = make_float2(sn, cs);
+  (void)RPB;
 }
 
 // Maximum of a lane's 16 logits with the 3-input maximum (no canonicalising
@@ -311,23 +268,79 @@ void k_attn_bf16(AttnArgs a) {
   const int seg_hi = min(seg_lo + S, nkeys);
   const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
-  // ---- rotated, scaled query as bf16 hi + lo (B operand), from k_attn_qprep:
-  // dims d = 16*s + 8*g + t of k-step s are group 2s + g
+  // ---- rotated, scaled query as bf16 hi + lo (B operand).  The lane's dims
+  // of k-step s are 16*s + 8*g + t (t < 8).  RoPE pairs (j, j + D/2) (half
+  // style) fall in k-steps s and s + NS/2 of the same lane, pairs (2j, 2j+1)
+  // (interleaved) in one 8-dim group: the rotation is lane-local, with the
+  // row's sines and cosines from k_attn_setup.  y = rotated q times
+  // softmax_scale * log2(e) in fp32; hi = bf16(y), lo = bf16(y - hi).
+  // (Loaded and formed by prep_q, which is called once the first K/V block's
+  // loads are out, so that their latencies overlap.)
   u32x4_t qh[QT][NS], ql[QT][NS];
+  auto prep_q = [&]() {
+    const float cq = a.scale_log2;
+    const bool half = a.style == CT_ROPE_HALF;
+    auto elem = [](const u32x4_t& w, int t) {
+      return (t & 1) ? bf16_hi_to_f32(w[t >> 1]) : bf16_lo_to_f32(w[t >> 1]);
+    };
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
-        a.qhl + ((size_t)(valid[qt] ? row[qt] : 0) * Hq + hq) * D * 2);
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qh[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
-      ql[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (valid[qt]) {
-        qh[qt][s] = qp[2 * (2 * s + g)];
-        ql[qt][s] = qp[2 * (2 * s + g) + 1];
+      for (int s = 0; s < NS; ++s) {
+        qh[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
+        ql[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
       }
+      if (!valid[qt]) continue;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row[qt] * Hq + hq) * D + 8 * g;
+      const float* sc = a.qsc + (size_t)row[qt] * D;  // [D/2][2]: sine, cosine
+      u32x4_t xw[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xw[s] = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
+      float y[NS][8];
+      if (half) {
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+          float4 t4[4];  // (sin, cos) of j = 16 s + 8 g + t, t < 8
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t4[i] = *reinterpret_cast<const float4*>(sc + 2 * (16 * s + 8 * g) + 4 * i);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float sn = (t & 1) ? t4[t >> 1].z : t4[t >> 1].x;
+            const float cs = (t & 1) ? t4[t >> 1].w : t4[t >> 1].y;
+            const float x = elem(xw[s], t), z = elem(xw[s + NS / 2], t);
+            y[s][t] = (x * cs - z * sn) * cq;
+            y[s + NS / 2][t] = (x * sn + z * cs) * cq;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float4 t4[2];  // (sin, cos) of j = 8 s + 4 g + t/2, t < 8
+#pragma unroll
+          for (int i = 0; i < 2; ++i) t4[i] = *reinterpret_cast<const float4*>(sc + 2 * (8 * s + 4 * g) + 4 * i);
+#pragma unroll
+          for (int t = 0; t < 8; t += 2) {
+            const float sn = (t & 2) ? t4[t >> 2].z : t4[t >> 2].x;
+            const float cs = (t & 2) ? t4[t >> 2].w : t4[t >> 2].y;
+            const float x = elem(xw[s], t), z = elem(xw[s], t + 1);
+            y[s][t] = (x * cs - z * sn) * cq;
+            y[s][t + 1] = (x * sn + z * cs) * cq;
+          }
+        }
+      }
+      // (the packed conversion rounds to nearest even, like bf16_bits_rne)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x2_t yy = {y[s][2 * w], y[s][2 * w + 1]};
+          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(yy, bf16x2_t));
+          const f32x2_t rr = {yy[0] - __uint_as_float(hb << 16), yy[1] - __uint_as_float(hb & 0xffff0000u)};
+          qh[qt][s][w] = hb;
+          ql[qt][s][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2_t));
+        }
     }
-  }
+  };
 
   // ---- staging: K rows as 16-byte chunks; V as 2 keys x DPG dims per thread
   const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k);
@@ -563,10 +576,13 @@ void k_attn_bf16(AttnArgs a) {
   // (the segment's flags are read by the lanes in parallel and combined)
   bool wide_v = false;
   for (int kb = kb0 + lane; kb < kb1; kb += 64) wide_v |= a.vflag[kvh * a.nblk + kb] != 0;
+  // The first block's loads go out before the flags are known (they stay in
+  // bounds either way; the bf16 pass reloads), then the query's.
+  load_fast(kb0);
+  prep_q();
   const bool redo = __any(wide_v);
   f32x16_t st[QT][2];
   if (!redo) {
-    load_fast(kb0);
     store_fast(0, 0);
     if (kb0 + 1 < kb1) {
       load_fast(kb0 + 1);
@@ -783,7 +799,8 @@ __device__ void build_schedule(const AttnArgs& a, char* smem) {
 }
 
 // Per-layer set-up of the attention, one launch: block 0 builds the work
-// list, then one block per (64-key V tile, KV head) and one per query row.
+// list, then one block per (64-key V tile, KV head) and one per 256/(D/2)
+// query rows (their RoPE sines and cosines).
 template <int D>
 constexpr int setup_lds_bytes() {
   return BK * (D + 2) * 2 > kSchedMax * 12 + 4 ? BK * (D + 2) * 2 : kSchedMax * 12 + 4;
@@ -798,7 +815,7 @@ __global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
   else if (b < nv)
     prep_v_tile<D>(a, b % a.nblk, b / a.nblk, reinterpret_cast<uint16_t*>(smem));
   else
-    prep_q_row<D>(a, b - nv, reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + D / 2);
+    prep_q_rows<D>(a, (b - nv) * (256 / (D / 2)));
 }
 
 // Combine the per-segment results of rows whose keys span several segments:
@@ -886,7 +903,9 @@ template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
   {
     TimedLaunch tl_("attention_setup", stream);
-    hipLaunchKernelGGL((k_attn_setup<D>), dim3(1 + a.nblk * a.H + a.n_q), dim3(256), 0, stream, a);
+    constexpr int rpb = 256 / (D / 2);  // query rows per set-up block
+    hipLaunchKernelGGL((k_attn_setup<D>), dim3(1 + a.nblk * a.H + (a.n_q + rpb - 1) / rpb), dim3(256), 0,
+                       stream, a);
   }
   if (ct_status s = check_launch("attention set-up")) return s;
   const int blocks = a.H * a.blocks_per_head;
@@ -942,7 +961,7 @@ void attn_plan(AttnArgs* a, int n_cu) {
 }
 
 // Workspace: [partial outputs fp32][partial outputs fp16][record formats]
-// [partial log2-sum-exp][V^T fp16 tiles][tile flags][prepared queries]
+// [partial log2-sum-exp][V^T fp16 tiles][tile flags][query RoPE sines/cosines]
 // [work list, per-head counters, list length]
 struct AttnWs { size_t o16, fmt, lse, vt, flag, q, sched, total; };
 static AttnWs ws_layout(const AttnArgs& a) {
@@ -960,7 +979,7 @@ static AttnWs ws_layout(const AttnArgs& a) {
   w.flag = off;
   off += align256((size_t)a.H * a.nblk * 4);
   w.q = off;
-  off += align256((size_t)a.n_q * a.Hq * a.D * 4);
+  off += align256((size_t)a.n_q * a.D * 4);
   w.sched = off;
   off += align256(((size_t)a.n_tg * a.nseg + a.H + 1) * 4);
   w.total = off;
@@ -985,7 +1004,7 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   a.part_lse = reinterpret_cast<float*>(w + L.lse);
   a.vt16 = reinterpret_cast<uint16_t*>(w + L.vt);
   a.vflag = reinterpret_cast<int32_t*>(w + L.flag);
-  a.qhl = reinterpret_cast<uint16_t*>(w + L.q);
+  a.qsc = reinterpret_cast<float*>(w + L.q);
   a.sched_order = reinterpret_cast<int32_t*>(w + L.sched);
   a.sched_cnt = a.sched_order + (size_t)a.n_tg * a.nseg;
   a.sched_n = a.sched_cnt + a.H;
