@@ -416,6 +416,22 @@ def test_attention_long_split(orc, syn):
     _attn_case(orc, syn, 9000, 1, 4, 128, 77, "bf16", 500000.0, 0)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_split_partial_head_group(orc, syn, D):
+    """Keys split over several segments with 6 query heads (groups of 3 over 2
+    KV heads): the merge takes heads in fours, so its second group holds 2
+    heads and half its lanes idle; D = 64 gives 4 dims per merge lane; both
+    RoPE styles."""
+    _attn_case(orc, syn, 9000, 2, 6, D, 70, "bf16", 500000.0, 0 if D == 128 else 1)
+
+
+def test_attention_split_wide_values(orc, syn):
+    """Split segments with V beyond the fp16 range in some of them: those
+    segments' partials are stored as fp32, the others as fp16, and one row's
+    merge can read both kinds."""
+    _attn_case(orc, syn, 9000, 1, 4, 128, 60, "bf16", 500000.0, 0, v_mul=([40, 3000, 8500], 2.0 ** 16))
+
+
 def test_attention_group8_long(orc, syn):
     _attn_case(orc, syn, 3000, 1, 8, 128, 70, "bf16", 500000.0, 0, scale=0.1)
 
