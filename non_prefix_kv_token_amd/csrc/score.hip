@@ -51,6 +51,7 @@ __device__ inline double f64_from_bf16(uint16_t h) {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Round a double to fp16 with a single rounding (round-to-odd to binary32,
 // then round to nearest even).
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
   }
 }
 
-// Energy per token from the Gram of one problem (256 threads):
+// Energy per token from the Gram of one problem (NTH threads):
 // coefficients of E * nf^2 = sum_k A_k cos(k phi) + B_k sin(k phi), k < 2kk-1.
 // With weights w_j (1 for DC and the Nyquist bin, 2 otherwise) and
 // RR = G[j][j'], SS = G[kk+j][kk+j'], RS = G[j][kk+j']:
@@ -314,9 +315,15 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
   const int kk = d.kk, P2 = 2 * kk, nf = d.nf, N = d.n;
   const int K2 = 2 * kk - 1;
   const bool even = (nf % 2) == 0;
-  for (int k = tid; k < K2; k += NTH) {
+  // With at least 8 threads per coefficient, the 8 lanes of a coefficient
+  // take every 8th j and their sums are combined by a fixed butterfly
+  // (deterministic); otherwise one thread sums all j of a coefficient.
+  const bool par = 8 * K2 <= NTH;
+  const int jstep = par ? 8 : 1;
+  for (int k0 = par ? (tid >> 3) : tid; k0 < (par ? NTH / 8 : K2); k0 += NTH) {
+    const int k = k0;
     double alpha = 0.0, beta = 0.0, gamma = 0.0, dpos = 0.0, dneg = 0.0;
-    for (int j = 0; j < kk; ++j) {
+    for (int j = par ? (tid & 7) : 0; j < kk && k < K2; j += jstep) {
       double wj = (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0;
       int jp = j - k;  // j - j' = k
       if (jp >= 0) {
@@ -338,27 +345,50 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
         gamma += w * G[(size_t)j * P2 + kk + js];
       }
     }
+    if (par) {
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        alpha += __shfl_xor(alpha, o);
+        beta += __shfl_xor(beta, o);
+        gamma += __shfl_xor(gamma, o);
+        dpos += __shfl_xor(dpos, o);
+        dneg += __shfl_xor(dneg, o);
+      }
+      if ((tid & 7) != 0 || k >= K2) continue;
+    }
     double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
     double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
-    coef[k] = A;
-    coef[K2 + k] = B;
+    coef[2 * k] = A;  // interleaved: one 16-byte load per Horner step
+    coef[2 * k + 1] = B;
   }
   __syncthreads();
 
-  // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.
+  // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.  Each
+  // thread carries two tokens, n0 and n0 + NTH, through one coefficient loop
+  // (every coefficient load serves both chains).
   const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+  const double2* cf = reinterpret_cast<const double2*>(coef);  // {A_k, B_k}
   double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
   const double inv = 1.0 / ((double)nf * (double)nf);
-  for (int n = tid; n < N; n += NTH) {
-    double2 z = trig[n];
-    double pr = coef[K2 - 1], pi = -coef[2 * K2 - 1];
+  for (int n0 = tid; n0 < N; n0 += 2 * NTH) {
+    const bool two = n0 + NTH < N;
+    const double2 z0 = trig[n0], z1 = trig[two ? n0 + NTH : n0];
+    const double2 top = cf[K2 - 1];
+    double ar = top.x, ai = -top.y, br = top.x, bi = -top.y;
+#pragma unroll 4
     for (int k = K2 - 2; k >= 0; --k) {
-      double nr = pr * z.x - pi * z.y + coef[k];
-      double ni = pr * z.y + pi * z.x - coef[K2 + k];
-      pr = nr;
-      pi = ni;
+      const double2 c = cf[k];
+      const double anr = ar * z0.x - ai * z0.y + c.x;
+      const double ani = ar * z0.y + ai * z0.x - c.y;
+      const double bnr = br * z1.x - bi * z1.y + c.x;
+      const double bni = br * z1.y + bi * z1.x - c.y;
+      ar = anr;
+      ai = ani;
+      br = bnr;
+      bi = bni;
     }
-    E[n] = pr * inv;
+    E[n0] = ar * inv;
+    if (two) E[n0 + NTH] = br * inv;
   }
 }
 
@@ -555,7 +585,7 @@ __global__ __launch_bounds__(256) void k_gram_eval(ScoreLaunch sl, char* ws, int
     const int kk = d.kk, P2 = 2 * kk, ppad = d.ppad, nf = d.nf, N = d.n;
     const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
     double* G = slot;                          // [P2][P2]
-    double* coef = slot + (size_t)P2 * P2;     // [2][2kk-1]: cos then sin coefficients
+    double* coef = slot + (size_t)P2 * P2;     // [2kk-1][2]: cos and sin coefficient of each k
     const int nblk = (P2 + 127) / 128;
 
     for (int bi = 0; bi < nblk; ++bi)
@@ -629,21 +659,39 @@ __device__ double block_reduce(double v, int op, double* red) {
 
 // ---- 2'. Gram on the matrix cores (problems with 2*kk <= 128) ----------------
 // G = Y Y^T over the C channels.  Y (fp32) is split per stage of 64 channels
-// into three bf16 planes Y = Y1 + Y2 + Y3 (exact to 2^-26), and
+// into three bf16 planes Y = Y1 + Y2 + Y3 (each the round-to-nearest-even
+// bf16 of the previous remainder, exact to 2^-26), and
 //   G = Y1Y1 + Y1Y2 + Y2Y1 + Y1Y3 + Y3Y1 + Y2Y2   (dropped terms < 2^-25 |G|)
 // with bf16 products exact in fp32; accumulation in fp32 over 256 channels,
-// then in fp64.  Only tiles on or above the diagonal are computed; each
-// writes both halves.  Both MFMA operands are "8 channels of one band row",
-// so A and B are read from the same plane rows (no transpose).
+// then in fp64.  Only tiles on or above the diagonal are computed, one per
+// wave (at most 10 of the 16 waves); each writes both halves.  Both MFMA
+// operands are "8 channels of one band row", so A and B are read from the
+// same plane rows (no transpose).  The planes are double-buffered: after the
+// one barrier of a stage, the waves take that stage's products and then
+// convert the next stage (loaded one stage ahead into registers) into the
+// other buffer, so conversion and loads overlap the matrix cores.
 constexpr int kGramCh = 64;            // channels per stage
 constexpr int kGramPS = kGramCh + 8;   // plane row stride (bf16): 144 B
+constexpr int kGramThreads = 1024;
 
-__global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
-  // bf16 planes during the accumulation, then the fp64 Gram and coefficients
+// x = h1 + h2 + h3 (bf16 pairs, element 0 in the low half), each part the
+// round-to-nearest-even bf16 of what the previous parts leave; the
+// remainders are exact in fp32.
+__device__ inline void split3_bf16(f32x2_t x, uint32_t& h1, uint32_t& h2, uint32_t& h3) {
+  h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  const f32x2_t r1 = {x[0] - __uint_as_float(h1 << 16), x[1] - __uint_as_float(h1 & 0xffff0000u)};
+  h2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2_t));
+  const f32x2_t r2 = {r1[0] - __uint_as_float(h2 << 16), r1[1] - __uint_as_float(h2 & 0xffff0000u)};
+  h3 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
+}
+
+__global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char* ws) {
+  // two buffers of three bf16 planes during the accumulation, then the fp64
+  // Gram and coefficients
   __shared__ __attribute__((aligned(16))) double lds_g[128 * 128 + 256];
   typedef uint16_t plane_t[128 * kGramPS];
-  plane_t* pl = reinterpret_cast<plane_t*>(lds_g);
-  static_assert(sizeof(uint16_t) * 3 * 128 * kGramPS <= sizeof(double) * 128 * 128, "plane alias");
+  plane_t* pl = reinterpret_cast<plane_t*>(lds_g);  // [buffer * 3 + plane]
+  static_assert(sizeof(uint16_t) * 6 * 128 * kGramPS <= sizeof(double) * 128 * 128, "plane alias");
   const int L = sl.L, C = sl.C;
   const int prob = blockIdx.x;
   const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
@@ -652,111 +700,111 @@ __global__ __launch_bounds__(512) void k_gram_mfma(ScoreLaunch sl, char* ws) {
   const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, col = lane & 31;
 
-  // upper tiles of the nt x nt tile grid; wave w owns tiles w and w + 8
-  int tI[2] = {0, 0}, tJ[2] = {0, 0};
-  bool own[2] = {false, false};
+  // upper tile number `wave` of the nt x nt tile grid (nt <= 4: at most 10)
+  int tI = 0, tJ = 0;
+  bool own = false;
   {
     int u = 0;
     for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj, ++u) {
-        if (u == wave) { tI[0] = ti; tJ[0] = tj; own[0] = true; }
-        if (u == wave + 8) { tI[1] = ti; tJ[1] = tj; own[1] = true; }
-      }
+      for (int tj = ti; tj < nt; ++tj, ++u)
+        if (u == wave) { tI = ti; tJ = tj; own = true; }
   }
-  f32x16_t acc[2];
-  double accd[2][16];
+  f32x16_t acc;
+  double accd[16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { acc[i][v] = 0.f; accd[i][v] = 0.0; }
+  for (int v = 0; v < 16; ++v) { acc[v] = 0.f; accd[v] = 0.0; }
 
-  // Y of the next stage is loaded into registers during the current stage's
-  // products (ppad <= 128 rows x 16 float4 = at most 4 per thread).
-  constexpr int kPf = 128 * (kGramCh / 4) / 512;
-  float4 pf[kPf];
-  auto load_stage = [&](int c0) {
+  // one stage of Y: ppad <= 128 rows x 16 float4, at most 2 per thread;
+  // two register sets, so that each stage is loaded two stages ahead
+  constexpr int kPf = 128 * (kGramCh / 4) / kGramThreads;
+  float4 pfa[kPf], pfb[kPf];
+  auto load_stage = [&](int stage, float4* pf) {
+    const int c0 = stage * kGramCh;
 #pragma unroll
     for (int it = 0; it < kPf; ++it) {
-      const int item = tid + 512 * it, r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
+      const int item = tid + kGramThreads * it, r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
       if (item < ppad * (kGramCh / 4)) pf[it] = *reinterpret_cast<const float4*>(Y + (size_t)r * C + c0 + q4);
     }
   };
-  load_stage(0);
-  for (int c0 = 0; c0 < C; c0 += kGramCh) {
-    __syncthreads();
+  auto convert = [&](int buf, const float4* pf) {
 #pragma unroll
     for (int it = 0; it < kPf; ++it) {
-      const int item = tid + 512 * it;
+      const int item = tid + kGramThreads * it;
       if (item >= ppad * (kGramCh / 4)) break;
       const int r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
-      const float4 v = pf[it];
-      const float x[4] = {v.x, v.y, v.z, v.w};
-      uint32_t h[3][4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t b1 = bf16_rne_from_f32_bits(__float_as_uint(x[e]));
-        const float r1 = x[e] - __uint_as_float(b1 << 16);
-        const uint32_t b2 = bf16_rne_from_f32_bits(__float_as_uint(r1));
-        const float r2 = r1 - __uint_as_float(b2 << 16);
-        h[0][e] = b1;
-        h[1][e] = b2;
-        h[2][e] = bf16_rne_from_f32_bits(__float_as_uint(r2));
-      }
+      uint32_t h[3][2];
+      split3_bf16((f32x2_t){pf[it].x, pf[it].y}, h[0][0], h[1][0], h[2][0]);
+      split3_bf16((f32x2_t){pf[it].z, pf[it].w}, h[0][1], h[1][1], h[2][1]);
 #pragma unroll
       for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<uint2*>(&pl[q][r * kGramPS + q4]) =
-            make_uint2(h[q][0] | (h[q][1] << 16), h[q][2] | (h[q][3] << 16));
+        *reinterpret_cast<uint2*>(&pl[3 * buf + q][r * kGramPS + q4]) = make_uint2(h[q][0], h[q][1]);
     }
+  };
+
+  const int nst = C / kGramCh;
+  // products of stage st on buffer st & 1; then stage st + 1 (loaded two
+  // stages ago) converted into the other buffer, and stage st + 3 loaded
+  // into the register set that conversion freed
+  auto stage_step = [&](int st, int buf, const float4* pf_next, float4* pf_free) {
+    // Stage st's planes are complete, and stage st-1's reads of the other
+    // buffer are done, once every wave has passed this barrier.
     __syncthreads();
-    if (c0 + kGramCh < C) load_stage(c0 + kGramCh);
+    if (own) {
+      const plane_t* pb = pl + 3 * buf;
 #pragma unroll
-    for (int ks = 0; ks < kGramCh / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (!own[i]) continue;
-        const int ra = (tI[i] * 32 + col) * kGramPS + 16 * ks + 8 * g;
-        const int rb = (tJ[i] * 32 + col) * kGramPS + 16 * ks + 8 * g;
+      for (int ks = 0; ks < kGramCh / 16; ++ks) {
+        const int ra = (tI * 32 + col) * kGramPS + 16 * ks + 8 * g;
+        const int rb = (tJ * 32 + col) * kGramPS + 16 * ks + 8 * g;
         bf16x8_t a[3], bb[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          a[q] = *reinterpret_cast<const bf16x8_t*>(&pl[q][ra]);
-          bb[q] = *reinterpret_cast<const bf16x8_t*>(&pl[q][rb]);
+          a[q] = *reinterpret_cast<const bf16x8_t*>(&pb[q][ra]);
+          bb[q] = *reinterpret_cast<const bf16x8_t*>(&pb[q][rb]);
         }
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[0], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[1], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[0], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[2], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], bb[0], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[1], acc[i], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], bb[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], bb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[1], acc, 0, 0, 0);
       }
     }
-    if (((c0 + kGramCh) % 256) == 0 || c0 + kGramCh >= C) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          accd[i][v] += (double)acc[i][v];
-          acc[i][v] = 0.f;
-        }
+    if (st + 1 < nst) {
+      convert(buf ^ 1, pf_next);
+      if (st + 3 < nst) load_stage(st + 3, pf_free);
     }
+    if ((((st + 1) * kGramCh) % 256) == 0 || st + 1 == nst) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        accd[v] += (double)acc[v];
+        acc[v] = 0.f;
+      }
+    }
+  };
+  load_stage(0, pfa);
+  if (nst > 1) load_stage(1, pfb);
+  convert(0, pfa);
+  if (nst > 2) load_stage(2, pfa);
+  for (int st = 0; st < nst; st += 2) {
+    stage_step(st, 0, pfb, pfb);  // pfb: stage st + 1, then st + 3
+    if (st + 1 >= nst) break;
+    stage_step(st + 1, 1, pfa, pfa);  // pfa: stage st + 2, then st + 4
   }
   __syncthreads();  // planes no longer read: the buffer now holds G [P2][P2]
   double* Gs = lds_g;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (!own[i]) continue;
+  if (own) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = tI[i] * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      const int c = tJ[i] * 32 + col;
+      const int r = tI * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int c = tJ * 32 + col;
       if (r < P2 && c < P2) {
-        Gs[r * P2 + c] = accd[i][v];
-        Gs[c * P2 + r] = accd[i][v];
+        Gs[r * P2 + c] = accd[v];
+        Gs[c * P2 + r] = accd[v];
       }
     }
   }
   __syncthreads();
-  poly_energy<512>(d, layer, kv, Gs, lds_g + 128 * 128, ws);
+  poly_energy<kGramThreads>(d, layer, kv, Gs, lds_g + 128 * 128, ws);
 }
 
 // ---- L2 variant: energies without the frequency analysis ----------------------
@@ -1334,7 +1382,7 @@ ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* s
     const int n_probs = sl.n_chunks * sl.L * 2;
     if (sl.slot_p2 <= 128) {
       TimedLaunch tl_("gram", stream);
-      hipLaunchKernelGGL(k_gram_mfma, dim3(n_probs), dim3(512), 0, stream, sl, ws);
+      hipLaunchKernelGGL(k_gram_mfma, dim3(n_probs), dim3(kGramThreads), 0, stream, sl, ws);
       if (ct_status s = check_launch("gram/energy")) return s;
     } else {
       const int grid = std::min(n_probs, sl.n_slots);
