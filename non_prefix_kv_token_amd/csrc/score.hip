@@ -489,7 +489,6 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
       *reinterpret_cast<u32x4_t*>(&buf[(q * 32 * NTL + r) * kTwStride + 8 * i]) = twr[it];
     }
   };
-  float xmax = 0.f;  // F16: largest |x| met (NaN is not counted: it stays NaN in fp16)
   auto compute = [&](const uint16_t* buf, const uint32_t* xs) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -501,8 +500,6 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
           // bf16 -> fp32 is exact; fp32 -> fp16 is exact below 65536
           const float a0 = __uint_as_float(w0 << 16), a1 = __uint_as_float(w1 << 16);
           const float c0_ = __uint_as_float(w0 & 0xffff0000u), c1_ = __uint_as_float(w1 & 0xffff0000u);
-          xmax = __builtin_fmaxf(xmax, __builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
-          xmax = __builtin_fmaxf(xmax, __builtin_fmaxf(__builtin_fabsf(c0_), __builtin_fabsf(c1_)));
           bu[0][h] = pack_f16(a0, a1);
           bu[1][h] = pack_f16(c0_, c1_);
         } else {
@@ -555,7 +552,22 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
     }
   }
 
-  if (F16 && __any(!(xmax < 65536.f)) && lane == 0) *flag = 1;  // (inactive lanes hold 0)
+  if constexpr (F16) {
+    // The range test costs nothing inside the loop: |x| >= 65536 becomes
+    // +-inf in fp16 and a NaN stays NaN, and the DC row (twiddle 1 at every
+    // token, in the first row block of every channel group) then turns
+    // non-finite; finite fp16 data cannot overflow the fp32 sums at these
+    // lengths (|Y| < 8192 * 65504).  So a non-finite sum marks exactly the
+    // problems that need the bf16 pass.  (Inactive lanes hold zeros.)
+    bool bad = false;
+#pragma unroll
+    for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
+    if (__any(bad) && lane == 0) *flag = 1;
+  }
   if (!active) return;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
 #pragma unroll
