@@ -151,6 +151,11 @@ class Workload:
 
         self.k_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
         self.v_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
+        # second assembled-cache buffer and side stream of the two-stream step
+        self.asm = [(self.k_asm, self.v_asm),
+                    (torch.empty((self.T, H, D), dtype=tdt, device="cuda"),
+                     torch.empty((self.T, H, D), dtype=tdt, device="cuda"))]
+        self.side = torch.cuda.Stream()
         self.out = torch.empty((self.n_q, Hq, D), dtype=tdt, device="cuda")
         ws = ct.cachetune_recompute_attn_ws(self.n_q, Hq, self.T, H, D,
                                             ct.CT_BF16 if self.dtype == "bf16" else ct.CT_F32)
@@ -190,21 +195,32 @@ class Workload:
         self._places[l] = out
         return out
 
-    def assemble(self, l):
+    def assemble(self, l, buf=0):
         ksf, vsf = self.sfx[l]
-        self.ct.cachetune_assemble_rope(self.places(l), self.k_asm, self.v_asm, self.H, self.D,
+        k_asm, v_asm = self.asm[buf]
+        self.ct.cachetune_assemble_rope(self.places(l), k_asm, v_asm, self.H, self.D,
                                         self.theta, k_sfx=ksf, v_sfx=vsf, n_sfx=self.n_sfx,
                                         sfx_offset=self.T_c)
 
-    def attend(self, l):
-        self.ct.cachetune_recompute_attn(self.q[l], self.qpos, self.k_asm, self.v_asm, self.scale,
+    def attend(self, l, buf=0):
+        k_asm, v_asm = self.asm[buf]
+        self.ct.cachetune_recompute_attn(self.q[l], self.qpos, k_asm, v_asm, self.scale,
                                          self.theta, out=self.out, ws=self.attn_ws)
 
-    def step(self):
+    def step_serial(self):
+        """The step with every call in order on the current stream."""
         self.score_and_select()
         for l in range(self.L):
             self.assemble(l)
             self.attend(l)
+
+    def step(self):
+        """The step with each layer's assembly on the side stream (two
+        assembled-cache buffers), overlapping the previous layer's attention."""
+        from non_prefix_kv_token_amd.schedule import run_layers
+
+        self.score_and_select()
+        run_layers(self.L, self.assemble, self.attend, self.side)
 
     # ---- algorithmic work -----------------------------------------------------------
     def attn_flops_per_layer(self) -> float:
@@ -931,6 +947,7 @@ def main():
 
     for _ in range(args.warmup):
         w.step()
+        w.step_serial()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
@@ -942,39 +959,52 @@ def main():
     start, stop = E(), E()
     ct.cachetune_timing_enable(True)
     torch.cuda.synchronize()
+    # per-kernel figures: the step with every call in order on one stream, so
+    # that no kernel shares the GPU with another
     start.record()
     for _ in range(args.steps):
-        w.step()
+        w.step_serial()
     stop.record()
     torch.cuda.synchronize()
     ct.cachetune_timing_enable(False)
     ms_total = start.elapsed_time(stop)
     ms_step_eager = ms_total / args.steps
-    ms_step, launch = ms_step_eager, "eager"
+
+    def timed(fn):
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    ms_step_two = timed(w.step)  # eager, assembly on the side stream
+    ms_step, launch = ms_step_two, "eager, two streams"
+    ms_serial_graph = None
     if not args.no_graph:
-        # the same step captured once in a HIP graph and replayed: the kernels
-        # and their arguments are those of the eager step, without the per-call
+        # the steps captured once in a HIP graph and replayed: the kernels and
+        # their arguments are those of the eager steps, without the per-call
         # launch cost (timing events are off while capturing)
-        try:
+        def graph_ms(fn):
             graph = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()
             cap.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(cap):
-                w.step()
+                fn()
             torch.cuda.current_stream().wait_stream(cap)
             torch.cuda.synchronize()
             with torch.cuda.graph(graph, stream=cap):
-                w.step()
+                fn()
             for _ in range(args.warmup):
                 graph.replay()
             torch.cuda.synchronize()
-            start.record()
-            for _ in range(args.steps):
-                graph.replay()
-            stop.record()
-            torch.cuda.synchronize()
-            ms_step, launch = start.elapsed_time(stop) / args.steps, "hip-graph"
+            ms = timed(graph.replay)
             del graph
+            return ms
+
+        try:
+            ms_serial_graph = graph_ms(w.step_serial)
+            ms_step, launch = graph_ms(w.step), "hip-graph, two streams"
         except RuntimeError as e:  # capture unsupported here: keep the eager figure
             print(f"[bench] graph capture failed ({e}); reporting the eager step", file=sys.stderr, flush=True)
             torch.cuda.synchronize()
@@ -1023,6 +1053,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_step_eager,
+        "ms_per_step_eager_two_streams": ms_step_two,
+        "ms_per_step_serial_graph": ms_serial_graph,
         "launch": launch,
         "higher_is_better": True,
         "scaling": "weak",
