@@ -7,9 +7,12 @@
 //   high word: bitwise complement of an order-preserving image of the fp32
 //              score (so ascending key = descending score; -0 == +0; NaN last)
 //   low word:  local index (so equal scores rank by lower index)
-// sorted ascending by a bitonic network in LDS (n <= 8192).  The ascending
-// recomputation set and complement come from a block-wide prefix count over
-// the membership flags in index order.
+// sorted ascending by a bitonic network (n <= 8192).  Stages whose stride is
+// at least 128 pair elements across waves and run in LDS with a block barrier;
+// the others stay inside one wave's 128-element segments and run in registers
+// (lane-pair exchanges), two elements per lane.  The ascending recomputation
+// set and complement come from a block-wide prefix count over the membership
+// flags in index order (wave scans, then the wave totals).
 #include "ct_internal.h"
 
 namespace ct {
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* s
                                                    int32_t* comp) {
   __shared__ unsigned long long key[kMaxN];
   __shared__ unsigned char flag[kMaxN];
-  __shared__ int cnt[kThreads];
+  __shared__ int cnt[kThreads / 64];
   const TopRChunk& c = tl.c[blockIdx.x];
   const int n = c.n, k = c.k, tid = threadIdx.x;
   int p2 = 1;
@@ -42,19 +45,60 @@ __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* s
                    : ~0ull;
   }
   __syncthreads();
-  for (int size = 2; size <= p2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < p2 / 2; i += kThreads) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        unsigned long long a = key[lo], b = key[hi];
-        if ((a > b) == up) {
-          key[lo] = b;
-          key[hi] = a;
-        }
+  // one compare-exchange stage in LDS: pairs (lo, lo + stride), ascending
+  // where bit `size` of lo is clear
+  auto lds_stage = [&](int size, int stride) {
+    for (int i = tid; i < p2 / 2; i += kThreads) {
+      int lo = 2 * i - (i & (stride - 1));
+      int hi = lo + stride;
+      bool up = (lo & size) == 0;
+      unsigned long long a = key[lo], b = key[hi];
+      if ((a > b) == up) {
+        key[lo] = b;
+        key[hi] = a;
+      }
+    }
+    __syncthreads();
+  };
+  if (p2 < 128) {
+    for (int size = 2; size <= p2; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) lds_stage(size, stride);
+  } else {
+    // Stages of stride <= 64 pair positions inside one 128-element segment:
+    // lane l holds positions x = base + l (a) and x + 64 (b).  At stride 64
+    // the pair is (a, b); below it, the partner of position x is x ^ s, in
+    // lane l ^ s.  The lower position of a pair keeps the smaller key where
+    // bit `size` of the position is clear, the larger one elsewhere.
+    const int wave = tid >> 6, lane = tid & 63, nseg = p2 >> 7;
+    auto wave_stages = [&](int size_lo, int size_hi, int s_first) {
+      for (int seg = wave; seg < nseg; seg += kThreads / 64) {
+        const int x = seg * 128 + lane;
+        unsigned long long a = key[x], b = key[x + 64];
+        for (int size = size_lo; size <= size_hi; size <<= 1)
+          for (int st = min(s_first, size >> 1); st > 0; st >>= 1) {
+            if (st == 64) {
+              if ((a > b) == ((x & size) == 0)) {
+                const unsigned long long t = a;
+                a = b;
+                b = t;
+              }
+            } else {
+              const unsigned long long pa = __shfl_xor(a, st), pb = __shfl_xor(b, st);
+              const bool lower = (x & st) == 0;
+              const bool min_a = lower == ((x & size) == 0), min_b = lower == (((x + 64) & size) == 0);
+              a = (min_a == (pa < a)) ? pa : a;
+              b = (min_b == (pb < b)) ? pb : b;
+            }
+          }
+        key[x] = a;
+        key[x + 64] = b;
       }
       __syncthreads();
+    };
+    wave_stages(2, 128, 64);  // every stage of the sizes up to 128
+    for (int size = 256; size <= p2; size <<= 1) {
+      for (int stride = size >> 1; stride >= 128; stride >>= 1) lds_stage(size, stride);
+      wave_stages(size, size, 64);
     }
   }
   for (int r = tid; r < n; r += kThreads) {
@@ -69,15 +113,15 @@ __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* s
   const int i0 = tid * per, i1 = min(n, i0 + per);
   int mine = 0;
   for (int i = i0; i < i1; ++i) mine += flag[i];
-  cnt[tid] = mine;
-  __syncthreads();
-  for (int s = 1; s < kThreads; s <<= 1) {  // inclusive Hillis-Steele scan
-    int v = tid >= s ? cnt[tid - s] : 0;
-    __syncthreads();
-    cnt[tid] += v;
-    __syncthreads();
+  int incl = mine;  // inclusive scan over the wave's lanes
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += t;
   }
-  int before = cnt[tid] - mine;  // selected indices below i0
+  if ((tid & 63) == 63) cnt[tid >> 6] = incl;  // wave totals
+  __syncthreads();
+  int before = incl - mine;  // selected indices below i0
+  for (int w = 0; w < (tid >> 6); ++w) before += cnt[w];
   for (int i = i0; i < i1; ++i) {
     if (flag[i]) {
       sel[c.sel_off + before] = i;
