@@ -17,7 +17,7 @@
 //  2. the channel Gram G = Y Y^T (fp64);
 //  3. E[n] as a trigonometric polynomial of degree 2(kk-1) in phi = 2*pi*n/nf,
 //     whose coefficients are diagonal and anti-diagonal sums of G; evaluated
-//     with a complex Horner scheme in fp64.
+//     in fp64 by Clenshaw's recurrence, once per token pair (n, nf - n).
 //  4. per token a = sqrt(E_K), b = sqrt(E_V), s = a/2 + b/2, per-layer
 //     normalisation, mean over layers (fp64, fixed-order reductions).
 #include "ct_internal.h"
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
 //   gamma_s = 2 sum_{j+j'=s} w w RS,     delta_d = 2 sum_{j-j'=d} w w RS,
 //   A_0 = (alpha_0 + beta_0)/2,  A_k = (2 alpha_k + beta_k)/2,
 //   B_k = (gamma_k - delta_k + delta_{-k})/2.
-// E is then evaluated for every token by a complex Horner scheme in fp64.
+// E is then evaluated in fp64 by Clenshaw's recurrence, once per token pair.
 template <int NTH>
 __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const double* G,
                             double* coef, char* ws) {
@@ -358,37 +358,46 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
     }
     double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
     double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
-    coef[2 * k] = A;  // interleaved: one 16-byte load per Horner step
+    coef[2 * k] = A;  // interleaved: one 16-byte load per recurrence step
     coef[2 * k + 1] = B;
   }
   __syncthreads();
 
-  // Horner in z = exp(i phi): sum_k (A_k - i B_k) z^k, real part.  Each
-  // thread carries two tokens, n0 and n0 + NTH, through one coefficient loop
-  // (every coefficient load serves both chains).
+  // E = U + V with U = sum_k A_k cos(k phi), V = sum_k B_k sin(k phi).  Tokens
+  // m and nf - m share U and have opposite V, so each thread evaluates both
+  // series once for a pair, by Clenshaw's recurrence for the cos/sin basis
+  // (b_k = c_k + 2 cos(phi) b_{k+1} - b_{k+2}; U = A_0 + b_1 cos(phi) - b_2,
+  // V = d_1 sin(phi)).  Token 0 (phi = 0) is the sum of the A_k, taken by
+  // wave 0 in a fixed order.
   const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
   const double2* cf = reinterpret_cast<const double2*>(coef);  // {A_k, B_k}
   double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
   const double inv = 1.0 / ((double)nf * (double)nf);
-  for (int n0 = tid; n0 < N; n0 += 2 * NTH) {
-    const bool two = n0 + NTH < N;
-    const double2 z0 = trig[n0], z1 = trig[two ? n0 + NTH : n0];
-    const double2 top = cf[K2 - 1];
-    double ar = top.x, ai = -top.y, br = top.x, bi = -top.y;
+  for (int m = tid + 1; m <= nf / 2; m += NTH) {
+    const double2 z = trig[m];
+    const double c2 = 2.0 * z.x;
+    double u1 = 0.0, u2 = 0.0, v1 = 0.0, v2 = 0.0;  // b_{k+1}, b_{k+2} of U and of V
 #pragma unroll 4
-    for (int k = K2 - 2; k >= 0; --k) {
-      const double2 c = cf[k];
-      const double anr = ar * z0.x - ai * z0.y + c.x;
-      const double ani = ar * z0.y + ai * z0.x - c.y;
-      const double bnr = br * z1.x - bi * z1.y + c.x;
-      const double bni = br * z1.y + bi * z1.x - c.y;
-      ar = anr;
-      ai = ani;
-      br = bnr;
-      bi = bni;
+    for (int k = K2 - 1; k >= 1; --k) {
+      const double2 ab = cf[k];
+      const double u0 = fma(c2, u1, ab.x - u2);
+      const double v0 = fma(c2, v1, ab.y - v2);
+      u2 = u1;
+      u1 = u0;
+      v2 = v1;
+      v1 = v0;
     }
-    E[n0] = ar * inv;
-    if (two) E[n0 + NTH] = br * inv;
+    const double U = cf[0].x + u1 * z.x - u2, V = v1 * z.y;
+    if (m < N) E[m] = (U + V) * inv;
+    const int mp = nf - m;
+    if (mp != m && mp < N) E[mp] = (U - V) * inv;
+  }
+  if (tid < 64) {
+    double a0 = 0.0;
+    for (int k = tid; k < K2; k += 64) a0 += cf[k].x;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a0 += __shfl_xor(a0, o);
+    if (tid == 0) E[0] = a0 * inv;
   }
 }
 
