@@ -692,7 +692,7 @@ def r_sweep(args):
         w = Workload(args.workload, r=r)
         ct = w.ct
         for _ in range(args.warmup):
-            w.step()
+            w.step_serial()
         torch.cuda.synchronize()
         for n in names:
             ct.cachetune_timing_read(n)
@@ -700,7 +700,7 @@ def r_sweep(args):
         ct.cachetune_timing_enable(True)
         a.record()
         for _ in range(args.steps):
-            w.step()
+            w.step_serial()  # one stream: no kernel shares the GPU with another
         z.record()
         torch.cuda.synchronize()
         ct.cachetune_timing_enable(False)
