@@ -315,51 +315,51 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
   const int kk = d.kk, P2 = 2 * kk, nf = d.nf, N = d.n;
   const int K2 = 2 * kk - 1;
   const bool even = (nf % 2) == 0;
-  // With at least 8 threads per coefficient, the 8 lanes of a coefficient
-  // take every 8th j and their sums are combined by a fixed butterfly
-  // (deterministic); otherwise one thread sums all j of a coefficient.
-  const bool par = 8 * K2 <= NTH;
-  const int jstep = par ? 8 : 1;
-  for (int k0 = par ? (tid >> 3) : tid; k0 < (par ? NTH / 8 : K2); k0 += NTH) {
-    const int k = k0;
-    double alpha = 0.0, beta = 0.0, gamma = 0.0, dpos = 0.0, dneg = 0.0;
-    for (int j = par ? (tid & 7) : 0; j < kk && k < K2; j += jstep) {
-      double wj = (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0;
-      int jp = j - k;  // j - j' = k
+  // the five sums of coefficient k over j = j0, j0 + jstep, ... < kk
+  struct Sums { double alpha, beta, gamma, dpos, dneg; };
+  auto wt = [&](int j) { return (j == 0 || (even && 2 * j == nf)) ? 1.0 : 2.0; };
+  auto sums = [&](int k, int j0, int jstep) {
+    Sums t = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int j = j0; j < kk; j += jstep) {
+      const double wj = wt(j);
+      const int jp = j - k;  // j - j' = k
       if (jp >= 0) {
-        double wjp = (jp == 0 || (even && 2 * jp == nf)) ? 1.0 : 2.0;
-        double w = wj * wjp;
-        alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
-        dpos += w * G[(size_t)j * P2 + kk + jp];
+        const double w = wj * wt(jp);
+        t.alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
+        t.dpos += w * G[(size_t)j * P2 + kk + jp];
       }
-      int jn = j + k;  // j - j' = -k
-      if (k > 0 && jn < kk) {
-        double wjn = (jn == 0 || (even && 2 * jn == nf)) ? 1.0 : 2.0;
-        dneg += wj * wjn * G[(size_t)j * P2 + kk + jn];
-      }
-      int js = k - j;  // j + j' = k
+      const int jn = j + k;  // j - j' = -k
+      if (k > 0 && jn < kk) t.dneg += wj * wt(jn) * G[(size_t)j * P2 + kk + jn];
+      const int js = k - j;  // j + j' = k
       if (js >= 0 && js < kk) {
-        double wjs = (js == 0 || (even && 2 * js == nf)) ? 1.0 : 2.0;
-        double w = wj * wjs;
-        beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
-        gamma += w * G[(size_t)j * P2 + kk + js];
+        const double w = wj * wt(js);
+        t.beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
+        t.gamma += w * G[(size_t)j * P2 + kk + js];
       }
     }
-    if (par) {
+    return t;
+  };
+  auto store = [&](int k, const Sums& t) {
+    coef[2 * k] = (k == 0) ? 0.5 * (t.alpha + t.beta) : 0.5 * ((k < kk ? 2.0 * t.alpha : 0.0) + t.beta);
+    coef[2 * k + 1] =  // (interleaved: one 16-byte load per recurrence step)
+        (k == 0) ? 0.0 : 0.5 * (2.0 * t.gamma - (k < kk ? 2.0 * (t.dpos - t.dneg) : 0.0));
+  };
+  if (8 * K2 <= NTH) {
+    // 8 lanes per coefficient, each taking every 8th j; a fixed butterfly
+    // combines their sums (deterministic)
+    const int k = tid >> 3;
+    Sums t = k < K2 ? sums(k, tid & 7, 8) : Sums{0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        alpha += __shfl_xor(alpha, o);
-        beta += __shfl_xor(beta, o);
-        gamma += __shfl_xor(gamma, o);
-        dpos += __shfl_xor(dpos, o);
-        dneg += __shfl_xor(dneg, o);
-      }
-      if ((tid & 7) != 0 || k >= K2) continue;
+    for (int o = 1; o < 8; o <<= 1) {
+      t.alpha += __shfl_xor(t.alpha, o);
+      t.beta += __shfl_xor(t.beta, o);
+      t.gamma += __shfl_xor(t.gamma, o);
+      t.dpos += __shfl_xor(t.dpos, o);
+      t.dneg += __shfl_xor(t.dneg, o);
     }
-    double A = (k == 0) ? 0.5 * (alpha + beta) : 0.5 * ((k < kk ? 2.0 * alpha : 0.0) + beta);
-    double B = (k == 0) ? 0.0 : 0.5 * (2.0 * gamma - (k < kk ? 2.0 * (dpos - dneg) : 0.0));
-    coef[2 * k] = A;  // interleaved: one 16-byte load per recurrence step
-    coef[2 * k + 1] = B;
+    if ((tid & 7) == 0 && k < K2) store(k, t);
+  } else {
+    for (int k = tid; k < K2; k += NTH) store(k, sums(k, 0, 1));
   }
   __syncthreads();
 
