@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
 //   B_k = (gamma_k - delta_k + delta_{-k})/2.
 // E is then evaluated in fp64 by Clenshaw's recurrence, once per token pair.
 template <int NTH>
-__device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const double* G,
+__device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const double* G, int ldg,
                             double* coef, char* ws) {
   const int tid = threadIdx.x;
   const int kk = d.kk, P2 = 2 * kk, nf = d.nf, N = d.n;
@@ -325,16 +325,16 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
       const int jp = j - k;  // j - j' = k
       if (jp >= 0) {
         const double w = wj * wt(jp);
-        t.alpha += w * (G[(size_t)j * P2 + jp] + G[(size_t)(kk + j) * P2 + kk + jp]);
-        t.dpos += w * G[(size_t)j * P2 + kk + jp];
+        t.alpha += w * (G[(size_t)j * ldg + jp] + G[(size_t)(kk + j) * ldg + kk + jp]);
+        t.dpos += w * G[(size_t)j * ldg + kk + jp];
       }
       const int jn = j + k;  // j - j' = -k
-      if (k > 0 && jn < kk) t.dneg += wj * wt(jn) * G[(size_t)j * P2 + kk + jn];
+      if (k > 0 && jn < kk) t.dneg += wj * wt(jn) * G[(size_t)j * ldg + kk + jn];
       const int js = k - j;  // j + j' = k
       if (js >= 0 && js < kk) {
         const double w = wj * wt(js);
-        t.beta += w * (G[(size_t)j * P2 + js] - G[(size_t)(kk + j) * P2 + kk + js]);
-        t.gamma += w * G[(size_t)j * P2 + kk + js];
+        t.beta += w * (G[(size_t)j * ldg + js] - G[(size_t)(kk + j) * ldg + kk + js]);
+        t.gamma += w * G[(size_t)j * ldg + kk + js];
       }
     }
     return t;
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(256) void k_gram_eval(ScoreLaunch sl, char* ws, int
       }
     __syncthreads();
 
-    poly_energy<256>(d, layer, kv, G, coef, ws);
+    poly_energy<256>(d, layer, kv, G, P2, coef, ws);
     __syncthreads();
   }
 }
@@ -709,10 +709,12 @@ __device__ inline void split3_bf16(f32x2_t x, uint32_t& h1, uint32_t& h2, uint32
 __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char* ws) {
   // two buffers of three bf16 planes during the accumulation, then the fp64
   // Gram and coefficients
-  __shared__ __attribute__((aligned(16))) double lds_g[128 * 128 + 256];
+  // G rows are P2 + 1 doubles apart: an odd stride puts the column-wise
+  // (transposed) writes and the coefficient sums' reads on different banks
+  __shared__ __attribute__((aligned(16))) double lds_g[128 * 129 + 256];
   typedef uint16_t plane_t[128 * kGramPS];
   plane_t* pl = reinterpret_cast<plane_t*>(lds_g);  // [buffer * 3 + plane]
-  static_assert(sizeof(uint16_t) * 6 * 128 * kGramPS <= sizeof(double) * 128 * 128, "plane alias");
+  static_assert(sizeof(uint16_t) * 6 * 128 * kGramPS <= sizeof(double) * 128 * 129, "plane alias");
   const int L = sl.L, C = sl.C;
   const int prob = blockIdx.x;
   const int b = prob / (2 * L), layer = (prob / 2) % L, kv = prob % 2;
@@ -811,21 +813,22 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char
     if (st + 1 >= nst) break;
     stage_step(st + 1, 1, pfa, pfa);  // pfa: stage st + 2, then st + 4
   }
-  __syncthreads();  // planes no longer read: the buffer now holds G [P2][P2]
+  __syncthreads();  // planes no longer read: the buffer now holds G [P2][P2 + 1]
   double* Gs = lds_g;
+  const int ldg = P2 + 1;
   if (own) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = tI * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       const int c = tJ * 32 + col;
       if (r < P2 && c < P2) {
-        Gs[r * P2 + c] = accd[v];
-        Gs[c * P2 + r] = accd[v];
+        Gs[r * ldg + c] = accd[v];
+        Gs[c * ldg + r] = accd[v];
       }
     }
   }
   __syncthreads();
-  poly_energy<kGramThreads>(d, layer, kv, Gs, lds_g + 128 * 128, ws);
+  poly_energy<kGramThreads>(d, layer, kv, Gs, ldg, lds_g + 128 * 129, ws);
 }
 
 // ---- L2 variant: energies without the frequency analysis ----------------------
