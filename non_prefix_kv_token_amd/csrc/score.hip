@@ -1140,8 +1140,8 @@ __global__ __launch_bounds__(kFinThreads) void k_layer_norm(ScoreLaunch sl, char
   double s[kFinPer];
   double part_sum = 0.0, part_max = -INFINITY, part_min = INFINITY;
 #pragma unroll
-  for (int i = 0; i < kFinPer; ++i) {
-    const int n = tid * kFinPer + i;
+  for (int i = 0; i < kFinPer; ++i) {  // token i * kFinThreads + tid: coalesced, all threads busy
+    const int n = i * kFinThreads + tid;
     s[i] = 0.0;
     if (n < N) {
       s[i] = 0.5 * sqrt(fmax(ek[n], 0.0)) + 0.5 * sqrt(fmax(ev[n], 0.0));
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(kFinThreads) void k_layer_norm(ScoreLaunch sl, char
   }
 #pragma unroll
   for (int i = 0; i < kFinPer; ++i) {
-    const int n = tid * kFinPer + i;
+    const int n = i * kFinThreads + tid;
     if (n < N) {
       double v = fill >= 0.0 ? fill : (s[i] - shift) / denom;
       if (sl.norm == CT_NORM_NONE) v = s[i];
@@ -1181,8 +1181,17 @@ __global__ __launch_bounds__(256) void k_layer_mean(ScoreLaunch sl, char* ws, fl
   const int n = blockIdx.x * 256 + threadIdx.x, N = d.n, L = sl.L;
   if (n >= N) return;
   const double* e = reinterpret_cast<const double*>(ws + d.e_off);
+  // sum in layer order; the loads of 8 layers are issued before they are added
   double acc = 0.0;
-  for (int l = 0; l < L; ++l) acc += e[(size_t)(l * 2) * N + n];
+  int l = 0;
+  for (; l + 8 <= L; l += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = e[(size_t)((l + u) * 2) * N + n];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; l < L; ++l) acc += e[(size_t)(l * 2) * N + n];
   score[d.tok_off + n] = (float)(acc / (double)L);
 }
 
