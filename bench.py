@@ -38,6 +38,10 @@ WORKLOADS = {
     "llama3-8b-16x2048-shuffled": dict(ns=[2048] * 16, L=32, H=8, Hq=32, D=128, dtype="bf16",
                                        alpha=(1, 16), r=(15, 100), theta=500000.0, n_sfx=128,
                                        seed=20260523, shuffle=True),
+    # 64 chunks with seeded lengths uniform in [512, 4096] (stream 1 of the seed), 36 layers
+    "qwen3-4b-64-ragged": dict(ns=None, ragged=(1, 64, 512, 4096), L=36, H=8, Hq=32, D=128,
+                               dtype="bf16", alpha=(1, 32), r=(15, 100), theta=1000000.0, n_sfx=128,
+                               seed=20260524, shuffle=False),
 }
 
 
@@ -61,6 +65,8 @@ class Workload:
         self.cfg = cfg
         self.ct = ct
         ns, self.L = cfg["ns"], cfg["L"] if layers is None else layers
+        if ns is None:  # seeded ragged chunk lengths
+            ns = [int(x) for x in syn.uniform_ints(cfg["seed"], *cfg["ragged"])]
         self.H, self.Hq, self.D = cfg["H"], cfg["Hq"], cfg["D"]
         self.theta, self.alpha, self.r = cfg["theta"], cfg["alpha"], (cfg["r"] if r is None else tuple(r))
         self.dtype = cfg["dtype"]
@@ -88,6 +94,8 @@ class Workload:
             v = syn.chunk(seed, syn.V, b, L, n, H, D, self.dtype)
             self.chunks.append((_dev(k), _dev(v)))
             del k, v
+            if b % 16 == 15:
+                print(f"[bench] {b + 1} of {nb} chunks generated", file=sys.stderr, flush=True)
         self.gen_seconds = time.time() - t0
 
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -147,6 +155,8 @@ class Workload:
             qrows[m] = syn.rows(seed, syn.Q, syn.SUFFIX_CHUNK, l, self.n_sfx, Hq, D, local[qpos[m]],
                                 self.dtype)
             self.q.append(_dev(qrows))
+            if l % 8 == 7:
+                print(f"[bench] {l + 1} of {L} layers of rows and queries generated", file=sys.stderr, flush=True)
         self.gen_seconds += time.time() - t0
 
         self.k_asm = torch.empty((self.T, H, D), dtype=tdt, device="cuda")
