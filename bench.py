@@ -10,7 +10,12 @@ Default workload: 8 chunks x 2048 tokens, Llama-3-8B-shaped (32 layers, 32 Q /
 RoPE theta 500000 at cumulative chunk offsets, 128-token suffix.
 
 Prints ONE JSON line (rank 0).  `value` = chunk-KV tokens (sum of chunk lengths)
-per second of whole-step time.
+per second through score -> top-r -> assembly with deferred RoPE of every layer
+(the metric's path, `ms_per_step`), with its fraction of the HBM peak under
+roofline.metric_path; the whole step with the attention is reported under
+`full_step`, the attention kernel's MFMA fraction under `roofline`.  The default
+run also times the 128K-context ragged workload (64 chunks, Qwen3-4B-shaped)
+under `ragged_128k`.
 """
 from __future__ import annotations
 
@@ -224,6 +229,13 @@ class Workload:
             self.assemble(l)
             self.attend(l)
 
+    def metric_step(self):
+        """The path the headline metric covers: score every chunk (all layers),
+        top-r, then every layer's assembly with deferred RoPE (one stream)."""
+        self.score_and_select()
+        for l in range(self.L):
+            self.assemble(l)
+
     def step(self):
         """The step with each layer's assembly on the side stream (two
         assembled-cache buffers), overlapping the previous layer's attention."""
@@ -260,26 +272,50 @@ class Workload:
         return float(self.T) * row * 2 * 2 + 4.0 * sum(self.ns)  # read + write K and V, indices
 
 
-def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
+def cpu_baseline(w: "Workload", attn_rows: int = 12):
     """The oracle timed on a bounded sample of the same workload, scaled to one
     step (score of every chunk and layer, top-r, assembly and attention of every
-    layer)."""
+    layer).  The same sample is compared with the GPU's outputs of the step
+    (untimed), so the line also reports the parity of what it measured."""
     import oracle as orc
     import synth as syn
+    import torch
 
+    ct = w.ct
     L, H, Hq, D = w.L, w.H, w.Hq, w.D
     n0 = w.ns[0]
-    k = syn.chunk(w.seed, syn.K, 0, budget_layers, n0, H, D, w.dtype)
-    v = syn.chunk(w.seed, syn.V, 0, budget_layers, n0, H, D, w.dtype)
+    edt = np.uint16 if w.dtype == "bf16" else np.float32
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    def widen(a):
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if a.dtype == np.uint16 \
+            else a.astype(np.float64)
+
+    # GPU outputs of the step for the sample: scores and set of chunk 0, the
+    # assembled layer 0 and its attention (re-run untimed into spare buffers)
+    w.score_and_select()
+    w.assemble(0, 1)
+    out0 = torch.empty_like(w.out)
+    ct.cachetune_recompute_attn(w.q[0], w.qpos, w.asm[1][0], w.asm[1][1], w.scale, w.theta, out=out0,
+                                ws=w.attn_ws)
+    torch.cuda.synchronize()
+    s_gpu = host(w.score)[:n0].astype(np.float64)
+    sel_gpu = w.sel_host[0]
+    k_gpu, v_gpu, o_gpu = host(w.asm[1][0]), host(w.asm[1][1]), host(out0)
+
+    k = syn.chunk(w.seed, syn.K, 0, L, n0, H, D, w.dtype)
+    v = syn.chunk(w.seed, syn.V, 0, L, n0, H, D, w.dtype)
     t0 = time.perf_counter()
     s = orc.score_chunk(k, v, *w.alpha)
-    t_score = (time.perf_counter() - t0) * (L / budget_layers) * (sum(w.ns) / n0)
+    t_score = (time.perf_counter() - t0) * (sum(w.ns) / n0)
     t0 = time.perf_counter()
     for _ in range(len(w.ns)):
-        orc.topr(s, orc.ksel(n0, *w.r))
+        _, sel_orc, _ = orc.topr(s, orc.ksel(n0, *w.r))
     t_topr = time.perf_counter() - t0
     # assembly of one layer
-    edt = np.uint16 if w.dtype == "bf16" else np.float32
     k_out = np.zeros((w.T, H, D), edt)
     v_out = np.zeros((w.T, H, D), edt)
     t_asm_layer = 0.0
@@ -292,25 +328,49 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
         t1 = time.perf_counter()  # generation above is not timed
         orc.assemble_chunk(ks_, vs_, kr, vr, sel, int(w.offsets[b]), w.theta, 0, k_out, v_out)
         t_asm_layer += time.perf_counter() - t1
-    ksf, vsf = (x.cpu() for x in w.sfx[0])
-    import torch as _t
-    ksf = ksf.view(_t.int16).numpy().view(np.uint16) if w.dtype == "bf16" else ksf.numpy()
-    vsf = vsf.view(_t.int16).numpy().view(np.uint16) if w.dtype == "bf16" else vsf.numpy()
+    ksf, vsf = (host(x) for x in w.sfx[0])
     t1 = time.perf_counter()
     orc.assemble_rows(ksf, vsf, w.T_c, w.theta, 0, k_out, v_out)
     t_asm_layer += time.perf_counter() - t1
     # attention of a sample of query rows, scaled by visible-key counts
     rows = np.linspace(0, w.n_q - 1, attn_rows).astype(np.int32)
-    q = w.q[0].cpu()
-    import torch
-    qh = q.view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else q.numpy()
+    qh = host(w.q[0])
     t0 = time.perf_counter()
-    orc.attention(qh, w.qpos_host, k_out, v_out, w.scale, w.theta, rows=rows)
+    o_ref, _ = orc.attention(qh, w.qpos_host, k_out, v_out, w.scale, w.theta, rows=rows)
     t_attn_sample = time.perf_counter() - t0
     frac = float(np.sum(w.qpos_host[rows] + 1.0)) / float(np.sum(w.qpos_host + 1.0))
     t_attn = t_attn_sample / frac * L
     t_step = t_score + t_topr + t_asm_layer * L + t_attn
+    t_metric = t_score + t_topr + t_asm_layer * L
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    # parity of the sample (the tolerances of the parity tests)
+    k_sel = orc.ksel(n0, *w.r)
+    kth = np.sort(s)[::-1][k_sel - 1]
+    diff = set(sel_gpu.tolist()) ^ set(sel_orc.tolist())
+    exempt = [i for i in diff if abs(s[i] - kth) <= 1e-6 * kth]
+    if w.dtype == "bf16":
+        def key(x):
+            x = x.astype(np.int32)
+            return np.where(x & 0x8000, -(x & 0x7FFF), x & 0x7FFF)
+        k_ulp = int(np.abs(key(k_gpu) - key(k_out)).max())
+    else:
+        k_ulp = float(np.abs(widen(k_gpu) - widen(k_out)).max())
+    a_err = np.abs(widen(o_gpu)[rows] - o_ref)
+    parity = {
+        "score_chunk0_max_rel_err": float(np.max(np.abs(s_gpu - s) / s)),
+        "score_tol_rel": 1e-4,
+        "index_set_chunk0_differences": len(diff),
+        "index_set_tie_exemptions": len(exempt),
+        "assembled_layer0_v_bit_exact": bool(np.array_equal(v_gpu, v_out)),
+        "assembled_layer0_k_max_ulp" if w.dtype == "bf16" else "assembled_layer0_k_max_abs_err": k_ulp,
+        "attention_layer0_rows": int(len(rows)),
+        "attention_max_abs_err": float(a_err.max()),
+        "attention_tol_abs": 2e-2,
+        "ok": bool(np.max(np.abs(s_gpu - s) / s) <= 1e-4 and len(exempt) == len(diff)
+                   and np.array_equal(v_gpu, v_out)),
+    }
+
     # the same score and attention samples on one thread (a child process with
     # OMP_NUM_THREADS=1), scaled the same way
     single = None
@@ -318,7 +378,8 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
         import subprocess
         import tempfile
         with tempfile.TemporaryDirectory() as td:
-            np.savez(os.path.join(td, "s.npz"), k=k, v=v, q=qh, qpos=w.qpos_host, ko=k_out, vo=v_out, rows=rows)
+            np.savez(os.path.join(td, "s.npz"), k=k[:2], v=v[:2], q=qh, qpos=w.qpos_host, ko=k_out, vo=v_out,
+                     rows=rows)
             code = ("import sys, time, json, numpy as np; sys.path.insert(0, %r); import oracle as orc; "
                     "d = np.load(%r); t0 = time.perf_counter(); orc.score_chunk(d['k'], d['v'], %d, %d); "
                     "t1 = time.perf_counter(); orc.attention(d['q'], d['qpos'], d['ko'], d['vo'], %r, %r, "
@@ -327,10 +388,12 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
             env = dict(os.environ, OMP_NUM_THREADS="1")
             r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
             ts, ta = json.loads(r.stdout.strip().splitlines()[-1])
-        t1_step = ts * (L / budget_layers) * (sum(w.ns) / n0) + t_topr + t_asm_layer * L * threads + ta / frac * L
-        single = {"value": sum(w.ns) / t1_step, "cores": 1,
-                  "note": "score and attention samples re-timed on one thread; top-r as measured, "
-                          "assembly scaled by the thread count"}
+        ts_all = ts * (L / 2) * (sum(w.ns) / n0)
+        t1_metric = ts_all + t_topr + t_asm_layer * L * threads
+        single = {"value": sum(w.ns) / t1_metric, "cores": 1,
+                  "whole_step_tokens_per_s": sum(w.ns) / (t1_metric + ta / frac * L),
+                  "note": "score sample (2 layers of chunk 0) and attention sample re-timed on one thread; "
+                          "top-r as measured, assembly scaled by the thread count"}
     except Exception as e:  # the baseline is a report, not the product: keep the multi-thread figure
         single = {"error": str(e)[:200]}
     model = ""
@@ -340,19 +403,20 @@ def cpu_baseline(w: "Workload", budget_layers: int = 2, attn_rows: int = 12):
     except OSError:
         pass
     return {
-        "value": sum(w.ns) / t_step,
+        "value": sum(w.ns) / t_metric,
         "unit": "chunk-KV tokens/s",
         "cores": threads,
         "cpu_model": model,
         "kind": "oracle",
-        "sample": (f"score: 1 chunk x {budget_layers} of {L} layers, scaled x{L // budget_layers} layers "
-                   f"x{len(w.ns)} chunks; top-r: all chunks; assembly: layer 0, scaled x{L}; "
-                   f"attention: {attn_rows} query rows x {Hq} heads of layer 0, scaled by visible keys "
-                   f"and x{L}"),
-        "seconds_est_per_step": t_step,
+        "sample": (f"score: chunk 0, all {L} layers, scaled x{len(w.ns)} chunks; top-r: all chunks; assembly: "
+                   f"layer 0, scaled x{L}; attention: {attn_rows} query rows x {Hq} heads of layer 0, scaled "
+                   f"by visible keys and x{L}"),
+        "whole_step_tokens_per_s": sum(w.ns) / t_step,
+        "seconds_est_per_step": t_metric,
         "stage_seconds_est": {"score": t_score, "topr": t_topr, "assemble": t_asm_layer * L,
                               "attention": t_attn},
         "single_thread": single,
+        "parity_of_sample": parity,
     }
 
 
@@ -409,9 +473,11 @@ def host_tier(args):
     T = T_c + n_sfx
     offs = [b * N for b in range(nb)]
     t0 = time.time()
-    pool = []
+    from non_prefix_kv_token_amd.hosttier import HostTierPipeline, build_host_pool
     ranking = torch.empty(T_c, dtype=torch.int32, device="cuda")
-    # score on the device in groups of chunks, rank-order, keep only the host pool
+    # score on the device, rank-order, keep the host pool (and, on the device,
+    # the leading half of each ranked layer, from which the recomputed rows of
+    # this synthetic request are drawn)
     score = torch.empty(T_c, dtype=torch.float32, device="cuda")
     dev = []
     for b in range(nb):
@@ -422,13 +488,12 @@ def host_tier(args):
     ct.cachetune_score_chunk(dev, L, H, D, alpha=alpha, score=score)
     ct.cachetune_select_topr(score, ns, r=(15, 100), ranking=ranking)
     rank_h = ranking.cpu().numpy()
+    pool = build_host_pool(dev, ranking, ns)
+    k_max = N // 2  # recomputed rows per chunk that the kept device rows cover
+    lead = []
     for b in range(nb):
         kr, vr = ct.cachetune_rank_order(dev[b][0], dev[b][1], ranking[offs[b]:offs[b] + N])
-        pk = torch.empty(kr.shape, dtype=kr.dtype, pin_memory=True)
-        pv = torch.empty(vr.shape, dtype=vr.dtype, pin_memory=True)
-        pk.copy_(kr)
-        pv.copy_(vr)
-        pool.append((pk, pv, kr[:, :N // 2].clone(), vr[:, :N // 2].clone()))  # device: leading rows
+        lead.append((kr[:, :k_max].clone(), vr[:, :k_max].clone()))
         del kr, vr
     del dev
     torch.cuda.synchronize()
@@ -457,13 +522,13 @@ def host_tier(args):
     copy_stream = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
     def setup(k_per_chunk):
-        """Per-ratio state (staging buffers, recomputed rows, queries, places);
+        """Per-ratio state (the package's pipeline, recomputed rows, queries);
         returns (request, rows staged per layer, n_q, release)."""
         ks = list(k_per_chunk)
-        rows = sum(N - k for k in ks)
-        k_stage = [torch.empty((rows, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-        v_stage = [torch.empty_like(k_stage[0]) for _ in range(2)]
+        if max(ks) > k_max:
+            raise ValueError(f"k = {max(ks)} recomputed rows exceed the {k_max} ranked rows kept on the device")
         # selected rows: the first k of each ranking; recomputed rows are the cached
         # rows plus seeded noise, in ascending local order
         sel_list, rec = [], []
@@ -477,8 +542,8 @@ def host_tier(args):
             perm = torch.from_numpy(order).cuda()
             lr = []
             for l in range(L):
-                kc = pool[b][2][l, :ks[b]].index_select(0, perm).float()
-                vc = pool[b][3][l, :ks[b]].index_select(0, perm).float()
+                kc = lead[b][0][l, :ks[b]].index_select(0, perm).float()
+                vc = lead[b][1][l, :ks[b]].index_select(0, perm).float()
                 kc += 0.25 * torch.randn(kc.shape, generator=gen, device="cuda")
                 vc += 0.25 * torch.randn(vc.shape, generator=gen, device="cuda")
                 lr.append((kc.bfloat16(), vc.bfloat16()))
@@ -488,6 +553,7 @@ def host_tier(args):
                                       [np.arange(T_c, T)])).astype(np.int32)
         n_q = len(qpos)
         qpos_d = _dev(qpos)
+        before_wait = after_attend = None
         if full:
             bf = torch.bfloat16
             mk = lambda n: torch.empty((n_q, n), dtype=bf, device="cuda")  # noqa: E731
@@ -496,73 +562,50 @@ def host_tier(args):
             qb, krb, vrb = mk(Hq * D), mk(H * D), mk(H * D)
             gub, ab = mk(2 * d_ff), mk(d_ff)
             row0 = [int(np.searchsorted(qpos, offs[b])) for b in range(nb)]
-            rec = [[(krb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D), vrb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D))
-                    for _ in range(L)] for b in range(nb)]
+            rec_fn = lambda l, b: (krb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D),  # noqa: E731
+                                   vrb[row0[b]:row0[b] + ks[b]].view(ks[b], H, D))
             qs = [qb.view(n_q, Hq, D)] * L
             s0 = n_q - n_sfx
-            sfx_l = [(krb[s0:].view(n_sfx, H, D), vrb[s0:].view(n_sfx, H, D))] * L
+            sfx_fn = lambda l: (krb[s0:].view(n_sfx, H, D), vrb[s0:].view(n_sfx, H, D))  # noqa: E731
+
+            def before_wait(l):  # the layer's own k / v rows for the selected and suffix tokens
+                ct.cachetune_rmsnorm(hb, g1, 1e-5, out=xb)
+                ct.cachetune_qkv_proj(xb, wqkv, Hq * D, H * D, q=qb, k=krb, v=vrb)
+
+            def after_attend(l):
+                ct.cachetune_linear(out.view(n_q, Hq * D), wo, residual=hb, out=h1b)
+                ct.cachetune_rmsnorm(h1b, g2, 1e-5, out=xb)
+                ct.cachetune_linear(xb, wgu, out=gub)
+                ct.cachetune_silu_mul(gub, out=ab)
+                ct.cachetune_linear(ab, wd, residual=h1b, out=hb)
         else:
             qs = [(2.0 * torch.randn((n_q, Hq, D), generator=gen, device="cuda")).bfloat16() for _ in range(L)]
-            sfx_l = sfx
+            rec_fn = lambda l, b: rec[b][l]  # noqa: E731
+            sfx_fn = lambda l: sfx[l]  # noqa: E731
+        pipe = HostTierPipeline(pool, ranking, ns, ks, offs, sel, rec_fn, sfx_fn, n_sfx, theta,
+                                copy_stream=copy_stream)
         ws = torch.empty(max(256, ct.cachetune_recompute_attn_ws(n_q, Hq, T, H, D)), dtype=torch.uint8,
                          device="cuda")
         out = torch.empty((n_q, Hq, D), dtype=torch.bfloat16, device="cuda")
-        places = []
-        for l in range(L):
-            pl = []
-            so, at = 0, 0
-            for b in range(nb):
-                k = ks[b]
-                pl.append(ct.make_place(k_stage[l % 2][at:], v_stage[l % 2][at:], N, k, offs[b],
-                                        src_rows=ranking[offs[b] + k:], sel=sel[so:],
-                                        k_rec=rec[b][l][0], v_rec=rec[b][l][1]))
-                so, at = so + k, at + N - k
-            places.append(pl)
         scale = 1.0 / math.sqrt(D)
-
-        # staging buffer l % 2 is free once the assembly that last read it is done
-        # (also across requests)
-        ev_free = [torch.cuda.Event(), torch.cuda.Event()]
-        used = [False, False]
-        state = [k_stage, v_stage, rec, qs, ws, out, places]
+        state = [pipe, rec, qs, ws, out]
         if full:
             state += [h0, hb, h1b, xb, qb, krb, vrb, gub, ab]
 
+        def attend(l, ka, va):
+            ct.cachetune_recompute_attn(qs[l], qpos_d, ka, va, scale, theta, out=out, ws=ws)
+
         def request():
-            ev_ready = [torch.cuda.Event() for _ in range(L)]
             if full:
-                with torch.cuda.stream(comp):
-                    hb.copy_(h0)
-            for l in range(L):
-                with torch.cuda.stream(copy_stream):
-                    if used[l % 2]:
-                        copy_stream.wait_event(ev_free[l % 2])
-                    ct.cachetune_stage_complement([(p[0], p[1]) for p in pool], l, ks, k_stage[l % 2],
-                                                  v_stage[l % 2], stream=copy_stream)
-                    ev_ready[l].record(copy_stream)
-                if full:  # the layer's own k / v rows for the selected and suffix tokens
-                    ct.cachetune_rmsnorm(hb, g1, 1e-5, out=xb, stream=comp)
-                    ct.cachetune_qkv_proj(xb, wqkv, Hq * D, H * D, q=qb, k=krb, v=vrb, stream=comp)
-                comp.wait_event(ev_ready[l])
-                ct.cachetune_assemble_rope(places[l], k_asm, v_asm, H, D, theta, k_sfx=sfx_l[l][0],
-                                           v_sfx=sfx_l[l][1], n_sfx=n_sfx, sfx_offset=T_c, stream=comp)
-                ev_free[l % 2].record(comp)
-                used[l % 2] = True
-                ct.cachetune_recompute_attn(qs[l], qpos_d, k_asm, v_asm, scale, theta, out=out, ws=ws,
-                                            stream=comp)
-                if full:
-                    ct.cachetune_linear(out.view(n_q, Hq * D), wo, residual=hb, out=h1b, stream=comp)
-                    ct.cachetune_rmsnorm(h1b, g2, 1e-5, out=xb, stream=comp)
-                    ct.cachetune_linear(xb, wgu, out=gub, stream=comp)
-                    ct.cachetune_silu_mul(gub, out=ab, stream=comp)
-                    ct.cachetune_linear(ab, wd, residual=h1b, out=hb, stream=comp)
+                hb.copy_(h0)
+            pipe.request(k_asm, v_asm, attend, before_wait=before_wait, after_attend=after_attend)
 
         def release():
             state.clear()
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
 
-        return request, rows, n_q, release
+        return request, pipe.rows, n_q, release
 
     def measure(request, steps):
         """Mean ms per request after two untimed requests (the first request of
@@ -612,7 +655,7 @@ def host_tier(args):
                 print(f"[bench] calibration probe r={r:.4f} (k={k}) {ms:.1f} ms", file=sys.stderr, flush=True)
                 return ms
 
-            r_star, n_probes = ct.cachetune_calibrate_ratio(t_c, t_i, cost, r_min=r_min, r_max=1.0,
+            r_star, n_probes = ct.cachetune_calibrate_ratio(t_c, t_i, cost, r_min=r_min, r_max=0.5,
                                                             half_width=0.1, eps=0.01)
             calibration["runs"].append({"r_min": r_min, "r_star": r_star, "probes": probes,
                                         "n_probes": n_probes})
@@ -897,6 +940,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3-8b-8x2048", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the 128K-context ragged workload that the default run also times")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager step only (no HIP-graph replay)")
     ap.add_argument("--host-tier", action="store_true",
@@ -955,90 +1000,38 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    for _ in range(args.warmup):
-        w.step()
-        w.step_serial()
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-
-    attn_names = ("attention_setup", "attention", "attention_merge")
-    names = ["twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
-    for n in names:  # drop records of earlier launches
-        ct.cachetune_timing_read(n)
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    start, stop = E(), E()
-    ct.cachetune_timing_enable(True)
-    torch.cuda.synchronize()
-    # per-kernel figures: the step with every call in order on one stream, so
-    # that no kernel shares the GPU with another
-    start.record()
-    for _ in range(args.steps):
-        w.step_serial()
-    stop.record()
-    torch.cuda.synchronize()
-    ct.cachetune_timing_enable(False)
-    ms_total = start.elapsed_time(stop)
-    ms_step_eager = ms_total / args.steps
-
-    def timed(fn):
-        start.record()
-        for _ in range(args.steps):
-            fn()
-        stop.record()
+    result = measure_workload(w, args, graph=not args.no_graph)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+    ref = stream_references()
+    result["stages"].update(ref)
+    result["stages"]["metric_frac_copy"] = result["roofline"]["metric_path"]["achieved"] / ref["copy_GBs"]
+    result["stages"]["metric_frac_read"] = result["roofline"]["metric_path"]["achieved"] / ref["read_GBs"]
+    if args.workload == "llama3-8b-8x2048" and not args.no_ragged:
+        # the largest workload, timed in the same run after the default one's
+        # buffers are released
+        del w
         torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps
+        torch.cuda.empty_cache()
+        print("[bench] building workload qwen3-4b-64-ragged", file=sys.stderr, flush=True)
+        w4 = Workload("qwen3-4b-64-ragged")
+        print(f"[bench] inputs generated in {w4.gen_seconds:.1f}s; T={w4.T} n_q={w4.n_q}", file=sys.stderr,
+              flush=True)
+        r4 = measure_workload(w4, argparse.Namespace(steps=2, warmup=1), graph=False)
+        result["ragged_128k"] = {k: r4[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                                      "stages", "full_step")}
+        del w4
+        torch.cuda.empty_cache()
+    print(json.dumps(result), flush=True)
 
-    ms_step_two = timed(w.step)  # eager, assembly on the side stream
-    ms_step, launch = ms_step_two, "eager, two streams"
-    ms_serial_graph = None
-    if not args.no_graph:
-        # the steps captured once in a HIP graph and replayed: the kernels and
-        # their arguments are those of the eager steps, without the per-call
-        # launch cost (timing events are off while capturing)
-        def graph_ms(fn):
-            graph = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                fn()
-            torch.cuda.current_stream().wait_stream(cap)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(graph, stream=cap):
-                fn()
-            for _ in range(args.warmup):
-                graph.replay()
-            torch.cuda.synchronize()
-            ms = timed(graph.replay)
-            del graph
-            return ms
 
-        try:
-            ms_serial_graph = graph_ms(w.step_serial)
-            ms_step, launch = graph_ms(w.step), "hip-graph, two streams"
-        except RuntimeError as e:  # capture unsupported here: keep the eager figure
-            print(f"[bench] graph capture failed ({e}); reporting the eager step", file=sys.stderr, flush=True)
-            torch.cuda.synchronize()
-    kt = {n: ct.cachetune_timing_read(n) for n in names}  # name -> (total ms, launches)
-
-    def per_step(*ns):
-        return sum(kt[n][0] for n in ns) / args.steps
-
-    def per_launch(n):
-        tot, cnt = kt[n]
-        return tot / cnt if cnt else float("nan")
-
-    tokens = float(sum(w.ns))
-    score_ms = per_step("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr")
-    asm_ms = per_step("assemble") / w.L
-    attn_call_ms = per_step(*attn_names) / w.L
-    attn_kernel_ms = per_launch("attention")
-    attn_flops = w.attn_flops_per_layer()
-    attn_tflops = attn_flops / (attn_kernel_ms * 1e-3) / 1e12
-    score_gbs = w.score_bytes() / (score_ms * 1e-3) / 1e9
-    asm_gbs = w.assemble_bytes_per_layer() / (asm_ms * 1e-3) / 1e9
-    traffic = measured_traffic("attention", w.name)
-    # reference: a plain 1 GiB device-to-device copy (read + write), the
-    # bandwidth a streaming kernel can reach on this part
+def stream_references():
+    """Bandwidth of plain streaming kernels on this part: a 1 GiB
+    device-to-device copy (read + write) and a read-only pass (torch's sum of a
+    1 GiB fp32 tensor, whose only write is the scalar result)."""
+    import torch
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -1050,22 +1043,124 @@ def main():
     cz.record()
     torch.cuda.synchronize()
     copy_gbs = 5 * 2.0 * (1 << 30) / (ca.elapsed_time(cz) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    x = src.view(torch.float32)
+    x.zero_()
+    x.sum()
+    torch.cuda.synchronize()
+    ca.record()
+    for _ in range(5):
+        x.sum()
+    cz.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * float(1 << 30) / (ca.elapsed_time(cz) * 1e-3) / 1e9
+    del src, x
+    torch.cuda.empty_cache()
+    return {"copy_GBs": copy_gbs, "read_GBs": read_gbs}
+
+
+def measure_workload(w, args, graph=True):
+    """Time one workload: per-kernel figures from the serial step (every call
+    in order on one stream, HIP events per kernel), the metric's path
+    (score -> top-r -> assemble, all layers) and the whole step (with the
+    selected-query attention), each replayed from a HIP graph when `graph`."""
+    import torch
+    ct = w.ct
+    for _ in range(args.warmup):
+        w.step()
+        w.step_serial()
+        w.metric_step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done", file=sys.stderr, flush=True)
+
+    attn_names = ("attention_setup", "attention", "attention_merge")
+    score_names = ("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr")
+    names = [*score_names, "assemble", *attn_names]
+    for n in names:  # drop records of earlier launches
+        ct.cachetune_timing_read(n)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, stop = E(), E()
+
+    def timed(fn):
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    # per-kernel figures: the serial step, so that no kernel shares the GPU with another
+    ct.cachetune_timing_enable(True)
+    torch.cuda.synchronize()
+    ms_step_eager = timed(w.step_serial)
+    ct.cachetune_timing_enable(False)
+    kt = {n: ct.cachetune_timing_read(n) for n in names}  # name -> (total ms, launches)
+    ms_metric_eager = timed(w.metric_step)
+    ms_step_two = timed(w.step)  # eager, assembly on the side stream
+    ms_metric, metric_launch = ms_metric_eager, "eager, one stream"
+    ms_step, launch = ms_step_two, "eager, two streams"
+    ms_serial_graph = None
+    if graph:
+        # the steps captured once in a HIP graph and replayed: the kernels and
+        # their arguments are those of the eager steps, without the per-call
+        # launch cost (timing events are off while capturing)
+        def graph_ms(fn):
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                fn()
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            ms = timed(g.replay)
+            del g
+            return ms
+
+        try:
+            ms_metric, metric_launch = graph_ms(w.metric_step), "hip-graph, one stream"
+            ms_serial_graph = graph_ms(w.step_serial)
+            ms_step, launch = graph_ms(w.step), "hip-graph, two streams"
+        except RuntimeError as e:  # capture unsupported here: keep the eager figures
+            print(f"[bench] graph capture failed ({e}); reporting the eager steps", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+
+    def per_step(*ns):
+        return sum(kt[n][0] for n in ns) / args.steps
+
+    def per_launch(n):
+        tot, cnt = kt[n]
+        return tot / cnt if cnt else float("nan")
+
+    tokens = float(sum(w.ns))
+    score_ms = per_step(*score_names)
+    asm_ms = per_step("assemble") / w.L
+    attn_call_ms = per_step(*attn_names) / w.L
+    attn_kernel_ms = per_launch("attention")
+    attn_flops = w.attn_flops_per_layer()
+    attn_tflops = attn_flops / (attn_kernel_ms * 1e-3) / 1e12
+    score_gbs = w.score_bytes() / (score_ms * 1e-3) / 1e9
+    asm_gbs = w.assemble_bytes_per_layer() / (asm_ms * 1e-3) / 1e9
+    metric_bytes = w.score_bytes() + w.L * w.assemble_bytes_per_layer()
+    metric_gbs = metric_bytes / (ms_metric * 1e-3) / 1e9
     band_ms = per_step("band")
     band_tflops = w.band_mfma_flops() / (band_ms * 1e-3) / 1e12 if band_ms > 0 else float("nan")
-
-    result = {
-        "metric": "chunk-KV tokens/s through score->top-r->RoPE-assemble (+ selected-query attention); %HBM peak",
-        "value": tokens / (ms_step * 1e-3),
+    print(f"[bench] {w.name}: metric path {ms_metric:.3f} ms ({tokens / ms_metric * 1e-3:.3g} M tokens/s, "
+          f"{metric_gbs / PEAK_HBM_GBS:.1%} of HBM); whole step {ms_step:.2f} ms; attention "
+          f"{attn_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    return {
+        "metric": "chunk-KV tokens/s through score->top-r->RoPE-assemble; %HBM peak",
+        "value": tokens / (ms_metric * 1e-3),
         "unit": "chunk-KV tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "ms_per_step_eager": ms_step_eager,
-        "ms_per_step_eager_two_streams": ms_step_two,
-        "ms_per_step_serial_graph": ms_serial_graph,
-        "launch": launch,
+        "ms_per_step": ms_metric,
+        "launch": metric_launch,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1076,7 +1171,8 @@ def main():
                          f"{w.L} layers, {w.Hq} Q / {w.H} KV heads x {w.D}, {w.dtype}, cutoff "
                          f"{w.alpha[0]}/{w.alpha[1]} of rFFT bins, r={w.r[0]}/{w.r[1]}, RoPE theta "
                          f"{w.theta:g}, {w.n_sfx}-token suffix"),
-            "name": w.name, "T": w.T, "n_q": w.n_q, "parallelism": "single GPU",
+            "name": w.name, "T": w.T, "n_q": w.n_q, "chunk_tokens": int(tokens), "parallelism": "single GPU",
+            "step": "score all chunks (all layers) -> top-r -> assemble every layer with deferred RoPE",
         },
         "roofline": {
             "kernel": "k_attn_bf16 (selected-query causal GQA attention, one layer)" if w.dtype == "bf16"
@@ -1086,32 +1182,38 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
+            "traffic": measured_traffic("attention", w.name),
             "traffic_unit": "bytes per launch",
             "launch_ms": attn_kernel_ms,
             "algorithmic_flops_per_launch": attn_flops,
+            "metric_path": {
+                "what": "score (all chunks, all layers) + top-r + assembly of every layer, one step",
+                "bound": "hbm", "achieved": metric_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": metric_gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_step": metric_bytes,
+                "ms_per_step": ms_metric,
+            },
+        },
+        "full_step": {
+            "what": "the metric path plus every layer's selected-query attention (Q RoPE + causal GQA)",
+            "ms_per_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3), "launch": launch,
+            "ms_per_step_eager_serial": ms_step_eager, "ms_per_step_eager_two_streams": ms_step_two,
+            "ms_per_step_serial_graph": ms_serial_graph,
         },
         "stages": {
-            "copy_GBs": copy_gbs,
+            "metric_ms_eager": ms_metric_eager,
             "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
-            "score_frac_copy": score_gbs / copy_gbs,
             "band_mfma_TFLOPs_issued": band_tflops, "band_frac_bf16_peak": band_tflops / PEAK_BF16_TFLOPS,
-            "score_kernels_ms": {n: per_step(n) for n in ("twiddle", "band", "band_redo", "gram", "layer_norm",
-                                                           "layer_mean", "topr")},
+            "score_kernels_ms": {n: per_step(n) for n in score_names},
             "assemble_ms_per_layer": asm_ms, "assemble_GBs": asm_gbs,
-            "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS, "assemble_frac_copy": asm_gbs / copy_gbs,
+            "assemble_frac_hbm": asm_gbs / PEAK_HBM_GBS,
             "attention_call_ms_per_layer": attn_call_ms,
             "attention_kernels_ms_per_layer": {n: per_step(n) / w.L for n in attn_names},
-            "attention_TFLOPs": attn_tflops,
+            "attention_TFLOPs": attn_tflops, "attention_frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
             "attention_flops_per_layer": attn_flops,
-            "score_plus_assemble_tokens_per_s": tokens / ((score_ms + asm_ms * w.L) * 1e-3),
+            "score_tokens_per_s": tokens / (score_ms * 1e-3),
+            "assemble_tokens_per_s": tokens / (asm_ms * w.L * 1e-3),
         },
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(result), flush=True)
-
 
 if __name__ == "__main__":
     main()

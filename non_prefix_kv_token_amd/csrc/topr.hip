@@ -1,7 +1,8 @@
 // Top-r selection -- "Adaptive KV Cache Reuse for Fast Long-Context LLM
-// Serving" (CacheTune), App. B.1: the top-ranked rN positions of a chunk form
-// the recomputation set, the rest its reuse complement; the full ranking is
-// stored so that another r only moves the cut.
+// Serving" (CacheTune), App. B.1.  Per chunk: sort the positions by score,
+// take the first floor(r * n) as the positions to recompute and keep the
+// others for reuse; the whole order is written out once, so a different r
+// later only changes where it is cut.
 //
 // One block (1024 threads) per chunk.  Each score becomes a 64-bit key
 //   high word: bitwise complement of an order-preserving image of the fp32

@@ -288,7 +288,7 @@ int orc_score_chunk(const void* K, const void* V, int dtype, int L, int N,
   return 0;
 }
 
-/* ---- top-r selection (App. B.1: the top-ranked rN positions) ---- */
+/* ---- top-r selection (App. B.1: the highest-scoring floor(rN) positions) ---- */
 
 static const double* g_sort_key;
 static int cmp_rank(const void* pa, const void* pb) {

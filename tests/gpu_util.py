@@ -5,6 +5,13 @@ import pytest
 import torch
 
 
+# Attention log-sum-exp (natural log of the softmax normaliser of the scaled
+# logits), checked per (row, query head): 2e-2 absolute, the output bound
+# applied to the normaliser's logarithm (a factor of at most e^0.02 in the
+# normaliser of every row).
+LSE_TOL = 2e-2
+
+
 def need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
