@@ -357,6 +357,12 @@ def cpu_baseline(w: "Workload", attn_rows: int = 12):
     else:
         k_ulp = float(np.abs(widen(k_gpu) - widen(k_out)).max())
     a_err = np.abs(widen(o_gpu)[rows] - o_ref)
+    # the parity tests' bound: 2e-2 plus half the spacing of the output type
+    # at the reference value (bf16 holds 8 significant bits)
+    if w.dtype == "bf16":
+        a_tol = 2e-2 + 0.5 * 2.0 ** (np.floor(np.log2(np.maximum(np.abs(o_ref), 2.0 ** -126))) - 7)
+    else:
+        a_tol = np.full(o_ref.shape, 2e-2)
     parity = {
         "score_chunk0_max_rel_err": float(np.max(np.abs(s_gpu - s) / s)),
         "score_tol_rel": 1e-4,
@@ -366,9 +372,11 @@ def cpu_baseline(w: "Workload", attn_rows: int = 12):
         "assembled_layer0_k_max_ulp" if w.dtype == "bf16" else "assembled_layer0_k_max_abs_err": k_ulp,
         "attention_layer0_rows": int(len(rows)),
         "attention_max_abs_err": float(a_err.max()),
-        "attention_tol_abs": 2e-2,
+        "attention_max_abs_err_where_abs_out_le_4": float(a_err[np.abs(o_ref) <= 4.0].max(initial=0.0)),
+        "attention_tol": "2e-2 + half a bf16 ulp of the output" if w.dtype == "bf16" else "2e-2",
+        "attention_max_err_over_tol": float((a_err / a_tol).max()),
         "ok": bool(np.max(np.abs(s_gpu - s) / s) <= 1e-4 and len(exempt) == len(diff)
-                   and np.array_equal(v_gpu, v_out)),
+                   and np.array_equal(v_gpu, v_out) and (a_err <= a_tol).all()),
     }
 
     # the same score and attention samples on one thread (a child process with
@@ -1028,8 +1036,8 @@ def main():
 
 def stream_references():
     """Bandwidth of plain streaming kernels on this part: a 1 GiB
-    device-to-device copy (read + write) and a read-only pass (torch's sum of a
-    1 GiB fp32 tensor, whose only write is the scalar result)."""
+    device-to-device copy (read + write) and read-only passes over 1 GiB
+    (torch reductions whose writes are negligible; the fastest is kept)."""
     import torch
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -1046,17 +1054,23 @@ def stream_references():
     del dst
     x = src.view(torch.float32)
     x.zero_()
-    x.sum()
-    torch.cuda.synchronize()
-    ca.record()
-    for _ in range(5):
-        x.sum()
-    cz.record()
-    torch.cuda.synchronize()
-    read_gbs = 5 * float(1 << 30) / (ca.elapsed_time(cz) * 1e-3) / 1e9
+    reads = {"sum": lambda: x.sum(), "rows_sum": lambda: x.view(-1, 4096).sum(dim=1),
+             "amax": lambda: x.amax(), "i64_sum": lambda: src.view(torch.int64).sum()}
+    read_rates = {}
+    for name, fn in reads.items():
+        fn()
+        torch.cuda.synchronize()
+        ca.record()
+        for _ in range(5):
+            fn()
+        cz.record()
+        torch.cuda.synchronize()
+        read_rates[name] = 5 * float(1 << 30) / (ca.elapsed_time(cz) * 1e-3) / 1e9
+    read_gbs = max(read_rates.values())
     del src, x
     torch.cuda.empty_cache()
-    return {"copy_GBs": copy_gbs, "read_GBs": read_gbs}
+    return {"copy_GBs": copy_gbs, "read_GBs": read_gbs,
+            "read_GBs_by_kernel": {k: round(v, 1) for k, v in read_rates.items()}}
 
 
 def measure_workload(w, args, graph=True):

@@ -265,21 +265,25 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
  *         (ascending order keeps the causal work of neighbouring rows alike)
  *  k, v:  device [T][H][D] assembled layer (keys already rotated)
  * Query head h uses KV head floor(h * H / Hq) (Hq % H == 0).  Each query is
- * rotated to its position, then attends to keys at positions <= its own:
- *   out = softmax(softmax_scale * q . k_t) . v_t
- * Arithmetic: fp32 accumulation on the matrix cores.  bf16 storage: the
- * rotated, scaled query enters as a bf16 pair carrying 16 significant bits,
- * probabilities and V as fp16 (V exact while |v| < 65536; otherwise that 64-key
- * block takes V as bf16 and the probabilities as a bf16 pair).  fp32 storage:
- * query, probabilities, K and V all enter as bf16 pairs.
+ * rotated to its position and stored rounded once to the storage type, like a
+ * rotated key (App. B.3: the angle, its sine and cosine and the rotation in
+ * fp64), then attends to keys at positions <= its own:
+ *   out = softmax(softmax_scale * q . k_t) . v_t,   softmax_scale > 0
+ * Arithmetic: fp32 accumulation on the matrix cores.  bf16 storage: the stored
+ * bf16 query against the bf16 keys (exact products); the scale is applied to
+ * the fp32 logits in the exponent; probabilities and V as fp16 (V exact while
+ * |v| < 65536; otherwise that 64-key block takes V as bf16 and the
+ * probabilities as a bf16 pair).  fp32 storage: query, probabilities, K and V
+ * all enter as bf16 pairs.
  *  out: device [n_q][Hq][D] in `dtype`
  *  lse: device float[n_q][Hq] natural-log sum of exp of the scaled logits, or NULL.
  *  ws/ws_bytes: device workspace of at least cachetune_recompute_attn_ws bytes
  *         (may be NULL when that size is 0), 256-byte aligned; for bf16 it
- *         holds the rotated queries as bf16 pairs, V as fp16 tiles, and the
+ *         holds the rotated bf16 queries, V as fp16 tiles, and the
  *         partial results of rows whose keys are split over several segments
  *         (fp16, or fp32 for a segment whose V exceeds the fp16 range).
- * D must be 64 or 128; n_q >= 0; T >= 1. */
+ * D must be 64 or 128; n_q >= 0; T >= 1; a softmax_scale that is not positive
+ * and finite is CT_E_INVALID. */
 ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                    int32_t Hq, const void* k, const void* v, int32_t T,
                                    int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,

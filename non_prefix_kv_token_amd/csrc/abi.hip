@@ -392,7 +392,8 @@ static ct_status attn_args(const void* q_pre, const int32_t* q_pos, int32_t n_q,
   if (H < 1 || Hq < 1 || Hq % H != 0) return fail(CT_E_INVALID, "need Hq % H == 0");
   if (style != CT_ROPE_HALF && style != CT_ROPE_INTERLEAVED) return fail(CT_E_INVALID, "unknown RoPE style");
   if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return fail(CT_E_INVALID, "rope_theta must be > 1");
-  if (!std::isfinite(softmax_scale)) return fail(CT_E_INVALID, "softmax_scale must be finite");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CT_E_INVALID, "softmax_scale must be positive and finite");
   if (n_q < 0 || T < 1) return fail(CT_E_INVALID, "need n_q >= 0, T >= 1");
   if (need_ptrs && n_q > 0 && (!q_pre || !q_pos || !k || !v || !out)) return fail(CT_E_INVALID, "NULL argument");
   if (need_ptrs && !(aligned16(q_pre) && aligned16(k) && aligned16(v) && aligned16(out)))

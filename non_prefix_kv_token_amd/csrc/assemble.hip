@@ -11,49 +11,13 @@
 // H*D elements move in one or two passes of the wave.  The rotation angle and
 // its sine and cosine are formed in fp64, the rotated value is rounded once to
 // the storage type.
+#include "ct_device.h"
 #include "ct_internal.h"
 
 namespace ct {
 namespace {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ inline uint16_t bf16_from_f64(double d) {
-  float f = __double2float_rz(d);
-  uint32_t u = __float_as_uint(f);
-  if ((double)f != d) u |= 1u;  // sticky bit: the second rounding cannot double-round
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-// sin and cos of pos * f in fp64 without branches: Cody-Waite reduction by
-// quarter turns (pi/2 split into two doubles), then Taylor polynomials on
-// |r| <= pi/4 (sin to degree 13, cos to degree 14: truncation below 1e-14).
-__device__ inline void sincos_pos(long long pos, double f, double* s, double* c) {
-  const double ang = (double)pos * f;
-  const double q = rint(ang * 0.6366197723675814);
-  double r = fma(-q, 1.5707963267948966, ang);
-  r = fma(-q, 6.123233995736766e-17, r);
-  const double r2 = r * r;
-  double ps = 1.6059043836821613e-10;
-  ps = fma(ps, r2, -2.505210838544172e-08);
-  ps = fma(ps, r2, 2.7557319223985893e-06);
-  ps = fma(ps, r2, -1.984126984126984e-04);
-  ps = fma(ps, r2, 8.333333333333333e-03);
-  ps = fma(ps, r2, -1.6666666666666666e-01);
-  const double sr = fma(ps * r2, r, r);
-  double pc = -1.1470745597729725e-11;
-  pc = fma(pc, r2, 2.08767569878681e-09);
-  pc = fma(pc, r2, -2.755731922398589e-07);
-  pc = fma(pc, r2, 2.48015873015873e-05);
-  pc = fma(pc, r2, -1.388888888888889e-03);
-  pc = fma(pc, r2, 4.1666666666666664e-02);
-  pc = fma(pc, r2, -0.5);
-  const double cr = fma(pc, r2, 1.0);
-  const int quad = (int)((long long)q & 3);
-  const double sv = (quad & 1) ? cr : sr, cv = (quad & 1) ? sr : cr;
-  *s = (quad & 2) ? -sv : sv;
-  *c = (quad == 1 || quad == 2) ? -cv : cv;
-}
 
 // 8 consecutive stored elements <-> 8 doubles.
 template <int DT> struct Vec8;
@@ -138,7 +102,7 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
   const bool half = al.style == CT_ROPE_HALF;
   // one angle per lane (frequency index j), then read back by every head
   // (the wave's own LDS slice: no barrier beyond the wave)
-  for (int j = lane; j < D / 2; j += 64) sincos_pos(gpos, al.inv_freq[j], &s_sc[wv][j][0], &s_sc[wv][j][1]);
+  for (int j = lane; j < D / 2; j += 64) rope_sincos((double)gpos * al.inv_freq[j], &s_sc[wv][j][0], &s_sc[wv][j][1]);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 

@@ -29,10 +29,11 @@
 // counter in the order the set-up launch computed from the query positions,
 // longest first.
 //
-// Precision.  Logits of these inputs reach the hundreds, so one bf16 rounding
-// of the rotated query would move outputs by O(1): the query (rotated in fp32
-// from an fp64-reduced angle, pre-multiplied by softmax_scale*log2(e)) enters
-// the matrix cores as a bf16 hi + lo pair (16 significant bits, two MFMAs).
+// Precision.  The recomputed query is stored rotated, like a rotated key: the
+// set-up launch rotates it to its position in fp64 and rounds it once to bf16,
+// and the products take that stored value (bf16 x bf16 exact in fp32, fp32
+// accumulation).  The softmax scale (times log2 e) is applied to the fp32
+// logits inside the exponent, exp2(s * c - m), one fused multiply-add.
 // Probabilities and V enter the PV product as fp16 (11 bits): bf16 V converts
 // to fp16 exactly whenever |v| < 65536 (values below 2^-14 land on the fp16
 // subnormal grid, an absolute change below 2^-25).  A 64-key block holding a
@@ -42,6 +43,7 @@
 // below 2^8 and most blocks skip the accumulator rescale.
 #include <climits>
 
+#include "ct_device.h"
 #include "ct_internal.h"
 
 namespace ct {
@@ -61,47 +63,12 @@ constexpr int BK = 64;              // keys per LDS block
 constexpr int VTS = BK + 8;         // V^T row stride (16-bit elements): 144 B
 constexpr float kLazyThr = 8.f;     // running-max slack before a rescale (log2 units)
 
-__device__ inline uint32_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ inline float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ inline uint32_t pack_f16(float a, float b) {
   f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-}
-
-// sin and cos of pos * f in fp64 without branches: Cody-Waite reduction by
-// quarter turns (pi/2 split into two doubles), then Taylor polynomials on
-// |r| <= pi/4 (sin to degree 13, cos to degree 14: truncation below 1e-14).
-__device__ inline void rope_sincos(int pos, double f, float* s, float* c) {
-  const double ang = (double)pos * f;
-  const double q = rint(ang * 0.6366197723675814);
-  double r = fma(-q, 1.5707963267948966, ang);
-  r = fma(-q, 6.123233995736766e-17, r);
-  const double r2 = r * r;
-  double ps = 1.6059043836821613e-10;              // 1/13!
-  ps = fma(ps, r2, -2.505210838544172e-08);        // -1/11!
-  ps = fma(ps, r2, 2.7557319223985893e-06);        // 1/9!
-  ps = fma(ps, r2, -1.984126984126984e-04);        // -1/7!
-  ps = fma(ps, r2, 8.333333333333333e-03);         // 1/5!
-  ps = fma(ps, r2, -1.6666666666666666e-01);       // -1/3!
-  const double sr = fma(ps * r2, r, r);
-  double pc = -1.1470745597729725e-11;             // -1/14!
-  pc = fma(pc, r2, 2.08767569878681e-09);          // 1/12!
-  pc = fma(pc, r2, -2.755731922398589e-07);        // -1/10!
-  pc = fma(pc, r2, 2.48015873015873e-05);          // 1/8!
-  pc = fma(pc, r2, -1.388888888888889e-03);        // -1/6!
-  pc = fma(pc, r2, 4.1666666666666664e-02);        // 1/4!
-  pc = fma(pc, r2, -0.5);
-  const double cr = fma(pc, r2, 1.0);
-  const int quad = (int)((long long)q & 3);
-  const double sv = (quad & 1) ? cr : sr, cv = (quad & 1) ? sr : cr;
-  *s = (float)((quad & 2) ? -sv : sv);
-  *c = (float)((quad == 1 || quad == 2) ? -cv : cv);
 }
 
 // Column of key u (0..63) in the permuted V^T layout: inside each group of 16
@@ -158,21 +125,84 @@ __device__ void prep_v_tile(const AttnArgs& a, int kb, int h, uint16_t* tile) {
   if (tid == 0) a.vflag[h * a.nblk + kb] = any_wide;
 }
 
-// Per-layer preparation of the query rotation: the sine and cosine of every
-// selected row's RoPE angles (position times each frequency), reduced and
-// evaluated in fp64 and stored as fp32 pairs, once per row for all its query
-// heads.  The attention kernel rotates the bf16 queries with them.  Rows
-// row0 .. row0 + 256/(D/2) - 1 per call.
+// Per-layer rotation of the queries: every selected row's query, turned to
+// the row's position in fp64 (angle, sine, cosine and rotation) and rounded
+// once to bf16 -- the stored rotated query, as the assembly stores rotated
+// keys.  kQRows rows per call: the sines and cosines of a row's D/2 angles are
+// formed once into LDS and shared by its Hq heads; a thread then rotates 8
+// pairs of one head (two 16-byte loads and stores), with the loads of all its
+// items issued before the arithmetic.
+constexpr int kQRows = 4;
 template <int D>
-__device__ void prep_q_rows(const AttnArgs& a, int row0) {
-  constexpr int RPB = 256 / (D / 2);
-  const int row = row0 + threadIdx.x / (D / 2), j = threadIdx.x % (D / 2);
-  if (row >= a.n_q) return;
-  const int pos = min(a.qpos[row], a.T - 1);
-  float sn, cs;
-  rope_sincos(pos, a.inv_freq[j], &sn, &cs);
-  *reinterpret_cast<float2*>(a.qsc + (size_t)row * D + 2 * j) = make_float2(sn, cs);
-  (void)RPB;
+__device__ void prep_q_rows(const AttnArgs& a, int row0, char* smem) {
+  constexpr int NP = D / 2;   // rotation pairs per head
+  constexpr int NG = NP / 8;  // groups of 8 pairs per head
+  double2* sc = reinterpret_cast<double2*>(smem);  // [kQRows][NP]: sine, cosine
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kQRows * NP; i += 256) {
+    const int row = row0 + i / NP, j = i % NP;
+    double sn = 0.0, cs = 1.0;
+    if (row < a.n_q) rope_sincos((double)min(a.qpos[row], a.T - 1) * a.inv_freq[j], &sn, &cs);
+    sc[i] = make_double2(sn, cs);
+  }
+  __syncthreads();
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  const bool half = a.style == CT_ROPE_HALF;
+  const int per_row = a.Hq * NG;
+  // Hq is at most a few hundred: per_row * kQRows items, up to kIt per thread
+  constexpr int kIt = 4;
+  for (int it0 = tid; it0 < kQRows * per_row; it0 += 256 * kIt) {
+    u32x4_t xa[kIt], xb[kIt];
+    size_t off_a[kIt], off_b[kIt];
+    bool ok[kIt];
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      const int it = it0 + 256 * u;
+      const int rr = it / per_row, h = (it % per_row) / NG, gq = it % NG;
+      ok[u] = it < kQRows * per_row && row0 + rr < a.n_q;
+      const size_t base = ((size_t)(ok[u] ? row0 + rr : 0) * a.Hq + (ok[u] ? h : 0)) * D;
+      // half: dims 8gq.. (first of each pair) and NP + 8gq.. (second);
+      // interleaved: dims 16gq .. 16gq + 15 (pairs side by side)
+      off_a[u] = base + (half ? 8 * gq : 16 * gq);
+      off_b[u] = base + (half ? NP + 8 * gq : 16 * gq + 8);
+      xa[u] = *reinterpret_cast<const u32x4_t*>(q + off_a[u]);
+      xb[u] = *reinterpret_cast<const u32x4_t*>(q + off_b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      if (!ok[u]) continue;
+      const int it = it0 + 256 * u;
+      const int rr = it / per_row, gq = it % NG;
+      const double2* scr = sc + rr * NP + 8 * gq;  // pairs 8gq .. 8gq + 7
+      auto el = [](const u32x4_t& w, int t) {
+        return (double)((t & 1) ? bf16_hi_to_f32(w[t >> 1]) : bf16_lo_to_f32(w[t >> 1]));
+      };
+      u32x4_t ya = {0u, 0u, 0u, 0u}, yb = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const double2 c = scr[t];
+        double x0, x1;
+        if (half) {
+          x0 = el(xa[u], t);
+          x1 = el(xb[u], t);
+        } else {
+          x0 = t < 4 ? el(xa[u], 2 * t) : el(xb[u], 2 * t - 8);
+          x1 = t < 4 ? el(xa[u], 2 * t + 1) : el(xb[u], 2 * t - 7);
+        }
+        const uint32_t y0 = bf16_from_f64(x0 * c.y - x1 * c.x), y1 = bf16_from_f64(x0 * c.x + x1 * c.y);
+        if (half) {
+          ya[t >> 1] |= y0 << (16 * (t & 1));
+          yb[t >> 1] |= y1 << (16 * (t & 1));
+        } else if (t < 4) {
+          ya[t] = y0 | (y1 << 16);
+        } else {
+          yb[t - 4] = y0 | (y1 << 16);
+        }
+      }
+      *reinterpret_cast<u32x4_t*>(a.qrot + off_a[u]) = ya;
+      *reinterpret_cast<u32x4_t*>(a.qrot + off_b[u]) = yb;
+    }
+  }
 }
 
 // Maximum of a lane's 16 logits with the 3-input maximum (no canonicalising
@@ -268,77 +298,20 @@ void k_attn_bf16(AttnArgs a) {
   const int seg_hi = min(seg_lo + S, nkeys);
   const int kb0 = seg_lo / BK, kb1 = (seg_hi + BK - 1) / BK;
 
-  // ---- rotated, scaled query as bf16 hi + lo (B operand).  The lane's dims
-  // of k-step s are 16*s + 8*g + t (t < 8).  RoPE pairs (j, j + D/2) (half
-  // style) fall in k-steps s and s + NS/2 of the same lane, pairs (2j, 2j+1)
-  // (interleaved) in one 8-dim group: the rotation is lane-local, with the
-  // row's sines and cosines from k_attn_setup.  y = rotated q times
-  // softmax_scale * log2(e) in fp32; hi = bf16(y), lo = bf16(y - hi).
-  // (Loaded and formed by prep_q, which is called once the first K/V block's
-  // loads are out, so that their latencies overlap.)
-  u32x4_t qh[QT][NS], ql[QT][NS];
+  // ---- the stored rotated query (B operand, bf16, written by the set-up
+  // launch).  The lane's dims of k-step s are 16*s + 8*g + t (t < 8).
+  // (Loaded by prep_q, which is called once the first K/V block's loads are
+  // out, so that their latencies overlap.)
+  u32x4_t qh[QT][NS];
   auto prep_q = [&]() {
-    const float cq = a.scale_log2;
-    const bool half = a.style == CT_ROPE_HALF;
-    auto elem = [](const u32x4_t& w, int t) {
-      return (t & 1) ? bf16_hi_to_f32(w[t >> 1]) : bf16_lo_to_f32(w[t >> 1]);
-    };
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
+      const uint16_t* qp = a.qrot + ((size_t)(valid[qt] ? row[qt] : 0) * Hq + hq) * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        qh[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
-        ql[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
+        qh[qt][s] = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
+        if (!valid[qt]) qh[qt][s] = (u32x4_t){0u, 0u, 0u, 0u};
       }
-      if (!valid[qt]) continue;
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row[qt] * Hq + hq) * D + 8 * g;
-      const float* sc = a.qsc + (size_t)row[qt] * D;  // [D/2][2]: sine, cosine
-      u32x4_t xw[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) xw[s] = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
-      float y[NS][8];
-      if (half) {
-#pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-          float4 t4[4];  // (sin, cos) of j = 16 s + 8 g + t, t < 8
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t4[i] = *reinterpret_cast<const float4*>(sc + 2 * (16 * s + 8 * g) + 4 * i);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float sn = (t & 1) ? t4[t >> 1].z : t4[t >> 1].x;
-            const float cs = (t & 1) ? t4[t >> 1].w : t4[t >> 1].y;
-            const float x = elem(xw[s], t), z = elem(xw[s + NS / 2], t);
-            y[s][t] = (x * cs - z * sn) * cq;
-            y[s + NS / 2][t] = (x * sn + z * cs) * cq;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          float4 t4[2];  // (sin, cos) of j = 8 s + 4 g + t/2, t < 8
-#pragma unroll
-          for (int i = 0; i < 2; ++i) t4[i] = *reinterpret_cast<const float4*>(sc + 2 * (8 * s + 4 * g) + 4 * i);
-#pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            const float sn = (t & 2) ? t4[t >> 2].z : t4[t >> 2].x;
-            const float cs = (t & 2) ? t4[t >> 2].w : t4[t >> 2].y;
-            const float x = elem(xw[s], t), z = elem(xw[s], t + 1);
-            y[s][t] = (x * cs - z * sn) * cq;
-            y[s][t + 1] = (x * sn + z * cs) * cq;
-          }
-        }
-      }
-      // (the packed conversion rounds to nearest even, like bf16_bits_rne)
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x2_t yy = {y[s][2 * w], y[s][2 * w + 1]};
-          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(yy, bf16x2_t));
-          const f32x2_t rr = {yy[0] - __uint_as_float(hb << 16), yy[1] - __uint_as_float(hb & 0xffff0000u)};
-          qh[qt][s][w] = hb;
-          ql[qt][s][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2_t));
-        }
     }
   };
 
@@ -468,11 +441,8 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, qh[qt][s]);
-        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, ql[qt][s]);
         st[qt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], bh, st[qt][0], 0, 0, 0);
         st[qt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], bh, st[qt][1], 0, 0, 0);
-        st[qt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], bl, st[qt][0], 0, 0, 0);
-        st[qt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], bl, st[qt][1], 0, 0, 0);
       }
       if (s + 1 < NS) {
         ka[0] = kn[0];
@@ -494,8 +464,9 @@ void k_attn_bf16(AttnArgs a) {
 
   // Online softmax of one 32-key tile of tile qt (16 logits per lane): lazy
   // maximum, probabilities exp2(s - m) in place.
+  const float cq = a.scale_log2;  // > 0: the scale commutes with the maximum
   auto softmax_tile = [&](int qt, f32x16_t& st) {
-    const float bm = max16(st);
+    const float bm = max16(st) * cq;
     if (__any(bm > m_run[qt] + kLazyThr)) {
       const float m_new = fmaxf(m_run[qt], fmaxf(bm, __shfl_xor(bm, 32)));
       const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
@@ -508,7 +479,7 @@ void k_attn_bf16(AttnArgs a) {
     }
     const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) st[v] = __builtin_amdgcn_exp2f(st[v] - mu);
+    for (int v = 0; v < 16; ++v) st[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], cq, -mu));
   };
 
   // P^T . V^T for one 64-key block (probabilities in st, fp16), row sums from
@@ -520,7 +491,7 @@ void k_attn_bf16(AttnArgs a) {
   auto pv = [&](const uint16_t* vbuf, f32x16_t (*st)[2]) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float bm = __builtin_elementwise_maximum(max16(st[qt][0]), max16(st[qt][1]));
+      const float bm = __builtin_elementwise_maximum(max16(st[qt][0]), max16(st[qt][1])) * cq;
       if (__any(bm > m_run[qt] + kLazyThr)) {
         const float m_new = fmaxf(m_run[qt], fmaxf(bm, __shfl_xor(bm, 32)));
         const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
@@ -538,7 +509,7 @@ void k_attn_bf16(AttnArgs a) {
       for (int qt = 0; qt < QT; ++qt) {
         const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) st[qt][kt][v] = __builtin_amdgcn_exp2f(st[qt][kt][v] - mu);
+        for (int v = 0; v < 16; ++v) st[qt][kt][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qt][kt][v], cq, -mu));
       }
       // O^T += V^T . P^T ; k-step (kt, h2) covers keys kt*32 + 16*h2 + [0, 16)
 #pragma unroll
@@ -595,7 +566,7 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qh[qt][s]), "+v"(ql[qt][s]));
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qh[qt][s]));
   for (int kb = kb0; kb < kb1 && !redo; ++kb) {
     const int i = kb - kb0, c = i & 3;
     const bool more = kb + 2 < kb1;
@@ -799,12 +770,13 @@ __device__ void build_schedule(const AttnArgs& a, char* smem) {
 }
 
 // Per-layer set-up of the attention, one launch: block 0 builds the work
-// list, then one block per (64-key V tile, KV head) and one per 256/(D/2)
-// query rows (their RoPE sines and cosines).
+// list, then one block per (64-key V tile, KV head) and one per kQRows query
+// rows (their rotated bf16 queries).
 template <int D>
 constexpr int setup_lds_bytes() {
   return BK * (D + 2) * 2 > kSchedMax * 12 + 4 ? BK * (D + 2) * 2 : kSchedMax * 12 + 4;
 }
+static_assert(kQRows * 64 * 16 <= kSchedMax * 12 + 4, "query rotation tables fit the set-up LDS");
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[setup_lds_bytes<D>()];
@@ -815,7 +787,7 @@ __global__ __launch_bounds__(256) void k_attn_setup(AttnArgs a) {
   else if (b < nv)
     prep_v_tile<D>(a, b % a.nblk, b / a.nblk, reinterpret_cast<uint16_t*>(smem));
   else
-    prep_q_rows<D>(a, (b - nv) * (256 / (D / 2)));
+    prep_q_rows<D>(a, (b - nv) * kQRows, smem);
 }
 
 // Combine the per-segment results of rows whose keys span several segments:
@@ -903,7 +875,7 @@ template <int D>
 ct_status launch(const AttnArgs& a, hipStream_t stream) {
   {
     TimedLaunch tl_("attention_setup", stream);
-    constexpr int rpb = 256 / (D / 2);  // query rows per set-up block
+    constexpr int rpb = kQRows;  // query rows per set-up block
     hipLaunchKernelGGL((k_attn_setup<D>), dim3(1 + a.nblk * a.H + (a.n_q + rpb - 1) / rpb), dim3(256), 0,
                        stream, a);
   }
@@ -961,7 +933,7 @@ void attn_plan(AttnArgs* a, int n_cu) {
 }
 
 // Workspace: [partial outputs fp32][partial outputs fp16][record formats]
-// [partial log2-sum-exp][V^T fp16 tiles][tile flags][query RoPE sines/cosines]
+// [partial log2-sum-exp][V^T fp16 tiles][tile flags][rotated bf16 queries]
 // [work list, per-head counters, list length]
 struct AttnWs { size_t o16, fmt, lse, vt, flag, q, sched, total; };
 static AttnWs ws_layout(const AttnArgs& a) {
@@ -979,7 +951,7 @@ static AttnWs ws_layout(const AttnArgs& a) {
   w.flag = off;
   off += align256((size_t)a.H * a.nblk * 4);
   w.q = off;
-  off += align256((size_t)a.n_q * a.D * 4);
+  off += align256((size_t)a.n_q * a.Hq * a.D * 2);
   w.sched = off;
   off += align256(((size_t)a.n_tg * a.nseg + a.H + 1) * 4);
   w.total = off;
@@ -1004,7 +976,7 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   a.part_lse = reinterpret_cast<float*>(w + L.lse);
   a.vt16 = reinterpret_cast<uint16_t*>(w + L.vt);
   a.vflag = reinterpret_cast<int32_t*>(w + L.flag);
-  a.qsc = reinterpret_cast<float*>(w + L.q);
+  a.qrot = reinterpret_cast<uint16_t*>(w + L.q);
   a.sched_order = reinterpret_cast<int32_t*>(w + L.sched);
   a.sched_cnt = a.sched_order + (size_t)a.n_tg * a.nseg;
   a.sched_n = a.sched_cnt + a.H;

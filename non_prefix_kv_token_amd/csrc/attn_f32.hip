@@ -21,6 +21,7 @@
 // col lane%32, k-group lane/32; D lane -> col lane%32, rows
 // 8*(v/4) + 4*(lane/32) + v%4.  The contraction index of a k-group only has
 // to agree between A and B, which lets P stay in the accumulator layout.
+#include "ct_device.h"
 #include "ct_internal.h"
 
 namespace ct {
@@ -33,18 +34,6 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;   // keys per block
 constexpr int VTS = 68;  // V^T row stride (bf16): 136 B keeps 8-byte reads conflict-free
-
-__device__ inline uint32_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ inline uint16_t bf16_from_f64(double d) {
-  float f = __double2float_rz(d);
-  uint32_t u = __float_as_uint(f);
-  if ((double)f != d) u |= 1u;
-  return (uint16_t)bf16_bits_rne(__uint_as_float(u));
-}
 
 template <int DT>
 __device__ inline double ld_q(const void* p, size_t i) {

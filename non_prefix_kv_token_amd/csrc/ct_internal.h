@@ -150,7 +150,7 @@ struct AttnArgs {
   int32_t nblk;      // 64-key tiles covering [0, T)
   uint16_t* vt16;    // [H][nblk][D][64] V^T tiles as fp16 (keys permuted)
   int32_t* vflag;    // [H][nblk] tile holds a V outside the fp16 range
-  float* qsc;        // [n_q][D/2][2] sine and cosine of each row's RoPE angles
+  uint16_t* qrot;    // [n_q][Hq][D] queries rotated to their positions, bf16
   int32_t blocks_per_head;  // persistent blocks serving each KV head
   int32_t* sched_order;     // [n_tg * nseg] work items (tg * nseg + seg), longest first
   int32_t* sched_cnt;       // [H] items taken so far by each head's blocks

@@ -8,6 +8,7 @@
 // RMSNorm and the gated activation are HBM-bound row kernels; the projections
 // are bf16 GEMMs on the matrix cores with the residual added before the single
 // rounding of each output.
+#include "ct_device.h"
 #include "ct_internal.h"
 
 namespace ct {
@@ -17,12 +18,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ inline uint32_t pack2(float a, float b) { return bf16_rne(a) | (bf16_rne(b) << 16); }
+__device__ inline uint32_t pack2(float a, float b) { return bf16_bits_rne(a) | (bf16_bits_rne(b) << 16); }
 
 constexpr int kNormThreads = 256;
 
@@ -229,7 +225,7 @@ void k_gemm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
         if (m >= M) continue;
         float val = acc[i][j][v];
         if (res) val += __uint_as_float(((uint32_t)res[(size_t)m * N + n]) << 16);
-        dst[(size_t)m * ld + c] = (uint16_t)bf16_rne(val);
+        dst[(size_t)m * ld + c] = (uint16_t)bf16_bits_rne(val);
       }
   }
 }

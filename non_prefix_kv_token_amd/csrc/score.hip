@@ -20,6 +20,7 @@
 //     in fp64 by Clenshaw's recurrence, once per token pair (n, nf - n).
 //  4. per token a = sqrt(E_K), b = sqrt(E_V), s = a/2 + b/2, per-layer
 //     normalisation, mean over layers (fp64, fixed-order reductions).
+#include "ct_device.h"
 #include "ct_internal.h"
 
 namespace ct {
@@ -31,18 +32,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---- rounding helpers ----------------------------------------------------
 
-__device__ inline uint32_t bf16_rne_from_f32_bits(uint32_t u) {
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Round a double to bf16 with a single rounding: truncate to binary32 with a
-// sticky bit (round-to-odd), then round to nearest even.
-__device__ inline uint16_t bf16_from_f64(double d) {
-  float f = __double2float_rz(d);
-  uint32_t u = __float_as_uint(f);
-  if ((double)f != d) u |= 1u;
-  return (uint16_t)bf16_rne_from_f32_bits(u);
-}
+__device__ inline uint32_t bf16_rne_from_f32_bits(uint32_t u) { return bf16_bits_rne(__uint_as_float(u)); }
 
 __device__ inline double f64_from_bf16(uint16_t h) {
   return (double)__uint_as_float(((uint32_t)h) << 16);

@@ -66,6 +66,15 @@ uint16_t orc_round_bf16(double v) {
   return sign | (uint16_t)((bits >> 16) & 0x7fff);
 }
 
+/* v rounded once to the storage type and widened back (exact). */
+static double round_to_storage(double v, int dtype) {
+  if (dtype == ORC_F32) return (double)(float)v;
+  uint32_t bits = (uint32_t)orc_round_bf16(v) << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
 static void store_elem(void* base, int dtype, size_t i, double v) {
   if (dtype == ORC_F32)
     ((float*)base)[i] = (float)v; /* C conversion rounds to nearest even */
@@ -426,7 +435,8 @@ void orc_assemble_rows(const void* k_rows, const void* v_rows, int n, int start,
 /* ---- selected-query causal attention (Sec. 4.1, App. B.2) ---- */
 
 /* For each requested query row r (rows[t], t < n_rows) at global position
- * qpos[r] and each query head h: q = RoPE(q_pre[r][h], qpos[r]); kv head
+ * qpos[r] and each query head h: q = RoPE(q_pre[r][h], qpos[r]) rounded once
+ * to the storage type (the stored rotated query); kv head
  * floor(h * H / Hq); logits z_t = scale * <q, k_t> over keys t <= qpos[r];
  * out = sum softmax(z)_t v_t.  k/v are the assembled (already rotated) [T][H][D]
  * buffers in storage dtype.  out: [n_rows][Hq][D] fp64; lse: [n_rows][Hq] fp64
@@ -452,6 +462,9 @@ int orc_attention(const void* q_pre, const int* qpos, int Hq, const void* k,
       for (int d = 0; d < D; ++d)
         x[d] = load_elem(q_pre, dtype, ((size_t)r * Hq + h) * D + d);
       orc_rope(x, D, (double)p, theta, style, q);
+      /* The recomputed query is stored rotated, like a rotated key (App. B.3):
+       * one rounding to the storage type before the products. */
+      for (int d = 0; d < D; ++d) q[d] = round_to_storage(q[d], dtype);
       int nk = p + 1;
       if (nk > T) nk = T;
       double mx = -INFINITY;

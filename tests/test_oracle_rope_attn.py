@@ -122,13 +122,22 @@ def test_assembly_fp32_offset_zero_is_plain_rope(orc, syn):
 
 # ---- attention -----------------------------------------------------------------
 
+def _stored_query(orc, q_pre_row, pos, theta):
+    """The rotated query as stored: RoPE, then one rounding to the storage type
+    (bf16 through the pinned round_bf16, fp32 by numpy's conversion)."""
+    y = orc.rope(orc.widen(q_pre_row), pos, theta)
+    if q_pre_row.dtype == np.uint16:
+        return orc.widen(orc.round_bf16(y))
+    return y.astype(np.float32).astype(np.float64)
+
+
 def _np_attention(q_pre, qpos, k, v, scale, theta, orc):
     n_q, Hq, D = q_pre.shape
     T, H, _ = k.shape
     out = np.zeros((n_q, Hq, D))
     for r in range(n_q):
         for h in range(Hq):
-            q = orc.rope(orc.widen(q_pre[r, h]), qpos[r], theta)
+            q = _stored_query(orc, q_pre[r, h], qpos[r], theta)
             kh = orc.widen(k[: qpos[r] + 1, h * H // Hq])
             vh = orc.widen(v[: qpos[r] + 1, h * H // Hq])
             z = scale * kh @ q
@@ -149,6 +158,30 @@ def test_attention_brute_force(orc, syn):
     q, qpos, k, v = _attn_inputs(syn)
     out, lse = orc.attention(q, qpos, k, v, 0.25, 10000.0)
     np.testing.assert_allclose(out, _np_attention(q, qpos, k, v, 0.25, 10000.0, orc), atol=1e-12)
+
+
+def test_attention_brute_force_fp32(orc, syn):
+    T, H, Hq, D, nq = 30, 1, 2, 8, 6
+    k = syn.rows(5, syn.K, 0, 0, T, H, D, np.arange(T), "f32")
+    v = syn.rows(5, syn.V, 0, 0, T, H, D, np.arange(T), "f32")
+    qpos = np.sort(RNG.choice(T, nq, replace=False)).astype(np.int32)
+    q = syn.rows(5, syn.Q, 0, 0, T, Hq, D, qpos, "f32")
+    out, _ = orc.attention(q, qpos, k, v, 0.4, 10000.0)
+    np.testing.assert_allclose(out, _np_attention(q, qpos, k, v, 0.4, 10000.0, orc), atol=1e-12)
+
+
+def test_attention_takes_the_stored_query(orc, syn):
+    """The bf16 query is rounded after the rotation: the unrounded rotation
+    gives a different output (by far more than the oracle's own rounding)."""
+    q, qpos, k, v = _attn_inputs(syn)
+    out, _ = orc.attention(q, qpos, k, v, 0.25, 10000.0)
+    T, H, _ = k.shape
+    r, h = 5, 1
+    qq = orc.rope(orc.widen(q[r, h]), qpos[r], 10000.0)  # not rounded
+    z = 0.25 * orc.widen(k[: qpos[r] + 1, h * H // q.shape[1]]) @ qq
+    p = np.exp(z - z.max())
+    unrounded = (p / p.sum()) @ orc.widen(v[: qpos[r] + 1, h * H // q.shape[1]])
+    assert np.abs(out[r, h] - unrounded).max() > 1e-9
 
 
 def test_attention_special_cases(orc, syn):
@@ -191,7 +224,7 @@ def test_attention_lse_normalises(orc, syn):
     q, qpos, k, v = _attn_inputs(syn, H=1, Hq=1, nq=3)
     _, lse = orc.attention(q, qpos, k, v, 0.25, 10000.0)
     for r, p in enumerate(qpos):
-        qq = orc.rope(orc.widen(q[r, 0]), p, 10000.0)
+        qq = _stored_query(orc, q[r, 0], p, 10000.0)
         z = 0.25 * orc.widen(k[: p + 1, 0]) @ qq
         assert abs(np.exp(z - lse[r, 0]).sum() - 1.0) < 1e-12
 
