@@ -295,6 +295,24 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
 ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
                                       ct_dtype dtype, size_t* bytes);
 
+/* ---- selected-query attention for callers that cannot allocate -------------
+ * For code that may not call hipMalloc (work captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation): cachetune_recompute_attn
+ * with the same arguments and results, whose workspace is a fixed array of
+ * 256 MiB (268435456 bytes) inside the library instead of a caller's buffer.
+ * Each device the library runs on holds its own copy of that array until the
+ * process ends; the call allocates nothing.  Shapes whose workspace
+ * (cachetune_recompute_attn_ws) exceeds 256 MiB are refused with
+ * CT_E_WORKSPACE (the 8 x 2048-token Llama-3-8B-shaped request needs about
+ * 235 MiB).  All calls on one device share the array, so calls that overlap
+ * in time on one device (other streams, other threads) race: order them on
+ * one stream or with events.  Errors otherwise as cachetune_recompute_attn. */
+ct_status cachetune_recompute_attn_noalloc(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+                                           int32_t Hq, const void* k, const void* v, int32_t T,
+                                           int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
+                                           double rope_theta, ct_rope style, void* out, float* lse,
+                                           hipStream_t stream);
+
 /* ---- host-tier sparse loading (App. B.1 stored ranking, App. B.2) ----------
  * Offline, when a chunk's cache is generated, its rows are stored in rank
  * order, so that for any r the reuse complement of a (chunk, layer) is the

@@ -48,7 +48,8 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_timing_enable", "cachetune_timing_read", "cachetune_rank_order",
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
-           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj"]
+           "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj",
+           "cachetune_recompute_attn_noalloc"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -77,6 +78,8 @@ def lib():
         L.cachetune_recompute_attn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
                                                f64, i32, vp, vp, vp, sz, vp]
         L.cachetune_recompute_attn_ws.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_recompute_attn_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
+                                                       f64, i32, vp, vp, vp]
         L.cachetune_timing_enable.argtypes = [i32]
         L.cachetune_rank_order.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.cachetune_stage_complement.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -324,6 +327,19 @@ def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, styl
                                           H, D, dt, float(softmax_scale), float(rope_theta), style,
                                           _ptr(out), _ptr(lse), _ptr(ws) if need else None,
                                           ws.numel() if need else 0, _stream(stream)))
+    return out, lse
+
+
+def cachetune_recompute_attn_noalloc(q_pre, q_pos, k, v, softmax_scale, rope_theta, out, style=CT_ROPE_HALF,
+                                     lse=None, stream=None):
+    """cachetune_recompute_attn with the library's own per-device scratch as the
+    workspace (the call allocates nothing).  `out` ([n_q][Hq][D]) and `lse`
+    ([n_q][Hq] fp32 or None) are caller-owned device tensors."""
+    n_q, Hq, D = (int(x) for x in q_pre.shape)
+    T, H = int(k.shape[0]), int(k.shape[1])
+    _check(lib().cachetune_recompute_attn_noalloc(_ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T, H, D,
+                                                  _dtype(q_pre), float(softmax_scale), float(rope_theta), style,
+                                                  _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

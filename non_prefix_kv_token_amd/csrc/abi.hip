@@ -451,6 +451,20 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
   CT_GUARD_END
 }
 
+ct_status cachetune_recompute_attn_noalloc(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+                                           int32_t Hq, const void* k, const void* v, int32_t T,
+                                           int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
+                                           double rope_theta, ct_rope style, void* out, float* lse,
+                                           hipStream_t stream) {
+  CT_GUARD_BEGIN
+  AttnArgs a;
+  if (ct_status s = attn_args(q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
+                              rope_theta, style, out, lse, true, &a))
+    return s;
+  return attn_run_noalloc(a, stream);
+  CT_GUARD_END
+}
+
 ct_status cachetune_rank_order(const void* k_src, const void* v_src, const int32_t* ranking,
                                int32_t n, int32_t L, int32_t H, int32_t D, ct_dtype dtype,
                                void* k_dst, void* v_dst, hipStream_t stream) {

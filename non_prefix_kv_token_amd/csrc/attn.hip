@@ -42,6 +42,7 @@
 // block's maximum exceeds it by more than 8 (log2 units), so probabilities stay
 // below 2^8 and most blocks skip the accumulator rescale.
 #include <climits>
+#include <mutex>
 
 #include "ct_device.h"
 #include "ct_internal.h"
@@ -981,6 +982,52 @@ ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   a.sched_cnt = a.sched_order + (size_t)a.n_tg * a.nseg;
   a.sched_n = a.sched_cnt + a.H;
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
+}
+
+// ---- the variant that allocates nothing ------------------------------------
+// A file-scope device array serves as the workspace of
+// cachetune_recompute_attn_noalloc.  Each device the library runs on holds its
+// own copy (kNoAllocScratchBytes) until the process ends.  In host code the
+// array's name is not a device address: the address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// pointer is handed to the kernels.  Every call on a device shares the array,
+// so calls that overlap on one device race.  Nothing in it has to start at
+// zero: the set-up launch writes the work list, its counters, the V^T tiles,
+// their flags and the rotated queries, and every partial record read by the
+// merge is written first by the attention kernel.
+namespace {
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ct_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CT_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CT_E_UNSUPPORTED, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CT_E_HIP, std::string("hipGetSymbolAddress of the attention scratch: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CT_OK;
+}
+}  // namespace
+
+ct_status attn_run_noalloc(const AttnArgs& a, hipStream_t stream) {
+  if (a.n_q == 0) return CT_OK;
+  const size_t need = attn_ws_bytes(a);
+  if (need > kNoAllocScratchBytes)
+    return fail(CT_E_WORKSPACE, "these shapes need " + std::to_string(need) + " bytes of attention workspace, above the " +
+                                    std::to_string(kNoAllocScratchBytes) + "-byte scratch of the no-alloc entry point");
+  void* ws = nullptr;
+  if (need > 0)
+    if (ct_status s = scratch_ptr(&ws)) return s;
+  return attn_run(a, ws, kNoAllocScratchBytes, stream);
 }
 
 }  // namespace ct

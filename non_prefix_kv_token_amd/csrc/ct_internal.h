@@ -159,6 +159,10 @@ struct AttnArgs {
 void attn_plan(AttnArgs* a, int n_cu);
 size_t attn_ws_bytes(const AttnArgs& a);
 ct_status attn_run(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream);
+// The same with the library's own per-device scratch array as the workspace
+// (no allocation; shapes needing more than kNoAllocScratchBytes are refused).
+constexpr size_t kNoAllocScratchBytes = size_t(256) << 20;
+ct_status attn_run_noalloc(const AttnArgs& a, hipStream_t stream);
 ct_status attn_f32_run(const AttnArgs& a, hipStream_t stream);
 int device_cu_count();
 
