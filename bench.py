@@ -105,6 +105,9 @@ class Workload:
 
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         self.score = torch.empty(sum(ns), dtype=torch.float32, device="cuda")
+        # constant tables of the scoring path, built once into the context
+        # (App. B.1: preprocessing shared by every chunk of a length)
+        ct.cachetune_prepare_scoring(ns, self.alpha)
         self.ws_bytes = ct.cachetune_score_chunk_ws(ns, L, H, D, self.alpha)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.ks = [(self.r[0] * n) // self.r[1] for n in ns]

@@ -17,7 +17,13 @@
  * Conventions shared by every call:
  *  - Memory: the caller owns all buffers.  "device" pointers are HIP device
  *    memory of the current device; "host" pointers are ordinary host memory
- *    read before the call returns.  The library allocates nothing.
+ *    read before the call returns.  The library allocates device memory only
+ *    in cachetune_prepare_scoring (constant tables kept by a handle, freed by
+ *    cachetune_destroy).
+ *  - Handle: the four calls take a ct_handle (cachetune_create) as their first
+ *    argument; NULL is accepted everywhere and makes each call self-contained
+ *    (the scoring tables are then rebuilt in the caller's workspace by every
+ *    call).  A handle's calls must run with its device current.
  *  - Asynchrony: arguments are validated synchronously; work is then enqueued
  *    on `stream` and the call returns without synchronising.  A call that
  *    fails validation enqueues nothing.
@@ -114,6 +120,33 @@ const char* cachetune_status_string(int32_t status);
 const char* cachetune_last_error(void);
 int32_t cachetune_version(void);
 
+/* ---- context handle --------------------------------------------------------
+ * A per-device context holding what the calls would otherwise recompute:
+ * the device's compute-unit count (launch planning of the attention) and the
+ * scoring path's constant tables -- the twiddle planes of the retained band
+ * (cos and sin of 2*pi*j*n/m for bins j < K_keep and tokens n) and the
+ * trigonometric table of each transform length m -- which App. B.1 treats as
+ * preprocessing amortised over every chunk of that length.
+ *
+ * cachetune_create: a context for HIP device `device`; *out receives it.
+ *   Allocates no device memory.  CT_E_INVALID for a device that does not
+ *   exist.
+ * cachetune_destroy: frees the context and its tables (NULL is ignored).  All
+ *   work enqueued with the handle must have completed.
+ * cachetune_prepare_scoring: builds, in device memory owned by the context,
+ *   the tables that score calls with these chunk lengths, alpha and fftlen
+ *   use (tables already held are kept); then synchronises `stream`, so the
+ *   tables are complete for calls on any stream.  Later score calls with the
+ *   handle use them instead of rebuilding them in the workspace (and their
+ *   workspace query no longer counts them).  Arguments and errors as
+ *   cachetune_score_chunk_ws; CT_E_HIP if an allocation fails. */
+typedef struct ct_ctx* ct_handle;
+ct_status cachetune_create(int32_t device, ct_handle* out);
+void cachetune_destroy(ct_handle h);
+ct_status cachetune_prepare_scoring(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks,
+                                    int32_t alpha_num, int32_t alpha_den, ct_fftlen fftlen,
+                                    hipStream_t stream);
+
 /* ---- scoring (App. B.1) ---------------------------------------------------
  * For each chunk and layer: along the token axis of every (head, channel)
  * sequence, a real DFT; bins at and above K_keep = max(1, floor(alpha * (m/2+1)))
@@ -125,7 +158,7 @@ int32_t cachetune_version(void);
  *
  * Workspace query: writes the required workspace size for these shapes.
  *   n_per_chunk: host, n_chunks entries. */
-ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+ct_status cachetune_score_chunk_ws(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                    int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                    ct_fftlen fftlen, size_t* bytes);
 
@@ -136,7 +169,7 @@ ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks,
  * layer_score: device float[L][sum n] normalised per-layer scores, or NULL
  * ws/ws_bytes: device workspace of at least cachetune_score_chunk_ws bytes,
  *              256-byte aligned; its contents are scratch. */
-ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+ct_status cachetune_score_chunk(ct_handle h, const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
                                 int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
                                 ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
@@ -159,10 +192,10 @@ ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_
  * Arguments, layouts and errors are those of cachetune_score_chunk(_ws); an
  * unknown variant is CT_E_INVALID. */
 typedef enum { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1, CT_SCORE_HIGHPASS = 2 } ct_score_variant;
-ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+ct_status cachetune_score_variant_ws(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                      int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                      ct_fftlen fftlen, ct_score_variant variant, size_t* bytes);
-ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+ct_status cachetune_score_variant(ct_handle h, const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
                                   int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
                                   ct_fftlen fftlen, ct_norm norm, ct_score_variant variant,
                                   float* score, float* layer_score, void* ws, size_t ws_bytes,
@@ -238,8 +271,12 @@ ct_status cachetune_qkv_proj(const void* x, const void* w_qkv, int32_t m, int32_
  *  ranking:     device int32[sum n] local indices in rank order, or NULL
  *  sel:         device int32[sum k] the first k of each ranking, ascending
  *  comp:        device int32[sum (n-k)] the rest, ascending, or NULL
- *  k_per_chunk: host int32[n_chunks], written before the call returns. */
-ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
+ *  k_per_chunk: host int32[n_chunks], written before the call returns.
+ * cachetune_select_topr_counts gives the same k_per_chunk without device work
+ * (to size sel and comp before the call). */
+ct_status cachetune_select_topr_counts(const int32_t* n_per_chunk, int32_t n_chunks, int32_t r_num,
+                                       int32_t r_den, int32_t* k_per_chunk);
+ct_status cachetune_select_topr(ct_handle h, const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
                                 int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
                                 int32_t* comp, int32_t* k_per_chunk, hipStream_t stream);
 
@@ -254,7 +291,7 @@ ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, 
  * The rotation angle pos * theta^(-2j/D) and its sine and cosine are formed in
  * fp64; the rotated value is rounded once to the storage type.
  * D must be 64 or 128; device index arrays are trusted (not range-checked). */
-ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, const void* k_sfx,
+ct_status cachetune_assemble_rope(ct_handle h, const ct_place* places, int32_t n_places, const void* k_sfx,
                                   const void* v_sfx, int32_t n_sfx, int32_t sfx_offset, int32_t H,
                                   int32_t D, ct_dtype dtype, double rope_theta, ct_rope style,
                                   void* k_out, void* v_out, int32_t T, hipStream_t stream);
@@ -284,15 +321,16 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
  *         (fp16, or fp32 for a segment whose V exceeds the fp16 range).
  * D must be 64 or 128; n_q >= 0; T >= 1; a softmax_scale that is not positive
  * and finite is CT_E_INVALID. */
-ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+ct_status cachetune_recompute_attn(ct_handle h, const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                    int32_t Hq, const void* k, const void* v, int32_t T,
                                    int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
                                    double rope_theta, ct_rope style, void* out, float* lse,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace query for cachetune_recompute_attn with these shapes on the
- * current device (the size depends on the device's compute-unit count). */
-ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
+ * handle's device, or the current device for a NULL handle (the size depends
+ * on the device's compute-unit count). */
+ct_status cachetune_recompute_attn_ws(ct_handle h, int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
                                       ct_dtype dtype, size_t* bytes);
 
 /* ---- selected-query attention for callers that cannot allocate -------------
@@ -307,7 +345,7 @@ ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_
  * 235 MiB).  All calls on one device share the array, so calls that overlap
  * in time on one device (other streams, other threads) race: order them on
  * one stream or with events.  Errors otherwise as cachetune_recompute_attn. */
-ct_status cachetune_recompute_attn_noalloc(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+ct_status cachetune_recompute_attn_noalloc(ct_handle h, const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                            int32_t Hq, const void* k, const void* v, int32_t T,
                                            int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
                                            double rope_theta, ct_rope style, void* out, float* lse,

@@ -49,7 +49,8 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_stage_complement", "cachetune_calibrate_ratio", "cachetune_score_variant_ws",
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
            "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj",
-           "cachetune_recompute_attn_noalloc"]
+           "cachetune_recompute_attn_noalloc", "cachetune_create", "cachetune_destroy",
+           "cachetune_prepare_scoring", "cachetune_select_topr_counts"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -69,16 +70,21 @@ def lib():
         L.cachetune_status_string.restype = C.c_char_p
         L.cachetune_last_error.restype = C.c_char_p
         L.cachetune_version.restype = i32
-        L.cachetune_score_chunk_ws.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
-        L.cachetune_score_chunk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+        L.cachetune_create.argtypes = [i32, C.POINTER(vp)]
+        L.cachetune_destroy.argtypes = [vp]
+        L.cachetune_destroy.restype = None
+        L.cachetune_prepare_scoring.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+        L.cachetune_score_chunk_ws.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
                                             vp, sz, vp]
-        L.cachetune_select_topr.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
-        L.cachetune_assemble_rope.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, f64, i32,
+        L.cachetune_select_topr_counts.argtypes = [vp, i32, i32, i32, vp]
+        L.cachetune_select_topr.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.cachetune_assemble_rope.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, f64, i32,
                                               vp, vp, i32, vp]
-        L.cachetune_recompute_attn.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
+        L.cachetune_recompute_attn.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
                                                f64, i32, vp, vp, vp, sz, vp]
-        L.cachetune_recompute_attn_ws.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
-        L.cachetune_recompute_attn_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
+        L.cachetune_recompute_attn_ws.argtypes = [vp, i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        L.cachetune_recompute_attn_noalloc.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, f32,
                                                        f64, i32, vp, vp, vp]
         L.cachetune_timing_enable.argtypes = [i32]
         L.cachetune_rank_order.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
@@ -86,9 +92,9 @@ def lib():
         L.cachetune_timing_read.argtypes = [C.c_char_p, C.POINTER(f64), C.POINTER(i32)]
         L.cachetune_calibrate_ratio.argtypes = [f64, f64, f64, f64, f64, f64, COST_FN, vp,
                                                 C.POINTER(f64), C.POINTER(i32)]
-        L.cachetune_score_variant_ws.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32,
+        L.cachetune_score_variant_ws.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                  C.POINTER(sz)]
-        L.cachetune_score_variant.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+        L.cachetune_score_variant.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                               vp, vp, vp, sz, vp]
         L.cachetune_band_energy_ws.argtypes = [vp, i32, i32, i32, i32, i32, C.POINTER(sz)]
         L.cachetune_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
@@ -97,9 +103,38 @@ def lib():
         L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         L.cachetune_qkv_proj.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in SYMBOLS[3:]:
-            getattr(L, name).restype = i32
+            if name != "cachetune_destroy":
+                getattr(L, name).restype = i32
         _lib = L
     return _lib
+
+
+_handles = {}
+
+
+def handle(device=None):
+    """The binding's context handle (cachetune_create) for `device` (the
+    current device by default), created on first use and kept for the
+    process; calls of this module pass it.  Without a GPU (argument checks
+    only) the handle is NULL."""
+    import torch
+    if not torch.cuda.is_available():
+        return None
+    dev = torch.cuda.current_device() if device is None else int(device)
+    if dev not in _handles:
+        h = C.c_void_p()
+        _check(lib().cachetune_create(dev, C.byref(h)))
+        _handles[dev] = h
+    return _handles[dev]
+
+
+def cachetune_prepare_scoring(n_per_chunk, alpha=(1, 16), fftlen=CT_FFT_EXACT_N, stream=None):
+    """Build the handle's scoring tables for these chunk lengths (allocates;
+    synchronises the stream), so that later score calls allocate and rebuild
+    nothing."""
+    arr = _i32_array(n_per_chunk)
+    _check(lib().cachetune_prepare_scoring(handle(), arr, len(n_per_chunk), alpha[0], alpha[1], fftlen,
+                                           _stream(stream)))
 
 
 def _check(status: int):
@@ -138,7 +173,7 @@ def cachetune_score_chunk_ws(n_per_chunk, L, H, D, alpha=(1, 16), fftlen=CT_FFT_
                              variant=CT_SCORE_LOWPASS) -> int:
     arr = _i32_array(n_per_chunk)
     out = C.c_size_t(0)
-    _check(lib().cachetune_score_variant_ws(arr, len(n_per_chunk), L, H, D, alpha[0], alpha[1],
+    _check(lib().cachetune_score_variant_ws(handle(), arr, len(n_per_chunk), L, H, D, alpha[0], alpha[1],
                                             fftlen, variant, C.byref(out)))
     return out.value
 
@@ -166,11 +201,11 @@ def cachetune_score_chunk(chunks, L, H, D, alpha=(1, 16), fftlen=CT_FFT_EXACT_N,
     for i, (k, v) in enumerate(chunks):
         arr[i].k, arr[i].v, arr[i].n = k.data_ptr(), v.data_ptr(), int(k.shape[1])
     if variant == CT_SCORE_LOWPASS:
-        _check(lib().cachetune_score_chunk(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
+        _check(lib().cachetune_score_chunk(handle(), arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
                                            alpha[1], fftlen, norm, _ptr(score), _ptr(layer_score),
                                            _ptr(ws), ws.numel(), _stream(stream)))
     else:
-        _check(lib().cachetune_score_variant(arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
+        _check(lib().cachetune_score_variant(handle(), arr, len(chunks), L, H, D, _dtype(chunks[0][0]), alpha[0],
                                              alpha[1], fftlen, norm, variant, _ptr(score),
                                              _ptr(layer_score), _ptr(ws), ws.numel(), _stream(stream)))
     return score, layer_score
@@ -261,16 +296,18 @@ def cachetune_select_topr(score, n_per_chunk, r=(15, 100), ranking=None, sel=Non
     import torch
     dev = score.device
     ns = [int(n) for n in n_per_chunk]
-    ks = [(r[0] * n) // r[1] for n in ns]
+    arr = _i32_array(ns)
+    kq = (C.c_int32 * len(ns))()
+    _check(lib().cachetune_select_topr_counts(arr, len(ns), r[0], r[1], kq))
+    ks = list(kq)
     if ranking is None and want_ranking:
         ranking = torch.empty(sum(ns), dtype=torch.int32, device=dev)
     if sel is None:
         sel = torch.empty(max(1, sum(ks)), dtype=torch.int32, device=dev)
     if comp is None and want_comp:
         comp = torch.empty(max(1, sum(ns) - sum(ks)), dtype=torch.int32, device=dev)
-    arr = _i32_array(ns)
     kout = (C.c_int32 * len(ns))()
-    _check(lib().cachetune_select_topr(_ptr(score), arr, len(ns), r[0], r[1], _ptr(ranking),
+    _check(lib().cachetune_select_topr(handle(), _ptr(score), arr, len(ns), r[0], r[1], _ptr(ranking),
                                        _ptr(sel), _ptr(comp), kout, _stream(stream)))
     return list(kout), ranking, sel, comp
 
@@ -295,7 +332,7 @@ def cachetune_assemble_rope(places, k_out, v_out, H, D, rope_theta, style=CT_ROP
                             k_sfx=None, v_sfx=None, n_sfx=0, sfx_offset=0, stream=None):
     arr = (ct_place * max(1, len(places)))(*places)
     T = int(k_out.shape[0])
-    _check(lib().cachetune_assemble_rope(arr, len(places), _ptr(k_sfx), _ptr(v_sfx), n_sfx,
+    _check(lib().cachetune_assemble_rope(handle(), arr, len(places), _ptr(k_sfx), _ptr(v_sfx), n_sfx,
                                          sfx_offset, H, D, _dtype(k_out), rope_theta, style,
                                          _ptr(k_out), _ptr(v_out), T, _stream(stream)))
 
@@ -304,7 +341,7 @@ def cachetune_assemble_rope(places, k_out, v_out, H, D, rope_theta, style=CT_ROP
 
 def cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dtype=CT_BF16) -> int:
     out = C.c_size_t(0)
-    _check(lib().cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dtype, C.byref(out)))
+    _check(lib().cachetune_recompute_attn_ws(handle(), n_q, Hq, T, H, D, dtype, C.byref(out)))
     return out.value
 
 
@@ -323,7 +360,7 @@ def cachetune_recompute_attn(q_pre, q_pos, k, v, softmax_scale, rope_theta, styl
     need = cachetune_recompute_attn_ws(n_q, Hq, T, H, D, dt)
     if need and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=q_pre.device)
-    _check(lib().cachetune_recompute_attn(_ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T,
+    _check(lib().cachetune_recompute_attn(handle(), _ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T,
                                           H, D, dt, float(softmax_scale), float(rope_theta), style,
                                           _ptr(out), _ptr(lse), _ptr(ws) if need else None,
                                           ws.numel() if need else 0, _stream(stream)))
@@ -337,7 +374,7 @@ def cachetune_recompute_attn_noalloc(q_pre, q_pos, k, v, softmax_scale, rope_the
     ([n_q][Hq] fp32 or None) are caller-owned device tensors."""
     n_q, Hq, D = (int(x) for x in q_pre.shape)
     T, H = int(k.shape[0]), int(k.shape[1])
-    _check(lib().cachetune_recompute_attn_noalloc(_ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T, H, D,
+    _check(lib().cachetune_recompute_attn_noalloc(handle(), _ptr(q_pre), _ptr(q_pos), n_q, Hq, _ptr(k), _ptr(v), T, H, D,
                                                   _dtype(q_pre), float(softmax_scale), float(rope_theta), style,
                                                   _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse

@@ -4,12 +4,39 @@
 #include <cmath>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "ct_internal.h"
 
 namespace ct {
+
+// Per-device context behind a ct_handle: the device, its compute units, and
+// the scoring tables cachetune_prepare_scoring built (device memory owned by
+// the context, freed by cachetune_destroy).
+struct Context {
+  int device = 0;
+  int cu = 256;
+  mutable std::mutex mu;
+  struct Entry {
+    int nf, kk, ntp;
+    ScoreTables t;
+    void* mem;
+  };
+  std::vector<Entry> tables;
+};
+
+bool context_find_tables(const Context* ctx, int nf, int kk, int ntp, ScoreTables* out) {
+  if (!ctx) return false;
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  for (const Context::Entry& e : ctx->tables)
+    if (e.nf == nf && e.kk == kk && e.ntp == ntp) {
+      *out = e.t;
+      return true;
+    }
+  return false;
+}
 
 static thread_local std::string g_last_error;
 
@@ -39,12 +66,18 @@ int device_cu_count() {
   return n;
 }
 
+int context_cu_count(const Context* ctx) { return ctx ? ctx->cu : device_cu_count(); }
+
 static void fill_inv_freq(double* f, int D, double theta) {
   for (int j = 0; j < 64; ++j) f[j] = 0.0;
   for (int j = 0; j < D / 2; ++j) f[j] = std::pow(theta, -2.0 * (double)j / (double)D);
 }
 
 }  // namespace ct
+
+struct ct_ctx {
+  ct::Context c;
+};
 
 using namespace ct;
 
@@ -73,7 +106,91 @@ const char* cachetune_status_string(int32_t s) {
 
 const char* cachetune_last_error(void) { return g_last_error.c_str(); }
 
-int32_t cachetune_version(void) { return 1; }
+int32_t cachetune_version(void) { return 2; }
+
+// A handle's calls must run with its device current.
+static ct_status ctx_of(ct_handle h, const Context** out) {
+  *out = nullptr;
+  if (!h) return CT_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CT_E_HIP, "hipGetDevice failed");
+  if (dev != h->c.device)
+    return fail(CT_E_INVALID, "the handle belongs to device " + std::to_string(h->c.device) +
+                                  ", the current device is " + std::to_string(dev));
+  *out = &h->c;
+  return CT_OK;
+}
+
+ct_status cachetune_create(int32_t device, ct_handle* out) {
+  CT_GUARD_BEGIN
+  if (!out) return fail(CT_E_INVALID, "out is NULL");
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) return fail(CT_E_HIP, "hipGetDeviceCount failed");
+  if (device < 0 || device >= n) return fail(CT_E_INVALID, "no device " + std::to_string(device));
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cu <= 0)
+    return fail(CT_E_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+  ct_ctx* h = new ct_ctx();
+  h->c.device = device;
+  h->c.cu = cu;
+  *out = h;
+  return CT_OK;
+  CT_GUARD_END
+}
+
+void cachetune_destroy(ct_handle h) {
+  if (!h) return;
+  for (Context::Entry& e : h->c.tables) (void)hipFree(e.mem);
+  delete h;
+}
+
+ct_status cachetune_prepare_scoring(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks,
+                                    int32_t alpha_num, int32_t alpha_den, ct_fftlen fftlen,
+                                    hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!h) return fail(CT_E_INVALID, "handle is NULL");
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
+  if (!n_per_chunk) return fail(CT_E_INVALID, "n_per_chunk is NULL");
+  if (n_chunks < 1 || n_chunks > 4096) return fail(CT_E_INVALID, "n_chunks must be in [1, 4096]");
+  if (alpha_den <= 0 || alpha_num <= 0 || alpha_num > alpha_den)
+    return fail(CT_E_INVALID, "alpha = alpha_num/alpha_den must lie in (0, 1]");
+  if (fftlen != CT_FFT_EXACT_N && fftlen != CT_FFT_ZEROPAD_POW2) return fail(CT_E_INVALID, "unknown fftlen mode");
+  for (int b = 0; b < n_chunks; ++b) {
+    const int n = n_per_chunk[b];
+    if (n < 2 || n > kMaxN) return fail(CT_E_INVALID, "chunk length must be in [2, 8192]");
+    if (fft_len(n, fftlen) > kMaxN) return fail(CT_E_UNSUPPORTED, "transform length above 8192");
+  }
+  Context& c = h->c;
+  bool built = false;
+  for (int b = 0; b < n_chunks; ++b) {
+    const int n = n_per_chunk[b];
+    const int nf = fft_len(n, fftlen), kk = kkeep(nf, alpha_num, alpha_den), ntp = (n + 31) / 32 * 32;
+    ScoreTables t;
+    if (context_find_tables(&c, nf, kk, ntp, &t)) continue;
+    size_t o16 = 0, otr = 0;
+    const size_t bytes = score_tables_bytes(nf, kk, ntp, &o16, &otr);
+    void* mem = nullptr;
+    if (hipMalloc(&mem, bytes) != hipSuccess) return fail(CT_E_HIP, "hipMalloc of the scoring tables failed");
+    t.tw = reinterpret_cast<uint16_t*>(mem);
+    t.tw16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(mem) + o16);
+    t.trig = reinterpret_cast<double2*>(reinterpret_cast<char*>(mem) + otr);
+    if (ct_status s = score_tables_build(nf, kk, ntp, CT_BF16, t, stream)) {
+      (void)hipFree(mem);
+      return s;
+    }
+    {
+      std::lock_guard<std::mutex> lock(c.mu);
+      c.tables.push_back(Context::Entry{nf, kk, ntp, t, mem});
+    }
+    built = true;
+  }
+  // later calls may run on other streams: the tables are complete on return
+  if (built && hipStreamSynchronize(stream) != hipSuccess) return fail(CT_E_HIP, "hipStreamSynchronize failed");
+  return CT_OK;
+  CT_GUARD_END
+}
 
 static ct_status check_score_shapes(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                     int32_t H, int32_t D, int32_t a_num, int32_t a_den,
@@ -96,11 +213,13 @@ static ct_status check_score_shapes(const int32_t* n_per_chunk, int32_t n_chunks
   return CT_OK;
 }
 
-ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+ct_status cachetune_score_variant_ws(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                      int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                      ct_fftlen fftlen, ct_score_variant variant, size_t* bytes) {
   CT_GUARD_BEGIN
   if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2 && variant != CT_SCORE_HIGHPASS)
     return fail(CT_E_INVALID, "unknown variant");
   if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
@@ -110,31 +229,33 @@ ct_status cachetune_score_variant_ws(const int32_t* n_per_chunk, int32_t n_chunk
   if (ct_status s = check_score_shapes(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen))
     return s;
   return score_plan(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen, bytes, nullptr,
-                    variant);
+                    variant, cc);
   CT_GUARD_END
 }
 
-ct_status cachetune_score_chunk_ws(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
+ct_status cachetune_score_chunk_ws(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                    int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                    ct_fftlen fftlen, size_t* bytes) {
-  return cachetune_score_variant_ws(n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen,
+  return cachetune_score_variant_ws(h, n_per_chunk, n_chunks, L, H, D, alpha_num, alpha_den, fftlen,
                                     CT_SCORE_LOWPASS, bytes);
 }
 
-ct_status cachetune_score_chunk(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+ct_status cachetune_score_chunk(ct_handle h, const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
                                 int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
                                 ct_fftlen fftlen, ct_norm norm, float* score, float* layer_score,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
-  return cachetune_score_variant(chunks, n_chunks, L, H, D, dtype, alpha_num, alpha_den, fftlen, norm,
+  return cachetune_score_variant(h, chunks, n_chunks, L, H, D, dtype, alpha_num, alpha_den, fftlen, norm,
                                  CT_SCORE_LOWPASS, score, layer_score, ws, ws_bytes, stream);
 }
 
-ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
+ct_status cachetune_score_variant(ct_handle h, const ct_chunk* chunks, int32_t n_chunks, int32_t L, int32_t H,
                                   int32_t D, ct_dtype dtype, int32_t alpha_num, int32_t alpha_den,
                                   ct_fftlen fftlen, ct_norm norm, ct_score_variant variant,
                                   float* score, float* layer_score, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   CT_GUARD_BEGIN
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   if (variant != CT_SCORE_LOWPASS && variant != CT_SCORE_L2 && variant != CT_SCORE_HIGHPASS)
     return fail(CT_E_INVALID, "unknown variant");
   if (variant == CT_SCORE_L2) {  // no transform: the cutoff and length are not used
@@ -156,12 +277,13 @@ ct_status cachetune_score_variant(const ct_chunk* chunks, int32_t n_chunks, int3
   size_t need = 0;
   std::vector<ScoreLaunch> launches;
   if (ct_status s = score_plan(ns.data(), n_chunks, L, H, D, alpha_num, alpha_den, fftlen, &need,
-                               &launches, variant))
+                               &launches, variant, cc))
     return s;
   if (!ws || ws_bytes < need)
     return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  score_bind(&launches, reinterpret_cast<char*>(ws));
   int b0 = 0;
   for (ScoreLaunch& sl : launches) {
     sl.dtype = dtype;
@@ -213,6 +335,7 @@ ct_status cachetune_band_energy(const ct_chunk* chunks, int32_t n_chunks, int32_
     return fail(CT_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return fail(CT_E_INVALID, "workspace must be 256-byte aligned");
+  score_bind(&launches, reinterpret_cast<char*>(ws));
   int b0 = 0;
   for (ScoreLaunch& sl : launches) {
     sl.dtype = dtype;
@@ -285,20 +408,36 @@ ct_status cachetune_qkv_proj(const void* x, const void* w_qkv, int32_t m, int32_
   CT_GUARD_END
 }
 
-ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
-                                int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
-                                int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {
-  CT_GUARD_BEGIN
-  if (!score || !n_per_chunk || !k_per_chunk) return fail(CT_E_INVALID, "NULL argument");
+static ct_status topr_counts(const int32_t* n_per_chunk, int32_t n_chunks, int32_t r_num, int32_t r_den,
+                             int32_t* ks) {
+  if (!n_per_chunk || !ks) return fail(CT_E_INVALID, "NULL argument");
   if (n_chunks < 1 || n_chunks > 65536) return fail(CT_E_INVALID, "n_chunks must be in [1, 65536]");
   if (r_den <= 0 || r_num < 0 || r_num > r_den) return fail(CT_E_INVALID, "r must lie in [0, 1]");
-  long long tok = 0, sk = 0, sc = 0;
-  std::vector<int32_t> ks(n_chunks);
   for (int b = 0; b < n_chunks; ++b) {
-    int n = n_per_chunk[b];
+    const int n = n_per_chunk[b];
     if (n < 1 || n > kMaxN) return fail(CT_E_INVALID, "chunk length must be in [1, 8192]");
     ks[b] = (int32_t)(((long long)r_num * n) / r_den);
   }
+  return CT_OK;
+}
+
+ct_status cachetune_select_topr_counts(const int32_t* n_per_chunk, int32_t n_chunks, int32_t r_num,
+                                       int32_t r_den, int32_t* k_per_chunk) {
+  CT_GUARD_BEGIN
+  return topr_counts(n_per_chunk, n_chunks, r_num, r_den, k_per_chunk);
+  CT_GUARD_END
+}
+
+ct_status cachetune_select_topr(ct_handle h, const float* score, const int32_t* n_per_chunk, int32_t n_chunks,
+                                int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
+                                int32_t* comp, int32_t* k_per_chunk, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
+  if (!score || !n_per_chunk || !k_per_chunk) return fail(CT_E_INVALID, "NULL argument");
+  std::vector<int32_t> ks((size_t)std::max(n_chunks, 1));
+  if (ct_status s = topr_counts(n_per_chunk, n_chunks, r_num, r_den, ks.data())) return s;
+  long long tok = 0, sk = 0, sc = 0;
   bool any_sel = false;
   for (int b = 0; b < n_chunks; ++b) any_sel |= ks[b] > 0;
   if (any_sel && !sel) return fail(CT_E_INVALID, "sel is NULL");
@@ -323,11 +462,13 @@ ct_status cachetune_select_topr(const float* score, const int32_t* n_per_chunk, 
   CT_GUARD_END
 }
 
-ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, const void* k_sfx,
+ct_status cachetune_assemble_rope(ct_handle h, const ct_place* places, int32_t n_places, const void* k_sfx,
                                   const void* v_sfx, int32_t n_sfx, int32_t sfx_offset, int32_t H,
                                   int32_t D, ct_dtype dtype, double rope_theta, ct_rope style,
                                   void* k_out, void* v_out, int32_t T, hipStream_t stream) {
   CT_GUARD_BEGIN
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   if (!dtype_ok(dtype)) return fail(CT_E_INVALID, "unknown dtype");
   if (D != 64 && D != 128) return fail(CT_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (H < 1) return fail(CT_E_INVALID, "H must be positive");
@@ -383,7 +524,7 @@ ct_status cachetune_assemble_rope(const ct_place* places, int32_t n_places, cons
   CT_GUARD_END
 }
 
-static ct_status attn_args(const void* q_pre, const int32_t* q_pos, int32_t n_q, int32_t Hq,
+static ct_status attn_args(const Context* cc, const void* q_pre, const int32_t* q_pos, int32_t n_q, int32_t Hq,
                            const void* k, const void* v, int32_t T, int32_t H, int32_t D,
                            int32_t dtype, float softmax_scale, double rope_theta, int32_t style,
                            void* out, float* lse, bool need_ptrs, AttnArgs* a) {
@@ -418,16 +559,18 @@ static ct_status attn_args(const void* q_pre, const int32_t* q_pos, int32_t n_q,
   a->scale = softmax_scale;
   a->scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   fill_inv_freq(a->inv_freq, D, rope_theta);
-  attn_plan(a, device_cu_count());
+  attn_plan(a, context_cu_count(cc));
   return CT_OK;
 }
 
-ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
+ct_status cachetune_recompute_attn_ws(ct_handle h, int32_t n_q, int32_t Hq, int32_t T, int32_t H, int32_t D,
                                       ct_dtype dtype, size_t* bytes) {
   CT_GUARD_BEGIN
   if (!bytes) return fail(CT_E_INVALID, "bytes is NULL");
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   AttnArgs a;
-  if (ct_status s = attn_args(nullptr, nullptr, n_q, Hq, nullptr, nullptr, T, H, D, dtype, 1.f,
+  if (ct_status s = attn_args(cc, nullptr, nullptr, n_q, Hq, nullptr, nullptr, T, H, D, dtype, 1.f,
                               10000.0, CT_ROPE_HALF, nullptr, nullptr, false, &a))
     return s;
   *bytes = attn_ws_bytes(a);
@@ -435,14 +578,16 @@ ct_status cachetune_recompute_attn_ws(int32_t n_q, int32_t Hq, int32_t T, int32_
   CT_GUARD_END
 }
 
-ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+ct_status cachetune_recompute_attn(ct_handle h, const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                    int32_t Hq, const void* k, const void* v, int32_t T,
                                    int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
                                    double rope_theta, ct_rope style, void* out, float* lse,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
   CT_GUARD_BEGIN
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   AttnArgs a;
-  if (ct_status s = attn_args(q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
+  if (ct_status s = attn_args(cc, q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
                               rope_theta, style, out, lse, true, &a))
     return s;
   if (ws && reinterpret_cast<uintptr_t>(ws) % 256 != 0)
@@ -451,14 +596,16 @@ ct_status cachetune_recompute_attn(const void* q_pre, const int32_t* q_pos, int3
   CT_GUARD_END
 }
 
-ct_status cachetune_recompute_attn_noalloc(const void* q_pre, const int32_t* q_pos, int32_t n_q,
+ct_status cachetune_recompute_attn_noalloc(ct_handle h, const void* q_pre, const int32_t* q_pos, int32_t n_q,
                                            int32_t Hq, const void* k, const void* v, int32_t T,
                                            int32_t H, int32_t D, ct_dtype dtype, float softmax_scale,
                                            double rope_theta, ct_rope style, void* out, float* lse,
                                            hipStream_t stream) {
   CT_GUARD_BEGIN
+  const Context* cc = nullptr;
+  if (ct_status s = ctx_of(h, &cc)) return s;
   AttnArgs a;
-  if (ct_status s = attn_args(q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
+  if (ct_status s = attn_args(cc, q_pre, q_pos, n_q, Hq, k, v, T, H, D, dtype, softmax_scale,
                               rope_theta, style, out, lse, true, &a))
     return s;
   return attn_run_noalloc(a, stream);

@@ -54,11 +54,14 @@ struct ScoreChunkDesc {
   int32_t kk;        // retained bins
   int32_t ppad;      // padded band rows (multiple of 32, >= 2*kk)
   int32_t ntok_pad;  // twiddle table row length (multiple of 32, >= n)
-  int32_t tw_owner;  // 1: this chunk writes the shared twiddle table
-  int64_t tw_off;    // bf16 twiddle planes [3][ppad][ntok_pad]
-  int64_t tw16_off;  // fp16 twiddle planes [2][ppad][ntok_pad]
-  int64_t flag_off;  // int32 [L][2]: 1 when the problem's X does not fit fp16
-  int64_t trig_off;  // fp64 (cos, sin) of 2*pi*m/nf, m < nf
+  int32_t tw_owner;  // 1: this launch writes the chunk's tables (not held by a context)
+  int64_t tw_off;    // workspace offsets of the tables when they live there
+  int64_t tw16_off;
+  int64_t trig_off;
+  uint16_t* tw;      // bf16 twiddle planes [3][ppad][ntok_pad] (device; set by score_bind)
+  uint16_t* tw16;    // fp16 twiddle planes [2][ppad][ntok_pad]
+  double2* trig;     // fp64 (cos, sin) of 2*pi*m/nf, m < nf
+  int64_t flag_off;  // int32 [L][2][kFlagBlocks]: 1 when a channel block's X does not fit fp16
   int64_t y_off;     // fp32 band coefficients [L][2][ppad][C]
   int64_t e_off;     // fp64 low-pass energies [L][2][n]
   int64_t tok_off;   // first token of this chunk in the concatenated score vector
@@ -79,9 +82,34 @@ struct ScoreLaunch {
   int32_t variant;     // ct_score_variant
 };
 
+// fp16-range flags per (problem, 512-channel block of the band projection)
+constexpr int kFlagBlocks = 16;
+
+// Twiddle and trigonometric tables of one (transform length, retained bins,
+// padded token count), device memory.
+struct ScoreTables {
+  uint16_t* tw;
+  uint16_t* tw16;
+  double2* trig;
+};
+// Per-device context (cachetune_create): device ordinal, compute units and the
+// scoring tables built by cachetune_prepare_scoring.
+struct Context;
+bool context_find_tables(const Context* ctx, int nf, int kk, int ntp, ScoreTables* out);
+int context_cu_count(const Context* ctx);  // the current device's when ctx is NULL
+
+// The plan of a score call.  Tables found in `ctx` are taken from there; the
+// others get a region of the workspace and are written by the call.
 ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
                      int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
-                     std::vector<ScoreLaunch>* launches, int32_t variant = CT_SCORE_LOWPASS);
+                     std::vector<ScoreLaunch>* launches, int32_t variant = CT_SCORE_LOWPASS,
+                     const Context* ctx = nullptr);
+// Points the descriptors' workspace tables at `ws` (context tables are set by
+// score_plan already).
+void score_bind(std::vector<ScoreLaunch>* launches, char* ws);
+// Writes one table set (k_twiddle) on `stream`.
+ct_status score_tables_build(int nf, int kk, int ntp, int dtype, const ScoreTables& t, hipStream_t stream);
+size_t score_tables_bytes(int nf, int kk, int ntp, size_t* tw16_off, size_t* trig_off);
 ct_status score_run(const std::vector<ScoreLaunch>& launches, char* ws, float* score,
                     float* layer_score, hipStream_t stream);
 // Band projection of every bin (plan with alpha = 1 and this variant: no Gram

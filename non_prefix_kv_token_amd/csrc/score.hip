@@ -78,17 +78,13 @@ __device__ inline void turn_sincos(long long m, int nf, double* s, double* c) {
 // ---- 1a. twiddle planes ----------------------------------------------------
 // Row p < kk holds cos(2*pi*p*n/nf); row kk + j holds sin(2*pi*j*n/nf);
 // rows >= 2kk are zero.  Each value is stored as three bf16 planes and as an
-// fp16 pair.  Also clears the chunk's fp16-range flags.
-__global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl, char* ws) {
+// fp16 pair (both are always written, so a table serves bf16 and fp32 data).
+__global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl) {
   const ScoreChunkDesc& d = sl.c[blockIdx.y];
-  if (blockIdx.x == 0 && sl.dtype == CT_BF16) {
-    int* flag = reinterpret_cast<int*>(ws + d.flag_off);
-    for (int i = threadIdx.x; i < 2 * sl.L; i += blockDim.x) flag[i] = 0;
-  }
   if (!d.tw_owner) return;
   const int ppad = d.ppad, ntp = d.ntok_pad, kk = d.kk, nf = d.nf;
-  uint16_t* tw = reinterpret_cast<uint16_t*>(ws + d.tw_off);
-  _Float16* tw16 = reinterpret_cast<_Float16*>(ws + d.tw16_off);
+  uint16_t* tw = d.tw;
+  _Float16* tw16 = reinterpret_cast<_Float16*>(d.tw16);
   const long long plane = (long long)ppad * ntp;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < plane;
        e += (long long)gridDim.x * blockDim.x) {
@@ -108,13 +104,11 @@ __global__ __launch_bounds__(256) void k_twiddle(ScoreLaunch sl, char* ws) {
     tw[e] = t1;
     tw[plane + e] = t2;
     tw[2 * plane + e] = t3;
-    if (sl.dtype == CT_BF16) {
-      const _Float16 h1 = f16_from_f64(v);
-      tw16[e] = h1;
-      tw16[plane + e] = f16_from_f64(v - (double)h1);
-    }
+    const _Float16 h1 = f16_from_f64(v);
+    tw16[e] = h1;
+    tw16[plane + e] = f16_from_f64(v - (double)h1);
   }
-  double2* trig = reinterpret_cast<double2*>(ws + d.trig_off);
+  double2* trig = d.trig;
   for (long long m = (long long)blockIdx.x * blockDim.x + threadIdx.x; m < nf;
        m += (long long)gridDim.x * blockDim.x) {
     double s, c;
@@ -157,7 +151,7 @@ __global__ __launch_bounds__(256) void k_band_fwd(ScoreLaunch sl, char* ws) {
   const bool active = cbase < C;
   const int c0 = cbase + 2 * col;
 
-  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + d.tw_off);
+  const uint16_t* tw = d.tw;
   const long long plane = (long long)ppad * ntp;
   const char* src = reinterpret_cast<const char*>(kv ? d.v : d.k);
   const size_t esz = DT == CT_BF16 ? 2 : 4;
@@ -359,7 +353,7 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
   // (b_k = c_k + 2 cos(phi) b_{k+1} - b_{k+2}; U = A_0 + b_1 cos(phi) - b_2,
   // V = d_1 sin(phi)).  Token 0 (phi = 0) is the sum of the A_k, taken by
   // wave 0 in a fixed order.
-  const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+  const double2* trig = d.trig;
   const double2* cf = reinterpret_cast<const double2*>(coef);  // {A_k, B_k}
   double* E = reinterpret_cast<double*>(ws + d.e_off) + (size_t)(layer * 2 + kv) * N;
   const double inv = 1.0 / ((double)nf * (double)nf);
@@ -417,8 +411,14 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
   const int layer = (prob / 2) % L;
   const int kv = prob % 2;
   const ScoreChunkDesc& d = sl.c[b];
-  int* flag = reinterpret_cast<int*>(ws + d.flag_off) + layer * 2 + kv;
-  if (!F16 && redo && *flag == 0) return;
+  // fp16-range flags of this problem, one per channel block (written by the
+  // first row block of each channel block in the fp16 pass, read by the redo)
+  int* flags = reinterpret_cast<int*>(ws + d.flag_off) + (layer * 2 + kv) * kFlagBlocks;
+  if (!F16 && redo) {
+    int any = 0;
+    for (int i = 0; i < (int)gridDim.x; ++i) any |= flags[i];
+    if (any == 0) return;
+  }
   const int pbase = blockIdx.y * 32 * NTL;
   if (pbase >= d.ppad) return;
   const int nrows = min(32 * NTL, d.ppad - pbase);  // rows this chunk has in the block
@@ -435,7 +435,7 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
   // num_records returns 0, which zero-fills tokens at and beyond N and rows a
   // chunk does not have.  The whole offset is kept in the VGPR operand (the
   // scalar offset is 0), so that range check covers every load.
-  const uint16_t* tw = reinterpret_cast<const uint16_t*>(ws + (F16 ? d.tw16_off : d.tw_off));
+  const uint16_t* tw = F16 ? d.tw16 : d.tw;
   const long long plane = (long long)ppad * ntp;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
@@ -565,7 +565,10 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
-    if (__any(bad) && lane == 0) *flag = 1;
+    // the first row block (which holds the DC row) writes the block's flag,
+    // 0 or 1, so nothing has to clear the flags between calls
+    const int any_bad = __syncthreads_or((int)bad);
+    if (blockIdx.y == 0 && tid == 0) flags[blockIdx.x] = any_bad;
   }
   if (!active) return;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
@@ -896,7 +899,7 @@ __global__ __launch_bounds__(512) void k_highpass(ScoreLaunch sl, char* ws) {
   const int nrow = min(n, N - 1);  // lanes past N read a valid row; their results are dropped
   const float* Y = reinterpret_cast<const float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
   const size_t xoff = ((size_t)layer * N + nrow) * C + 8 * g;
-  const double2* trig = reinterpret_cast<const double2*>(ws + d.trig_off);
+  const double2* trig = d.trig;
   constexpr int XW = DT == CT_BF16 ? 4 : 8;  // dwords of X per lane per 16-channel step
 
   double etot = 0.0, cross = 0.0;
@@ -1204,9 +1207,18 @@ int kkeep(int nf, int a_num, int a_den) {
   return (int)k;
 }
 
+size_t score_tables_bytes(int nf, int kk, int ntp, size_t* tw16_off, size_t* trig_off) {
+  const int ppad = band_rows_padded(kk);
+  size_t off = align256((size_t)3 * ppad * ntp * 2);
+  if (tw16_off) *tw16_off = off;
+  off = align256(off + (size_t)2 * ppad * ntp * 2);
+  if (trig_off) *trig_off = off;
+  return align256(off + (size_t)nf * 16);
+}
+
 ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, int32_t H,
                      int32_t D, int32_t a_num, int32_t a_den, ct_fftlen fftlen, size_t* bytes,
-                     std::vector<ScoreLaunch>* launches, int32_t variant) {
+                     std::vector<ScoreLaunch>* launches, int32_t variant, const Context* ctx) {
   const int C = H * D;
   const bool band = variant != CT_SCORE_L2;  // the L2 variant needs only the energies
   size_t off = 0;
@@ -1227,17 +1239,25 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
     tok += d.n;
     if (2 * d.kk > max_p2) max_p2 = 2 * d.kk;
     if (!band) continue;
+    // tables held by the context are used as they are; the others get a
+    // workspace region, written by the first chunk of the call that needs it
+    ScoreTables held;
+    if (ctx && context_find_tables(ctx, d.nf, d.kk, d.ntok_pad, &held)) {
+      d.tw = held.tw;
+      d.tw16 = held.tw16;
+      d.trig = held.trig;
+      d.tw_off = d.tw16_off = d.trig_off = -1;
+      continue;
+    }
     int found = -1;
     for (size_t t = 0; t < tabs.size(); ++t)
       if (tabs[t].nf == d.nf && tabs[t].kk == d.kk && tabs[t].ntp == d.ntok_pad) found = (int)t;
     if (found < 0) {
-      Tab t{d.nf, d.kk, d.ntok_pad, 0, 0, 0};
-      t.tw = (int64_t)off;
-      off = align256(off + (size_t)3 * d.ppad * d.ntok_pad * 2);
-      t.tw16 = (int64_t)off;
-      off = align256(off + (size_t)2 * d.ppad * d.ntok_pad * 2);
-      t.trig = (int64_t)off;
-      off = align256(off + (size_t)d.nf * 16);
+      Tab t{d.nf, d.kk, d.ntok_pad, (int64_t)off, 0, 0};
+      size_t o16 = 0, otr = 0;
+      off += score_tables_bytes(d.nf, d.kk, d.ntok_pad, &o16, &otr);
+      t.tw16 = t.tw + (int64_t)o16;
+      t.trig = t.tw + (int64_t)otr;
       tabs.push_back(t);
       d.tw_owner = 1;
       found = (int)tabs.size() - 1;
@@ -1248,7 +1268,7 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   }
   for (int b = 0; b < n_chunks && band; ++b) {
     desc[b].flag_off = (int64_t)off;
-    off = align256(off + (size_t)L * 2 * 4);
+    off = align256(off + (size_t)L * 2 * kFlagBlocks * 4);
   }
   for (int b = 0; b < n_chunks && band; ++b) {
     desc[b].y_off = (int64_t)off;
@@ -1294,17 +1314,55 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
   return CT_OK;
 }
 
-// Twiddle planes and the band projection Y of every problem of a launch.
-static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t stream) {
+void score_bind(std::vector<ScoreLaunch>* launches, char* ws) {
+  for (ScoreLaunch& sl : *launches)
+    for (int i = 0; i < sl.n_chunks; ++i) {
+      ScoreChunkDesc& d = sl.c[i];
+      if (d.tw_off < 0) continue;  // held by the context
+      d.tw = reinterpret_cast<uint16_t*>(ws + d.tw_off);
+      d.tw16 = reinterpret_cast<uint16_t*>(ws + d.tw16_off);
+      d.trig = reinterpret_cast<double2*>(ws + d.trig_off);
+    }
+}
+
+static ct_status launch_twiddle(const ScoreLaunch& sl, hipStream_t stream) {
   int max_elems = 0;
-  for (int i = 0; i < sl.n_chunks; ++i)
-    max_elems = std::max(max_elems, sl.c[i].ppad * sl.c[i].ntok_pad);
+  bool any = false;
+  for (int i = 0; i < sl.n_chunks; ++i) {
+    if (!sl.c[i].tw_owner) continue;
+    any = true;
+    max_elems = std::max(max_elems, std::max(sl.c[i].ppad * sl.c[i].ntok_pad, sl.c[i].nf));
+  }
+  if (!any) return CT_OK;
   dim3 gt((max_elems + 255) / 256 < 2048 ? (max_elems + 255) / 256 : 2048, sl.n_chunks);
   {
     TimedLaunch tl_("twiddle", stream);
-    hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl, ws);
+    hipLaunchKernelGGL(k_twiddle, gt, dim3(256), 0, stream, sl);
   }
-  if (ct_status s = check_launch("twiddle")) return s;
+  return check_launch("twiddle");
+}
+
+ct_status score_tables_build(int nf, int kk, int ntp, int dtype, const ScoreTables& t, hipStream_t stream) {
+  ScoreLaunch sl{};
+  sl.n_chunks = 1;
+  sl.dtype = dtype;
+  ScoreChunkDesc& d = sl.c[0];
+  d.nf = nf;
+  d.kk = kk;
+  d.ppad = band_rows_padded(kk);
+  d.ntok_pad = ntp;
+  d.n = ntp;
+  d.tw_owner = 1;
+  d.tw = t.tw;
+  d.tw16 = t.tw16;
+  d.trig = t.trig;
+  return launch_twiddle(sl, stream);
+}
+
+// Twiddle planes (tables not held by a context) and the band projection Y of
+// every problem of a launch.
+static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t stream) {
+  if (ct_status s = launch_twiddle(sl, stream)) return s;
 
   dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
   if (sl.dtype == CT_BF16) {

@@ -53,13 +53,13 @@ def test_score_ws_validation(lib):
     import non_prefix_kv_token_amd as ct
     n = (C.c_int32 * 2)(2048, 2048)
     out = C.c_size_t(0)
-    assert lib.cachetune_score_chunk_ws(n, 2, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_OK
+    assert lib.cachetune_score_chunk_ws(None, n, 2, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_OK
     assert out.value > 0
     bad = (C.c_int32 * 1)(1)  # chunk shorter than 2 tokens
-    assert lib.cachetune_score_chunk_ws(bad, 1, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_E_INVALID
+    assert lib.cachetune_score_chunk_ws(None, bad, 1, 32, 8, 128, 1, 16, 0, C.byref(out)) == ct.CT_E_INVALID
     assert b"chunk length" in lib.cachetune_last_error()
-    assert lib.cachetune_score_chunk_ws(n, 2, 32, 8, 128, 3, 2, 0, C.byref(out)) == ct.CT_E_INVALID
-    assert lib.cachetune_score_chunk_ws(n, 2, 32, 3, 7, 1, 16, 0, C.byref(out)) == ct.CT_E_UNSUPPORTED
+    assert lib.cachetune_score_chunk_ws(None, n, 2, 32, 8, 128, 3, 2, 0, C.byref(out)) == ct.CT_E_INVALID
+    assert lib.cachetune_score_chunk_ws(None, n, 2, 32, 3, 7, 1, 16, 0, C.byref(out)) == ct.CT_E_UNSUPPORTED
 
 
 def test_calls_reject_bad_arguments_without_device_work(lib):
@@ -67,21 +67,46 @@ def test_calls_reject_bad_arguments_without_device_work(lib):
     kout = (C.c_int32 * 1)()
     n = (C.c_int32 * 1)(100)
     # r outside [0, 1]
-    assert lib.cachetune_select_topr(C.c_void_p(16), n, 1, 3, 2, None, C.c_void_p(16), None, kout,
+    assert lib.cachetune_select_topr(None, C.c_void_p(16), n, 1, 3, 2, None, C.c_void_p(16), None, kout,
                                      None) == ct.CT_E_INVALID
     # head_dim not supported
-    assert lib.cachetune_assemble_rope(None, 0, None, None, 0, 0, 8, 96, ct.CT_BF16, 10000.0, 0,
+    assert lib.cachetune_assemble_rope(None, None, 0, None, None, 0, 0, 8, 96, ct.CT_BF16, 10000.0, 0,
                                        C.c_void_p(16), C.c_void_p(16), 10, None) == ct.CT_E_UNSUPPORTED
     # misaligned output
-    assert lib.cachetune_assemble_rope(None, 0, None, None, 0, 0, 8, 128, ct.CT_BF16, 10000.0, 0,
+    assert lib.cachetune_assemble_rope(None, None, 0, None, None, 0, 0, 8, 128, ct.CT_BF16, 10000.0, 0,
                                        C.c_void_p(18), C.c_void_p(16), 10, None) == ct.CT_E_INVALID
     # Hq not a multiple of H
-    assert lib.cachetune_recompute_attn(None, None, 0, 6, None, None, 10, 4, 128, ct.CT_BF16, 0.1,
+    assert lib.cachetune_recompute_attn(None, None, None, 0, 6, None, None, 10, 4, 128, ct.CT_BF16, 0.1,
                                         10000.0, 0, None, None, None, 0, None) == ct.CT_E_INVALID
     out = C.c_size_t(1)
-    assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 128, ct.CT_BF16, C.byref(out)) == ct.CT_OK
-    assert lib.cachetune_recompute_attn_ws(100, 32, 16512, 8, 100, ct.CT_BF16,
+    assert lib.cachetune_recompute_attn_ws(None, 100, 32, 16512, 8, 128, ct.CT_BF16, C.byref(out)) == ct.CT_OK
+    assert lib.cachetune_recompute_attn_ws(None, 100, 32, 16512, 8, 100, ct.CT_BF16,
                                            C.byref(out)) == ct.CT_E_UNSUPPORTED
+
+
+def test_select_topr_counts(lib, orc):
+    """k = floor(r n) per chunk from the library's host query, the oracle's count."""
+    import non_prefix_kv_token_amd as ct
+    ns = [512, 2048, 1, 8192, 333]
+    arr = (C.c_int32 * len(ns))(*ns)
+    for r in [(15, 100), (0, 1), (1, 1), (1, 3)]:
+        k = (C.c_int32 * len(ns))()
+        assert lib.cachetune_select_topr_counts(arr, len(ns), r[0], r[1], k) == ct.CT_OK
+        assert list(k) == [orc.ksel(n, *r) for n in ns]
+    k = (C.c_int32 * len(ns))()
+    assert lib.cachetune_select_topr_counts(arr, len(ns), 3, 2, k) == ct.CT_E_INVALID
+    assert lib.cachetune_select_topr_counts(None, len(ns), 1, 2, k) == ct.CT_E_INVALID
+
+
+def test_handle_calls_reject_bad_arguments(lib):
+    import non_prefix_kv_token_amd as ct
+    h = C.c_void_p()
+    assert lib.cachetune_create(-1, C.byref(h)) in (ct.CT_E_INVALID, ct.CT_E_HIP)
+    assert h.value is None
+    assert lib.cachetune_create(0, None) == ct.CT_E_INVALID
+    lib.cachetune_destroy(None)  # ignored
+    n = (C.c_int32 * 1)(2048)
+    assert lib.cachetune_prepare_scoring(None, n, 1, 1, 16, 0, None) == ct.CT_E_INVALID
 
 
 # ---- hardware-aware ratio search: host logic, callable without a GPU ---------------------
@@ -127,13 +152,13 @@ def test_score_variant_ws(lib):
     sz = {}
     for v in (ct.CT_SCORE_LOWPASS, ct.CT_SCORE_L2, ct.CT_SCORE_HIGHPASS):
         out = C.c_size_t(0)
-        assert lib.cachetune_score_variant_ws(n, 2, 4, 8, 128, 1, 16, 0, v, C.byref(out)) == ct.CT_OK
+        assert lib.cachetune_score_variant_ws(None, n, 2, 4, 8, 128, 1, 16, 0, v, C.byref(out)) == ct.CT_OK
         sz[v] = out.value
     # the high-frequency view runs the band path first: same workspace; L2 needs only energies
     assert sz[ct.CT_SCORE_HIGHPASS] == sz[ct.CT_SCORE_LOWPASS]
     assert 0 < sz[ct.CT_SCORE_L2] < sz[ct.CT_SCORE_LOWPASS]
     out = C.c_size_t(0)
-    assert lib.cachetune_score_variant_ws(n, 2, 4, 8, 128, 1, 16, 0, 3, C.byref(out)) == ct.CT_E_INVALID
+    assert lib.cachetune_score_variant_ws(None, n, 2, 4, 8, 128, 1, 16, 0, 3, C.byref(out)) == ct.CT_E_INVALID
     assert b"unknown variant" in lib.cachetune_last_error()
 
 

@@ -47,7 +47,7 @@ def test_noalloc_matches_workspace_call_twice(syn):
     qb = torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda")
     kb = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device="cuda")
     lib = ct.lib()
-    st = lib.cachetune_recompute_attn_noalloc(ctypes.c_void_p(qb.data_ptr()), ctypes.c_void_p(qpos.data_ptr()), 20573,
+    st = lib.cachetune_recompute_attn_noalloc(ct.handle(), ctypes.c_void_p(qb.data_ptr()), ctypes.c_void_p(qpos.data_ptr()), 20573,
                                               32, ctypes.c_void_p(kb.data_ptr()), ctypes.c_void_p(kb.data_ptr()), 136643,
                                               8, 128, ct.CT_BF16, 0.088, 500000.0, 0, ctypes.c_void_p(qb.data_ptr()),
                                               None, None)
