@@ -478,7 +478,7 @@ def host_tier(args):
 
     ns, L, H, Hq, D = [2048] * 32, 32, 8, 32, 128
     theta, alpha, n_sfx, seed = 500000.0, (1, 16), 128, 20260525
-    r_list = [(5, 100), (10, 100), (15, 100), (20, 100), (30, 100)]
+    r_list = [(2, 100), (5, 100), (10, 100), (15, 100), (20, 100), (30, 100)]
     nb, N = len(ns), ns[0]
     T_c = sum(ns)
     T = T_c + n_sfx
@@ -645,15 +645,18 @@ def host_tier(args):
 
     calibration = None
     if args.calibrate:
-        # App. C.1: per-token costs from two profiling probes -- at r = 5 % the
-        # request is bound by the complement transfer, at r = 30 % by the
-        # recomputed rows' work -- then App. C.2's warm-started golden-section
+        # App. C.1: t_c, t_i and the fixed per-layer overhead t_o fitted to the
+        # sweep's request times (the library's least-squares fit of the
+        # overlapped cost model), then App. C.2's warm-started golden-section
         # search on the measured request time, with and without the 15 % floor.
-        tok = float(T_c) * L
-        t_i = results[0]["ms_per_request"] / (tok * (1.0 - 0.05))
-        t_c = results[-1]["ms_per_request"] / (tok * 0.30)
+        rs = [int(x["r"].split("/")[0]) / int(x["r"].split("/")[1]) for x in results]
+        ts = [x["ms_per_request"] for x in results]
+        t_c, t_i, t_o = ct.cachetune_fit_cost_model(rs, ts, L, T_c)
+        model = [L * (t_o + max(r * T_c * t_c, (1 - r) * T_c * t_i)) for r in rs]
         calibration = {"t_c_us_per_token_layer": t_c * 1e3, "t_i_us_per_token_layer": t_i * 1e3,
-                       "warm_start": t_i / (t_c + t_i), "eps": 0.01, "half_width": 0.1, "runs": []}
+                       "t_o_ms_per_layer": t_o, "warm_start": t_i / (t_c + t_i),
+                       "model_ms_per_request": dict(zip([x["r"] for x in results], model)),
+                       "eps": 0.01, "half_width": 0.1, "runs": []}
         for r_min in (0.15, 0.02):
             probes = []
 

@@ -421,6 +421,28 @@ ct_status cachetune_timing_read(const char* kernel, double* total_ms, int32_t* l
  * r_min > r_max, a range outside [0, 1], half_width <= 0, eps <= 0, a NULL
  * callback or output, or a cost that is not finite (the search stops there). */
 typedef double (*ct_cost_fn)(double r, void* user);
+
+/* The App. C.1 cost model fitted to measured request times (host logic):
+ * per layer the pipeline overlaps recomputing r*N tokens (t_c each) with
+ * loading the other (1 - r)*N (t_i each), plus a fixed per-layer overhead t_o
+ * (kernel launches, event waits, buffer management):
+ *   T(r) = L * (t_o + max(r*N*t_c, (1 - r)*N*t_i)).
+ * The probes (r[i], t[i]), i < n, are split by ratio into a loading-bound lower
+ * part and a recomputation-bound upper part of at least two probes each (one
+ * probe would fit any slope); every split is a
+ * linear least-squares problem in (t_o, t_c, t_i).  A split counts when
+ * t_c, t_i > 0, t_o >= 0 and each probe lies on its side of the balance ratio
+ * t_i / (t_c + t_i); the smallest squared residual wins (the lower split on a
+ * tie).  t_o shifts every ratio's time alike, so the warm start of
+ * cachetune_calibrate_ratio, t_i / (t_c + t_i), does not depend on it.
+ *  r, t: host double[n], n in [4, 1024]; r in [0, 1]; t finite (any unit)
+ *  L, N: layers and reusable tokens of the measured request
+ *  t_c, t_i, t_o: host outputs, per token and layer (t_o per layer), in the
+ *        unit of t.
+ * CT_E_INVALID for bad arguments or probes that show no loading-bound and
+ * recomputation-bound parts. */
+ct_status cachetune_fit_cost_model(const double* r, const double* t, int32_t n, int32_t L, int32_t N,
+                                   double* t_c, double* t_i, double* t_o);
 ct_status cachetune_calibrate_ratio(double t_c, double t_i, double r_min, double r_max,
                                     double half_width, double eps, ct_cost_fn cost, void* user,
                                     double* r_out, int32_t* n_probes);

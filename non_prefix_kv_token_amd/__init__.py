@@ -50,7 +50,7 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
            "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj",
            "cachetune_recompute_attn_noalloc", "cachetune_create", "cachetune_destroy",
-           "cachetune_prepare_scoring", "cachetune_select_topr_counts"]
+           "cachetune_prepare_scoring", "cachetune_select_topr_counts", "cachetune_fit_cost_model"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -98,6 +98,8 @@ def lib():
                                               vp, vp, vp, sz, vp]
         L.cachetune_band_energy_ws.argtypes = [vp, i32, i32, i32, i32, i32, C.POINTER(sz)]
         L.cachetune_band_energy.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.cachetune_fit_cost_model.argtypes = [vp, vp, i32, i32, i32, C.POINTER(f64), C.POINTER(f64),
+                                                C.POINTER(f64)]
         L.cachetune_rmsnorm.argtypes = [vp, vp, i32, i32, f32, i32, vp, vp]
         L.cachetune_silu_mul.argtypes = [vp, i32, i32, i32, vp, vp]
         L.cachetune_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
@@ -410,6 +412,17 @@ def cachetune_calibrate_ratio(t_c, t_i, cost, r_min=0.15, r_max=1.0, half_width=
         raise err[0]
     _check(st)
     return r_out.value, n.value
+
+
+def cachetune_fit_cost_model(r, times, L, N):
+    """App. C.1 cost model from measured request times: returns (t_c, t_i,
+    t_o) in the unit of `times` (per token and layer; t_o per layer)."""
+    n = len(r)
+    ra = (C.c_double * n)(*[float(x) for x in r])
+    ta = (C.c_double * n)(*[float(x) for x in times])
+    tc, ti, to = C.c_double(0.0), C.c_double(0.0), C.c_double(0.0)
+    _check(lib().cachetune_fit_cost_model(ra, ta, n, int(L), int(N), C.byref(tc), C.byref(ti), C.byref(to)))
+    return tc.value, ti.value, to.value
 
 
 def cachetune_timing_read(kernel: str):

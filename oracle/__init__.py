@@ -278,6 +278,50 @@ def attention(q_pre, qpos, k, v, scale, theta, style=ROPE_HALF, rows=None):
 
 # ---- hardware-aware recomputation ratio (App. C.1, App. C.2) ----------------
 
+def cost_model_time(r, t_c, t_i, t_o, L, N):
+    """App. C.1 (reading): per layer the pipeline overlaps recomputing r*N
+    tokens with loading the other (1 - r)*N, so the longer of the two sets the
+    layer's time, plus the fixed per-layer overhead t_o; L layers."""
+    r = np.asarray(r, dtype=np.float64)
+    return L * (t_o + np.maximum(r * N * t_c, (1.0 - r) * N * t_i))
+
+
+def fit_cost_model(r, times, L, N):
+    """App. C.1: t_c, t_i and t_o from measured request times at several
+    ratios.  Every split of the probes (sorted by r) into a lower part bounded
+    by loading and an upper part bounded by recomputation, at least two probes
+    each (a single probe fits any slope), is a linear least-squares problem in
+    (t_o, t_c, t_i): lower probes satisfy
+    T / L = t_o + (1 - r) N t_i, upper ones T / L = t_o + r N t_c.  A split
+    counts when t_c, t_i > 0, t_o >= 0 and every probe lies on its side of the
+    balance ratio t_i / (t_c + t_i); the one with the smallest squared
+    residual of the model wins (the lower split on a tie).
+    Returns (t_c, t_i, t_o), or None when no split counts."""
+    r = np.asarray(r, dtype=np.float64)
+    times = np.asarray(times, dtype=np.float64)
+    order = np.argsort(r, kind="stable")
+    r, times = r[order], times[order]
+    n = len(r)
+    best = None
+    for k in range(2, n - 1):
+        A = np.zeros((n, 3))
+        A[:, 0] = 1.0
+        A[k:, 1] = r[k:] * N
+        A[:k, 2] = (1.0 - r[:k]) * N
+        if np.linalg.matrix_rank(A) < 3:
+            continue
+        (t_o, t_c, t_i), *_ = np.linalg.lstsq(A, times / L, rcond=None)
+        if not (t_c > 0 and t_i > 0 and t_o >= 0):
+            continue
+        rb = t_i / (t_c + t_i)
+        if not (np.all(r[:k] <= rb) and np.all(r[k:] >= rb)):
+            continue
+        res = float(np.sum((times - cost_model_time(r, t_c, t_i, t_o, L, N)) ** 2))
+        if best is None or res < best[0]:
+            best = (res, float(t_c), float(t_i), float(t_o))
+    return None if best is None else best[1:]
+
+
 def warm_start_ratio(t_c: float, t_i: float, r_min: float, r_max: float) -> float:
     """App. C.1: per layer, recomputing r*N tokens costs r*N*t_c and loading the
     other (1 - r)*N costs (1 - r)*N*t_i; the two are equal at

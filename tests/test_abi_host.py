@@ -132,6 +132,29 @@ def test_calibrate_ratio_matches_oracle(lib, orc, case):
     assert abs(r_lib - r_orc) <= 1e-12
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_fit_cost_model_matches_oracle(lib, orc, seed):
+    """The library's App. C.1 fit equals the oracle's (numpy least squares) on
+    noisy probes, and refuses what the oracle finds no fit for."""
+    import numpy as np
+    import non_prefix_kv_token_amd as ct
+    rng = np.random.default_rng(seed)
+    r = np.array([0.02, 0.05, 0.10, 0.15, 0.20, 0.30, 0.12, 0.25])
+    L, N = 32, 65536
+    times = orc.cost_model_time(r, 0.6e-3 * (1 + 0.3 * rng.random()), 0.09e-3, 0.9, L, N) * \
+        (1 + 0.02 * rng.standard_normal(r.shape))
+    want = orc.fit_cost_model(r, times, L, N)
+    got = ct.cachetune_fit_cost_model(r, times, L, N)
+    assert want is not None
+    assert np.allclose(got, want, rtol=1e-9, atol=1e-12)
+    one_sided = L * (0.5 + (1 - r) * N * 1e-4)
+    assert orc.fit_cost_model(r, one_sided, L, N) is None
+    with pytest.raises(RuntimeError):
+        ct.cachetune_fit_cost_model(r, one_sided, L, N)
+    with pytest.raises(RuntimeError):
+        ct.cachetune_fit_cost_model(r[:3], times[:3], L, N)
+
+
 def test_calibrate_ratio_rejects_bad_arguments(lib):
     import non_prefix_kv_token_amd as ct
     good = lambda r: r  # noqa: E731

@@ -76,3 +76,63 @@ def test_matches_grid_search(orc):
         grid = np.linspace(0.1, 0.5833333333333334, 200001)
         best = grid[np.argmin(np.abs(grid - c) ** p)]
         assert abs(r - best) <= 1e-3
+
+
+# ---- App. C.1 cost model with the fixed per-layer overhead t_o ----------------------
+
+SWEEP = [0.02, 0.05, 0.10, 0.15, 0.20, 0.30]
+
+
+@pytest.mark.parametrize("t_c,t_i,t_o", [(0.636e-3, 0.085e-3, 1.0), (1.17e-3, 0.12e-3, 0.4),
+                                          (2.0e-3, 0.3e-3, 0.05)])
+def test_fit_recovers_exact_costs(orc, t_c, t_i, t_o):
+    """Times made by the model from known costs (probes on both sides of the
+    balance) give back those costs."""
+    L, N = 32, 65536
+    times = orc.cost_model_time(np.array(SWEEP), t_c, t_i, t_o, L, N)
+    got = orc.fit_cost_model(SWEEP, times, L, N)
+    assert got is not None
+    for a, b in zip(got, (t_c, t_i, t_o)):
+        assert abs(a - b) <= 1e-9 * max(1.0, abs(b))
+
+
+def test_fit_invariances(orc):
+    """Scaling every time scales all three costs; adding c*L to every time
+    adds c to t_o only; the order of the probes does not matter."""
+    L, N = 32, 65536
+    rng = np.random.default_rng(3)
+    times = orc.cost_model_time(np.array(SWEEP), 0.7e-3, 0.1e-3, 0.8, L, N) * (1 + 0.01 * rng.standard_normal(len(SWEEP)))
+    t_c, t_i, t_o = orc.fit_cost_model(SWEEP, times, L, N)
+    s = orc.fit_cost_model(SWEEP, 3.0 * times, L, N)
+    assert np.allclose(s, (3 * t_c, 3 * t_i, 3 * t_o), rtol=1e-9)
+    a = orc.fit_cost_model(SWEEP, times + 0.25 * L, L, N)
+    assert np.allclose(a, (t_c, t_i, t_o + 0.25), rtol=1e-9)
+    perm = rng.permutation(len(SWEEP))
+    p = orc.fit_cost_model(np.array(SWEEP)[perm], times[perm], L, N)
+    assert np.allclose(p, (t_c, t_i, t_o), rtol=1e-12)
+
+
+def test_fit_is_the_best_split_by_brute_force(orc):
+    """With noise, the fitted costs give the smallest residual among all
+    (split, positive costs) candidates found by a brute-force grid around the
+    fit, and the model's balance point lies between the two parts."""
+    L, N = 32, 65536
+    rng = np.random.default_rng(11)
+    times = orc.cost_model_time(np.array(SWEEP), 0.64e-3, 0.085e-3, 1.0, L, N) * (1 + 0.02 * rng.standard_normal(len(SWEEP)))
+    t_c, t_i, t_o = orc.fit_cost_model(SWEEP, times, L, N)
+    base = np.sum((times - orc.cost_model_time(np.array(SWEEP), t_c, t_i, t_o, L, N)) ** 2)
+    for dc in (0.97, 1.0, 1.03):
+        for di in (0.97, 1.0, 1.03):
+            for do in (-0.05, 0.0, 0.05):
+                res = np.sum((times - orc.cost_model_time(np.array(SWEEP), t_c * dc, t_i * di, t_o + do, L, N)) ** 2)
+                assert res >= base * (1 - 1e-12)
+    rb = t_i / (t_c + t_i)
+    assert SWEEP[0] <= rb <= SWEEP[-1]
+
+
+def test_fit_rejects_one_sided_probes(orc):
+    """Probes that are all loading-bound (times falling with r) have no split
+    with positive costs on both sides."""
+    L, N = 32, 65536
+    times = L * (0.5 + (1 - np.array(SWEEP)) * N * 1e-4)
+    assert orc.fit_cost_model(SWEEP, times, L, N) is None
