@@ -54,9 +54,15 @@
 
 #ifdef __cplusplus
 extern "C" {
+/* C++ gives the enums a fixed 32-bit underlying type, so that any int32 value a
+ * C caller passes is a value of the type (and is then rejected by the call's
+ * validation) rather than undefined behaviour; C sees int-sized enums. */
+#define CT_ENUM_BASE : int32_t
+#else
+#define CT_ENUM_BASE
 #endif
 
-typedef enum {
+typedef enum CT_ENUM_BASE {
   CT_OK = 0,
   CT_E_INVALID = -1,     /* bad argument (null pointer, size, ratio ...) */
   CT_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim) */
@@ -64,23 +70,23 @@ typedef enum {
   CT_E_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } ct_status;
 
-typedef enum { CT_F32 = 0, CT_BF16 = 1 } ct_dtype;
+typedef enum CT_ENUM_BASE { CT_F32 = 0, CT_BF16 = 1 } ct_dtype;
 
 /* Per-layer normalisation of the chunk scores (App. B.1 states only that the
  * scores are normalised within each layer).  CT_NORM_SUM divides by the layer
  * sum (a layer whose sum is 0 becomes uniform 1/n); CT_NORM_MAX divides by the
  * layer maximum; CT_NORM_MINMAX maps [min, max] to [0, 1]; CT_NORM_NONE keeps
  * the raw values.  Degenerate MAX / MINMAX layers become 0. */
-typedef enum { CT_NORM_SUM = 0, CT_NORM_MAX = 1, CT_NORM_MINMAX = 2, CT_NORM_NONE = 3 } ct_norm;
+typedef enum CT_ENUM_BASE { CT_NORM_SUM = 0, CT_NORM_MAX = 1, CT_NORM_MINMAX = 2, CT_NORM_NONE = 3 } ct_norm;
 
 /* RoPE pairing: rotate-half pairs (j, j + D/2); interleaved pairs (2j, 2j+1).
  * Pair j turns by pos * theta^(-2j/D). */
-typedef enum { CT_ROPE_HALF = 0, CT_ROPE_INTERLEAVED = 1 } ct_rope;
+typedef enum CT_ENUM_BASE { CT_ROPE_HALF = 0, CT_ROPE_INTERLEAVED = 1 } ct_rope;
 
 /* Transform length of a chunk of n tokens: the exact length n (App. B.1), or
  * the next power of two with the chunk zero-padded (the retained-bin count is
  * then taken over that length's bins and positions [0, n) are scored). */
-typedef enum { CT_FFT_EXACT_N = 0, CT_FFT_ZEROPAD_POW2 = 1 } ct_fftlen;
+typedef enum CT_ENUM_BASE { CT_FFT_EXACT_N = 0, CT_FFT_ZEROPAD_POW2 = 1 } ct_fftlen;
 
 /* One independently encoded chunk: pre-RoPE keys and values, [L][n][H][D],
  * device memory.  n in [2, 8192]. */
@@ -191,7 +197,7 @@ ct_status cachetune_score_chunk(ct_handle h, const ct_chunk* chunks, int32_t n_c
  * caller-supplied seeded uniform scores selects a uniformly random set.
  * Arguments, layouts and errors are those of cachetune_score_chunk(_ws); an
  * unknown variant is CT_E_INVALID. */
-typedef enum { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1, CT_SCORE_HIGHPASS = 2 } ct_score_variant;
+typedef enum CT_ENUM_BASE { CT_SCORE_LOWPASS = 0, CT_SCORE_L2 = 1, CT_SCORE_HIGHPASS = 2 } ct_score_variant;
 ct_status cachetune_score_variant_ws(ct_handle h, const int32_t* n_per_chunk, int32_t n_chunks, int32_t L,
                                      int32_t H, int32_t D, int32_t alpha_num, int32_t alpha_den,
                                      ct_fftlen fftlen, ct_score_variant variant, size_t* bytes);
