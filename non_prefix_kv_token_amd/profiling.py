@@ -3,6 +3,10 @@
   python -m non_prefix_kv_token_amd.profiling stats  <kernel_stats.csv> --title T --command C --out F
   python -m non_prefix_kv_token_amd.profiling traffic --fetch DIR --write DIR --kernel-substr S \
          --name attention --workload W --source FILE --command-fetch C1 --command-write C2 --out F
+  python -m non_prefix_kv_token_amd.profiling counters DIR --title T --command C --out F
+
+`counters` tabulates every counter of a `rocprofv3 --pmc` run per kernel
+(mean per dispatch, as rocprofv3 reports them: summed over the device).
 
 `traffic` reads two `rocprofv3 --pmc` runs of the same program (FETCH_SIZE,
 then WRITE_SIZE; both in KiB per dispatch) that also ran a 1 GiB device copy
@@ -74,9 +78,32 @@ def copy_reading(pmc_dir: str, counter: str) -> float:
     return statistics.mean(top)
 
 
+def counters_table(pmc_dir: str) -> str:
+    rows = _rows(pmc_dir, "*counter_collection.csv")
+    per = {}
+    for r in rows:
+        per.setdefault(short_name(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    names = sorted({c for d in per.values() for c in d})
+    kernels = sorted(per)
+    lines = ["| Counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+             "|---|" + "---:|" * len(kernels)]
+    lines.append("| dispatches | " + " | ".join(str(len(next(iter(per[k].values())))) for k in kernels) + " |")
+    for c in names:
+        vals = [f"{statistics.mean(per[k][c]):.4g}" if c in per[k] else "" for k in kernels]
+        lines.append(f"| {c} | " + " | ".join(vals) + " |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--title", required=True)
@@ -95,6 +122,15 @@ def main():
     b.add_argument("--command-write", required=True)
     b.add_argument("--out", required=True)
     args = ap.parse_args()
+
+    if args.cmd == "counters":
+        text = f"# {args.title}\n\nCommand (from the repository root on the GPU box):\n\n    {args.command}\n\n"
+        if args.note:
+            text += args.note + "\n\n"
+        text += counters_table(args.dir) + "\n"
+        with open(args.out, "w") as f:
+            f.write(text)
+        return
 
     if args.cmd == "stats":
         text = f"# {args.title}\n\nCommand (from the repository root on the GPU box):\n\n    {args.command}\n\n"
