@@ -388,10 +388,14 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // bf16 data: the same projection, software-pipelined.  X (the HBM stream) is
 // loaded two 32-token steps ahead into registers; the twiddle slab of the
 // next step is loaded one step ahead and written to the other of two LDS
-// buffers after the current step's MFMAs, so each step has one barrier and
-// no exposed load latency.  NTL = 32-row band tiles per block (the launch's
-// largest; rows a chunk does not have are zero).  The step loop is unrolled
-// by two so that both register and LDS buffers are compile-time.
+// buffers after the current step's MFMAs, so each step has one barrier.  The
+// step loop is unrolled by two so that both register and LDS buffers are
+// compile-time, and its body has no conditional code: vector-memory loads
+// complete in issue order, and a branch around a load or a compute block
+// makes the compiler's wait counts at the loop head assume the worst path,
+// which would hold each step until the next step's loads had landed.
+// NTL = 32-row band tiles per block (the launch's largest; rows a chunk does
+// not have are zero).
 // FULL: every chunk's padded band is a whole number of blocks of 32*NTL rows,
 // so no block holds padding tiles and the tile loop carries no per-tile test
 // (the branches would break up the matrix-core issue).
@@ -526,29 +530,34 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
     }
   };
 
-  load_x(0, xa);
-  if (nsteps > 1) load_x(1, xb);
+  // Loads of steps at or past nsteps read past both buffers' ranges and return
+  // zeros, so the loop issues them without a test: a straight-line body with
+  // one back edge lets every wait count only the loads of the step it needs.
+  // A wave with no channels computes on zeros (its loads are all out of range).
+  // The prologue leaves the loads in the order the loop body issues them
+  // (X of this step, then the twiddles and X of the next), so the loop entry
+  // needs no stricter waits than the back edge.
   load_tw(0);
+  load_x(0, xa);
   store_tw(lds[0]);
-  if (nsteps > 1) load_tw(1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tw(1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(1, xb);
   for (int step = 0; step < nsteps; step += 2) {
     // even step: LDS buffer 0, registers xa
     __syncthreads();
-    if (active) compute(lds[0], xa);
-    if (step + 1 < nsteps) store_tw(lds[1]);
-    if (step + 2 < nsteps) {
-      load_tw(step + 2);
-      load_x(step + 2, xa);
-    }
-    if (step + 1 >= nsteps) break;
-    // odd step: LDS buffer 1, registers xb
+    compute(lds[0], xa);
+    store_tw(lds[1]);
+    load_tw(step + 2);
+    load_x(step + 2, xa);
+    // odd step: LDS buffer 1, registers xb (past the end when nsteps is odd:
+    // zero operands leave the sums unchanged)
     __syncthreads();
-    if (active) compute(lds[1], xb);
-    if (step + 2 < nsteps) store_tw(lds[0]);
-    if (step + 3 < nsteps) {
-      load_tw(step + 3);
-      load_x(step + 3, xb);
-    }
+    compute(lds[1], xb);
+    store_tw(lds[0]);
+    load_tw(step + 3);
+    load_x(step + 3, xb);
   }
 
   if constexpr (F16) {
