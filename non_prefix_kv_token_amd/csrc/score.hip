@@ -739,38 +739,47 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char
 #pragma unroll
   for (int v = 0; v < 16; ++v) { acc[v] = 0.f; accd[v] = 0.0; }
 
-  // one stage of Y: ppad <= 128 rows x 16 float4, at most 2 per thread;
-  // two register sets, so that each stage is loaded two stages ahead
+  // one stage of Y: 128 rows x 16 float4, 2 per thread; two register sets,
+  // so that each stage is loaded two stages ahead.  Loads go through a buffer
+  // resource whose range check returns zeros for rows at or past ppad and,
+  // through an offset past the range, for stages at or past nst: no load or
+  // conversion is conditional, and the loop below has no conditional code
+  // around them (vector-memory loads complete in issue order, and a branch
+  // around a load makes the compiler's wait counts assume the worst path).
   constexpr int kPf = 128 * (kGramCh / 4) / kGramThreads;
-  float4 pfa[kPf], pfb[kPf];
-  auto load_stage = [&](int stage, float4* pf) {
-    const int c0 = stage * kGramCh;
+  static_assert(kPf * kGramThreads == 128 * (kGramCh / 4), "Y stage split");
+  const int nst = C / kGramCh;
+  const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Y), 0, ppad * C * 4, 0x00020000);
+  u32x4_t pfa[kPf], pfb[kPf];
+  auto load_stage = [&](int stage, u32x4_t* pf) {
+    const int sbase = stage < nst ? stage * kGramCh * 4 : ppad * C * 4;
 #pragma unroll
     for (int it = 0; it < kPf; ++it) {
       const int item = tid + kGramThreads * it, r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
-      if (item < ppad * (kGramCh / 4)) pf[it] = *reinterpret_cast<const float4*>(Y + (size_t)r * C + c0 + q4);
+      pf[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(yres, sbase + (r * C + q4) * 4, 0, 0));
     }
   };
-  auto convert = [&](int buf, const float4* pf) {
+  // rows at or past ppad convert zeros into plane rows no tile reads
+  auto convert = [&](int buf, const u32x4_t* pf) {
 #pragma unroll
     for (int it = 0; it < kPf; ++it) {
       const int item = tid + kGramThreads * it;
-      if (item >= ppad * (kGramCh / 4)) break;
       const int r = item / (kGramCh / 4), q4 = 4 * (item % (kGramCh / 4));
       uint32_t h[3][2];
-      split3_bf16((f32x2_t){pf[it].x, pf[it].y}, h[0][0], h[1][0], h[2][0]);
-      split3_bf16((f32x2_t){pf[it].z, pf[it].w}, h[0][1], h[1][1], h[2][1]);
+      split3_bf16((f32x2_t){__uint_as_float(pf[it][0]), __uint_as_float(pf[it][1])}, h[0][0], h[1][0], h[2][0]);
+      split3_bf16((f32x2_t){__uint_as_float(pf[it][2]), __uint_as_float(pf[it][3])}, h[0][1], h[1][1], h[2][1]);
 #pragma unroll
       for (int q = 0; q < 3; ++q)
         *reinterpret_cast<uint2*>(&pl[3 * buf + q][r * kGramPS + q4]) = make_uint2(h[q][0], h[q][1]);
     }
   };
 
-  const int nst = C / kGramCh;
   // products of stage st on buffer st & 1; then stage st + 1 (loaded two
   // stages ago) converted into the other buffer, and stage st + 3 loaded
-  // into the register set that conversion freed
-  auto stage_step = [&](int st, int buf, const float4* pf_next, float4* pf_free) {
+  // into the register set that conversion freed.  With nst odd the last
+  // call runs on stage nst, all zeros, and adds nothing.
+  auto stage_step = [&](int st, int buf, const u32x4_t* pf_next, u32x4_t* pf_free) {
     // Stage st's planes are complete, and stage st-1's reads of the other
     // buffer are done, once every wave has passed this barrier.
     __syncthreads();
@@ -794,10 +803,8 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], bb[1], acc, 0, 0, 0);
       }
     }
-    if (st + 1 < nst) {
-      convert(buf ^ 1, pf_next);
-      if (st + 3 < nst) load_stage(st + 3, pf_free);
-    }
+    convert(buf ^ 1, pf_next);
+    load_stage(st + 3, pf_free);
     if ((((st + 1) * kGramCh) % 256) == 0 || st + 1 == nst) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -806,13 +813,16 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_mfma(ScoreLaunch sl, char
       }
     }
   };
+  // the prologue leaves stage 1, then stage 2, in flight: the order the loop
+  // body issues its loads in
   load_stage(0, pfa);
-  if (nst > 1) load_stage(1, pfb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(1, pfb);
   convert(0, pfa);
-  if (nst > 2) load_stage(2, pfa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(2, pfa);
   for (int st = 0; st < nst; st += 2) {
-    stage_step(st, 0, pfb, pfb);  // pfb: stage st + 1, then st + 3
-    if (st + 1 >= nst) break;
+    stage_step(st, 0, pfb, pfb);      // pfb: stage st + 1, then st + 3
     stage_step(st + 1, 1, pfa, pfa);  // pfa: stage st + 2, then st + 4
   }
   __syncthreads();  // planes no longer read: the buffer now holds G [P2][P2 + 1]
