@@ -1119,7 +1119,7 @@ def measure_workload(w, args, graph=True):
     ms_step_two = timed(w.step)  # eager, assembly on the side stream
     ms_metric, metric_launch = ms_metric_eager, "eager, one stream"
     ms_step, launch = ms_step_two, "eager, two streams"
-    ms_serial_graph = None
+    ms_serial_graph = ms_metric_graph = ms_step_graph = None
     if graph:
         # the steps captured once in a HIP graph and replayed: the kernels and
         # their arguments are those of the eager steps, without the per-call
@@ -1142,12 +1142,20 @@ def measure_workload(w, args, graph=True):
             return ms
 
         try:
-            ms_metric, metric_launch = graph_ms(w.metric_step), "hip-graph, one stream"
+            ms_metric_graph = graph_ms(w.metric_step)
             ms_serial_graph = graph_ms(w.step_serial)
-            ms_step, launch = graph_ms(w.step), "hip-graph, two streams"
+            ms_step_graph = graph_ms(w.step)
         except RuntimeError as e:  # capture unsupported here: keep the eager figures
             print(f"[bench] graph capture failed ({e}); reporting the eager steps", file=sys.stderr, flush=True)
             torch.cuda.synchronize()
+        else:
+            # the same kernels either way: the faster launch mode is reported
+            # (on some parts the replayed graph spaces its 39 short kernels
+            # further apart than eager launches on one stream do)
+            if ms_metric_graph < ms_metric:
+                ms_metric, metric_launch = ms_metric_graph, "hip-graph, one stream"
+            if ms_step_graph < ms_step:
+                ms_step, launch = ms_step_graph, "hip-graph, two streams"
 
     def per_step(*ns):
         return sum(kt[n][0] for n in ns) / args.steps
@@ -1217,10 +1225,10 @@ def measure_workload(w, args, graph=True):
             "what": "the metric path plus every layer's selected-query attention (Q RoPE + causal GQA)",
             "ms_per_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3), "launch": launch,
             "ms_per_step_eager_serial": ms_step_eager, "ms_per_step_eager_two_streams": ms_step_two,
-            "ms_per_step_serial_graph": ms_serial_graph,
+            "ms_per_step_serial_graph": ms_serial_graph, "ms_per_step_two_streams_graph": ms_step_graph,
         },
         "stages": {
-            "metric_ms_eager": ms_metric_eager,
+            "metric_ms_eager": ms_metric_eager, "metric_ms_graph": ms_metric_graph,
             "score_ms": score_ms, "score_GBs": score_gbs, "score_frac_hbm": score_gbs / PEAK_HBM_GBS,
             "band_mfma_TFLOPs_issued": band_tflops, "band_frac_bf16_peak": band_tflops / PEAK_BF16_TFLOPS,
             "score_kernels_ms": {n: per_step(n) for n in score_names},
