@@ -26,6 +26,13 @@ The side stream joins back into the current stream before the function
 returns (the current stream waited for the last assembly), so the function
 can be captured into a HIP graph on the current stream.  Both streams keep
 the default priority.
+
+``run_assemblies`` is the same hand-off without the attention: the path that
+only assembles every layer (score, top-r, assembly) issues even layers on the
+current stream into buffer 0 and odd layers on the side stream into buffer 1.
+Neighbouring layers' assemblies write different buffers and read only the
+selection and their own rows, so each launch's ramp-down overlaps the next
+one's ramp-up; a layer two apart writes the same buffer on the same stream.
 """
 from __future__ import annotations
 
@@ -54,3 +61,20 @@ def run_layers(n_layers: int, assemble: Callable[[int, int], None], attend: Call
         done = torch.cuda.Event()
         done.record(main)
         last_read[b] = done
+
+
+def run_assemblies(n_layers: int, assemble: Callable[[int, int], None], side) -> None:
+    """Issue ``assemble(l, b)`` for l < n_layers with b = l % 2: buffer 0 on
+    the current stream, buffer 1 on ``side``, after everything already issued
+    on the current stream; the current stream then waits for the side one."""
+    import torch
+
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    for l in range(n_layers):
+        if l % 2 == 0:
+            assemble(l, 0)
+        else:
+            with torch.cuda.stream(side):
+                assemble(l, 1)
+    main.wait_stream(side)

@@ -6,7 +6,10 @@
   results to the eager step every time.
 * The two-stream step (each layer's assembly on a side stream into one of
   two buffers, overlapping the previous layer's attention) gives the serial
-  step's outputs bit for bit, eager and replayed."""
+  step's outputs bit for bit, eager and replayed.
+* The assembly-only path (neighbouring layers' assemblies on two streams
+  into two buffers) gives every layer's serial assembly bit for bit, eager
+  and replayed."""
 import math
 
 import numpy as np
@@ -139,3 +142,34 @@ def test_two_stream_step_matches_serial(syn):
     got = _replays_match(step, out, (*asm[0], *asm[1], *out))
     for l in range(L):
         assert torch.equal(got[l], want[l]), f"layer {l}: two-stream output differs from the serial step"
+
+
+@pytest.mark.parametrize("L", [1, 4, 5])
+def test_two_stream_assemblies_match_serial(syn, L):
+    """``run_assemblies`` (even layers on the current stream into buffer 0,
+    odd ones on a side stream into buffer 1): after the step each buffer
+    holds the last layer assembled into it, equal bit for bit to that
+    layer's serial assembly, eager and replayed from a HIP graph."""
+    from non_prefix_kv_token_amd.schedule import run_assemblies
+
+    ct = need_gpu()
+    score, sel, comp, asm, out, select, assemble, attend = _request(ct, syn, L)
+    select()
+    want = {}
+    for l in range(L):
+        assemble(l, 0)
+        torch.cuda.synchronize()
+        want[l % 2] = (asm[0][0].clone(), asm[0][1].clone())  # the last layer of each parity
+    for t in (*asm[0], *asm[1]):
+        t.fill_(-1)
+    side = torch.cuda.Stream()
+
+    def step():
+        select()
+        run_assemblies(L, assemble, side)
+
+    bufs = [t for b in range(min(L, 2)) for t in asm[b]]
+    got = _replays_match(step, bufs, bufs)
+    for b in range(min(L, 2)):
+        assert torch.equal(got[2 * b], want[b][0]) and torch.equal(got[2 * b + 1], want[b][1]), \
+            f"buffer {b}: two-stream assembly differs from the serial one"

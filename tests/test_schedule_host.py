@@ -1,4 +1,5 @@
-"""Host logic of the two-stream layer schedule (``schedule.run_layers``),
+"""Host logic of the two-stream layer schedules (``schedule.run_layers``,
+``schedule.run_assemblies``),
 checked on the CPU with recording stand-ins for torch's streams and events:
 for every layer the assembly and the attention land on the right streams and
 buffers, and the event waits give exactly the orderings the schedule needs
@@ -123,3 +124,39 @@ def test_run_layers_streams_buffers_and_order(monkeypatch, n_layers):
     # and no more ordering than needed: assembly l + 1 is not made to wait for attention l
     if n_layers >= 2:
         assert not _happens_before(streams, where(("attend", 0, 0)), where(("assemble", 1, 1)))
+
+
+@pytest.mark.parametrize("n_layers", [1, 2, 5])
+def test_run_assemblies_streams_buffers_and_order(monkeypatch, n_layers):
+    log = _Log()
+    main, side = _Stream(log, "main"), _Stream(log, "side")
+    monkeypatch.setitem(sys.modules, "torch", _fake_torch(log, main))
+    main.queue.append(("op", "select"))
+    calls = []
+
+    def assemble(l, b):
+        calls.append((l, b, log.current.name))
+        log.current.queue.append(("op", ("assemble", l, b)))
+
+    schedule.run_assemblies(n_layers, assemble, side)
+    streams = {"main": main, "side": side}
+
+    def where(op):
+        for name, s in streams.items():
+            for i, (kind, obj) in enumerate(s.queue):
+                if kind == "op" and obj == op:
+                    return name, i
+        raise AssertionError(f"{op} not issued")
+
+    # even layers on the current stream into buffer 0, odd ones on the side stream into buffer 1
+    assert calls == [(l, l % 2, "main" if l % 2 == 0 else "side") for l in range(n_layers)]
+    sel = where("select")
+    main.queue.append(("op", "after"))
+    for l in range(n_layers):
+        a = where(("assemble", l, l % 2))
+        assert _happens_before(streams, sel, a), f"layer {l}: assembly may start before the selection"
+        if l >= 2:  # the same buffer two layers back is written first
+            assert _happens_before(streams, where(("assemble", l - 2, l % 2)), a)
+        assert _happens_before(streams, a, where("after")), f"layer {l}: not joined into the current stream"
+    if n_layers >= 2:  # neighbours may overlap
+        assert not _happens_before(streams, where(("assemble", 0, 0)), where(("assemble", 1, 1)))
