@@ -55,6 +55,7 @@ def _rel_close(got, want, rtol=1e-4, floor=0.0):
     ([130, 77], 1, 1, 64, (1, 1)),                  # alpha = 1: every bin (odd N, Nyquist)
     ([600, 4096], 1, 1, 64, (1, 32)),               # 1/32 cutoff, shortest/longest lengths
     ([2, 8192, 3], 1, 1, 64, (1, 16)),              # the smallest and largest chunk lengths
+    ([64, 33], 1, 64, 128, (1, 16)),                # H*D = 8192, the most channels a call takes
 ])
 def test_score_parity_bf16(orc, syn, ns, L, H, D, alpha):
     s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
