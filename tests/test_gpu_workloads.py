@@ -228,17 +228,20 @@ def test_workload_qwen3_4b_ragged(orc, syn):
     T_c = sum(ns)
     T = T_c + n_sfx
     sel_list = [sl[sum(ks[:b]):sum(ks[:b]) + ks[b]] for b in range(nb)]
-    layer = 2
-    k_out, v_out, rec, sfx, _ = _request(ct, syn, seed, ns, offs, layer, H, D, "bf16", sel_list, comp,
-                                         sel, theta, n_sfx, T, [(k[layer], v[layer]) for k, v in dev])
-    k_ref, v_ref = _oracle_layer(orc, [(k[layer], v[layer]) for k, v in host], rec, sfx, sel_list, offs,
-                                 T, H, D, "bf16", theta, n_sfx)
-    kg, vg = to_host(k_out), to_host(v_out)
-    np.testing.assert_array_equal(vg, v_ref)
-    ulp = ulp_distance_bf16(kg, k_ref)
-    assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
     qpos = np.sort(np.concatenate([offs[b] + sel_list[b] for b in range(nb)] +
                                   [np.arange(T_c, T)])).astype(np.int32)
-    q = _queries(syn, seed, ns, offs, layer, Hq, D, "bf16", qpos, T_c, n_sfx)
-    _check_attention(ct, orc, q, qpos, k_out, v_out, k_ref, v_ref, theta, _rows_sample(len(qpos), rng, 12),
-                     "bf16")
+    # a middle layer and the last one: the whole assembled layer, and sampled
+    # attention rows (the first, the last and seeded ones) over all heads
+    for layer, n_rows in ((2, 192), (L - 1, 64)):
+        k_out, v_out, rec, sfx, _ = _request(ct, syn, seed, ns, offs, layer, H, D, "bf16", sel_list, comp,
+                                             sel, theta, n_sfx, T, [(k[layer], v[layer]) for k, v in dev])
+        k_ref, v_ref = _oracle_layer(orc, [(k[layer], v[layer]) for k, v in host], rec, sfx, sel_list,
+                                     offs, T, H, D, "bf16", theta, n_sfx)
+        kg, vg = to_host(k_out), to_host(v_out)
+        np.testing.assert_array_equal(vg, v_ref)
+        ulp = ulp_distance_bf16(kg, k_ref)
+        assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+        q = _queries(syn, seed, ns, offs, layer, Hq, D, "bf16", qpos, T_c, n_sfx)
+        _check_attention(ct, orc, q, qpos, k_out, v_out, k_ref, v_ref, theta,
+                         _rows_sample(len(qpos), rng, n_rows), "bf16")
+        del k_out, v_out
