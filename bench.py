@@ -978,8 +978,8 @@ def main():
                     help="time the scoring variants (low-pass, L2-norm, high-frequency) on the workload instead")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the hot path is single-GPU; see the design notes for how it would shard).",
+        print(f"bench.py measures the hot path on one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels run on one GPU's share; the design notes say how the path would shard).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -124,7 +124,7 @@ def main():
     args = ap.parse_args()
 
     if args.cmd == "counters":
-        text = f"# {args.title}\n\nCommand (from the repository root on the GPU box):\n\n    {args.command}\n\n"
+        text = f"# {args.title}\n\nCommand (from the repository root, on an MI355X):\n\n    {args.command}\n\n"
         if args.note:
             text += args.note + "\n\n"
         text += counters_table(args.dir) + "\n"
@@ -133,7 +133,7 @@ def main():
         return
 
     if args.cmd == "stats":
-        text = f"# {args.title}\n\nCommand (from the repository root on the GPU box):\n\n    {args.command}\n\n"
+        text = f"# {args.title}\n\nCommand (from the repository root, on an MI355X):\n\n    {args.command}\n\n"
         if args.note:
             text += args.note + "\n\n"
         text += kernel_stats_table(args.csv) + "\n"
@@ -160,7 +160,7 @@ def main():
             f"| total | | | {total:.4g} |\n\n")
     if args.algorithmic_bytes:
         text += f"Algorithmic bytes per launch: {args.algorithmic_bytes:.4g} (ratio {total / args.algorithmic_bytes:.2f}).\n\n"
-    text += ("Commands (from the repository root on the GPU box):\n\n"
+    text += ("Commands (from the repository root, on an MI355X):\n\n"
              f"    {args.command_fetch}\n    {args.command_write}\n\n"
              f"Kernel source: `{args.source}`.\n\n"
              f"traffic-record: kernel={args.name} workload={args.workload} source_sha256={sha} "
