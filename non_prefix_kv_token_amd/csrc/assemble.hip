@@ -10,7 +10,7 @@
 // 32-byte fp32 vectors), so all loads and stores are full vectors and a row's
 // H*D elements move in one or two passes of the wave.  The rotation angle and
 // its sine and cosine are formed in fp64, the rotated value is rounded once to
-// the storage type.
+// the storage type (for bf16 through fp32 where that is the same rounding).
 #include "ct_device.h"
 #include "ct_internal.h"
 
@@ -118,28 +118,67 @@ __global__ __launch_bounds__(256) void k_assemble(AsmLaunch al, void* k_out, voi
     va.load(vs, so + ea);
     vb.load(vs, so + eb);
     Vec8<DT> ya = xa, yb = xb;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      // pair t of this lane: frequency index 8c + t
+    // pair t of this lane (frequency index 8c + t) rotated in fp64; y0 and y1
+    // go to output elements s0(t) and s1(t) of the 16 (0..7 in ya, 8..15 in yb)
+    auto rot = [&](const Vec8<DT>& va_, const Vec8<DT>& vb_, int t, double& y0, double& y1) {
       const double sn = s_sc[wv][8 * c + t][0], cs = s_sc[wv][8 * c + t][1];
       double x0, x1;
       if (half) {
-        x0 = xa.get(t);
-        x1 = xb.get(t);
+        x0 = va_.get(t);
+        x1 = vb_.get(t);
       } else {  // interleaved: pairs (2t', 2t'+1) of the 16 elements
-        x0 = t < 4 ? xa.get(2 * t) : xb.get(2 * t - 8);
-        x1 = t < 4 ? xa.get(2 * t + 1) : xb.get(2 * t - 7);
+        x0 = t < 4 ? va_.get(2 * t) : vb_.get(2 * t - 8);
+        x1 = t < 4 ? va_.get(2 * t + 1) : vb_.get(2 * t - 7);
       }
-      const double y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-      if (half) {
-        ya.set(t, y0);
-        yb.set(t, y1);
-      } else if (t < 4) {
-        ya.set(2 * t, y0);
-        ya.set(2 * t + 1, y1);
-      } else {
-        yb.set(2 * t - 8, y0);
-        yb.set(2 * t - 7, y1);
+      y0 = x0 * cs - x1 * sn;
+      y1 = x0 * sn + x1 * cs;
+    };
+    auto s0 = [&](int t) { return half ? t : 2 * t; };
+    auto s1 = [&](int t) { return half ? 8 + t : 2 * t + 1; };
+    if constexpr (DT == CT_BF16) {
+      // Round to fp32 (RNE), then to bf16 (RNE).  The two roundings give the
+      // one rounding of the fp64 value unless the fp32 result lies exactly on
+      // a bf16 midpoint (low 16 bits 0x8000): fp32 holds every bf16 midpoint,
+      // so otherwise the fp32 result and the fp64 value are on the same side
+      // of every midpoint.  A wave in which some lane meets a midpoint forms
+      // its 16 values again and rounds them once, on the fp64 bits.
+      uint32_t fb[16];
+      bool mid = false;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        double y0, y1;
+        rot(xa, xb, t, y0, y1);
+        const uint32_t f0 = __float_as_uint((float)y0), f1 = __float_as_uint((float)y1);
+        mid |= ((f0 & 0xffffu) == 0x8000u) | ((f1 & 0xffffu) == 0x8000u);
+        fb[s0(t)] = f0;
+        fb[s1(t)] = f1;
+      }
+      if (__builtin_expect(__any(mid), 0)) {
+        // the inputs pass through an empty asm, so the rotation is formed again
+        // here instead of its fp64 results being held from above
+        Vec8<DT> xa2 = xa, xb2 = xb;
+        asm volatile("" : "+v"(xa2.w), "+v"(xb2.w));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          double y0, y1;
+          rot(xa2, xb2, t, y0, y1);
+          fb[s0(t)] = (uint32_t)bf16_from_f64(y0) << 16;  // a bf16 value: the rounding below keeps it
+          fb[s1(t)] = (uint32_t)bf16_from_f64(y1) << 16;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ya.w[i] = bf16_bits_rne(__uint_as_float(fb[2 * i])) | (bf16_bits_rne(__uint_as_float(fb[2 * i + 1])) << 16);
+        yb.w[i] = bf16_bits_rne(__uint_as_float(fb[8 + 2 * i])) | (bf16_bits_rne(__uint_as_float(fb[9 + 2 * i])) << 16);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        double y0, y1;
+        rot(xa, xb, t, y0, y1);
+        const int e0 = s0(t), e1 = s1(t);
+        if (e0 < 8) ya.set(e0, y0); else yb.set(e0 - 8, y0);
+        if (e1 < 8) ya.set(e1, y1); else yb.set(e1 - 8, y1);
       }
     }
     ya.store(k_out, dof + ea);

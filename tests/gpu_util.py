@@ -51,6 +51,20 @@ def ulp_distance_bf16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
+def assert_rotated_keys(got: np.ndarray, want: np.ndarray, ulp_fn=None) -> None:
+    """Assembled (rotated) keys against the oracle's.  Both sides rotate in
+    fp64 and round once; they differ only in the sine and cosine, a few fp64
+    ulps apart, so an element may round the other way only when its exact
+    value lies that close to a rounding boundary (about one in 10^9).  At
+    most one element in a million may differ, by one ulp.  A rounding slip of
+    the kind double rounding makes (one value in 2^16) fails this at the
+    full workload sizes."""
+    ulp = (ulp_fn or ulp_distance_bf16)(got, want)
+    assert ulp.max() <= 1, f"max {ulp.max()} ulp"
+    n_off = int((ulp != 0).sum())
+    assert n_off <= max(1, ulp.size // 1_000_000), f"{n_off} of {ulp.size} keys differ by one ulp"
+
+
 def ulp_distance_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     def key(x):
         x = x.view(np.int32).astype(np.int64)
