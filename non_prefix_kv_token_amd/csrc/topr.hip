@@ -4,16 +4,21 @@
 // others for reuse; the whole order is written out once, so a different r
 // later only changes where it is cut.
 //
-// One block (1024 threads) per chunk.  Each score becomes a 64-bit key
+// Each score becomes a 64-bit key
 //   high word: bitwise complement of an order-preserving image of the fp32
 //              score (so ascending key = descending score; -0 == +0; NaN last)
 //   low word:  local index (so equal scores rank by lower index)
-// sorted ascending by a bitonic network (n <= 8192).  Stages whose stride is
+// and the ranking is the ascending order of the keys.  When the caller stores
+// the ranking, every element's rank is counted in parallel (below), then one
+// block per chunk forms the lists.  Otherwise one block (1024 threads) per
+// chunk sorts the keys ascending by a bitonic network (n <= 8192).  Stages whose stride is
 // at least 128 pair elements across waves and run in LDS with a block barrier;
 // the others stay inside one wave's 128-element segments and run in registers
 // (lane-pair exchanges), two elements per lane.  The ascending recomputation
 // set and complement come from a block-wide prefix count over the membership
 // flags in index order (wave scans, then the wave totals).
+#include <algorithm>
+
 #include "ct_internal.h"
 
 namespace ct {
@@ -28,6 +33,34 @@ __device__ inline uint32_t score_order_key(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) ord = 0u;     // NaN: lowest score
   else ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~ord;
+}
+
+// Ascending membership lists from the per-index flags (in LDS): each thread
+// owns a contiguous index range; a block prefix count places its entries.
+__device__ void compact(const TopRChunk& c, const unsigned char* flag, int* cnt, int32_t* sel,
+                        int32_t* comp) {
+  const int n = c.n, tid = threadIdx.x;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = tid * per, i1 = min(n, i0 + per);
+  int mine = 0;
+  for (int i = i0; i < i1; ++i) mine += flag[i];
+  int incl = mine;  // inclusive scan over the wave's lanes
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += t;
+  }
+  if ((tid & 63) == 63) cnt[tid >> 6] = incl;  // wave totals
+  __syncthreads();
+  int before = incl - mine;  // selected indices below i0
+  for (int w = 0; w < (tid >> 6); ++w) before += cnt[w];
+  for (int i = i0; i < i1; ++i) {
+    if (flag[i]) {
+      sel[c.sel_off + before] = i;
+      ++before;
+    } else if (comp) {
+      comp[c.comp_off + (i - before)] = i;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* score,
@@ -108,41 +141,80 @@ __global__ __launch_bounds__(kThreads) void k_topr(TopRLaunch tl, const float* s
     flag[idx] = r < k ? 1 : 0;
   }
   __syncthreads();
+  compact(c, flag, cnt, sel, comp);
+}
 
-  // ascending membership lists: each thread owns a contiguous index range
-  const int per = (n + kThreads - 1) / kThreads;
-  const int i0 = tid * per, i1 = min(n, i0 + per);
-  int mine = 0;
-  for (int i = i0; i < i1; ++i) mine += flag[i];
-  int incl = mine;  // inclusive scan over the wave's lanes
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if ((tid & 63) >= o) incl += t;
-  }
-  if ((tid & 63) == 63) cnt[tid >> 6] = incl;  // wave totals
+// ---- when the ranking is stored: ranks by counting ----------------------------
+// The keys are distinct (the index is part of them), so an element's rank is
+// the number of keys of its chunk below its own.  kRankSlices threads share an
+// element, each counting over every kRankSlices-th key (consecutive lanes read
+// consecutive keys: no bank conflicts), and the chunk's keys sit in LDS once
+// per block.  Every chunk is spread over n / kRankElems blocks, so the whole
+// GPU takes part instead of one block per chunk.
+constexpr int kRankThreads = 256;
+constexpr int kRankSlices = 8;
+constexpr int kRankElems = kRankThreads / kRankSlices;
+
+__global__ __launch_bounds__(kRankThreads) void k_topr_rank(TopRLaunch tl, const float* score,
+                                                            int32_t* ranking) {
+  extern __shared__ unsigned long long skey[];  // [n]
+  const TopRChunk& c = tl.c[blockIdx.y];
+  const int n = c.n, tid = threadIdx.x;
+  const int e = blockIdx.x * kRankElems + tid / kRankSlices, sl = tid % kRankSlices;
+  if (blockIdx.x * kRankElems >= n) return;  // uniform over the block
+  for (int i = tid; i < n; i += kRankThreads)
+    skey[i] = ((unsigned long long)score_order_key(score[c.tok_off + i]) << 32) | (uint32_t)i;
   __syncthreads();
-  int before = incl - mine;  // selected indices below i0
-  for (int w = 0; w < (tid >> 6); ++w) before += cnt[w];
-  for (int i = i0; i < i1; ++i) {
-    if (flag[i]) {
-      sel[c.sel_off + before] = i;
-      ++before;
-    } else if (comp) {
-      comp[c.comp_off + (i - before)] = i;
-    }
-  }
+  const unsigned long long mine = e < n ? skey[e] : 0ull;
+  int below = 0;
+#pragma unroll 8
+  for (int j = sl; j < n; j += kRankSlices) below += skey[j] < mine ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < kRankSlices; o <<= 1) below += __shfl_xor(below, o);
+  if (sl == 0 && e < n) ranking[c.tok_off + below] = e;
+}
+
+// The ascending set and complement from the stored ranking: its first k
+// entries are the selected indices.
+__global__ __launch_bounds__(kThreads) void k_topr_compact(TopRLaunch tl, const int32_t* ranking,
+                                                           int32_t* sel, int32_t* comp) {
+  __shared__ unsigned char flag[kMaxN];
+  __shared__ int cnt[kThreads / 64];
+  const TopRChunk& c = tl.c[blockIdx.x];
+  const int n = c.n, k = c.k, tid = threadIdx.x;
+  for (int i = tid; i < n; i += kThreads) flag[i] = 0;
+  __syncthreads();
+  for (int r = tid; r < k; r += kThreads) flag[ranking[c.tok_off + r]] = 1;
+  __syncthreads();
+  compact(c, flag, cnt, sel, comp);
 }
 
 }  // namespace
 
 ct_status topr_run(const TopRLaunch& tl, const float* score, int32_t* ranking, int32_t* sel,
                    int32_t* comp, hipStream_t stream) {
-  {
+  if (!ranking) {  // one sort per chunk, the ranking kept in LDS only
     TimedLaunch tl_("topr", stream);
     hipLaunchKernelGGL(k_topr, dim3(tl.n_chunks), dim3(kThreads), 0, stream, tl, score, ranking,
-                     sel, comp);
+                       sel, comp);
+    return check_launch("top-r");
   }
-  return check_launch("top-r");
+  int max_n = 0;
+  for (int i = 0; i < tl.n_chunks; ++i) max_n = std::max(max_n, (int)tl.c[i].n);
+  if (max_n <= 0) return CT_OK;
+  {
+    TimedLaunch tl_("topr", stream);
+    hipLaunchKernelGGL(k_topr_rank, dim3((max_n + kRankElems - 1) / kRankElems, tl.n_chunks),
+                       dim3(kRankThreads), (size_t)max_n * sizeof(unsigned long long), stream, tl, score,
+                       ranking);
+  }
+  if (ct_status s = check_launch("top-r ranks")) return s;
+  {
+    TimedLaunch tl_("topr", stream);
+    hipLaunchKernelGGL(k_topr_compact, dim3(tl.n_chunks), dim3(kThreads), 0, stream, tl, ranking, sel,
+                       comp);
+  }
+  return check_launch("top-r lists");
 }
 
 }  // namespace ct

@@ -127,20 +127,25 @@ def test_score_deterministic(syn):
 # ---- selection ---------------------------------------------------------------
 
 def _topr_exact(orc, scores_list, r):
+    """Both top-r paths against the oracle: with the ranking stored (ranks by
+    counting, then the lists) and without it (one sort per chunk)."""
     ct = need_gpu()
     ns = [len(s) for s in scores_list]
     flat = np.concatenate(scores_list).astype(np.float32)
-    ks, ranking, sel, comp = ct.cachetune_select_topr(to_dev(flat), ns, r=r)
-    torch.cuda.synchronize()
-    ranking, sel, comp = to_host(ranking), to_host(sel), to_host(comp)
-    o = so = co = 0
-    for n, k, s in zip(ns, ks, scores_list):
-        assert k == orc.ksel(n, *r)
-        want_r, want_s, want_c = orc.topr(np.asarray(s, np.float32).astype(np.float64), k)
-        np.testing.assert_array_equal(ranking[o:o + n], want_r)
-        np.testing.assert_array_equal(sel[so:so + k], want_s)
-        np.testing.assert_array_equal(comp[co:co + n - k], want_c)
-        o, so, co = o + n, so + k, co + n - k
+    for want_ranking in (True, False):
+        ks, ranking, sel, comp = ct.cachetune_select_topr(to_dev(flat), ns, r=r, want_ranking=want_ranking)
+        torch.cuda.synchronize()
+        sel, comp = to_host(sel), to_host(comp)
+        ranking = to_host(ranking) if want_ranking else None
+        o = so = co = 0
+        for n, k, s in zip(ns, ks, scores_list):
+            assert k == orc.ksel(n, *r)
+            want_r, want_s, want_c = orc.topr(np.asarray(s, np.float32).astype(np.float64), k)
+            if want_ranking:
+                np.testing.assert_array_equal(ranking[o:o + n], want_r)
+            np.testing.assert_array_equal(sel[so:so + k], want_s)
+            np.testing.assert_array_equal(comp[co:co + n - k], want_c)
+            o, so, co = o + n, so + k, co + n - k
 
 
 def test_topr_exact_on_oracle_scores(orc, syn):
