@@ -716,7 +716,7 @@ def score_variants(w, args):
     ct = w.ct
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = {}
-    names = ("twiddle", "band", "band_redo", "gram", "energy_l2", "highpass", "layer_norm", "layer_mean")
+    names = ("twiddle", "band", "gram", "energy_l2", "highpass", "layer_norm", "layer_mean")
     for name, variant in (("lowpass", ct.CT_SCORE_LOWPASS), ("l2", ct.CT_SCORE_L2),
                           ("highpass", ct.CT_SCORE_HIGHPASS)):
         need = ct.cachetune_score_chunk_ws(w.ns, w.L, w.H, w.D, w.alpha, variant=variant)
@@ -756,7 +756,7 @@ def r_sweep(args):
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = []
     attn_names = ("attention_setup", "attention", "attention_merge")
-    names = ["twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
+    names = ["twiddle", "band", "gram", "layer_norm", "layer_mean", "topr", "assemble", *attn_names]
     for r in [(5, 100), (10, 100), (15, 100), (20, 100), (30, 100)]:
         w = Workload(args.workload, r=r)
         ct = w.ct
@@ -776,7 +776,7 @@ def r_sweep(args):
         ms = a.elapsed_time(z) / args.steps
         kt = {n: ct.cachetune_timing_read(n)[0] / args.steps for n in names}
         tokens = float(sum(w.ns))
-        score_ms = sum(kt[n] for n in ("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr"))
+        score_ms = sum(kt[n] for n in ("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"))
         asm_ms = kt["assemble"]
         attn_ms = sum(kt[n] for n in attn_names)
         attn_tf = w.attn_flops_per_layer() * w.L / (kt["attention"] * 1e-3) / 1e12
@@ -917,7 +917,7 @@ def recompute_layers(w, args):
         m.step()
     torch.cuda.synchronize()
     names = ["linear", "rmsnorm", "silu_mul", "assemble", "attention_setup", "attention", "attention_merge",
-             "twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr"]
+             "twiddle", "band", "gram", "layer_norm", "layer_mean", "topr"]
     for n in names:
         ct.cachetune_timing_read(n)
     a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1096,7 +1096,7 @@ def measure_workload(w, args, graph=True):
     print(f"[bench] {w.name}: warmup done", file=sys.stderr, flush=True)
 
     attn_names = ("attention_setup", "attention", "attention_merge")
-    score_names = ("twiddle", "band", "band_redo", "gram", "layer_norm", "layer_mean", "topr")
+    score_names = ("twiddle", "band", "gram", "layer_norm", "layer_mean", "topr")
     names = [*score_names, "assemble", *attn_names]
     for n in names:  # drop records of earlier launches
         ct.cachetune_timing_read(n)

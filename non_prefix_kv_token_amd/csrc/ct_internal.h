@@ -61,7 +61,6 @@ struct ScoreChunkDesc {
   uint16_t* tw;      // bf16 twiddle planes [3][ppad][ntok_pad] (device; set by score_bind)
   uint16_t* tw16;    // fp16 twiddle planes [2][ppad][ntok_pad]
   double2* trig;     // fp64 (cos, sin) of 2*pi*m/nf, m < nf
-  int64_t flag_off;  // int32 [L][2][kFlagBlocks]: 1 when a channel block's X does not fit fp16
   int64_t y_off;     // fp32 band coefficients [L][2][ppad][C]
   int64_t e_off;     // fp64 low-pass energies [L][2][n]
   int64_t tok_off;   // first token of this chunk in the concatenated score vector
@@ -82,8 +81,6 @@ struct ScoreLaunch {
   int32_t variant;     // ct_score_variant
 };
 
-// fp16-range flags per (problem, 512-channel block of the band projection)
-constexpr int kFlagBlocks = 16;
 
 // Twiddle and trigonometric tables of one (transform length, retained bins,
 // padded token count), device memory.

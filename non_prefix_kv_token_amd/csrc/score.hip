@@ -11,7 +11,7 @@
 //     channels at once.  bf16 data enter the fp16 matrix cores, where they
 //     are exact below 65536, against the twiddles as an fp16 hi + lo pair
 //     (t = t1 + t2 to 2^-24): two MFMAs give fp32-accurate coefficients.  A
-//     problem holding a larger or non-finite value is redone with the
+//     tile that meets a larger or non-finite value is redone at once with the
 //     twiddles as three bf16 planes (t1 + t2 + t3 to ~2^-25) against the bf16
 //     data (three MFMAs); fp32 data are split the same way (six MFMAs).
 //  2. the channel Gram G = Y Y^T (fp64);
@@ -400,38 +400,39 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // so no block holds padding tiles and the tile loop carries no per-tile test
 // (the branches would break up the matrix-core issue).
 // F16: X converted to fp16 in registers against the fp16 twiddle pair (two
-// MFMAs per tile and k-step); a block that meets |x| >= 65536 or a non-finite
-// value raises the problem's flag.  Otherwise X stays bf16 against the three
-// bf16 planes (three MFMAs); with redo set, only flagged problems run.
+// MFMAs per tile and k-step); a tile that meets |x| >= 65536 or a non-finite
+// value returns true without writing Y.  Otherwise X stays bf16 against the
+// three bf16 planes (three MFMAs).
+template <int NTL, bool F16>
+struct BandLds {
+  static constexpr int kPlanes = F16 ? 2 : 3;  // twiddle planes
+  uint16_t buf[2][kPlanes * 32 * NTL * kTwStride];
+};
+
+// One 512-channel x (32 * NTL)-row tile (channel block cblk, row block rblk)
+// of problem prob, by the 512 threads of the calling block, in `sh`.  Returns
+// together on every thread (every condition below is uniform over the block):
+// true when the fp16 pass met a value outside fp16's range.
 template <int NTL, bool FULL, bool F16>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
+__device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
+                                          BandLds<NTL, F16>& sh) {
   constexpr int NPL = F16 ? 2 : 3;  // twiddle planes
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][NPL * 32 * NTL * kTwStride];
+  auto& lds = sh.buf;
 
   const int L = sl.L, C = sl.C;
-  const int prob = blockIdx.z;
   const int b = prob / (2 * L);
   const int layer = (prob / 2) % L;
   const int kv = prob % 2;
   const ScoreChunkDesc& d = sl.c[b];
-  // fp16-range flags of this problem, one per channel block (written by the
-  // first row block of each channel block in the fp16 pass, read by the redo)
-  int* flags = reinterpret_cast<int*>(ws + d.flag_off) + (layer * 2 + kv) * kFlagBlocks;
-  if (!F16 && redo) {
-    int any = 0;
-    for (int i = 0; i < (int)gridDim.x; ++i) any |= flags[i];
-    if (any == 0) return;
-  }
-  const int pbase = blockIdx.y * 32 * NTL;
-  if (pbase >= d.ppad) return;
+  const int pbase = rblk * 32 * NTL;
+  if (pbase >= d.ppad) return false;
   const int nrows = min(32 * NTL, d.ppad - pbase);  // rows this chunk has in the block
   const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
   const int nsteps = (N + 31) / 32;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, col = lane & 31;
-  const int cbase = blockIdx.x * 512 + wave * 64;
+  const int cbase = cblk * 512 + wave * 64;
   const bool active = cbase < C;
   const int c0 = cbase + 2 * col;
 
@@ -560,13 +561,14 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
     load_x(step + 3, xb);
   }
 
+  int any_bad = 0;
   if constexpr (F16) {
     // The range test costs nothing inside the loop: |x| >= 65536 becomes
-    // +-inf in fp16 and a NaN stays NaN, and the DC row (twiddle 1 at every
-    // token, in the first row block of every channel group) then turns
-    // non-finite; finite fp16 data cannot overflow the fp32 sums at these
-    // lengths (|Y| < 8192 * 65504).  So a non-finite sum marks exactly the
-    // problems that need the bf16 pass.  (Inactive lanes hold zeros.)
+    // +-inf in fp16 and a NaN stays NaN, and every product with it is
+    // non-finite (a zero twiddle gives NaN), so every tile of the channel
+    // block sees a non-finite sum; finite fp16 data cannot overflow the fp32
+    // sums at these lengths (|Y| < 8192 * 65504).  So a non-finite sum marks
+    // exactly the tiles that need the bf16 pass.  (Inactive lanes hold zeros.)
     bool bad = false;
 #pragma unroll
     for (int pt = 0; pt < NTL; ++pt)
@@ -574,12 +576,10 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
-    // the first row block (which holds the DC row) writes the block's flag,
-    // 0 or 1, so nothing has to clear the flags between calls
-    const int any_bad = __syncthreads_or((int)bad);
-    if (blockIdx.y == 0 && tid == 0) flags[blockIdx.x] = any_bad;
+    any_bad = __syncthreads_or((int)bad);
+    if (any_bad) return true;  // the caller redoes the tile in bf16
   }
-  if (!active) return;
+  if (!active) return any_bad;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
 #pragma unroll
   for (int pt = 0; pt < NTL; ++pt) {
@@ -589,6 +589,22 @@ void k_band_bf16(ScoreLaunch sl, char* ws, int redo) {
       const int row = pbase + pt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
     }
+  }
+  return false;
+}
+
+// One tile per block: the fp16 pass, and for a tile that meets |x| >= 65536
+// or a non-finite value, the bf16 pass of the same tile right after it (the
+// three-plane layout is the larger, so it holds both passes' LDS).
+template <int NTL, bool FULL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_band_bf16(ScoreLaunch sl, char* ws) {
+  __shared__ __attribute__((aligned(16))) BandLds<NTL, false> sh;
+  static_assert(sizeof(BandLds<NTL, true>) <= sizeof(BandLds<NTL, false>), "LDS of the fp16 pass");
+  if (band_tile<NTL, FULL, true>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z,
+                                 *reinterpret_cast<BandLds<NTL, true>*>(&sh))) {
+    __syncthreads();  // the fp16 pass's LDS reads are done
+    band_tile<NTL, FULL, false>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z, sh);
   }
 }
 
@@ -1286,10 +1302,6 @@ ct_status score_plan(const int32_t* n_per_chunk, int32_t n_chunks, int32_t L, in
     d.trig_off = tabs[found].trig;
   }
   for (int b = 0; b < n_chunks && band; ++b) {
-    desc[b].flag_off = (int64_t)off;
-    off = align256(off + (size_t)L * 2 * kFlagBlocks * 4);
-  }
-  for (int b = 0; b < n_chunks && band; ++b) {
     desc[b].y_off = (int64_t)off;
     off = align256(off + (size_t)L * 2 * desc[b].ppad * C * 4);
   }
@@ -1407,30 +1419,21 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
     // 8 waves x 64 channels per block: every twiddle slab staged in LDS
     // serves 512 channels (the slabs, not X, are most of the L2 traffic)
     dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
-#define CT_BAND(N, F16, REDO)                                                                   \
-  if (full)                                                                                     \
-    hipLaunchKernelGGL((k_band_bf16<N, true, F16>), gq, dim3(512), 0, stream, sl, ws, REDO);    \
-  else                                                                                          \
-    hipLaunchKernelGGL((k_band_bf16<N, false, F16>), gq, dim3(512), 0, stream, sl, ws, REDO);
-#define CT_BAND_NTL(F16, REDO)            \
-  switch (ntl) {                          \
-    case 5: CT_BAND(5, F16, REDO) break;  \
-    case 4: CT_BAND(4, F16, REDO) break;  \
-    case 3: CT_BAND(3, F16, REDO) break;  \
-    case 2: CT_BAND(2, F16, REDO) break;  \
-    default: CT_BAND(1, F16, REDO) break; \
-  }
+#define CT_BAND(N)                                                                         \
+  if (full)                                                                                \
+    hipLaunchKernelGGL((k_band_bf16<N, true>), gq, dim3(512), 0, stream, sl, ws);          \
+  else                                                                                     \
+    hipLaunchKernelGGL((k_band_bf16<N, false>), gq, dim3(512), 0, stream, sl, ws);
     {
       TimedLaunch tl_("band", stream);
-      CT_BAND_NTL(true, 0)
+      switch (ntl) {
+        case 5: CT_BAND(5) break;
+        case 4: CT_BAND(4) break;
+        case 3: CT_BAND(3) break;
+        case 2: CT_BAND(2) break;
+        default: CT_BAND(1) break;
+      }
     }
-    if (ct_status s = check_launch("band projection")) return s;
-    {
-      // problems whose X does not fit fp16: the three-plane bf16 pass
-      TimedLaunch tl_("band_redo", stream);
-      CT_BAND_NTL(false, 1)
-    }
-#undef CT_BAND_NTL
 #undef CT_BAND
   } else {
     TimedLaunch tl_("band", stream);
