@@ -259,16 +259,25 @@ class Workload:
         return float(sum(self.ns)) * self.L * 2 * self.H * self.D * esz  # one read of K and V
 
     def band_mfma_flops(self) -> float:
-        """Matrix-core flops the band projection issues per step: per (chunk,
-        layer, K|V), the padded band rows x the padded tokens x the channels x 2,
-        two fp16 twiddle planes (bf16 data that fit fp16; a problem that does
-        not is redone with three bf16 planes) or six products (fp32 data)."""
+        """Matrix-core flops the band projection issues per step, per (chunk,
+        layer, K|V).  bf16 data: the cosine and sine tiles of the retained bins
+        (32 rows each) x the folded token columns (ceil(N/2), padded to 32) x
+        the channels x 2, three fp16 products (a problem whose folded sums
+        leave fp16's range is redone unfolded with three bf16 planes).  fp32
+        data: the padded band rows x the padded tokens x the channels x 2, six
+        products."""
         flops = 0.0
         for n in self.ns:
             nb = n // 2 + 1
             kk = min(nb, max(1, (self.alpha[0] * nb) // self.alpha[1]))
-            ppad = -(-2 * kk // 32) * 32
-            flops += self.L * 2 * ppad * (-(-n // 32) * 32) * self.H * self.D * 2 * (2 if self.dtype == "bf16" else 6)
+            C = self.H * self.D
+            if self.dtype == "bf16":
+                rows = 2 * 32 * (-(-kk // 32))
+                cols = 32 * (-(-((n + 1) // 2) // 32))
+                flops += self.L * 2 * rows * cols * C * 2 * 3
+            else:
+                ppad = -(-2 * kk // 32) * 32
+                flops += self.L * 2 * ppad * (-(-n // 32) * 32) * C * 2 * 6
         return flops
 
     def assemble_bytes_per_layer(self) -> float:

@@ -8,12 +8,16 @@
 // is computed exactly (up to rounding) without forming xlow:
 //  1. band projection on the matrix cores: Y = [cos | sin](j*n) . X, i.e. the
 //     real and imaginary parts R_j, S_j (j < kk) of the retained bins for all
-//     channels at once.  bf16 data enter the fp16 matrix cores, where they
-//     are exact below 65536, against the twiddles as an fp16 hi + lo pair
-//     (t = t1 + t2 to 2^-24): two MFMAs give fp32-accurate coefficients.  A
-//     tile that meets a larger or non-finite value is redone at once with the
-//     twiddles as three bf16 planes (t1 + t2 + t3 to ~2^-25) against the bf16
-//     data (three MFMAs); fp32 data are split the same way (six MFMAs).
+//     channels at once.  For bf16 data the transform is folded on its
+//     real-input symmetry (tokens n and nf - n share their twiddles, up to the
+//     sine's sign), so the cosine rows take x[n] + x[nf-n] and the sine rows
+//     x[n] - x[nf-n] over half the tokens.  Those sums enter the fp16 matrix
+//     cores as an exact fp16 hi + lo pair, against the twiddles as an fp16
+//     hi + lo pair (t = t1 + t2 to 2^-24): three MFMAs give fp32-accurate
+//     coefficients.  A tile whose sums leave fp16's range, or that meets a
+//     non-finite value, is redone at once unfolded, with the twiddles as three
+//     bf16 planes (t1 + t2 + t3 to ~2^-25) against the bf16 data (three
+//     MFMAs); fp32 data are split the same way (six MFMAs).
 //  2. the channel Gram G = Y Y^T (fp64);
 //  3. E[n] as a trigonometric polynomial of degree 2(kk-1) in phi = 2*pi*n/nf,
 //     whose coefficients are diagonal and anti-diagonal sums of G; evaluated
@@ -394,29 +398,76 @@ __device__ void poly_energy(const ScoreChunkDesc& d, int layer, int kv, const do
 // complete in issue order, and a branch around a load or a compute block
 // makes the compiler's wait counts at the loop head assume the worst path,
 // which would hold each step until the next step's loads had landed.
-// NTL = 32-row band tiles per block (the launch's largest; rows a chunk does
-// not have are zero).
-// FULL: every chunk's padded band is a whole number of blocks of 32*NTL rows,
-// so no block holds padding tiles and the tile loop carries no per-tile test
-// (the branches would break up the matrix-core issue).
-// F16: X converted to fp16 in registers against the fp16 twiddle pair (two
-// MFMAs per tile and k-step); a tile that meets |x| >= 65536 or a non-finite
-// value returns true without writing Y.  Otherwise X stays bf16 against the
-// three bf16 planes (three MFMAs).
+
+// Rows of a band block.  A block of NTL = 2 * NC tiles of 32 rows serves the
+// bins b0 .. b0 + 32 NC - 1 (b0 = rblk * 32 NC): tile pt < NC holds their
+// cosine rows and tile NC + pt their sine rows, so that no tile mixes the two
+// kinds.  The table (and Y) row of bin b is b for the cosine and kk + b for
+// the sine; bins at or past kk have none.
+template <int NC>
+__device__ inline int band_table_row(int r, int b0, int kk) {
+  const int pt = r >> 5, bin = b0 + 32 * (pt % NC) + (r & 31);
+  if (bin >= kk) return -1;
+  return pt < NC ? bin : kk + bin;
+}
+// Y row a tile row is stored to: as above, and a sine tile's rows past the
+// last bin fill the padding rows 2kk .. ppad - 1 (with zeros: their twiddle
+// rows read zeros); -1 for rows stored nowhere.
+template <int NC>
+__device__ inline int band_y_row(int pt, int rt, int b0, int kk, int ppad) {
+  const int bin = b0 + 32 * (pt % NC) + rt;
+  if (pt < NC) return bin < kk ? bin : -1;
+  return kk + bin < ppad ? kk + bin : -1;
+}
+
+// FULL: every chunk's kk is a whole number of blocks of 32 NC bins, so no
+// block holds tiles past its chunk's last bin and the tile loop carries no
+// per-tile test (the branches would break up the matrix-core issue).
 template <int NTL, bool F16>
 struct BandLds {
   static constexpr int kPlanes = F16 ? 2 : 3;  // twiddle planes
   uint16_t buf[2][kPlanes * 32 * NTL * kTwStride];
 };
 
-// One 512-channel x (32 * NTL)-row tile (channel block cblk, row block rblk)
-// of problem prob, by the 512 threads of the calling block, in `sh`.  Returns
-// together on every thread (every condition below is uniform over the block):
-// true when the fp16 pass met a value outside fp16's range.
-template <int NTL, bool FULL, bool F16>
-__device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
-                                          BandLds<NTL, F16>& sh) {
-  constexpr int NPL = F16 ? 2 : 3;  // twiddle planes
+// x = hi + lo with hi the round-to-nearest-even fp16 of x and lo the fp16 of
+// the remainder.  For x the fp32 sum or difference of two bf16 values the
+// split is exact (unless the remainder falls below fp16's normal range, 2^-14,
+// where it is rounded by at most 2^-25): when the two do not nearly cancel,
+// the larger one's 8 significant bits lie within hi's 11, so the remainder is
+// made of the smaller one's bits; hi is rounded up only when the smaller one
+// reaches half of hi's last place, and then the remainder spans at most 9
+// bits.  (Nearly cancelling operands leave at most 10 bits, all in hi.)
+// |lo| <= 2^-11 |x|.  |x| >= 65520, or a non-finite x, gives a non-finite hi.
+// The remainders are formed by the mixed-precision FMA, x - 1.0 * hi with hi
+// read as fp16 from its half of the packed register (one instruction each,
+// exact: the difference is representable in fp32).
+__device__ inline uint2 split_f16(float a, float b) {
+  const uint32_t h = pack_f16(a, b);
+  float ra, rb;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(h), "v"(a));
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(h), "v"(b));
+  return make_uint2(h, pack_f16(ra, rb));
+}
+
+// One 512-channel x (32 * 2NC)-row tile (channel block cblk, bin block rblk)
+// of problem prob, by the 512 threads of the calling block, fp16 pass.
+// The real-input symmetry of the transform halves its length: for 0 < n <
+// nf/2 the twiddles of tokens n and nf - n are equal (cosine) and opposite
+// (sine), so
+//   R_j = x[0] + sum_{0<n<nf/2} cos(2 pi j n/nf) (x[n] + x[nf-n]) [+ (-1)^j x[nf/2]],
+//   S_j =        sum_{0<n<nf/2} sin(2 pi j n/nf) (x[n] - x[nf-n]),
+// the bracket for even nf (tokens past N are zeros).  u = x[n] + x[nf-n] and
+// v = x[n] - x[nf-n] are formed in fp32 from the bf16 data and split exactly
+// into fp16 hi + lo; against the twiddle pair t = t1 + t2 the products
+// t1*hi + t2*hi + t1*lo (three MFMAs per tile and k-step, on half the
+// tokens) leave out t2*lo, below 2^-23 |u|.  The nf/2 term is added in fp32
+// after the loop.  Returns together on every thread (every condition below
+// is uniform over the block): true when a tile met a value outside fp16's
+// range (|u| or |v| >= 65520, or non-finite data), without writing Y.
+template <int NC, bool FULL>
+__device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
+                                          BandLds<2 * NC, true>& sh) {
+  constexpr int NTL = 2 * NC, NPL = 2;
   auto& lds = sh.buf;
 
   const int L = sl.L, C = sl.C;
@@ -424,11 +475,14 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
   const int layer = (prob / 2) % L;
   const int kv = prob % 2;
   const ScoreChunkDesc& d = sl.c[b];
-  const int pbase = rblk * 32 * NTL;
-  if (pbase >= d.ppad) return false;
-  const int nrows = min(32 * NTL, d.ppad - pbase);  // rows this chunk has in the block
-  const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
-  const int nsteps = (N + 31) / 32;
+  const int kk = d.kk, b0 = rblk * 32 * NC;
+  if (b0 >= kk) return false;
+  const int nlive = min(NC, (kk - b0 + 31) / 32);  // tiles of each kind with bins
+  const int N = d.n, nf = d.nf, ntp = d.ntok_pad, ppad = d.ppad;
+  const int nh = (nf + 1) / 2;      // folded columns n = 0 .. nh - 1
+  const int nsteps = (nh + 31) / 32;
+  const int m0 = nf - nh + 1;       // first mirrored token
+  const int nfwd = min(nh, N), nmir = max(0, N - m0);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, col = lane & 31;
@@ -437,17 +491,27 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
   const int c0 = cbase + 2 * col;
 
   // Buffer resources (gfx9 word 3): a load whose VGPR offset is at or past
-  // num_records returns 0, which zero-fills tokens at and beyond N and rows a
-  // chunk does not have.  The whole offset is kept in the VGPR operand (the
-  // scalar offset is 0), so that range check covers every load.
-  const uint16_t* tw = F16 ? d.tw16 : d.tw;
+  // num_records returns 0.  fres covers the tokens n < nh (and < N) and mres
+  // the mirrored tokens m0 .. N - 1, so every folded column at or past nh,
+  // and the mirror of column 0 (token nf), reads zeros on both sides.  The
+  // whole offset is kept in the VGPR operand (the scalar offset is 0), so the
+  // range check covers every load; a mirrored offset that would be negative
+  // is clamped to the end of the range.
+  const uint16_t* tw = d.tw16;
   const long long plane = (long long)ppad * ntp;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(src + (size_t)layer * N * C), 0, N * C * 2, 0x00020000);
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k) + (size_t)layer * N * C;
+  const __amdgpu_buffer_rsrc_t fres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src), 0, nfwd * C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src + (size_t)min(m0, N) * C), 0, nmir * C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(tw), 0, (int)(NPL * plane * 2), 0x00020000);
-  const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;  // inactive lanes read zeros
+  const int fvoff = active ? (c0 + 8 * g * C) * 2 : nfwd * C * 2;
+  // mirror of column n: token nf - n, at (nh - 1 - n) tokens into mres.  An
+  // inactive wave's offsets stay past the range for every column the loop
+  // loads (n < 32 * nsteps + 96 <= nh + 127).
+  const int mvoff = active ? ((nh - 1 - 8 * g) * C + c0) * 2 : (nmir + nh + 128) * C * 2;
+  const uint32_t mend = (uint32_t)(nmir * C * 2);
 
   f32x16_t acc[NTL][2];
 #pragma unroll
@@ -457,16 +521,20 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][m][v] = 0.f;
 
-  // X of a step: 2 k-steps x 8 tokens x (2 channels in one dword)
-  uint32_t xa[16], xb[16];
-  auto load_x = [&](int step, uint32_t* dst) {
+  // X of a step: 2 k-steps x 8 columns x (2 channels in one dword), the
+  // columns' own tokens (xf) and their mirrors (xm)
+  uint32_t xfa[16], xma[16], xfb[16], xmb[16];
+  auto load_x = [&](int step, uint32_t* xf, uint32_t* xm) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        dst[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, xvoff + (step * 32 + 16 * s2 + t) * C * 2, 0, 0);
+      for (int t = 0; t < 8; ++t) {
+        const int k = (step * 32 + 16 * s2 + t) * C * 2;
+        xf[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(fres, fvoff + k, 0, 0);
+        xm[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(mres, (int)min((uint32_t)(mvoff - k), mend), 0, 0);
+      }
   };
-  // twiddle slab of a step: NPL planes x 32*NTL rows x 32 tokens (16-byte chunks)
+  // twiddle slab of a step: NPL planes x 32*NTL rows x 32 columns (16-byte chunks)
   constexpr int TWN = NPL * 32 * NTL * 4;  // chunks per slab
   constexpr int TWI = (TWN + 511) / 512;   // chunks per thread (the last may be partial)
   u32x4_t twr[TWI];
@@ -475,8 +543,208 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
   for (int it = 0; it < TWI; ++it) {
     const int item = tid + 512 * it;
     const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
-    // rows this chunk does not have read past the table (zeros)
-    twoff[it] = (item < TWN && r < nrows) ? (int)((q * plane + (long long)(pbase + r) * ntp + 8 * i) * 2)
+    const int trow = band_table_row<NC>(r, b0, kk);
+    // rows without a bin read past the table (zeros)
+    twoff[it] = (item < TWN && trow >= 0) ? (int)((q * plane + (long long)trow * ntp + 8 * i) * 2)
+                                          : (int)(NPL * plane * 2);
+  }
+  auto load_tw = [&](int step) {
+#pragma unroll
+    for (int it = 0; it < TWI; ++it)
+      twr[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tres, twoff[it] + step * 64, 0, 0));
+  };
+  auto store_tw = [&](uint16_t* buf) {
+#pragma unroll
+    for (int it = 0; it < TWI; ++it) {
+      const int item = tid + 512 * it;
+      if (TWN % 512 != 0 && item >= TWN) break;
+      const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
+      *reinterpret_cast<u32x4_t*>(&buf[(q * 32 * NTL + r) * kTwStride + 8 * i]) = twr[it];
+    }
+  };
+  // the three products of one tile and k-step against the B pair (hi, lo) of
+  // both channel halves
+  auto tile3 = [&](const uint16_t* buf, int pt, int s2, const u32x4_t* hi, const u32x4_t* lo) {
+    const uint16_t* ap = &buf[(pt * 32 + col) * kTwStride + 16 * s2 + 8 * g];
+    const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(ap);
+    const f16x8_t a2 = *reinterpret_cast<const f16x8_t*>(ap + 32 * NTL * kTwStride);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, hi[m]), acc[pt][m], 0, 0, 0);
+      acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, __builtin_bit_cast(f16x8_t, hi[m]), acc[pt][m], 0, 0, 0);
+      acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, lo[m]), acc[pt][m], 0, 0, 0);
+    }
+  };
+  auto compute = [&](const uint16_t* buf, const uint32_t* xf, const uint32_t* xm) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      // B fragments: column pairs (2h, 2h+1) of channel half m, as the fp16
+      // hi and lo of u = x[n] + x[nf-n] and v = x[n] - x[nf-n]
+      u32x4_t uh[2], ul[2], vh[2], vl[2];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t f0 = xf[8 * s2 + 2 * h], f1 = xf[8 * s2 + 2 * h + 1];
+        const uint32_t r0 = xm[8 * s2 + 2 * h], r1 = xm[8 * s2 + 2 * h + 1];
+        // bf16 -> fp32 is exact
+        const float fa0 = __uint_as_float(f0 << 16), fa1 = __uint_as_float(f1 << 16);
+        const float ra0 = __uint_as_float(r0 << 16), ra1 = __uint_as_float(r1 << 16);
+        const float fb0 = __uint_as_float(f0 & 0xffff0000u), fb1 = __uint_as_float(f1 & 0xffff0000u);
+        const float rb0 = __uint_as_float(r0 & 0xffff0000u), rb1 = __uint_as_float(r1 & 0xffff0000u);
+        const uint2 u0 = split_f16(fa0 + ra0, fa1 + ra1), u1 = split_f16(fb0 + rb0, fb1 + rb1);
+        const uint2 v0 = split_f16(fa0 - ra0, fa1 - ra1), v1 = split_f16(fb0 - rb0, fb1 - rb1);
+        uh[0][h] = u0.x; ul[0][h] = u0.y; uh[1][h] = u1.x; ul[1][h] = u1.y;
+        vh[0][h] = v0.x; vl[0][h] = v0.y; vh[1][h] = v1.x; vl[1][h] = v1.y;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pt = 0; pt < NC; ++pt) {
+        if (!FULL && pt >= nlive) break;  // no bins in this tile: no products of padding
+        tile3(buf, pt, s2, uh, ul);
+      }
+#pragma unroll
+      for (int pt = 0; pt < NC; ++pt) {
+        if (!FULL && pt >= nlive) break;
+        tile3(buf, NC + pt, s2, vh, vl);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Loads of steps at or past nsteps read past the buffers' ranges and return
+  // zeros, so the loop issues them without a test: a straight-line body with
+  // one back edge lets every wait count only the loads of the step it needs.
+  // A wave with no channels computes on zeros (its loads are all out of range).
+  // The prologue leaves the loads in the order the loop body issues them
+  // (X of this step, then the twiddles and X of the next), so the loop entry
+  // needs no stricter waits than the back edge.
+  load_tw(0);
+  load_x(0, xfa, xma);
+  store_tw(lds[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tw(1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(1, xfb, xmb);
+  for (int step = 0; step < nsteps; step += 2) {
+    // even step: LDS buffer 0, registers xfa/xma
+    __syncthreads();
+    compute(lds[0], xfa, xma);
+    store_tw(lds[1]);
+    load_tw(step + 2);
+    // the twiddles ahead of X: the next store waits only for them
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(step + 2, xfa, xma);
+    // odd step: LDS buffer 1, registers xfb/xmb (past the end when nsteps is
+    // odd: zero operands leave the sums unchanged)
+    __syncthreads();
+    compute(lds[1], xfb, xmb);
+    store_tw(lds[0]);
+    load_tw(step + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(step + 3, xfb, xmb);
+  }
+
+  // The range test costs nothing inside the loop: |u| >= 65520 becomes +-inf
+  // in fp16 and a NaN stays NaN, and every product with it is non-finite (a
+  // zero twiddle gives NaN), so every tile of the channel block of that kind
+  // sees a non-finite sum; finite fp16 data cannot overflow the fp32 sums at
+  // these lengths.  So a non-finite sum marks exactly the blocks that need the
+  // bf16 pass.  (Inactive lanes hold zeros.)
+  bool bad = false;
+#pragma unroll
+  for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
+  if (__syncthreads_or((int)bad)) return true;  // the caller redoes the tile in bf16
+  if (!active) return false;
+
+  // even nf: the column nf/2 pairs with itself, with cosine (-1)^j and sine 0.
+  // A row's bin parity is its accumulator index's (b0 and the tile and group
+  // offsets are even).
+  if ((nf & 1) == 0 && nf / 2 < N) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (size_t)(nf / 2) * C + c0);
+    const float xn[2] = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+#pragma unroll
+    for (int pt = 0; pt < NC; ++pt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[pt][m][v] += (v & 1) ? -xn[m] : xn[m];
+  }
+  float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+#pragma unroll
+  for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = band_y_row<NC>(pt, 8 * (v >> 2) + 4 * g + (v & 3), b0, kk, ppad);
+      if (row >= 0) *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
+    }
+  return false;
+}
+
+// The same tile over all tokens with X as bf16 against the twiddles as three
+// bf16 planes (three MFMAs per tile and k-step): every bf16 value enters
+// exactly, whatever its range.
+template <int NC, bool FULL>
+__device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
+                                          BandLds<2 * NC, false>& sh) {
+  constexpr int NTL = 2 * NC, NPL = 3;
+  auto& lds = sh.buf;
+
+  const int L = sl.L, C = sl.C;
+  const int b = prob / (2 * L);
+  const int layer = (prob / 2) % L;
+  const int kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int kk = d.kk, b0 = rblk * 32 * NC;
+  if (b0 >= kk) return;
+  const int nlive = min(NC, (kk - b0 + 31) / 32);
+  const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
+  const int nsteps = (N + 31) / 32;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int cbase = cblk * 512 + wave * 64;
+  const bool active = cbase < C;
+  const int c0 = cbase + 2 * col;
+
+  // range-checked buffer loads as in the fp16 pass: tokens at and past N and
+  // rows without a bin read zeros
+  const long long plane = (long long)ppad * ntp;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src + (size_t)layer * N * C), 0, N * C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(d.tw), 0, (int)(NPL * plane * 2), 0x00020000);
+  const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;
+
+  f32x16_t acc[NTL][2];
+#pragma unroll
+  for (int i = 0; i < NTL; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][m][v] = 0.f;
+
+  uint32_t xa[16], xb[16];
+  auto load_x = [&](int step, uint32_t* dst) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        dst[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, xvoff + (step * 32 + 16 * s2 + t) * C * 2, 0, 0);
+  };
+  constexpr int TWN = NPL * 32 * NTL * 4;
+  constexpr int TWI = (TWN + 511) / 512;
+  u32x4_t twr[TWI];
+  int twoff[TWI];
+#pragma unroll
+  for (int it = 0; it < TWI; ++it) {
+    const int item = tid + 512 * it;
+    const int q = item / (128 * NTL), r = (item / 4) % (32 * NTL), i = item % 4;
+    const int trow = band_table_row<NC>(r, b0, kk);
+    twoff[it] = (item < TWN && trow >= 0) ? (int)((q * plane + (long long)trow * ntp + 8 * i) * 2)
                                           : (int)(NPL * plane * 2);
   }
   auto load_tw = [&](int step) {
@@ -500,44 +768,23 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const uint32_t w0 = xs[8 * s2 + 2 * h], w1 = xs[8 * s2 + 2 * h + 1];
-        if constexpr (F16) {
-          // bf16 -> fp32 is exact; fp32 -> fp16 is exact below 65536
-          const float a0 = __uint_as_float(w0 << 16), a1 = __uint_as_float(w1 << 16);
-          const float c0_ = __uint_as_float(w0 & 0xffff0000u), c1_ = __uint_as_float(w1 & 0xffff0000u);
-          bu[0][h] = pack_f16(a0, a1);
-          bu[1][h] = pack_f16(c0_, c1_);
-        } else {
-          bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
-          bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
-        }
+        bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
+        bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
       }
 #pragma unroll
       for (int pt = 0; pt < NTL; ++pt) {
-        if (!FULL && pt * 32 >= nrows) break;  // the band ends inside this block: no products of padding
+        if (!FULL && pt % NC >= nlive) continue;
 #pragma unroll
         for (int q = 0; q < NPL; ++q) {
-          const uint16_t* ap = &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g];
-          if constexpr (F16) {
-            const f16x8_t a = *reinterpret_cast<const f16x8_t*>(ap);
-            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
-            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
-          } else {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ap);
-            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
-            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
-          }
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+              &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
+          acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
+          acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
         }
       }
     }
   };
 
-  // Loads of steps at or past nsteps read past both buffers' ranges and return
-  // zeros, so the loop issues them without a test: a straight-line body with
-  // one back edge lets every wait count only the loads of the step it needs.
-  // A wave with no channels computes on zeros (its loads are all out of range).
-  // The prologue leaves the loads in the order the loop body issues them
-  // (X of this step, then the twiddles and X of the next), so the loop entry
-  // needs no stricter waits than the back edge.
   load_tw(0);
   load_x(0, xa);
   store_tw(lds[0]);
@@ -546,14 +793,11 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
   __builtin_amdgcn_sched_barrier(0);
   load_x(1, xb);
   for (int step = 0; step < nsteps; step += 2) {
-    // even step: LDS buffer 0, registers xa
     __syncthreads();
     compute(lds[0], xa);
     store_tw(lds[1]);
     load_tw(step + 2);
     load_x(step + 2, xa);
-    // odd step: LDS buffer 1, registers xb (past the end when nsteps is odd:
-    // zero operands leave the sums unchanged)
     __syncthreads();
     compute(lds[1], xb);
     store_tw(lds[0]);
@@ -561,50 +805,29 @@ __device__ __forceinline__ bool band_tile(const ScoreLaunch& sl, char* ws, int c
     load_x(step + 3, xb);
   }
 
-  int any_bad = 0;
-  if constexpr (F16) {
-    // The range test costs nothing inside the loop: |x| >= 65536 becomes
-    // +-inf in fp16 and a NaN stays NaN, and every product with it is
-    // non-finite (a zero twiddle gives NaN), so every tile of the channel
-    // block sees a non-finite sum; finite fp16 data cannot overflow the fp32
-    // sums at these lengths (|Y| < 8192 * 65504).  So a non-finite sum marks
-    // exactly the tiles that need the bf16 pass.  (Inactive lanes hold zeros.)
-    bool bad = false;
-#pragma unroll
-    for (int pt = 0; pt < NTL; ++pt)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
-    any_bad = __syncthreads_or((int)bad);
-    if (any_bad) return true;  // the caller redoes the tile in bf16
-  }
-  if (!active) return any_bad;
+  if (!active) return;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
 #pragma unroll
-  for (int pt = 0; pt < NTL; ++pt) {
-    if (pt * 32 >= nrows) break;
+  for (int pt = 0; pt < NTL; ++pt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = pbase + pt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
+      const int row = band_y_row<NC>(pt, 8 * (v >> 2) + 4 * g + (v & 3), b0, kk, ppad);
+      if (row >= 0) *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
     }
-  }
-  return false;
 }
 
-// One tile per block: the fp16 pass, and for a tile that meets |x| >= 65536
-// or a non-finite value, the bf16 pass of the same tile right after it (the
+// One tile per block: the fp16 pass, and for a tile that meets a value
+// outside fp16's range, the bf16 pass of the same tile right after it (the
 // three-plane layout is the larger, so it holds both passes' LDS).
-template <int NTL, bool FULL>
+template <int NC, bool FULL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_band_bf16(ScoreLaunch sl, char* ws) {
-  __shared__ __attribute__((aligned(16))) BandLds<NTL, false> sh;
-  static_assert(sizeof(BandLds<NTL, true>) <= sizeof(BandLds<NTL, false>), "LDS of the fp16 pass");
-  if (band_tile<NTL, FULL, true>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z,
-                                 *reinterpret_cast<BandLds<NTL, true>*>(&sh))) {
+  __shared__ __attribute__((aligned(16))) BandLds<2 * NC, false> sh;
+  static_assert(sizeof(BandLds<2 * NC, true>) <= sizeof(BandLds<2 * NC, false>), "LDS of the fp16 pass");
+  if (band_fold<NC, FULL>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z,
+                          *reinterpret_cast<BandLds<2 * NC, true>*>(&sh))) {
     __syncthreads();  // the fp16 pass's LDS reads are done
-    band_tile<NTL, FULL, false>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z, sh);
+    band_bf16<NC, FULL>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z, sh);
   }
 }
 
@@ -1397,28 +1620,17 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
 
   dim3 gb((sl.C + 255) / 256, (sl.max_ppad + 127) / 128, sl.n_chunks * sl.L * 2);
   if (sl.dtype == CT_BF16) {
-    // Band tiles per block: the whole of the launch's largest band when it
-    // has at most 5 tiles (160 rows), else that band split evenly over the
-    // fewest blocks of at most 5 tiles.  Each block streams X from HBM
-    // once, so more blocks per band means more reads of X.
-    // The fp16 kernel with 5 tiles and padding tiles runs out of registers:
-    // such launches take at most 4 tiles per block.
-    const int tiles = sl.max_ppad / 32;
-    auto tiles_per_block = [&](int cap) {
-      const int nyb = (tiles + cap - 1) / cap;
-      return (tiles + nyb - 1) / nyb;
-    };
-    auto whole = [&](int ntl) {
-      bool f = true;
-      for (int i = 0; i < sl.n_chunks; ++i) f = f && sl.c[i].ppad % (32 * ntl) == 0;
-      return f;
-    };
-    int ntl = tiles_per_block(5);
-    if (ntl == 5 && !whole(5)) ntl = tiles_per_block(4);
-    const bool full = whole(ntl);
+    // Bins per block: 32 (2 tiles) when no chunk keeps more, else 64 (4
+    // tiles, 128 accumulator registers).  Each block streams X from HBM once,
+    // so more blocks per band means more reads of X.
+    int max_kk = 0;
+    for (int i = 0; i < sl.n_chunks; ++i) max_kk = std::max(max_kk, sl.c[i].kk);
+    const int nc = max_kk <= 32 ? 1 : 2;
+    bool full = true;
+    for (int i = 0; i < sl.n_chunks; ++i) full = full && sl.c[i].kk % (32 * nc) == 0;
     // 8 waves x 64 channels per block: every twiddle slab staged in LDS
     // serves 512 channels (the slabs, not X, are most of the L2 traffic)
-    dim3 gq((sl.C + 511) / 512, (sl.max_ppad + 32 * ntl - 1) / (32 * ntl), sl.n_chunks * sl.L * 2);
+    dim3 gq((sl.C + 511) / 512, (max_kk + 32 * nc - 1) / (32 * nc), sl.n_chunks * sl.L * 2);
 #define CT_BAND(N)                                                                         \
   if (full)                                                                                \
     hipLaunchKernelGGL((k_band_bf16<N, true>), gq, dim3(512), 0, stream, sl, ws);          \
@@ -1426,12 +1638,10 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
     hipLaunchKernelGGL((k_band_bf16<N, false>), gq, dim3(512), 0, stream, sl, ws);
     {
       TimedLaunch tl_("band", stream);
-      switch (ntl) {
-        case 5: CT_BAND(5) break;
-        case 4: CT_BAND(4) break;
-        case 3: CT_BAND(3) break;
-        case 2: CT_BAND(2) break;
-        default: CT_BAND(1) break;
+      if (nc == 1) {
+        CT_BAND(1)
+      } else {
+        CT_BAND(2)
       }
     }
 #undef CT_BAND

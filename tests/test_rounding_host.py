@@ -1,12 +1,18 @@
-"""The rounding identity the assembly kernel relies on for bf16 keys (host
-arithmetic, numpy): rounding an fp64 value to fp32 and then to bf16, both to
+"""Rounding identities the kernels rely on (host arithmetic, numpy).
+
+The assembly kernel's bf16 keys: rounding an fp64 value to fp32 and then to bf16, both to
 nearest even, gives the bf16 nearest to the fp64 value whenever the fp32
 result is not exactly halfway between two bf16 values.  The kernel takes the
 two hardware conversions except in that case, where it rounds once from the
 fp64 bits.  Checked against an exact one-step rounding on random values over
 a wide exponent range and on values placed within a few fp32 ulps of bf16
 midpoints (where double rounding goes wrong when the midpoint case is not
-set aside)."""
+set aside).
+
+The band projection's folded data: the fp32 sum or difference u of two bf16
+values splits exactly into hi = fp16(u) (to nearest even) and lo = fp16(u -
+hi), apart from a remainder below fp16's normal range (rounded by at most
+2^-25), with |lo| <= 2^-11 |u|; |u| >= 65520 gives an infinite hi."""
 import numpy as np
 
 
@@ -37,3 +43,35 @@ def test_double_rounding_is_single_rounding_off_midpoints():
     assert np.array_equal(got[~mid], want[~mid])
     # and the case set aside is real: some midpoint results do round differently
     assert (got[mid] != want[mid]).any()
+
+
+def _bf16(x):
+    """float32 values rounded to bf16 (nearest even), as float32."""
+    u = x.astype(np.float32).view(np.uint32)
+    return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+
+
+def test_fold_split_is_exact():
+    rng = np.random.default_rng(11)
+    n = 600_000
+    # operands over a wide range of exponent gaps and both signs, up to the
+    # fp16 limit; a quarter of the pairs within 2 binades of each other
+    ea = rng.uniform(-20, 15.9, n)
+    eb = np.where(rng.random(n) < 0.25, ea + rng.uniform(-2, 2, n), rng.uniform(-30, 15.9, n))
+    a = _bf16(np.exp2(ea) * rng.choice([-1.0, 1.0], n) * rng.uniform(1, 2, n) / 2)
+    b = _bf16(np.exp2(np.minimum(eb, 15.9)) * rng.choice([-1.0, 1.0], n) * rng.uniform(1, 2, n) / 2)
+    for u in (a + b, a - b):  # float32 arithmetic, nearest even, as on the GPU
+        with np.errstate(over="ignore"):
+            hi = u.astype(np.float16)
+        fin = np.abs(u) < 65520
+        assert np.isinf(hi[~fin]).all() and np.isfinite(hi[fin]).all()
+        u, hi = u[fin], hi[fin]
+        r = u - hi.astype(np.float32)          # exact in fp32
+        lo = r.astype(np.float16)
+        err = np.abs(hi.astype(np.float64) + lo.astype(np.float64) - u.astype(np.float64))
+        normal = (r == 0) | (np.abs(r) >= 2.0 ** -14)
+        assert (err[normal] == 0).all()
+        assert (err[~normal] <= 2.0 ** -25).all()
+        assert (np.abs(lo.astype(np.float64)) <= 2.0 ** -11 * np.abs(u.astype(np.float64))).all()
+        # the split is not trivial: remainders of both signs occur in the normal range
+        assert ((r > 0) & normal & (u > 0)).sum() > 1000 and ((r < 0) & normal & (u > 0)).sum() > 1000
