@@ -420,9 +420,8 @@ __device__ inline int band_y_row(int pt, int rt, int b0, int kk, int ppad) {
   return kk + bin < ppad ? kk + bin : -1;
 }
 
-// FULL: every chunk's kk is a whole number of blocks of 32 NC bins, so no
-// block holds tiles past its chunk's last bin and the tile loop carries no
-// per-tile test (the branches would break up the matrix-core issue).
+// LDS of a band block: two buffers of the twiddle slab of one step (F16: the
+// fp16 pair, else the three bf16 planes), rows 80 bytes apart.
 template <int NTL, bool F16>
 struct BandLds {
   static constexpr int kPlanes = F16 ? 2 : 3;  // twiddle planes
@@ -464,7 +463,7 @@ __device__ inline uint2 split_f16(float a, float b) {
 // after the loop.  Returns together on every thread (every condition below
 // is uniform over the block): true when a tile met a value outside fp16's
 // range (|u| or |v| >= 65520, or non-finite data), without writing Y.
-template <int NC, bool FULL>
+template <int NC>
 __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
                                           BandLds<2 * NC, true>& sh) {
   constexpr int NTL = 2 * NC, NPL = 2;
@@ -477,7 +476,6 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
   const ScoreChunkDesc& d = sl.c[b];
   const int kk = d.kk, b0 = rblk * 32 * NC;
   if (b0 >= kk) return false;
-  const int nlive = min(NC, (kk - b0 + 31) / 32);  // tiles of each kind with bins
   const int N = d.n, nf = d.nf, ntp = d.ntok_pad, ppad = d.ppad;
   const int nh = (nf + 1) / 2;      // folded columns n = 0 .. nh - 1
   const int nsteps = (nh + 31) / 32;
@@ -597,15 +595,9 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int pt = 0; pt < NC; ++pt) {
-        if (!FULL && pt >= nlive) break;  // no bins in this tile: no products of padding
-        tile3(buf, pt, s2, uh, ul);
-      }
+      for (int pt = 0; pt < NC; ++pt) tile3(buf, pt, s2, uh, ul);
 #pragma unroll
-      for (int pt = 0; pt < NC; ++pt) {
-        if (!FULL && pt >= nlive) break;
-        tile3(buf, NC + pt, s2, vh, vl);
-      }
+      for (int pt = 0; pt < NC; ++pt) tile3(buf, NC + pt, s2, vh, vl);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -683,13 +675,16 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
   return false;
 }
 
-// The same tile over all tokens with X as bf16 against the twiddles as three
-// bf16 planes (three MFMAs per tile and k-step): every bf16 value enters
-// exactly, whatever its range.
-template <int NC, bool FULL>
-__device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
-                                          BandLds<2 * NC, false>& sh) {
-  constexpr int NTL = 2 * NC, NPL = 3;
+// The same tile unfolded, over all tokens.  F16: X converted to fp16 in
+// registers (exact below 65536) against the fp16 twiddle pair, two MFMAs per
+// tile and k-step; returns true, without writing Y, when a tile met a value
+// outside fp16's range (the same finiteness test as the folded pass).
+// Otherwise X stays bf16 against the three bf16 planes (three MFMAs): every
+// bf16 value enters exactly, whatever its range; returns false.
+template <int NC, bool F16>
+__device__ __forceinline__ bool band_unfolded(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
+                                              BandLds<2 * NC, F16>& sh) {
+  constexpr int NTL = 2 * NC, NPL = F16 ? 2 : 3;
   auto& lds = sh.buf;
 
   const int L = sl.L, C = sl.C;
@@ -698,8 +693,7 @@ __device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int c
   const int kv = prob % 2;
   const ScoreChunkDesc& d = sl.c[b];
   const int kk = d.kk, b0 = rblk * 32 * NC;
-  if (b0 >= kk) return;
-  const int nlive = min(NC, (kk - b0 + 31) / 32);
+  if (b0 >= kk) return false;
   const int N = d.n, ntp = d.ntok_pad, ppad = d.ppad;
   const int nsteps = (N + 31) / 32;
 
@@ -709,14 +703,14 @@ __device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int c
   const bool active = cbase < C;
   const int c0 = cbase + 2 * col;
 
-  // range-checked buffer loads as in the fp16 pass: tokens at and past N and
+  // range-checked buffer loads as in the folded pass: tokens at and past N and
   // rows without a bin read zeros
   const long long plane = (long long)ppad * ntp;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(src + (size_t)layer * N * C), 0, N * C * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(d.tw), 0, (int)(NPL * plane * 2), 0x00020000);
+      const_cast<uint16_t*>(F16 ? d.tw16 : d.tw), 0, (int)(NPL * plane * 2), 0x00020000);
   const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;
 
   f32x16_t acc[NTL][2];
@@ -768,18 +762,29 @@ __device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int c
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const uint32_t w0 = xs[8 * s2 + 2 * h], w1 = xs[8 * s2 + 2 * h + 1];
-        bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
-        bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+        if constexpr (F16) {
+          // bf16 -> fp32 is exact; fp32 -> fp16 is exact below 65536
+          bu[0][h] = pack_f16(__uint_as_float(w0 << 16), __uint_as_float(w1 << 16));
+          bu[1][h] = pack_f16(__uint_as_float(w0 & 0xffff0000u), __uint_as_float(w1 & 0xffff0000u));
+        } else {
+          bu[0][h] = (w0 & 0xffffu) | (w1 << 16);
+          bu[1][h] = (w0 >> 16) | (w1 & 0xffff0000u);
+        }
       }
 #pragma unroll
       for (int pt = 0; pt < NTL; ++pt) {
-        if (!FULL && pt % NC >= nlive) continue;
 #pragma unroll
         for (int q = 0; q < NPL; ++q) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g]);
-          acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
-          acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
+          const uint16_t* ap = &buf[(q * 32 * NTL + pt * 32 + col) * kTwStride + 16 * s2 + 8 * g];
+          if constexpr (F16) {
+            const f16x8_t a = *reinterpret_cast<const f16x8_t*>(ap);
+            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
+            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
+          } else {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ap);
+            acc[pt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[0]), acc[pt][0], 0, 0, 0);
+            acc[pt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bu[1]), acc[pt][1], 0, 0, 0);
+          }
         }
       }
     }
@@ -797,15 +802,27 @@ __device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int c
     compute(lds[0], xa);
     store_tw(lds[1]);
     load_tw(step + 2);
+    __builtin_amdgcn_sched_barrier(0);
     load_x(step + 2, xa);
     __syncthreads();
     compute(lds[1], xb);
     store_tw(lds[0]);
     load_tw(step + 3);
+    __builtin_amdgcn_sched_barrier(0);
     load_x(step + 3, xb);
   }
 
-  if (!active) return;
+  if constexpr (F16) {
+    bool bad = false;
+#pragma unroll
+    for (int pt = 0; pt < NTL; ++pt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
+    if (__syncthreads_or((int)bad)) return true;  // the caller redoes the tile in bf16
+  }
+  if (!active) return false;
   float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
 #pragma unroll
   for (int pt = 0; pt < NTL; ++pt)
@@ -814,20 +831,44 @@ __device__ __forceinline__ void band_bf16(const ScoreLaunch& sl, char* ws, int c
       const int row = band_y_row<NC>(pt, 8 * (v >> 2) + 4 * g + (v & 3), b0, kk, ppad);
       if (row >= 0) *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[pt][0][v], acc[pt][1][v]);
     }
+  return false;
 }
 
-// One tile per block: the fp16 pass, and for a tile that meets a value
-// outside fp16's range, the bf16 pass of the same tile right after it (the
-// three-plane layout is the larger, so it holds both passes' LDS).
-template <int NC, bool FULL>
+// One tile per block: an fp16 pass, and for a tile that meets a value outside
+// fp16's range, the bf16 pass of the same tile right after it (the
+// three-plane layout is the larger, so it holds both passes' LDS).  With
+// NC = 2 a block whose bins fill two tiles of each kind takes the folded fp16
+// pass: there the quarter of the MFMAs the fold saves outweighs its vector
+// work (the split of every data value).  A block with one tile's worth of
+// bins (a shorter chunk of the launch) runs as the NC = 1 block of its first
+// 32 bins, unfolded, and so does every block of an NC = 1 launch.  No loop
+// then carries a per-tile test; tiles with some bins past kk multiply zero
+// twiddle rows.
+template <int NC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_band_bf16(ScoreLaunch sl, char* ws) {
   __shared__ __attribute__((aligned(16))) BandLds<2 * NC, false> sh;
   static_assert(sizeof(BandLds<2 * NC, true>) <= sizeof(BandLds<2 * NC, false>), "LDS of the fp16 pass");
-  if (band_fold<NC, FULL>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z,
-                          *reinterpret_cast<BandLds<2 * NC, true>*>(&sh))) {
-    __syncthreads();  // the fp16 pass's LDS reads are done
-    band_bf16<NC, FULL>(sl, ws, blockIdx.x, blockIdx.y, blockIdx.z, sh);
+  const int cblk = blockIdx.x, prob = blockIdx.z;
+  if constexpr (NC == 2) {
+    const int kk = sl.c[prob / (2 * sl.L)].kk, rblk = blockIdx.y;
+    if (kk - rblk * 64 > 32) {
+      if (band_fold<2>(sl, ws, cblk, rblk, prob, *reinterpret_cast<BandLds<4, true>*>(&sh))) {
+        __syncthreads();  // the fp16 pass's LDS reads are done
+        band_unfolded<2, false>(sl, ws, cblk, rblk, prob, sh);
+      }
+      return;
+    }
+    // bins rblk * 64 .. kk - 1 (at most 32; none when the chunk ends before)
+    if (band_unfolded<1, true>(sl, ws, cblk, 2 * rblk, prob, *reinterpret_cast<BandLds<2, true>*>(&sh))) {
+      __syncthreads();
+      band_unfolded<1, false>(sl, ws, cblk, 2 * rblk, prob, *reinterpret_cast<BandLds<2, false>*>(&sh));
+    }
+  } else {
+    if (band_unfolded<1, true>(sl, ws, cblk, blockIdx.y, prob, *reinterpret_cast<BandLds<2, true>*>(&sh))) {
+      __syncthreads();
+      band_unfolded<1, false>(sl, ws, cblk, blockIdx.y, prob, sh);
+    }
   }
 }
 
@@ -1626,25 +1667,16 @@ static ct_status band_project(const ScoreLaunch& sl, char* ws, hipStream_t strea
     int max_kk = 0;
     for (int i = 0; i < sl.n_chunks; ++i) max_kk = std::max(max_kk, sl.c[i].kk);
     const int nc = max_kk <= 32 ? 1 : 2;
-    bool full = true;
-    for (int i = 0; i < sl.n_chunks; ++i) full = full && sl.c[i].kk % (32 * nc) == 0;
     // 8 waves x 64 channels per block: every twiddle slab staged in LDS
     // serves 512 channels (the slabs, not X, are most of the L2 traffic)
     dim3 gq((sl.C + 511) / 512, (max_kk + 32 * nc - 1) / (32 * nc), sl.n_chunks * sl.L * 2);
-#define CT_BAND(N)                                                                         \
-  if (full)                                                                                \
-    hipLaunchKernelGGL((k_band_bf16<N, true>), gq, dim3(512), 0, stream, sl, ws);          \
-  else                                                                                     \
-    hipLaunchKernelGGL((k_band_bf16<N, false>), gq, dim3(512), 0, stream, sl, ws);
     {
       TimedLaunch tl_("band", stream);
-      if (nc == 1) {
-        CT_BAND(1)
-      } else {
-        CT_BAND(2)
-      }
+      if (nc == 1)
+        hipLaunchKernelGGL((k_band_bf16<1>), gq, dim3(512), 0, stream, sl, ws);
+      else
+        hipLaunchKernelGGL((k_band_bf16<2>), gq, dim3(512), 0, stream, sl, ws);
     }
-#undef CT_BAND
   } else {
     TimedLaunch tl_("band", stream);
     hipLaunchKernelGGL(k_band_fwd<CT_F32>, gb, dim3(256), 0, stream, sl, ws);
