@@ -286,6 +286,20 @@ ct_status cachetune_select_topr(ct_handle h, const float* score, const int32_t* 
                                 int32_t r_num, int32_t r_den, int32_t* ranking, int32_t* sel,
                                 int32_t* comp, int32_t* k_per_chunk, hipStream_t stream);
 
+/* ---- checking a device index array ------------------------------------------
+ * The selection (sel, comp, ranking), assembly and attention (q_pos) calls
+ * trust their device index arrays (survey convention: trusted in release
+ * builds).  This call checks one such array without trusting it, in place of
+ * a device-side trap (which would take the whole device down): idx[0..count)
+ * (device) must lie in [0, bound) and, with ascending != 0, each entry must
+ * be above its predecessor.  *bad (device, one int32) receives the number of
+ * entries that break a rule.  The array is only read; none of its values is
+ * used as an address.  Enqueues two small kernels on stream (the first sets
+ * *bad to 0) and returns; read *bad after the stream.  count may be 0.
+ * CT_E_INVALID: bad NULL, count or bound negative, idx NULL with count > 0. */
+ct_status cachetune_check_indices(const int32_t* idx, int32_t count, int32_t bound, int32_t ascending,
+                                  int32_t* bad, hipStream_t stream);
+
 /* ---- assembly with deferred RoPE (App. B.2, B.3) ---------------------------
  * Builds one layer's working buffer k_out/v_out [T][H][D] (device):
  *   reused rows: V copied, K rotated at the row's global position;

@@ -50,7 +50,8 @@ SYMBOLS = ["cachetune_status_string", "cachetune_last_error", "cachetune_version
            "cachetune_score_variant", "cachetune_band_energy_ws", "cachetune_band_energy",
            "cachetune_rmsnorm", "cachetune_silu_mul", "cachetune_linear", "cachetune_qkv_proj",
            "cachetune_recompute_attn_noalloc", "cachetune_create", "cachetune_destroy",
-           "cachetune_prepare_scoring", "cachetune_select_topr_counts", "cachetune_fit_cost_model"]
+           "cachetune_prepare_scoring", "cachetune_select_topr_counts", "cachetune_fit_cost_model",
+           "cachetune_check_indices"]
 
 # cost(r, user) -> double, the callback type of cachetune_calibrate_ratio
 COST_FN = C.CFUNCTYPE(C.c_double, C.c_double, C.c_void_p)
@@ -78,6 +79,7 @@ def lib():
         L.cachetune_score_chunk.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
                                             vp, sz, vp]
         L.cachetune_select_topr_counts.argtypes = [vp, i32, i32, i32, vp]
+        L.cachetune_check_indices.argtypes = [vp, i32, i32, i32, vp, vp]
         L.cachetune_select_topr.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.cachetune_assemble_rope.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, f64, i32,
                                               vp, vp, i32, vp]
@@ -312,6 +314,22 @@ def cachetune_select_topr(score, n_per_chunk, r=(15, 100), ranking=None, sel=Non
     _check(lib().cachetune_select_topr(handle(), _ptr(score), arr, len(ns), r[0], r[1], _ptr(ranking),
                                        _ptr(sel), _ptr(comp), kout, _stream(stream)))
     return list(kout), ranking, sel, comp
+
+
+# ---- checking device index arrays ---------------------------------------------
+
+def cachetune_check_indices(idx, bound, ascending=True, stream=None) -> int:
+    """Number of entries of the device int32 array idx outside [0, bound) or
+    (ascending) not above their predecessor; waits for the stream."""
+    import torch
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 device tensor")
+    bad = torch.empty(1, dtype=torch.int32, device=idx.device)
+    stream = torch.cuda.current_stream() if stream is None else stream
+    _check(lib().cachetune_check_indices(_ptr(idx), idx.numel(), bound, int(bool(ascending)), _ptr(bad),
+                                         _stream(stream)))
+    stream.synchronize()
+    return int(bad.item())
 
 
 # ---- assembly -----------------------------------------------------------------

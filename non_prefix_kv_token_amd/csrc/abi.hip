@@ -421,6 +421,16 @@ static ct_status topr_counts(const int32_t* n_per_chunk, int32_t n_chunks, int32
   return CT_OK;
 }
 
+ct_status cachetune_check_indices(const int32_t* idx, int32_t count, int32_t bound, int32_t ascending,
+                                  int32_t* bad, hipStream_t stream) {
+  CT_GUARD_BEGIN
+  if (!bad) return fail(CT_E_INVALID, "bad is NULL");
+  if (count < 0 || bound < 0) return fail(CT_E_INVALID, "count and bound must be >= 0");
+  if (count > 0 && !idx) return fail(CT_E_INVALID, "idx is NULL");
+  return check_indices_run(idx, count, bound, ascending != 0, bad, stream);
+  CT_GUARD_END
+}
+
 ct_status cachetune_select_topr_counts(const int32_t* n_per_chunk, int32_t n_chunks, int32_t r_num,
                                        int32_t r_den, int32_t* k_per_chunk) {
   CT_GUARD_BEGIN

@@ -124,6 +124,10 @@ struct TopRLaunch {
   TopRChunk c[kMaxChunksPerLaunch];
   int32_t n_chunks;
 };
+// Index-array check (topr.hip): *bad = entries outside [0, bound), plus
+// (ascending) entries not above their predecessor.
+ct_status check_indices_run(const int32_t* idx, int32_t count, int32_t bound, bool ascending, int32_t* bad,
+                            hipStream_t stream);
 ct_status topr_run(const TopRLaunch& tl, const float* score, int32_t* ranking, int32_t* sel,
                    int32_t* comp, hipStream_t stream);
 

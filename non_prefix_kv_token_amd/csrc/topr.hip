@@ -191,6 +191,37 @@ __global__ __launch_bounds__(kThreads) void k_topr_compact(TopRLaunch tl, const 
 
 }  // namespace
 
+// ---- checking a device index array ------------------------------------------
+// The array is only read; a value out of range is counted, never followed.
+namespace {
+__global__ __launch_bounds__(64) void k_check_clear(int32_t* bad) {
+  if (threadIdx.x == 0) bad[0] = 0;
+}
+__global__ __launch_bounds__(256) void k_check_indices(const int32_t* idx, int32_t count, int32_t bound,
+                                                       int32_t ascending, int32_t* bad) {
+  int n_bad = 0;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count; i += (long long)gridDim.x * 256) {
+    const int32_t v = idx[i];
+    bool b = v < 0 || v >= bound;
+    if (ascending && i > 0) b = b || v <= idx[i - 1];
+    n_bad += b;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n_bad += __shfl_xor(n_bad, o);
+  if ((threadIdx.x & 63) == 0 && n_bad) atomicAdd(bad, n_bad);
+}
+}  // namespace
+
+ct_status check_indices_run(const int32_t* idx, int32_t count, int32_t bound, bool ascending, int32_t* bad,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(k_check_clear, dim3(1), dim3(64), 0, stream, bad);
+  if (ct_status s = check_launch("index check")) return s;
+  if (count == 0) return CT_OK;
+  const int blocks = (int)std::min<long long>(((long long)count + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_check_indices, dim3(blocks), dim3(256), 0, stream, idx, count, bound, (int32_t)ascending, bad);
+  return check_launch("index check");
+}
+
 ct_status topr_run(const TopRLaunch& tl, const float* score, int32_t* ranking, int32_t* sel,
                    int32_t* comp, hipStream_t stream) {
   if (!ranking) {  // one sort per chunk, the ranking kept in LDS only

@@ -25,6 +25,12 @@ static double quad(double r, void* user) { (void)user; return (r - 0.23) * (r - 
 int main(void) {
   for (int s = -6; s <= 1; ++s) CHECK(cachetune_status_string(s) != NULL);
   CHECK(cachetune_version() >= 1);
+  /* index-array check: argument validation (no device work before it) */
+  int32_t dummy_bad = 0;
+  CHECK(cachetune_check_indices(NULL, 4, 10, 1, &dummy_bad, NULL) == CT_E_INVALID);
+  CHECK(cachetune_check_indices((const int32_t*)256, -1, 10, 1, &dummy_bad, NULL) == CT_E_INVALID);
+  CHECK(cachetune_check_indices((const int32_t*)256, 4, -1, 1, &dummy_bad, NULL) == CT_E_INVALID);
+  CHECK(cachetune_check_indices((const int32_t*)256, 4, 10, 1, NULL, NULL) == CT_E_INVALID);
   /* scoring: workspace queries and argument checks */
   int32_t ns[3] = {2048, 777, 2};
   size_t bytes = 0;

@@ -78,6 +78,11 @@ def test_calls_reject_bad_arguments_without_device_work(lib):
     # Hq not a multiple of H
     assert lib.cachetune_recompute_attn(None, None, None, 0, 6, None, None, 10, 4, 128, ct.CT_BF16, 0.1,
                                         10000.0, 0, None, None, None, 0, None) == ct.CT_E_INVALID
+    # index-array check: NULL array with entries, negative count or bound, NULL result
+    assert lib.cachetune_check_indices(None, 4, 10, 1, C.c_void_p(16), None) == ct.CT_E_INVALID
+    assert lib.cachetune_check_indices(C.c_void_p(16), -1, 10, 1, C.c_void_p(16), None) == ct.CT_E_INVALID
+    assert lib.cachetune_check_indices(C.c_void_p(16), 4, -1, 1, C.c_void_p(16), None) == ct.CT_E_INVALID
+    assert lib.cachetune_check_indices(C.c_void_p(16), 4, 10, 1, None, None) == ct.CT_E_INVALID
     out = C.c_size_t(1)
     assert lib.cachetune_recompute_attn_ws(None, 100, 32, 16512, 8, 128, ct.CT_BF16, C.byref(out)) == ct.CT_OK
     assert lib.cachetune_recompute_attn_ws(None, 100, 32, 16512, 8, 100, ct.CT_BF16,

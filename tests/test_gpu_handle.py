@@ -57,3 +57,34 @@ def test_prepared_tables_give_identical_scores(syn, alpha):
     torch.cuda.synchronize()
     assert torch.equal(c_a, c_b)
     assert torch.isfinite(c_a).all() and not torch.equal(c_a, s1)
+
+
+def test_check_indices_counts_broken_entries():
+    """cachetune_check_indices reads an index array without trusting it: the
+    selection's own arrays pass, and planted entries (out of range, negative,
+    repeated, descending) are each counted once; values are never followed."""
+    ct = need_gpu()
+    import numpy as np
+    n_per_chunk = [300, 2048, 7]
+    g = torch.Generator(device="cuda").manual_seed(5)
+    score = torch.rand(sum(n_per_chunk), generator=g, device="cuda", dtype=torch.float32)
+    k, ranking, sel, comp = ct.cachetune_select_topr(score, n_per_chunk, r=(15, 100))
+    # each chunk's lists are ascending local indices below its length
+    assert ct.cachetune_check_indices(ranking[:300], 300, ascending=False) == 0
+    o_s = o_c = 0
+    for n, kb in zip(n_per_chunk, k):
+        assert ct.cachetune_check_indices(sel[o_s:o_s + kb], n) == 0
+        assert ct.cachetune_check_indices(comp[o_c:o_c + n - kb], n) == 0
+        o_s += kb
+        o_c += n - kb
+    idx = torch.tensor([0, 3, 5, 5, 12, -1, 7, 2, 9], dtype=torch.int32, device="cuda")
+    # ascending: 5 (repeat), 12 (>= 10), -1 (< 0), 2 (below 7) -> 4
+    assert ct.cachetune_check_indices(idx, 10) == 4
+    # range only: 12 and -1
+    assert ct.cachetune_check_indices(idx, 10, ascending=False) == 2
+    assert ct.cachetune_check_indices(idx[:0], 10) == 0
+    # a long array across many blocks: every 1000th entry out of range
+    big = torch.arange(300_000, dtype=torch.int32, device="cuda")
+    big[::1000] = 400_000
+    want = int(np.count_nonzero(np.arange(300_000) % 1000 == 0))
+    assert ct.cachetune_check_indices(big, 300_000, ascending=False) == want
