@@ -675,6 +675,224 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
   return false;
 }
 
+// Radix-4 form of the fp16 pass, for transform lengths nf divisible by 128
+// (M = nf/4 a whole number of pairs of 16-column k-steps).  With n = q M + m (q < 4,
+// m < M), W^{jn} = W^{jm} (-i)^{jq}, so bin j needs only the sums
+//   y0 = (x0 + x2) + (x1 + x3),  y2 = (x0 + x2) - (x1 + x3),
+//   a = x0 - x2,  b = x1 - x3      (xq = x[q M + m]),
+// over M columns, against cos and sin of 2 pi j m / nf (the first M columns of
+// the same table):
+//   j = 0, 2 mod 4:  R = sum c y,          S = sum s y      (y = y0, y2)
+//   j = 1 mod 4:     R = sum (c a - s b),  S = sum (s a + c b)
+//   j = 3 mod 4:     R = sum (c a + s b),  S = sum (s a - c b).
+// The block's 64 bins b0 .. b0 + 63 form four tiles by class k = j mod 4:
+// rows i < 16 the cosine rows (R) of bins b0 + 4i + k, rows 16 + i their sine
+// rows (S).  The b products of classes 1 and 3 take the tile's rows swapped
+// (row i reads row i ^ 16), the sine half negated for class 1 and the cosine
+// half for class 3.  Each sum enters as an fp16 hi + lo pair (hi the nearest
+// fp16, lo the fp16 of the remainder: exact for a and b, the difference of two
+// bf16 values; the four-term y0 and y2 are rounded in fp32 and their remainder
+// can need more than fp16's 11 bits, which bounds the pair's error by 2^-22 of
+// the sum plus 2^-23 of the four values' magnitudes), against the twiddle
+// pair.  Six product groups of three MFMAs per channel half and k-step (class
+// 0 with y0, 2 with y2, 1 and 3 with a and with b): 36 MFMAs per 64 tokens
+// (48 folded, 64 unfolded).  Returns together on every thread: true when a
+// tile met a value outside fp16's range (a sum reaching 65520 included).
+__device__ __forceinline__ int band_r4_table_row(int r, int b0, int kk) {
+  const int k = r >> 5, i = r & 31, bin = b0 + 4 * (i & 15) + k;
+  if (bin >= kk) return -1;
+  return i < 16 ? bin : kk + bin;
+}
+__device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
+                                        BandLds<4, true>& sh) {
+  constexpr int NPL = 2, TS = 24;  // twiddle planes; LDS row stride of a 16-column slab
+  uint16_t* lds0 = &sh.buf[0][0];
+  uint16_t* lds1 = &sh.buf[1][0];
+
+  const int L = sl.L, C = sl.C;
+  const int b = prob / (2 * L);
+  const int layer = (prob / 2) % L;
+  const int kv = prob % 2;
+  const ScoreChunkDesc& d = sl.c[b];
+  const int kk = d.kk, b0 = rblk * 64;
+  if (b0 >= kk) return false;
+  const int N = d.n, nf = d.nf, ntp = d.ntok_pad, ppad = d.ppad;
+  const int M = nf / 4;
+  const int nks = M / 16;  // k-steps of 16 columns (even)
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int cbase = cblk * 512 + wave * 64;
+  const bool active = cbase < C;
+  const int c0 = cbase + 2 * col;
+
+  // X through a buffer resource over the chunk's N tokens: tokens q M + m at
+  // or past N (zero padding) read zeros.  Offsets grow with q and m.
+  const long long plane = (long long)ppad * ntp;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? d.v : d.k) + (size_t)layer * N * C;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src), 0, N * C * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(d.tw16), 0, (int)(NPL * plane * 2), 0x00020000);
+  const int xvoff = active ? (c0 + 8 * g * C) * 2 : N * C * 2;
+  const int qstep = M * C * 2;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][m][v] = 0.f;
+
+  // X of a k-step: 4 quarters x 8 columns x (2 channels in one dword)
+  uint32_t xa[32], xb[32];
+  // (the k-step's base offset passes through an empty asm, so that each
+  // load's offset is formed when it is issued instead of being kept in a
+  // register of its own across the loop)
+  auto load_x = [&](int j, uint32_t* dst) {
+    int base = xvoff + j * 16 * C * 2;
+    asm volatile("" : "+v"(base));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        dst[8 * q + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, base + q * qstep + t * C * 2, 0, 0);
+  };
+  // twiddle slab of a k-step: 2 planes x 128 rows x 16 columns, one 16-byte
+  // chunk per thread
+  u32x4_t twr;
+  int twoff;
+  {
+    const int q = tid >> 8, r = (tid >> 1) & 127, i = tid & 1;
+    const int trow = band_r4_table_row(r, b0, kk);
+    twoff = trow >= 0 ? (int)((q * plane + (long long)trow * ntp + 8 * i) * 2) : (int)(NPL * plane * 2);
+  }
+  auto load_tw = [&](int j) {
+    twr = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tres, twoff + j * 32, 0, 0));
+  };
+  auto store_tw = [&](uint16_t* buf) {
+    const int q = tid >> 8, r = (tid >> 1) & 127, i = tid & 1;
+    *reinterpret_cast<u32x4_t*>(&buf[(q * 128 + r) * TS + 8 * i]) = twr;
+  };
+  auto prod3 = [&](f32x16_t& ac, const f16x8_t& a1, const f16x8_t& a2, const u32x4_t& hi, const u32x4_t& lo) {
+    ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, hi), ac, 0, 0, 0);
+    ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, __builtin_bit_cast(f16x8_t, hi), ac, 0, 0, 0);
+    ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, lo), ac, 0, 0, 0);
+  };
+  const uint32_t neg1 = col < 16 ? 0x80008000u : 0u, neg3 = col < 16 ? 0u : 0x80008000u;
+  auto frag_a = [&](const uint16_t* buf, int row, f16x8_t& a1, f16x8_t& a2, uint32_t neg) {
+    const uint16_t* ap = &buf[row * TS + 8 * g];
+    u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(ap);
+    u32x4_t w2 = *reinterpret_cast<const u32x4_t*>(ap + 128 * TS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w1[i] ^= neg;
+      w2[i] ^= neg;
+    }
+    a1 = __builtin_bit_cast(f16x8_t, w1);
+    a2 = __builtin_bit_cast(f16x8_t, w2);
+  };
+  // the quarters' values of column pair (2h, 2h+1) in channel half m (bf16 ->
+  // fp32 is exact): v[q][e] = x[q M + column 2h + e]
+  auto quarters = [&](const uint32_t* xs, int m, int h, float (*v)[2]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w = xs[8 * q + 2 * h + e];
+        v[q][e] = __uint_as_float(m == 0 ? w << 16 : w & 0xffff0000u);
+      }
+  };
+  // one k-step, channel half by channel half: the four data terms split in
+  // one pass over the quarters' values, then the half's 18 products
+  auto compute = [&](const uint16_t* buf, const uint32_t* xs) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      u32x4_t hi[4], lo[4];  // terms y0, y2, a, b
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float v[4][2];
+        quarters(xs, m, h, v);
+        float p[4][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float s02 = v[0][e] + v[2][e], s13 = v[1][e] + v[3][e];
+          p[0][e] = s02 + s13;
+          p[1][e] = s02 - s13;
+          p[2][e] = v[0][e] - v[2][e];
+          p[3][e] = v[1][e] - v[3][e];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint2 w = split_f16(p[t][0], p[t][1]);
+          hi[t][h] = w.x;
+          lo[t][h] = w.y;
+        }
+      }
+      f16x8_t a1, a2;
+      frag_a(buf, col, a1, a2, 0u);
+      prod3(acc[0][m], a1, a2, hi[0], lo[0]);
+      frag_a(buf, 64 + col, a1, a2, 0u);
+      prod3(acc[2][m], a1, a2, hi[1], lo[1]);
+      frag_a(buf, 32 + col, a1, a2, 0u);
+      prod3(acc[1][m], a1, a2, hi[2], lo[2]);
+      frag_a(buf, 96 + col, a1, a2, 0u);
+      prod3(acc[3][m], a1, a2, hi[2], lo[2]);
+      frag_a(buf, 32 + (col ^ 16), a1, a2, neg1);
+      prod3(acc[1][m], a1, a2, hi[3], lo[3]);
+      frag_a(buf, 96 + (col ^ 16), a1, a2, neg3);
+      prod3(acc[3][m], a1, a2, hi[3], lo[3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // software pipeline as in the other passes: X two k-steps ahead, the
+  // twiddle slab one ahead through the other LDS buffer, one barrier per
+  // k-step, a straight-line body (loads past the end read zeros)
+  load_tw(0);
+  load_x(0, xa);
+  store_tw(lds0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tw(1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(1, xb);
+  for (int j = 0; j < nks; j += 2) {
+    __syncthreads();
+    compute(lds0, xa);
+    store_tw(lds1);
+    load_tw(j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(j + 2, xa);
+    __syncthreads();
+    compute(lds1, xb);
+    store_tw(lds0);
+    load_tw(j + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(j + 3, xb);
+  }
+
+  bool bad = false;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) bad |= !(__builtin_fabsf(acc[pt][m][v]) < __builtin_inff());
+  if (__syncthreads_or((int)bad)) return true;  // the caller redoes the tile in bf16
+  if (!active) return false;
+  float* Y = reinterpret_cast<float*>(ws + d.y_off) + ((size_t)(layer * 2 + kv) * ppad) * C;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = 8 * (v >> 2) + 4 * g + (v & 3), bin = b0 + 4 * (i & 15) + k;
+      const int row = i < 16 ? (bin < kk ? bin : -1) : (kk + bin < ppad ? kk + bin : -1);
+      if (row >= 0) *reinterpret_cast<float2*>(Y + (size_t)row * C + c0) = make_float2(acc[k][0][v], acc[k][1][v]);
+    }
+  return false;
+}
+
 // The same tile unfolded, over all tokens.  F16: X converted to fp16 in
 // registers (exact below 65536) against the fp16 twiddle pair, two MFMAs per
 // tile and k-step; returns true, without writing Y, when a tile met a value
@@ -837,9 +1055,10 @@ __device__ __forceinline__ bool band_unfolded(const ScoreLaunch& sl, char* ws, i
 // One tile per block: an fp16 pass, and for a tile that meets a value outside
 // fp16's range, the bf16 pass of the same tile right after it (the
 // three-plane layout is the larger, so it holds both passes' LDS).  With
-// NC = 2 a block whose bins fill two tiles of each kind takes the folded fp16
-// pass: there the quarter of the MFMAs the fold saves outweighs its vector
-// work (the split of every data value).  A block with one tile's worth of
+// NC = 2 a block whose bins fill two tiles of each kind takes the radix-4
+// fp16 pass when the transform length is a multiple of 128, else the folded
+// one: there the MFMAs these forms save (a quarter folded, nearly half in
+// radix-4) outweigh their vector work (the split of every data value).  A block with one tile's worth of
 // bins (a shorter chunk of the launch) runs as the NC = 1 block of its first
 // 32 bins, unfolded, and so does every block of an NC = 1 launch.  No loop
 // then carries a per-tile test; tiles with some bins past kk multiply zero
@@ -851,9 +1070,11 @@ void k_band_bf16(ScoreLaunch sl, char* ws) {
   static_assert(sizeof(BandLds<2 * NC, true>) <= sizeof(BandLds<2 * NC, false>), "LDS of the fp16 pass");
   const int cblk = blockIdx.x, prob = blockIdx.z;
   if constexpr (NC == 2) {
-    const int kk = sl.c[prob / (2 * sl.L)].kk, rblk = blockIdx.y;
+    const ScoreChunkDesc& d = sl.c[prob / (2 * sl.L)];
+    const int kk = d.kk, rblk = blockIdx.y;
     if (kk - rblk * 64 > 32) {
-      if (band_fold<2>(sl, ws, cblk, rblk, prob, *reinterpret_cast<BandLds<4, true>*>(&sh))) {
+      auto& sh16 = *reinterpret_cast<BandLds<4, true>*>(&sh);
+      if (d.nf % 128 == 0 ? band_r4(sl, ws, cblk, rblk, prob, sh16) : band_fold<2>(sl, ws, cblk, rblk, prob, sh16)) {
         __syncthreads();  // the fp16 pass's LDS reads are done
         band_unfolded<2, false>(sl, ws, cblk, rblk, prob, sh);
       }

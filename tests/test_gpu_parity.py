@@ -90,6 +90,26 @@ def test_score_parity_bf16_wide_values(orc, syn):
     _rel_close(ls_gpu, ls_orc)
 
 
+def test_score_parity_bf16_radix4_overflow(orc, syn):
+    """A 2048-token chunk (transform length divisible by 128: the radix-4 band
+    pass) whose four quarter-aligned tokens n, n + 512, n + 1024, n + 1536
+    carry 20480 in every channel, with signs (+, +, +, +) in V and (+, -, +, -)
+    in K: the four-term sums y0 (V) and y2 (K) reach 81920, past fp16's range,
+    while every value and every pair sum stays inside it, so the radix-4 tiles
+    are redone with the three bf16 twiddle planes."""
+    big = np.uint16(0x46A0)  # bf16 20480
+    def edit(host):
+        for kv, signs in ((1, (1, 1, 1, 1)), (0, (1, -1, 1, -1))):
+            for q, sg in enumerate(signs):
+                host[0][kv][0, 7 + 512 * q] = big if sg > 0 else big | np.uint16(0x8000)
+        for kv in (0, 1):
+            x = (host[0][kv].astype(np.uint32) << 16).view(np.float32)
+            assert np.abs(x).max() == 20480.0 and 2 * np.abs(x).max() < 65504
+    s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, [2048], 2, 2, 64, "bf16", (1, 16), edit=edit)
+    _rel_close(s_gpu, s_orc)
+    _rel_close(ls_gpu, ls_orc)
+
+
 def test_score_parity_fp32_single_chunk(orc, syn):
     """The 1 x 512-token fp32 workload: L=1, 8 KV heads x 64."""
     s_gpu, ls_gpu, s_orc, _ = _score_both(orc, syn, [512], 1, 8, 64, "f32", (1, 16))

@@ -12,7 +12,15 @@ set aside).
 The band projection's folded data: the fp32 sum or difference u of two bf16
 values splits exactly into hi = fp16(u) (to nearest even) and lo = fp16(u -
 hi), apart from a remainder below fp16's normal range (rounded by at most
-2^-25), with |lo| <= 2^-11 |u|; |u| >= 65520 gives an infinite hi."""
+2^-25), with |lo| <= 2^-11 |u|; |u| >= 65520 gives an infinite hi.
+
+The band projection's radix-4 form (transform lengths divisible by 128): bin
+j of an nf-point transform from the four quarter sums y0, y2, a, b over nf/4
+columns, with the tile mechanics the kernel uses (bins grouped by j mod 4, the
+b products of classes 1 and 3 reading the tile's rows swapped, half of them
+negated), checked against the transform's definition; and the fp16 hi + lo
+pair of a four-term fp32 sum within 2^-22 of the sum plus the fp32 rounding
+of its partial sums."""
 import numpy as np
 
 
@@ -75,3 +83,70 @@ def test_fold_split_is_exact():
         assert (np.abs(lo.astype(np.float64)) <= 2.0 ** -11 * np.abs(u.astype(np.float64))).all()
         # the split is not trivial: remainders of both signs occur in the normal range
         assert ((r > 0) & normal & (u > 0)).sum() > 1000 and ((r < 0) & normal & (u > 0)).sum() > 1000
+
+
+def _radix4_tiles(x, b0, kk):
+    """Cosine and sine sums of bins b0 .. b0 + 63 (< kk) as the radix-4 band
+    kernel forms them: four 32-row tiles, one per class k = j mod 4, rows
+    i < 16 the cosine rows of bins b0 + 4i + k and rows 16 + i their sine
+    rows, against the quarter sums over the first nf/4 columns."""
+    nf = x.size
+    M = nf // 4
+    xq = x.reshape(4, M)
+    terms = {"y0": (xq[0] + xq[2]) + (xq[1] + xq[3]), "y2": (xq[0] + xq[2]) - (xq[1] + xq[3]),
+             "a": xq[0] - xq[2], "b": xq[1] - xq[3]}
+    m = np.arange(M)
+    R, S = {}, {}
+    for k in range(4):
+        i = np.arange(32)
+        bins = b0 + 4 * (i & 15) + k
+        ang = 2 * np.pi * np.outer(bins, m) / nf
+        tile = np.where((i < 16)[:, None], np.cos(ang), np.sin(ang))
+        tile[bins >= kk] = 0.0
+        if k in (0, 2):
+            acc = tile @ terms["y0" if k == 0 else "y2"]
+        else:
+            neg = (i < 16) if k == 1 else (i >= 16)
+            swapped = tile[i ^ 16] * np.where(neg, -1.0, 1.0)[:, None]
+            acc = tile @ terms["a"] + swapped @ terms["b"]
+        for r in range(32):
+            if bins[r] < kk:
+                (R if r < 16 else S)[int(bins[r])] = acc[r]
+    return R, S
+
+
+def test_radix4_classes_give_the_dft():
+    rng = np.random.default_rng(21)
+    for nf, kk in ((256, 128), (512, 70), (128, 64)):
+        x = rng.standard_normal(nf)
+        n = np.arange(nf)
+        for b0 in range(0, kk, 64):
+            R, S = _radix4_tiles(x, b0, kk)
+            assert sorted(R) == sorted(S) == list(range(b0, min(b0 + 64, kk)))
+            for j in R:
+                ang = 2 * np.pi * j * n / nf
+                np.testing.assert_allclose(R[j], np.dot(np.cos(ang), x), atol=1e-9)
+                np.testing.assert_allclose(S[j], np.dot(np.sin(ang), x), atol=1e-9)
+
+
+def test_radix4_sum_split_bound():
+    rng = np.random.default_rng(23)
+    n = 400_000
+    e = rng.uniform(-24, 13, (4, n))
+    e = np.where(rng.random((4, n)) < 0.3, e[0] + rng.uniform(-1, 1, (4, n)), e)
+    x = _bf16(np.exp2(e) * rng.choice([-1.0, 1.0], (4, n)) * rng.uniform(1, 2, (4, n)) / 2)
+    exact = {"y0": (x[0].astype(np.float64) + x[2] + x[1] + x[3]),
+             "y2": (x[0].astype(np.float64) + x[2] - x[1] - x[3])}
+    s02, s13 = x[0] + x[2], x[1] + x[3]     # float32, as on the GPU
+    for name, s in (("y0", s02 + s13), ("y2", s02 - s13)):
+        with np.errstate(over="ignore"):
+            hi = s.astype(np.float16)
+        fin = np.abs(s) < 65520
+        assert np.isfinite(hi[fin]).all() and np.isinf(hi[~fin]).all()
+        r = s[fin] - hi[fin].astype(np.float32)  # exact in fp32
+        lo = r.astype(np.float16)
+        got = hi[fin].astype(np.float64) + lo.astype(np.float64)
+        want = exact[name][fin]
+        mag = np.abs(x[:, fin].astype(np.float64)).sum(axis=0)
+        bound = 2.0 ** -22 * np.abs(want) + 2.0 ** -23 * mag + 2.0 ** -25
+        assert (np.abs(got - want) <= bound).all()
