@@ -92,18 +92,24 @@ def test_score_parity_bf16_wide_values(orc, syn):
 
 def test_score_parity_bf16_radix4_overflow(orc, syn):
     """A 2048-token chunk (transform length divisible by 128: the radix-4 band
-    pass) whose four quarter-aligned tokens n, n + 512, n + 1024, n + 1536
-    carry 20480 in every channel, with signs (+, +, +, +) in V and (+, -, +, -)
-    in K: the four-term sums y0 (V) and y2 (K) reach 81920, past fp16's range,
-    while every value and every pair sum stays inside it, so the radix-4 tiles
-    are redone with the three bf16 twiddle planes."""
+    pass) whose layer 0 is scaled by 2^9 (exact; its largest value becomes
+    17024) and then carries 20480 in every channel at the four quarter-aligned
+    tokens n, n + 512, n + 1024, n + 1536, with signs (+, +, +, +) in V and
+    (+, -, +, -) in K: the four-term sums y0 (V) and y2 (K) reach 81920, past
+    fp16's range, while every value and every pair sum stays inside it, so
+    the radix-4 tiles of layer 0 are redone with the three bf16 twiddle
+    planes; layer 1 stays on the fp16 pairs.  (Unscaled, the planted values
+    would stand 10^4 standard deviations above the rest, and the scores of
+    that layer would then be conditioned far worse than fp32 arithmetic
+    resolves to 1e-4, on every band path alike.)"""
     big = np.uint16(0x46A0)  # bf16 20480
     def edit(host):
         for kv, signs in ((1, (1, 1, 1, 1)), (0, (1, -1, 1, -1))):
+            a = host[0][kv]
+            a[0] = _bf16_scaled(a[0], 2.0 ** 9)
             for q, sg in enumerate(signs):
-                host[0][kv][0, 7 + 512 * q] = big if sg > 0 else big | np.uint16(0x8000)
-        for kv in (0, 1):
-            x = (host[0][kv].astype(np.uint32) << 16).view(np.float32)
+                a[0, 7 + 512 * q] = big if sg > 0 else big | np.uint16(0x8000)
+            x = (a.astype(np.uint32) << 16).view(np.float32)
             assert np.abs(x).max() == 20480.0 and 2 * np.abs(x).max() < 65504
     s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, [2048], 2, 2, 64, "bf16", (1, 16), edit=edit)
     _rel_close(s_gpu, s_orc)
