@@ -259,22 +259,41 @@ class Workload:
         return float(sum(self.ns)) * self.L * 2 * self.H * self.D * esz  # one read of K and V
 
     def band_mfma_flops(self) -> float:
-        """Matrix-core flops the band projection issues per step, per (chunk,
-        layer, K|V).  bf16 data: the cosine and sine tiles of the retained bins
-        (32 rows each) x the folded token columns (ceil(N/2), padded to 32) x
-        the channels x 2, three fp16 products (a problem whose folded sums
-        leave fp16's range is redone unfolded with three bf16 planes).  fp32
-        data: the padded band rows x the padded tokens x the channels x 2, six
-        products."""
+        """Matrix-core flops the band projection issues per step, summed over
+        (chunk, layer, K|V), as the kernel dispatches its blocks.  bf16 data,
+        per 64 channels (one wave; 32 x 32 x 16 MFMAs): a launch whose chunks
+        keep at most 32 bins runs 32-bin blocks, each 8 MFMAs per 16 tokens
+        over the tokens padded to 32; otherwise 64-bin blocks, whose bins past
+        the first 32 take the radix-4 pass (36 MFMAs per 64 tokens) when the
+        transform length is a multiple of 128, else the folded pass (48 per 32
+        folded columns, ceil(N/2) padded to 32), and a block with at most 32
+        bins left runs as a 32-bin block.  (A problem whose fp16 pass meets a
+        value outside fp16's range is redone with three bf16 planes; not on
+        this data.)  fp32 data: the padded band rows x the padded tokens x the
+        channels x 2, six products."""
         flops = 0.0
+        kks = []
         for n in self.ns:
             nb = n // 2 + 1
-            kk = min(nb, max(1, (self.alpha[0] * nb) // self.alpha[1]))
-            C = self.H * self.D
+            kks.append(min(nb, max(1, (self.alpha[0] * nb) // self.alpha[1])))
+        nc = 1 if max(kks) <= 32 else 2
+        C = self.H * self.D
+        for n, kk in zip(self.ns, kks):
             if self.dtype == "bf16":
-                rows = 2 * 32 * (-(-kk // 32))
-                cols = 32 * (-(-((n + 1) // 2) // 32))
-                flops += self.L * 2 * rows * cols * C * 2 * 3
+                ntp = -(-n // 32) * 32
+                narrow = 8 * ntp // 16
+                mfmas = 0
+                if nc == 1:
+                    mfmas = narrow * -(-kk // 32)
+                else:
+                    for rb in range(-(-kk // 64)):
+                        if kk - 64 * rb <= 32:
+                            mfmas += narrow
+                        elif n % 128 == 0:
+                            mfmas += 36 * n // 64
+                        else:
+                            mfmas += 48 * -(-((n + 1) // 2) // 32)
+                flops += self.L * 2 * mfmas * (32 * 32 * 16 * 2) * (C // 64)
             else:
                 ppad = -(-2 * kk // 32) * 32
                 flops += self.L * 2 * ppad * (-(-n // 32) * 32) * C * 2 * 6

@@ -689,7 +689,7 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
 // rows i < 16 the cosine rows (R) of bins b0 + 4i + k, rows 16 + i their sine
 // rows (S).  The b products of classes 1 and 3 take the tile's rows swapped
 // (row i reads row i ^ 16), the sine half negated for class 1 and the cosine
-// half for class 3.  Each sum enters as an fp16 hi + lo pair (hi the nearest
+// half for class 3 (a signed copy of those rows is kept in LDS).  Each sum enters as an fp16 hi + lo pair (hi the nearest
 // fp16, lo the fp16 of the remainder: exact for a and b, the difference of two
 // bf16 values; the four-term y0 and y2 are rounded in fp32 and their remainder
 // can need more than fp16's 11 bits, which bounds the pair's error by 2^-22 of
@@ -706,6 +706,7 @@ __device__ __forceinline__ int band_r4_table_row(int r, int b0, int kk) {
 __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cblk, int rblk, int prob,
                                         BandLds<4, true>& sh) {
   constexpr int NPL = 2, TS = 24;  // twiddle planes; LDS row stride of a 16-column slab
+  static_assert((2 * 128 + 2 * 64) * TS <= 2 * 32 * 4 * kTwStride, "radix-4 slab exceeds an LDS buffer");
   uint16_t* lds0 = &sh.buf[0][0];
   uint16_t* lds1 = &sh.buf[1][0];
 
@@ -751,7 +752,7 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
   // load's offset is formed when it is issued instead of being kept in a
   // register of its own across the loop)
   auto load_x = [&](int j, uint32_t* dst) {
-    int base = xvoff + j * 16 * C * 2;
+    int base = j < nks ? xvoff + j * 16 * C * 2 : N * C * 2;  // past the last k-step: no reads
     asm volatile("" : "+v"(base));
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -769,29 +770,36 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
     twoff = trow >= 0 ? (int)((q * plane + (long long)trow * ntp + 8 * i) * 2) : (int)(NPL * plane * 2);
   }
   auto load_tw = [&](int j) {
-    twr = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tres, twoff + j * 32, 0, 0));
+    const int off = j < nks ? twoff + j * 32 : (int)(NPL * plane * 2);  // past the last k-step: no reads
+    twr = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
   };
+  // The slab in LDS: rows 0 .. 127 of each plane as read from the table, then
+  // 64 rows per plane for the b products of classes 1 and 3 (row 32 (k >> 1)
+  // + i holds tile row i ^ 16 of class k, negated where the b product
+  // subtracts it), written by the threads of those rows (whole waves).
   auto store_tw = [&](uint16_t* buf) {
     const int q = tid >> 8, r = (tid >> 1) & 127, i = tid & 1;
     *reinterpret_cast<u32x4_t*>(&buf[(q * 128 + r) * TS + 8 * i]) = twr;
+    if (r & 32) {
+      const int k = r >> 5, ii = r & 31;
+      const uint32_t sgn = (k == 1 ? ii >= 16 : ii < 16) ? 0x80008000u : 0u;
+      u32x4_t w = twr;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] ^= sgn;
+      *reinterpret_cast<u32x4_t*>(&buf[(256 + q * 64 + 32 * (k >> 1) + (ii ^ 16)) * TS + 8 * i]) = w;
+    }
   };
   auto prod3 = [&](f32x16_t& ac, const f16x8_t& a1, const f16x8_t& a2, const u32x4_t& hi, const u32x4_t& lo) {
     ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, hi), ac, 0, 0, 0);
     ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, __builtin_bit_cast(f16x8_t, hi), ac, 0, 0, 0);
     ac = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, lo), ac, 0, 0, 0);
   };
-  const uint32_t neg1 = col < 16 ? 0x80008000u : 0u, neg3 = col < 16 ? 0u : 0x80008000u;
-  auto frag_a = [&](const uint16_t* buf, int row, f16x8_t& a1, f16x8_t& a2, uint32_t neg) {
+  // twiddle fragments (hi and lo planes) of slab row `row`, planes `pstride`
+  // rows apart
+  auto frag_a = [&](const uint16_t* buf, int row, int pstride, f16x8_t& a1, f16x8_t& a2) {
     const uint16_t* ap = &buf[row * TS + 8 * g];
-    u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(ap);
-    u32x4_t w2 = *reinterpret_cast<const u32x4_t*>(ap + 128 * TS);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w1[i] ^= neg;
-      w2[i] ^= neg;
-    }
-    a1 = __builtin_bit_cast(f16x8_t, w1);
-    a2 = __builtin_bit_cast(f16x8_t, w2);
+    a1 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(ap));
+    a2 = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(ap + pstride * TS));
   };
   // the quarters' values of column pair (2h, 2h+1) in channel half m (bf16 ->
   // fp32 is exact): v[q][e] = x[q M + column 2h + e]
@@ -831,17 +839,17 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
         }
       }
       f16x8_t a1, a2;
-      frag_a(buf, col, a1, a2, 0u);
+      frag_a(buf, col, 128, a1, a2);
       prod3(acc[0][m], a1, a2, hi[0], lo[0]);
-      frag_a(buf, 64 + col, a1, a2, 0u);
+      frag_a(buf, 64 + col, 128, a1, a2);
       prod3(acc[2][m], a1, a2, hi[1], lo[1]);
-      frag_a(buf, 32 + col, a1, a2, 0u);
+      frag_a(buf, 32 + col, 128, a1, a2);
       prod3(acc[1][m], a1, a2, hi[2], lo[2]);
-      frag_a(buf, 96 + col, a1, a2, 0u);
+      frag_a(buf, 96 + col, 128, a1, a2);
       prod3(acc[3][m], a1, a2, hi[2], lo[2]);
-      frag_a(buf, 32 + (col ^ 16), a1, a2, neg1);
+      frag_a(buf, 256 + col, 64, a1, a2);
       prod3(acc[1][m], a1, a2, hi[3], lo[3]);
-      frag_a(buf, 96 + (col ^ 16), a1, a2, neg3);
+      frag_a(buf, 288 + col, 64, a1, a2);
       prod3(acc[3][m], a1, a2, hi[3], lo[3]);
       __builtin_amdgcn_sched_barrier(0);
     }
