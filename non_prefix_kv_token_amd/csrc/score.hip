@@ -751,15 +751,18 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
   // (the k-step's base offset passes through an empty asm, so that each
   // load's offset is formed when it is issued instead of being kept in a
   // register of its own across the loop)
-  auto load_x = [&](int j, uint32_t* dst) {
+  auto x_base = [&](int j) {
     int base = j < nks ? xvoff + j * 16 * C * 2 : N * C * 2;  // past the last k-step: no reads
     asm volatile("" : "+v"(base));
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        dst[8 * q + t] = __builtin_amdgcn_raw_buffer_load_b32(xres, base + q * qstep + t * C * 2, 0, 0);
+    return base;
   };
+  // loads u0 .. u1 - 1 of a k-step's 32 (quarter u / 8, column u % 8)
+  auto load_x_part = [&](int base, uint32_t* dst, int u0, int u1) {
+#pragma unroll
+    for (int u = u0; u < u1; ++u)
+      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(xres, base + (u >> 3) * qstep + (u & 7) * C * 2, 0, 0);
+  };
+  auto load_x = [&](int j, uint32_t* dst) { load_x_part(x_base(j), dst, 0, 32); };
   // twiddle slab of a k-step: 2 planes x 128 rows x 16 columns, one 16-byte
   // chunk per thread
   u32x4_t twr;
@@ -812,52 +815,62 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
         v[q][e] = __uint_as_float(m == 0 ? w << 16 : w & 0xffff0000u);
       }
   };
-  // one k-step, channel half by channel half: the four data terms split in
-  // one pass over the quarters' values, then the half's 18 products
-  auto compute = [&](const uint16_t* buf, const uint32_t* xs) {
+  // the four data terms of channel half m (y0, y2, a, b), split in one pass
+  // over the quarters' values
+  auto split = [&](const uint32_t* xs, int m, u32x4_t* hi, u32x4_t* lo) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      u32x4_t hi[4], lo[4];  // terms y0, y2, a, b
+    for (int h = 0; h < 4; ++h) {
+      float v[4][2];
+      quarters(xs, m, h, v);
+      float p[4][2];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float v[4][2];
-        quarters(xs, m, h, v);
-        float p[4][2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float s02 = v[0][e] + v[2][e], s13 = v[1][e] + v[3][e];
-          p[0][e] = s02 + s13;
-          p[1][e] = s02 - s13;
-          p[2][e] = v[0][e] - v[2][e];
-          p[3][e] = v[1][e] - v[3][e];
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint2 w = split_f16(p[t][0], p[t][1]);
-          hi[t][h] = w.x;
-          lo[t][h] = w.y;
-        }
+      for (int e = 0; e < 2; ++e) {
+        const float s02 = v[0][e] + v[2][e], s13 = v[1][e] + v[3][e];
+        p[0][e] = s02 + s13;
+        p[1][e] = s02 - s13;
+        p[2][e] = v[0][e] - v[2][e];
+        p[3][e] = v[1][e] - v[3][e];
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint2 w = split_f16(p[t][0], p[t][1]);
+        hi[t][h] = w.x;
+        lo[t][h] = w.y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // channel half m's 18 products in six groups (class 0 with y0, 2 with y2,
+  // 1 and 3 with a and with b); after each group, a sixth of the loads of
+  // X for k-step jn (nothing when dst is null)
+  auto products = [&](const uint16_t* buf, int m, const u32x4_t* hi, const u32x4_t* lo, int jn, uint32_t* dst) {
+    constexpr int row[6] = {0, 64, 32, 96, 256, 288}, ps[6] = {128, 128, 128, 128, 64, 64};
+    constexpr int cls[6] = {0, 2, 1, 3, 1, 3}, term[6] = {0, 1, 2, 2, 3, 3};
+    const int base = dst ? x_base(jn) : 0;
+#pragma unroll
+    for (int gi = 0; gi < 6; ++gi) {
       f16x8_t a1, a2;
-      frag_a(buf, col, 128, a1, a2);
-      prod3(acc[0][m], a1, a2, hi[0], lo[0]);
-      frag_a(buf, 64 + col, 128, a1, a2);
-      prod3(acc[2][m], a1, a2, hi[1], lo[1]);
-      frag_a(buf, 32 + col, 128, a1, a2);
-      prod3(acc[1][m], a1, a2, hi[2], lo[2]);
-      frag_a(buf, 96 + col, 128, a1, a2);
-      prod3(acc[3][m], a1, a2, hi[2], lo[2]);
-      frag_a(buf, 256 + col, 64, a1, a2);
-      prod3(acc[1][m], a1, a2, hi[3], lo[3]);
-      frag_a(buf, 288 + col, 64, a1, a2);
-      prod3(acc[3][m], a1, a2, hi[3], lo[3]);
+      frag_a(buf, row[gi] + col, ps[gi], a1, a2);
+      prod3(acc[cls[gi]][m], a1, a2, hi[term[gi]], lo[term[gi]]);
+      if (dst) load_x_part(base, dst, (32 * gi) / 6, (32 * (gi + 1)) / 6);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // one k-step on the slab in buf and the X in xs; the loads of X for k-step
+  // jn go into xs as its values are used up (during half 1's products), so
+  // the loads of a block's waves do not all reach the memory pipeline at once
+  auto compute = [&](const uint16_t* buf, uint32_t* xs, int jn) {
+    u32x4_t hi[4], lo[4];
+    split(xs, 0, hi, lo);
+    products(buf, 0, hi, lo, 0, nullptr);
+    split(xs, 1, hi, lo);
+    products(buf, 1, hi, lo, jn, xs);
+  };
 
-  // software pipeline as in the other passes: X two k-steps ahead, the
-  // twiddle slab one ahead through the other LDS buffer, one barrier per
-  // k-step, a straight-line body (loads past the end read zeros)
+  // software pipeline: X two k-steps ahead, the twiddle slab one ahead (each
+  // k-step writes the next one's slab to the other LDS buffer, last read
+  // before this k-step's barrier), one barrier per k-step, a straight-line
+  // body (loads past the end read nothing)
   load_tw(0);
   load_x(0, xa);
   store_tw(lds0);
@@ -867,17 +880,15 @@ __device__ __forceinline__ bool band_r4(const ScoreLaunch& sl, char* ws, int cbl
   load_x(1, xb);
   for (int j = 0; j < nks; j += 2) {
     __syncthreads();
-    compute(lds0, xa);
     store_tw(lds1);
     load_tw(j + 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_x(j + 2, xa);
+    compute(lds0, xa, j + 2);
     __syncthreads();
-    compute(lds1, xb);
     store_tw(lds0);
     load_tw(j + 3);
     __builtin_amdgcn_sched_barrier(0);
-    load_x(j + 3, xb);
+    compute(lds1, xb, j + 3);
   }
 
   bool bad = false;
