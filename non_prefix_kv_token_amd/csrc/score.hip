@@ -522,15 +522,18 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
   // X of a step: 2 k-steps x 8 columns x (2 channels in one dword), the
   // columns' own tokens (xf) and their mirrors (xm)
   uint32_t xfa[16], xma[16], xfb[16], xmb[16];
+  // columns t0 .. t1 - 1 of k-step s2 of a step
+  auto load_x_part = [&](int step, uint32_t* xf, uint32_t* xm, int s2, int t0, int t1) {
+#pragma unroll
+    for (int t = t0; t < t1; ++t) {
+      const int k = (step * 32 + 16 * s2 + t) * C * 2;
+      xf[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(fres, fvoff + k, 0, 0);
+      xm[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(mres, (int)min((uint32_t)(mvoff - k), mend), 0, 0);
+    }
+  };
   auto load_x = [&](int step, uint32_t* xf, uint32_t* xm) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int k = (step * 32 + 16 * s2 + t) * C * 2;
-        xf[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(fres, fvoff + k, 0, 0);
-        xm[8 * s2 + t] = __builtin_amdgcn_raw_buffer_load_b32(mres, (int)min((uint32_t)(mvoff - k), mend), 0, 0);
-      }
+    load_x_part(step, xf, xm, 0, 0, 8);
+    load_x_part(step, xf, xm, 1, 0, 8);
   };
   // twiddle slab of a step: NPL planes x 32*NTL rows x 32 columns (16-byte chunks)
   constexpr int TWN = NPL * 32 * NTL * 4;  // chunks per slab
@@ -573,7 +576,10 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
       acc[pt][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, __builtin_bit_cast(f16x8_t, lo[m]), acc[pt][m], 0, 0, 0);
     }
   };
-  auto compute = [&](const uint16_t* buf, const uint32_t* xf, const uint32_t* xm) {
+  // one step; the loads of X for step sn go into xf and xm as their values
+  // are used up (k-step s2's columns, during its products), so the loads of a
+  // block's waves do not all reach the memory pipeline at once
+  auto compute = [&](const uint16_t* buf, uint32_t* xf, uint32_t* xm, int sn) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       // B fragments: column pairs (2h, 2h+1) of channel half m, as the fp16
@@ -595,10 +601,14 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int pt = 0; pt < NC; ++pt) tile3(buf, pt, s2, uh, ul);
-#pragma unroll
-      for (int pt = 0; pt < NC; ++pt) tile3(buf, NC + pt, s2, vh, vl);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int pt = 0; pt < 2 * NC; ++pt) {
+        if (pt < NC)
+          tile3(buf, pt, s2, uh, ul);
+        else
+          tile3(buf, pt, s2, vh, vl);
+        load_x_part(sn, xf, xm, s2, (8 * pt) / (2 * NC), (8 * (pt + 1)) / (2 * NC));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -617,22 +627,21 @@ __device__ __forceinline__ bool band_fold(const ScoreLaunch& sl, char* ws, int c
   __builtin_amdgcn_sched_barrier(0);
   load_x(1, xfb, xmb);
   for (int step = 0; step < nsteps; step += 2) {
-    // even step: LDS buffer 0, registers xfa/xma
+    // even step: LDS buffer 0, registers xfa/xma.  The next step's slab goes
+    // to the other buffer first (its last reads came before the barrier),
+    // then the twiddle load of the step after, ahead of X
     __syncthreads();
-    compute(lds[0], xfa, xma);
     store_tw(lds[1]);
     load_tw(step + 2);
-    // the twiddles ahead of X: the next store waits only for them
     __builtin_amdgcn_sched_barrier(0);
-    load_x(step + 2, xfa, xma);
+    compute(lds[0], xfa, xma, step + 2);
     // odd step: LDS buffer 1, registers xfb/xmb (past the end when nsteps is
     // odd: zero operands leave the sums unchanged)
     __syncthreads();
-    compute(lds[1], xfb, xmb);
     store_tw(lds[0]);
     load_tw(step + 3);
     __builtin_amdgcn_sched_barrier(0);
-    load_x(step + 3, xfb, xmb);
+    compute(lds[1], xfb, xmb, step + 3);
   }
 
   // The range test costs nothing inside the loop: |u| >= 65520 becomes +-inf
