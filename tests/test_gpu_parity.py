@@ -56,7 +56,8 @@ def _rel_close(got, want, rtol=1e-4, floor=0.0):
     ([600, 4096], 1, 1, 64, (1, 32)),               # 1/32 cutoff, shortest/longest lengths
     ([2, 8192, 3], 1, 1, 64, (1, 16)),              # the smallest and largest chunk lengths
     ([64, 33], 1, 64, 128, (1, 16)),                # H*D = 8192, the most channels a call takes
-    ([1024, 700], 1, 64, 128, (1, 8)),              # the folded band pass at 8192 channels (64 and 43 bins)
+    ([1024, 700], 1, 64, 128, (1, 8)),              # radix-4 and folded band passes at 8192 channels (64 and 43 bins)
+    ([1152, 640, 384], 1, 2, 64, (1, 4)),           # radix-4 at lengths 9, 5 and 3 x 128: 144, 80 and 48 bins
 ])
 def test_score_parity_bf16(orc, syn, ns, L, H, D, alpha):
     s_gpu, ls_gpu, s_orc, ls_orc = _score_both(orc, syn, ns, L, H, D, "bf16", alpha)
@@ -126,8 +127,9 @@ def test_score_parity_fp32_single_chunk(orc, syn):
 @pytest.mark.parametrize("alpha", [(1, 16), (1, 8)])
 def test_score_parity_zeropad(orc, syn, mode, alpha):
     """Transform lengths padded to 512 and 1024; at alpha 1/8 the 700-token
-    chunk keeps 64 bins and takes the folded band pass, whose mirrored tokens
-    then lie partly past the chunk's end (zeros)."""
+    chunk keeps 64 bins and takes the radix-4 band pass (length 1024), whose
+    last quarter lies past the chunk's end (zeros).  Padded lengths are powers
+    of two, so every block with more than 32 bins takes the radix-4 pass."""
     s_gpu, _, s_orc, _ = _score_both(orc, syn, [300, 700], 2, 1, 64, "bf16", alpha, mode=mode)
     _rel_close(s_gpu, s_orc)
 
