@@ -124,12 +124,14 @@ def test_score_parity_fp32_single_chunk(orc, syn):
 
 
 @pytest.mark.parametrize("mode", [1])
-@pytest.mark.parametrize("alpha", [(1, 16), (1, 8)])
+@pytest.mark.parametrize("alpha", [(1, 16), (1, 8), (1, 2)])
 def test_score_parity_zeropad(orc, syn, mode, alpha):
     """Transform lengths padded to 512 and 1024; at alpha 1/8 the 700-token
     chunk keeps 64 bins and takes the radix-4 band pass (length 1024), whose
-    last quarter lies past the chunk's end (zeros).  Padded lengths are powers
-    of two, so every block with more than 32 bins takes the radix-4 pass."""
+    last quarter lies past the chunk's end (zeros); at alpha 1/2 both chunks
+    take it (128 and 256 bins), the 300-token one with its last quarter
+    (tokens 384 .. 511) entirely past the end.  Padded lengths are powers of
+    two, so every block with more than 32 bins takes the radix-4 pass."""
     s_gpu, _, s_orc, _ = _score_both(orc, syn, [300, 700], 2, 1, 64, "bf16", alpha, mode=mode)
     _rel_close(s_gpu, s_orc)
 
