@@ -179,8 +179,7 @@ __device__ void prep_q_rows(const AttnArgs& a, int row0, char* smem) {
         return (double)((t & 1) ? bf16_hi_to_f32(w[t >> 1]) : bf16_lo_to_f32(w[t >> 1]));
       };
       u32x4_t ya = {0u, 0u, 0u, 0u}, yb = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      auto rot = [&](int t, double& r0, double& r1) {
         const double2 c = scr[t];
         double x0, x1;
         if (half) {
@@ -190,7 +189,36 @@ __device__ void prep_q_rows(const AttnArgs& a, int row0, char* smem) {
           x0 = t < 4 ? el(xa[u], 2 * t) : el(xb[u], 2 * t - 8);
           x1 = t < 4 ? el(xa[u], 2 * t + 1) : el(xb[u], 2 * t - 7);
         }
-        const uint32_t y0 = bf16_from_f64(x0 * c.y - x1 * c.x), y1 = bf16_from_f64(x0 * c.x + x1 * c.y);
+        r0 = x0 * c.y - x1 * c.x;
+        r1 = x0 * c.x + x1 * c.y;
+      };
+      // Rounded to fp32 and then to bf16 (both to nearest even): the one
+      // rounding of the fp64 value unless the fp32 result lies exactly on a
+      // bf16 midpoint (fp32 holds every bf16 midpoint, so otherwise the two
+      // lie on the same side of each); a lane that meets one rounds its 16
+      // values once from the fp64 bits instead.
+      uint32_t f0[8], f1[8];
+      bool mid = false;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        double r0, r1;
+        rot(t, r0, r1);
+        f0[t] = __float_as_uint((float)r0);
+        f1[t] = __float_as_uint((float)r1);
+        mid |= ((f0[t] & 0xffffu) == 0x8000u) | ((f1[t] & 0xffffu) == 0x8000u);
+      }
+      if (__builtin_expect(mid, 0)) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          double r0, r1;
+          rot(t, r0, r1);
+          f0[t] = (uint32_t)bf16_from_f64(r0) << 16;  // a bf16 value: the rounding below keeps it
+          f1[t] = (uint32_t)bf16_from_f64(r1) << 16;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t y0 = bf16_bits_rne(__uint_as_float(f0[t])), y1 = bf16_bits_rne(__uint_as_float(f1[t]));
         if (half) {
           ya[t >> 1] |= y0 << (16 * (t & 1));
           yb[t >> 1] |= y1 << (16 * (t & 1));
